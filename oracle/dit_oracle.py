@@ -1,0 +1,420 @@
+"""fp64 CPU oracle of one packed diffusion-transformer block.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module.  It shares no code,
+constant table or helper with the HIP library.
+
+Every function is the plain definition, in float64, of one step of the block as
+the pages define it.  Matrix products use numpy's ``@`` as a library primitive;
+nothing is blocked, fused or reordered beyond what the definition states.
+
+Citation tags (web pages, cited by title and the item on the page):
+
+* [MMH3]   docs.rs source page of cortiq-engine 0.5.72, ``src/mmh3.rs``
+* [SIGLIP] docs.rs source page of ffai-argus 0.7.0, ``src/siglip.rs``
+* [ENC]    docs.rs source page of inferencelayer 0.2.1, ``src/encoder_cpu.rs``
+* [ZIMG]   ollama fork, ``x/imagegen/models/zimage/transformer.go``
+
+Pins (tests/test_oracle_pins.py) tie each function to something other than
+itself: printed test points, closed forms, library routines (numpy.interp,
+torch's scaled-dot-product attention, layer_norm and rms_norm in float64),
+invariants and pure-Python brute force on tiny inputs.  One result has no
+printed value to pin it: the whole block's output at the workloads' shapes
+(no golden forward is published on the pages).  It is pinned only through its
+pinned parts, brute force at tiny sizes and block-level invariants
+(permutation equivariance, zero-gate identity, RoPE translation invariance).
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+F64 = np.float64
+
+# ---------------------------------------------------------------------------
+# Flow-schedule remap ([MMH3] ``time_shift_sigma`` / ``time_shift_slope``)
+# ---------------------------------------------------------------------------
+
+
+def _to_base(sigma: float, shift: float) -> float:
+    """Point u of the shared base grid whose shifted sigma is ``sigma``.
+
+    A schedule with shift k maps u to k*u / (1 + (k-1)*u); this is its inverse,
+    u = sigma / (k - (k-1)*sigma)."""
+    return sigma / (shift - (shift - 1.0) * sigma)
+
+
+def _from_base(u: float, shift: float) -> float:
+    return shift * u / (1.0 + (shift - 1.0) * u)
+
+
+def sigma_remap(sigma: float, from_shift: float, to_shift: float) -> float:
+    """sigma on the ``to_shift`` schedule at the same base-grid point as
+    ``sigma`` on the ``from_shift`` schedule ([MMH3] ``time_shift_sigma``)."""
+    return _from_base(_to_base(sigma, from_shift), to_shift)
+
+
+def sigma_remap_slope(sigma: float, from_shift: float, to_shift: float) -> float:
+    """d sigma_to / d sigma_from by the chain rule through the base grid
+    ([MMH3] ``time_shift_slope``): d(from_base)/du at u times du/dsigma."""
+    u = _to_base(sigma, from_shift)
+    d_out_du = to_shift / (1.0 + (to_shift - 1.0) * u) ** 2
+    du_dsigma = from_shift / (from_shift - (from_shift - 1.0) * sigma) ** 2
+    return d_out_du * du_dsigma
+
+
+def resolve_sigmas(plan: Sequence[tuple]) -> List[float]:
+    """Slot sigmas from a workload's slot plan: ("value", v) or
+    ("remap", src_slot, from_shift, to_shift)."""
+    out: List[float] = []
+    for item in plan:
+        if item[0] == "value":
+            out.append(float(item[1]))
+        else:
+            _, src, a, b = item
+            out.append(sigma_remap(out[src], a, b))
+    return out
+
+
+def mmh3_timestep(sigma: float) -> float:
+    """Slot timestep t = 1 - max(sigma, 1e-6) ([MMH3] ``MiniMaxH3::forward``)."""
+    return 1.0 - max(sigma, 1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Rank-r adaLN ([MMH3] module docs and ``Adaln::eval``)
+# ---------------------------------------------------------------------------
+
+
+def adaln_coords(table: np.ndarray, t: float) -> np.ndarray:
+    """Curve coordinates at timestep t: linear interpolation of the [G, r]
+    table at p = clamp(t, 0, 1) * (G - 1), the last interval kept whole so
+    that t = 1 reads row G - 1 with weight 1 ([MMH3] ``Adaln::eval``).
+    The grid coordinate is kept in fp64."""
+    tab = np.asarray(table, dtype=F64)
+    G = tab.shape[0]
+    p = min(max(t, 0.0), 1.0) * (G - 1)
+    i0 = min(int(math.floor(p)), G - 2)
+    f = p - i0
+    return tab[i0] + f * (tab[i0 + 1] - tab[i0])
+
+
+def adaln_mods(basis: np.ndarray, bias: Optional[np.ndarray], table: np.ndarray,
+               ts: Sequence[float], tags: int, chunks: int, D: int) -> np.ndarray:
+    """Modulation rows [S*tags, chunks*D].
+
+    Element (r, e, d) of row r = s*tags + tag is flat index (r*chunks + e)*D + d
+    of the modulation buffer ([MMH3] ``Adaln::eval`` layout).  Flat element j
+    is bias[j] + sum_k basis[j, k] * c_s[k], evaluated at its own slot's
+    coordinates c_s = adaln_coords(table, ts[s]) (slot-major basis: rows
+    [s*tags*chunks*D, (s+1)*tags*chunks*D) belong to slot s)."""
+    B = np.asarray(basis, dtype=F64)
+    per_slot = tags * chunks * D
+    S = len(ts)
+    assert B.shape[0] == S * per_slot, "basis rows must cover every slot"
+    out = np.empty(S * per_slot, dtype=F64)
+    for s, t in enumerate(ts):
+        c = adaln_coords(table, t)
+        blk = slice(s * per_slot, (s + 1) * per_slot)
+        out[blk] = B[blk] @ c
+        if bias is not None:
+            out[blk] += np.asarray(bias, dtype=F64)[blk]
+    return out.reshape(S * tags, chunks * D)
+
+
+# ---------------------------------------------------------------------------
+# Norms and activations
+# ---------------------------------------------------------------------------
+
+
+def rms_norm(x: np.ndarray, g: Optional[np.ndarray], eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * g over the last axis ([MMH3]
+    ``rms_norm_into``; per head for qk-norm, [ENC] ``rms_norm_heads``)."""
+    x = np.asarray(x, dtype=F64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    y = x / np.sqrt(ms + eps)
+    return y if g is None else y * np.asarray(g, dtype=F64)
+
+
+def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float) -> np.ndarray:
+    """(x - mean) / sqrt(var + eps) * g + b, variance biased and taken in a
+    second pass over (x - mean) ([ENC] ``layer_norm_rows``)."""
+    x = np.asarray(x, dtype=F64)
+    mu = np.mean(x, axis=-1, keepdims=True)
+    var = np.mean((x - mu) ** 2, axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * np.asarray(g, F64) + np.asarray(b, F64)
+
+
+def modulate(xn: np.ndarray, shift: Optional[np.ndarray], scale: np.ndarray) -> np.ndarray:
+    """x * (1 + scale) + shift ([MMH3] ``modulate``; no shift in [ZIMG])."""
+    y = xn * (1.0 + scale)
+    return y if shift is None else y + shift
+
+
+def silu(v: np.ndarray) -> np.ndarray:
+    """v / (1 + e^-v) ([MMH3] ``silu``)."""
+    v = np.asarray(v, dtype=F64)
+    return v / (1.0 + np.exp(-v))
+
+
+def gelu_tanh(v: np.ndarray) -> np.ndarray:
+    """Tanh-form GELU, 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))
+    ([SIGLIP] ``GeluBiasOp``, the ``gelu_pytorch_tanh`` activation)."""
+    v = np.asarray(v, dtype=F64)
+    return 0.5 * v * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (v + 0.044715 * v ** 3)))
+
+
+# ---------------------------------------------------------------------------
+# 3-axis RoPE
+# ---------------------------------------------------------------------------
+
+
+def rope_angles(pos: np.ndarray, axes: Sequence[int], theta: float) -> np.ndarray:
+    """Rotation angles [n, P], P = sum(axes)/2.
+
+    Axis a (t, h, w in order) with d_a dims contributes d_a/2 angles
+    pos[a] * theta^(-2m/d_a), m < d_a/2, concatenated in axis order
+    ([MMH3] ``rope_angles``; per-axis frequencies as in [ZIMG]
+    ``prepareRoPE3D``)."""
+    pos = np.asarray(pos, dtype=F64)
+    parts = []
+    for a, d in enumerate(axes):
+        m = np.arange(d // 2, dtype=F64)
+        omega = float(theta) ** (-2.0 * m / d)
+        parts.append(pos[:, a:a + 1] * omega[None, :])
+    return np.concatenate(parts, axis=1)
+
+
+def rope_rotate(x: np.ndarray, ang: np.ndarray, mode: str) -> np.ndarray:
+    """Rotate pairs of the last axis by ``ang`` (broadcast over leading axes).
+
+    split_half: pair (j, j + P) ([MMH3] ``norm_rope_w``);
+    interleaved: pair (2j, 2j + 1) ([ZIMG] ``applyRoPE3D``).
+    Each pair (a, b) becomes (a cos - b sin, a sin + b cos)."""
+    x = np.array(x, dtype=F64, copy=True)
+    P = ang.shape[-1]
+    c, s = np.cos(ang), np.sin(ang)
+    if mode == "split_half":
+        a, b = x[..., :P].copy(), x[..., P:2 * P].copy()
+        x[..., :P] = a * c - b * s
+        x[..., P:2 * P] = a * s + b * c
+    elif mode == "interleaved":
+        a, b = x[..., 0:2 * P:2].copy(), x[..., 1:2 * P:2].copy()
+        x[..., 0:2 * P:2] = a * c - b * s
+        x[..., 1:2 * P:2] = a * s + b * c
+    else:
+        raise ValueError(mode)
+    return x
+
+
+# ---------------------------------------------------------------------------
+# Attention ([MMH3] ``attention`` host loop and ``softmax_inplace``)
+# ---------------------------------------------------------------------------
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Full bidirectional softmax attention per head, no mask.
+
+    q [H, m, hd], k and v [H, n, hd] -> [H, m, hd].  Scores are
+    scale * q.k; each row has its maximum subtracted before exp and is divided
+    by its sum."""
+    H = q.shape[0]
+    out = np.empty((H, q.shape[1], v.shape[2]), dtype=F64)
+    for h in range(H):
+        s = scale * (np.asarray(q[h], F64) @ np.asarray(k[h], F64).T)
+        s = s - s.max(axis=1, keepdims=True)
+        e = np.exp(s)
+        p = e / e.sum(axis=1, keepdims=True)
+        out[h] = p @ np.asarray(v[h], F64)
+    return out
+
+
+def _heads(y: np.ndarray, H: int, hd: int) -> np.ndarray:
+    """[m, H*hd] -> [H, m, hd] (head h is columns [h*hd, (h+1)*hd))."""
+    return np.ascontiguousarray(y.reshape(y.shape[0], H, hd).transpose(1, 0, 2))
+
+
+def _merge(o: np.ndarray) -> np.ndarray:
+    """[H, m, hd] -> [m, H*hd]."""
+    H, m, hd = o.shape
+    return np.ascontiguousarray(o.transpose(1, 0, 2).reshape(m, H * hd))
+
+
+def _lin(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray] = None) -> np.ndarray:
+    """x @ W^T (+ b), W stored [out, in]."""
+    y = np.asarray(x, F64) @ np.asarray(w, F64).T
+    return y if b is None else y + np.asarray(b, F64)
+
+
+def _sel(qrows: Optional[np.ndarray], n: int) -> np.ndarray:
+    return np.arange(n) if qrows is None else np.asarray(qrows, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# MiniMax-H3 block ([MMH3] ``block_forward``, ``ffn_tail``, ``residual``)
+# ---------------------------------------------------------------------------
+
+
+def mmh3_block(spec, x: np.ndarray, rows: np.ndarray, pos: Optional[np.ndarray],
+               sigmas: Sequence[float], w: Dict[str, np.ndarray],
+               qrows: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """One MiniMax-H3 block over the packed sequence.
+
+    Stages (fp64): mods [R, 6D]; xn [n, D]; q, k, v [H, *, hd] (q and k after
+    qk-norm and RoPE, q unscaled); o [m, D]; x1, xn2 [m, D]; a [m, F];
+    out [m, D], where m indexes ``qrows`` (all tokens if None).  K and V always
+    cover every token, because every query attends to all of them."""
+    D, H, hd, F = spec.D, spec.H, spec.hd, spec.F
+    n = x.shape[0]
+    x = np.asarray(x, F64)
+    rows = np.asarray(rows, dtype=np.int64)
+    R = spec.slots * spec.tags
+    if rows.size and (rows.min() < 0 or rows.max() >= R):
+        raise ValueError("modulation row out of range")
+    ts = [mmh3_timestep(s) for s in sigmas]
+    mods = adaln_mods(w["adaln_basis"], w.get("adaln_bias"), w["adaln_table"], ts,
+                      spec.tags, 6, D)
+    chunk = lambda r, e: mods[r, e * D:(e + 1) * D]  # noqa: E731
+
+    # pre-norm + modulate (chunks 0 shift, 1 scale)
+    xn = modulate(rms_norm(x, w["norm1"], spec.eps), chunk(rows, 0), chunk(rows, 1))
+    sel = _sel(qrows, n)
+
+    # QKV (no bias), head split; qk-norm then RoPE on q and k
+    wq, wk, wv = (w["w_qkv"][i * D:(i + 1) * D] for i in range(3))
+    k = rms_norm(_heads(_lin(xn, wk), H, hd), w["k_norm"], spec.qk_eps)
+    v = _heads(_lin(xn, wv), H, hd)
+    q = rms_norm(_heads(_lin(xn[sel], wq), H, hd), w["q_norm"], spec.qk_eps)
+    if spec.rope != "none":
+        ang = rope_angles(pos, spec.rope_axes, spec.rope_theta)
+        k = rope_rotate(k, ang[None], spec.rope)
+        q = rope_rotate(q, ang[sel][None], spec.rope)
+
+    o = _merge(attention(q, k, v, 1.0 / math.sqrt(hd)))
+    rs = rows[sel]
+    x1 = x[sel] + chunk(rs, 2) * _lin(o, w["w_out"])
+
+    # FFN half: chunks 3 shift, 4 scale, 5 gate; fc1 rows are [gate | up]
+    xn2 = modulate(rms_norm(x1, w["norm2"], spec.eps), chunk(rs, 3), chunk(rs, 4))
+    gu = _lin(xn2, w["w_fc1"])
+    a = silu(gu[:, :F]) * gu[:, F:]
+    out = x1 + chunk(rs, 5) * _lin(a, w["w_fc2"])
+    return dict(mods=mods, xn=xn, q=q, k=k, v=v, o=o, x1=x1, xn2=xn2, a=a, out=out)
+
+
+# ---------------------------------------------------------------------------
+# SigLIP encoder layer ([SIGLIP] ``Layer::forward``, ``finish_attention``)
+# ---------------------------------------------------------------------------
+
+
+def siglip_layer(spec, x: np.ndarray, w: Dict[str, np.ndarray],
+                 qrows: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Pre-LN encoder layer: LN1 -> qkv (+bias) -> attention (scores scaled by
+    hd^-1/2) -> out (+bias) + residual -> LN2 -> fc1 (+bias) -> GELU-tanh ->
+    fc2 (+bias) + residual.  Stages as in ``mmh3_block`` (no mods)."""
+    D, H, hd = spec.D, spec.H, spec.hd
+    n = x.shape[0]
+    x = np.asarray(x, F64)
+    sel = _sel(qrows, n)
+    xn = layer_norm(x, w["ln1_w"], w["ln1_b"], spec.eps)
+    wq, wk, wv = (w["w_qkv"][i * D:(i + 1) * D] for i in range(3))
+    bq, bk, bv = (w["b_qkv"][i * D:(i + 1) * D] for i in range(3))
+    k = _heads(_lin(xn, wk, bk), H, hd)
+    v = _heads(_lin(xn, wv, bv), H, hd)
+    q = _heads(_lin(xn[sel], wq, bq), H, hd)
+    o = _merge(attention(q, k, v, 1.0 / math.sqrt(hd)))
+    x1 = x[sel] + _lin(o, w["w_out"], w["b_out"])
+    xn2 = layer_norm(x1, w["ln2_w"], w["ln2_b"], spec.eps)
+    a = gelu_tanh(_lin(xn2, w["w_fc1"], w["b_fc1"]))
+    out = x1 + _lin(a, w["w_fc2"], w["b_fc2"])
+    return dict(xn=xn, q=q, k=k, v=v, o=o, x1=x1, xn2=xn2, a=a, out=out)
+
+
+# ---------------------------------------------------------------------------
+# Z-Image block ([ZIMG] ``TimestepEmbedder``, ``TransformerBlock.Forward``)
+# ---------------------------------------------------------------------------
+
+
+def timestep_embedding(t: float, dim: int) -> np.ndarray:
+    """[cos(t f_i) | sin(t f_i)], f_i = exp(-ln(10000) i / (dim/2)), i < dim/2
+    ([ZIMG] ``TimestepEmbedder.Forward``)."""
+    half = dim // 2
+    f = np.exp(-math.log(10000.0) * np.arange(half, dtype=F64) / half)
+    return np.concatenate([np.cos(t * f), np.sin(t * f)])
+
+
+def zimage_mods(spec, t: float, w: Dict[str, np.ndarray]) -> np.ndarray:
+    """[1, 4D] = adaLN(temb), temb = L2(silu(L1(sinusoid(t * t_scale)))); the
+    block's adaLN linear takes temb directly ([ZIMG] ``Forward`` and
+    ``TransformerBlock.Forward``).  Chunks: scale_msa, gate_msa, scale_mlp,
+    gate_mlp."""
+    e = timestep_embedding(t * spec.t_scale, spec.temb_freq)
+    h = silu(_lin(e[None], w["temb_w1"], w["temb_b1"]))
+    temb = _lin(h, w["temb_w2"], w["temb_b2"])
+    return _lin(temb, w["ada_w"], w["ada_b"])
+
+
+def zimage_block(spec, x: np.ndarray, pos: np.ndarray, t: float, w: Dict[str, np.ndarray],
+                 qrows: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Modulated Z-Image block: x1 = x + tanh(gate_msa) * RMSNorm(Attn(RMSNorm(x)
+    * (1 + scale_msa))); out = x1 + tanh(gate_mlp) * RMSNorm(W2(silu(W1 xf) *
+    W3 xf)) with xf = RMSNorm(x1) * (1 + scale_mlp).  Interleaved RoPE.
+    fc1 rows are [W1 (gate) | W3 (up)].  Extra stages: mods [1, 4D], y (out
+    projection before its norm), y2 (fc2 output before its norm)."""
+    D, H, hd, F = spec.D, spec.H, spec.hd, spec.F
+    n = x.shape[0]
+    x = np.asarray(x, F64)
+    sel = _sel(qrows, n)
+    mods = zimage_mods(spec, t, w)
+    sc_msa, g_msa, sc_mlp, g_mlp = (mods[0, i * D:(i + 1) * D] for i in range(4))
+    xn = modulate(rms_norm(x, w["norm1"], spec.eps), None, sc_msa)
+    wq, wk, wv = (w["w_qkv"][i * D:(i + 1) * D] for i in range(3))
+    ang = rope_angles(pos, spec.rope_axes, spec.rope_theta)
+    k = rope_rotate(rms_norm(_heads(_lin(xn, wk), H, hd), w["k_norm"], spec.qk_eps),
+                    ang[None], spec.rope)
+    v = _heads(_lin(xn, wv), H, hd)
+    q = rope_rotate(rms_norm(_heads(_lin(xn[sel], wq), H, hd), w["q_norm"], spec.qk_eps),
+                    ang[sel][None], spec.rope)
+    o = _merge(attention(q, k, v, 1.0 / math.sqrt(hd)))
+    y = _lin(o, w["w_out"])
+    x1 = x[sel] + np.tanh(g_msa) * rms_norm(y, w["post_attn_norm"], spec.eps)
+    xn2 = modulate(rms_norm(x1, w["norm2"], spec.eps), None, sc_mlp)
+    gu = _lin(xn2, w["w_fc1"])
+    a = silu(gu[:, :F]) * gu[:, F:]
+    y2 = _lin(a, w["w_fc2"])
+    out = x1 + np.tanh(g_mlp) * rms_norm(y2, w["post_ffn_norm"], spec.eps)
+    return dict(mods=mods, xn=xn, q=q, k=k, v=v, o=o, y=y, x1=x1, xn2=xn2, a=a, y2=y2,
+                out=out)
+
+
+def block(spec, x, rows, pos, sigmas, w, qrows=None) -> Dict[str, np.ndarray]:
+    """Dispatch on the block variant.  ``sigmas``: slot sigmas (mmh3) or
+    [t] (zimage); ignored for siglip."""
+    if spec.variant == "mmh3":
+        return mmh3_block(spec, x, rows, pos, sigmas, w, qrows)
+    if spec.variant == "siglip":
+        return siglip_layer(spec, x, w, qrows)
+    if spec.variant == "zimage":
+        return zimage_block(spec, x, pos, sigmas[0], w, qrows)
+    raise ValueError(spec.variant)
+
+
+def rel_rms(a: np.ndarray, ref: np.ndarray) -> float:
+    """||a - ref||_2 / ||ref||_2 (the parity metric)."""
+    a = np.asarray(a, F64)
+    ref = np.asarray(ref, F64)
+    den = float(np.sqrt(np.sum(ref * ref)))
+    num = float(np.sqrt(np.sum((a - ref) ** 2)))
+    return num / den if den > 0 else num
+
+
+__all__ = [
+    "sigma_remap", "sigma_remap_slope", "resolve_sigmas", "mmh3_timestep",
+    "adaln_coords", "adaln_mods", "rms_norm", "layer_norm", "modulate", "silu",
+    "gelu_tanh", "rope_angles", "rope_rotate", "attention", "mmh3_block",
+    "siglip_layer", "timestep_embedding", "zimage_mods", "zimage_block", "block",
+    "rel_rms",
+]

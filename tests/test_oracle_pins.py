@@ -1,0 +1,626 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test ties one oracle function to a printed test point, a closed form, an
+independent library routine, an invariant of the definition or a pure-Python
+brute force on tiny inputs.  No GPU is used.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from synth import workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- remap ----
+
+def test_remap_involution_printed_points():
+    g = gold("sigma_remap.json")
+    for s in g["involution_points"]:
+        a = O.sigma_remap(s, g["from_shift"], g["to_shift"])
+        back = O.sigma_remap(a, g["to_shift"], g["from_shift"])
+        assert abs(back - s) < g["involution_tol"]
+
+
+def test_remap_closed_form_12_to_3():
+    # Derived by hand: u = s/(12 - 11 s), 3u/(1 + 2u) = s / (4 - 3 s).
+    for s in np.linspace(0.0, 1.0, 101):
+        assert abs(O.sigma_remap(s, 12.0, 3.0) - s / (4.0 - 3.0 * s)) < 1e-14
+    assert abs(O.sigma_remap(0.972973, 12.0, 3.0) - 0.9000001) < 1e-7
+    assert O.sigma_remap(1.0, 12.0, 3.0) == 1.0
+    assert O.sigma_remap(0.0, 12.0, 3.0) == 0.0
+
+
+def test_remap_slope_finite_difference_printed_points():
+    g = gold("sigma_remap.json")
+    h = g["slope_step"]
+    for s in g["slope_points"]:
+        num = (O.sigma_remap(s + h, 12.0, 3.0) - O.sigma_remap(s - h, 12.0, 3.0)) / (2 * h)
+        assert abs(num - O.sigma_remap_slope(s, 12.0, 3.0)) < g["slope_tol"]
+        # closed form d/ds [s/(4-3s)] = 4/(4-3s)^2
+        assert abs(O.sigma_remap_slope(s, 12.0, 3.0) - 4.0 / (4.0 - 3.0 * s) ** 2) < 1e-12
+
+
+def test_timestep_of_sigma():
+    assert O.mmh3_timestep(0.3) == pytest.approx(0.7, abs=1e-15)
+    assert O.mmh3_timestep(0.0) == 1.0 - 1e-6
+    assert O.mmh3_timestep(-5.0) == 1.0 - 1e-6
+
+
+def test_resolve_sigmas_plan():
+    s = O.resolve_sigmas([("value", 0.5), ("remap", 0, 12.0, 3.0)])
+    assert s == [0.5, pytest.approx(0.2, abs=1e-15)]
+
+
+# ---------------------------------------------------------------- adaLN ----
+
+def test_adaln_lerp_special_points():
+    rng = np.random.default_rng(1)
+    tab = rng.standard_normal((1025, 24))
+    for k in (0, 1, 17, 512, 1023):
+        np.testing.assert_array_equal(O.adaln_coords(tab, k / 1024.0), tab[k])
+    # t >= 1 lands on the last row with weight 1 (f = 1 on the last interval)
+    np.testing.assert_allclose(O.adaln_coords(tab, 1.0), tab[1024], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(O.adaln_coords(tab, 1.7), tab[1024], rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(O.adaln_coords(tab, -0.3), tab[0])
+    k = 300
+    np.testing.assert_allclose(O.adaln_coords(tab, (k + 0.25) / 1024.0),
+                               0.75 * tab[k] + 0.25 * tab[k + 1], rtol=0, atol=1e-13)
+
+
+def test_adaln_coords_match_numpy_interp():
+    rng = np.random.default_rng(2)
+    tab = rng.standard_normal((1025, 24))
+    grid = np.arange(1025) / 1024.0
+    for t in rng.uniform(0, 1, 50):
+        want = np.array([np.interp(t, grid, tab[:, j]) for j in range(24)])
+        np.testing.assert_allclose(O.adaln_coords(tab, t), want, rtol=0, atol=1e-12)
+
+
+def test_adaln_rank_basis_equals_full_matrix_map():
+    """A full adaLN map W_full applied to an embedding that lies on the curve
+    spanned by A equals the rank-r basis map with basis W_full A."""
+    rng = np.random.default_rng(3)
+    D, r, S, T, E = 16, 24, 2, 3, 6
+    tab = rng.standard_normal((1025, r))
+    A = rng.standard_normal((D, r))
+    Wf = rng.standard_normal((S * T * E * D, D))
+    bias = rng.standard_normal(S * T * E * D)
+    ts = [0.123, 0.877]
+    got = O.adaln_mods(Wf @ A, bias, tab, ts, T, E, D)
+    grid = np.arange(1025) / 1024.0
+    per = T * E * D
+    for s, t in enumerate(ts):
+        c = np.array([np.interp(t, grid, tab[:, j]) for j in range(r)])
+        emb = A @ c  # the full map's input
+        want = Wf[s * per:(s + 1) * per] @ emb + bias[s * per:(s + 1) * per]
+        np.testing.assert_allclose(got[s * T:(s + 1) * T].ravel(), want, rtol=1e-12, atol=1e-10)
+
+
+def test_adaln_one_hot_basis_returns_coords_and_layout():
+    rng = np.random.default_rng(4)
+    D, r, T, E = 8, 24, 3, 6
+    tab = rng.standard_normal((1025, r))
+    basis = np.zeros((2 * T * E * D, r))
+    # row j picks coordinate j % r
+    basis[np.arange(basis.shape[0]), np.arange(basis.shape[0]) % r] = 1.0
+    ts = [0.25, 0.5]
+    m = O.adaln_mods(basis, None, tab, ts, T, E, D)
+    assert m.shape == (2 * T, E * D)
+    for s, t in enumerate(ts):
+        c = tab[int(t * 1024)]
+        for tag in range(T):
+            for e in range(E):
+                for d in range(D):
+                    j = ((s * T + tag) * E + e) * D + d
+                    assert m[s * T + tag, e * D + d] == c[j % r]
+
+
+# ---------------------------------------------------------- norms/acts ----
+
+def test_rms_norm_unit_gain_closed_form_and_torch():
+    import torch
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((7, 64)) * 3.0
+    eps = 1e-5
+    y = O.rms_norm(x, None, eps)
+    ms = np.mean(x * x, axis=1)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), np.sqrt(ms / (ms + eps)),
+                               rtol=1e-13)
+    g = 1.0 + 0.02 * rng.standard_normal(64)
+    want = torch.nn.functional.rms_norm(torch.from_numpy(x), (64,), torch.from_numpy(g), eps)
+    np.testing.assert_allclose(O.rms_norm(x, g, eps), want.numpy(), rtol=1e-13, atol=1e-13)
+    # scale invariance as eps -> 0
+    np.testing.assert_allclose(O.rms_norm(5.0 * x, g, 0.0), O.rms_norm(x, g, 0.0), rtol=1e-13)
+
+
+def test_layer_norm_matches_torch():
+    import torch
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((5, 96)) * 2.0 + 1.5
+    g = 1.0 + 0.02 * rng.standard_normal(96)
+    b = 0.02 * rng.standard_normal(96)
+    want = torch.nn.functional.layer_norm(torch.from_numpy(x), (96,), torch.from_numpy(g),
+                                          torch.from_numpy(b), 1e-6)
+    np.testing.assert_allclose(O.layer_norm(x, g, b, 1e-6), want.numpy(), rtol=1e-12, atol=1e-12)
+    y = O.layer_norm(x, np.ones(96), np.zeros(96), 0.0)
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-13)
+    np.testing.assert_allclose((y * y).mean(axis=1), 1.0, rtol=1e-12)
+
+
+def test_silu_against_expit():
+    from scipy.special import expit
+    v = np.linspace(-40, 40, 2001)
+    np.testing.assert_allclose(O.silu(v), v * expit(v), rtol=1e-13, atol=1e-300)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert abs(O.silu(np.array([50.0]))[0] - 50.0) < 1e-15 * 50 + 1e-18
+
+
+def test_gelu_landmarks_printed():
+    g = gold("gelu_landmarks.json")
+    y = O.gelu_tanh(np.array(g["xs"]))
+    assert abs(y[0]) < g["abs_at_minus_10_below"]
+    assert abs(y[3]) < g["abs_at_zero_below"]
+    assert abs(y[6] - 10.0) < g["abs_err_at_10_below"]
+    lo, hi = g["dip_range_at_minus_0_75"]
+    assert lo < y[2] < hi
+    assert y[1] < 0.0
+    tail = y[g["monotone_from_index"]:]
+    assert np.all(np.diff(tail) >= -g["monotone_slack"])
+
+
+def test_gelu_tanh_close_to_erf_gelu():
+    # The tanh form approximates x * Phi(x) to within a few 1e-4 everywhere.
+    v = np.linspace(-8, 8, 4001)
+    exact = np.array([0.5 * x * (1.0 + math.erf(x / math.sqrt(2.0))) for x in v])
+    assert np.max(np.abs(O.gelu_tanh(v) - exact)) < 1e-3
+
+
+def test_gelu_tanh_matches_torch():
+    import torch
+    v = np.linspace(-12, 12, 3001)
+    want = torch.nn.functional.gelu(torch.from_numpy(v), approximate="tanh").numpy()
+    np.testing.assert_allclose(O.gelu_tanh(v), want, rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------------------------ RoPE ----
+
+def test_rope_angles_axis_structure():
+    pos = np.array([[3.0, 5.0, 7.0]])
+    ang = O.rope_angles(pos, (32, 48, 48), 1e4)
+    assert ang.shape == (1, 64)
+    # the first frequency of every axis is 1: the angle is the coordinate
+    assert ang[0, 0] == 3.0 and ang[0, 16] == 5.0 and ang[0, 40] == 7.0
+    # the last frequency of axis a is theta^(-(d_a - 2)/d_a)
+    assert ang[0, 15] == pytest.approx(3.0 * 1e4 ** (-30.0 / 32.0), rel=1e-14)
+    assert ang[0, 39] == pytest.approx(5.0 * 1e4 ** (-46.0 / 48.0), rel=1e-14)
+    assert ang[0, 63] == pytest.approx(7.0 * 1e4 ** (-46.0 / 48.0), rel=1e-14)
+    # [ZIMG] frequencies exp(-ln(theta) i / half) are the same numbers
+    half = 24
+    f = np.exp(-math.log(256.0) * np.arange(half) / half)
+    np.testing.assert_allclose(O.rope_angles(np.array([[0.0, 1.0, 0.0]]), (32, 48, 48), 256.0)[0, 16:40],
+                               f, rtol=1e-14)
+
+
+def test_rope_split_half_is_complex_rotation():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((3, 5, 128))
+    ang = rng.uniform(-600, 600, (5, 64))
+    y = O.rope_rotate(x, ang[None], "split_half")
+    z = (x[..., :64] + 1j * x[..., 64:]) * np.exp(1j * ang)[None]
+    np.testing.assert_allclose(y[..., :64], z.real, atol=1e-12)
+    np.testing.assert_allclose(y[..., 64:], z.imag, atol=1e-12)
+    # norms preserved, zero angle is the identity
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    np.testing.assert_array_equal(O.rope_rotate(x, np.zeros((1, 5, 64)), "split_half"), x)
+
+
+def test_rope_interleaved_is_permuted_split_half():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((2, 4, 128))
+    ang = rng.uniform(-50, 50, (4, 64))
+    perm = np.concatenate([np.arange(0, 128, 2), np.arange(1, 128, 2)])  # interleaved -> split
+    inv = np.argsort(perm)
+    got = O.rope_rotate(x, ang[None], "interleaved")
+    via = O.rope_rotate(x[..., perm], ang[None], "split_half")[..., inv]
+    np.testing.assert_allclose(got, via, atol=1e-13)
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * ang)[None]
+    np.testing.assert_allclose(got[..., 0::2], z.real, atol=1e-12)
+
+
+# ------------------------------------------------------------- attention ----
+
+def _brute_attention(q, k, v, scale):
+    H, m, hd = q.shape
+    n = k.shape[1]
+    out = np.zeros((H, m, v.shape[2]))
+    for h in range(H):
+        for i in range(m):
+            s = [scale * sum(q[h, i, d] * k[h, j, d] for d in range(hd)) for j in range(n)]
+            mx = max(s)
+            e = [math.exp(si - mx) for si in s]
+            tot = sum(e)
+            for d in range(v.shape[2]):
+                out[h, i, d] = sum(e[j] * v[h, j, d] for j in range(n)) / tot
+    return out
+
+
+def test_attention_brute_force_tiny():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((2, 5, 8)) * 2
+    k = rng.standard_normal((2, 11, 8)) * 2
+    v = rng.standard_normal((2, 11, 8))
+    np.testing.assert_allclose(O.attention(q, k, v, 0.35), _brute_attention(q, k, v, 0.35),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_attention_matches_torch_sdpa():
+    import torch
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((3, 40, 64))
+    k = rng.standard_normal((3, 70, 64))
+    v = rng.standard_normal((3, 70, 64))
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=0.125).numpy()
+    np.testing.assert_allclose(O.attention(q, k, v, 0.125), want, rtol=1e-11, atol=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(11)
+    k = rng.standard_normal((2, 33, 16))
+    q = rng.standard_normal((2, 9, 16))
+    vconst = np.broadcast_to(rng.standard_normal((2, 1, 16)), (2, 33, 16)).copy()
+    np.testing.assert_allclose(O.attention(q, k, vconst, 1.0), np.broadcast_to(vconst[:, :1], (2, 9, 16)),
+                               rtol=1e-13)
+    v = rng.standard_normal((2, 33, 16))
+    np.testing.assert_allclose(O.attention(np.zeros_like(q), k, v, 1.0),
+                               np.broadcast_to(v.mean(axis=1, keepdims=True), (2, 9, 16)), rtol=1e-12)
+
+
+def test_attention_extreme_scores_finite():
+    g = gold("softmax_extremes.json")
+    lo, hi = g["extreme_score_range"]
+    rng = np.random.default_rng(12)
+    # one-dimensional heads so the score is q*k: choose q=1, k in [lo, hi]
+    k = rng.uniform(lo, hi, (1, 8, 1))
+    q = np.ones((1, 8, 1))
+    v = rng.standard_normal((1, 8, 4))
+    o = O.attention(q, k, v, 1.0)
+    assert np.all(np.isfinite(o))
+    np.testing.assert_allclose(o, _brute_attention(q, k, v, 1.0), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- layouts ----
+
+def test_layout_t2va_printed():
+    g = gold("layouts.json")
+    lay = W.build_layout(*g["t2va_args"])
+    assert lay.frame_rows == g["t2va_frame_rows"]
+    assert lay.seq_len == g["t2va_seq_len"]
+    assert [s[0] for s in lay.segments] == g["t2va_order"]
+    v = lay.segment("video")
+    t0 = lay.pos[v[1], 0]
+    t1 = lay.pos[v[1] + lay.frame_rows, 0]
+    assert abs(t1 - t0 - g["video_t_first_step"]) < 1e-12
+
+
+def test_layout_keyframes_printed():
+    g = gold("layouts.json")
+    tl, lt, lh, lw, at = g["t2va_args"]
+    base = W.build_layout(tl, lt, lh, lw, at)
+    lay = W.build_layout(tl, lt, lh, lw, at, keyframes=[tuple(k) for k in g["keyframes"]])
+    assert lay.cond_rows() == 2 * lay.frame_rows
+    assert lay.seq_len == base.seq_len + 2 * lay.frame_rows
+    assert [s[0] for s in lay.segments] == g["keyframe_order"]
+    a0, v0 = lay.segment("audio"), lay.segment("video")
+    assert lay.pos[a0[1], 0] == base.pos[base.segment("audio")[1], 0]
+    assert lay.pos[v0[1], 0] == base.pos[base.segment("video")[1], 0]
+    conds = [s for s in lay.segments if s[0] == "cond"]
+    assert lay.pos[conds[0][1], 0] == tl
+    spans = sum(5.0 / 3.0 * (1.0, 4.0, 4.0, 4.0, 4.0)[k % 5] for k in range(lt))
+    assert abs(lay.pos[conds[1][1], 0] - (tl + spans - 5.0 / 3.0)) < 1e-12
+    assert lay.pos[conds[0][1], 1] == lay.pos[v0[1], 1]
+
+
+def test_workload_shapes():
+    for spec in W.SPECS:
+        pos, rows = W.layout_for(spec)
+        if pos is not None:
+            assert pos.shape == (spec.n, 3)
+        if rows is not None:
+            assert rows.shape == (spec.n,)
+            assert rows.min() >= 0 and rows.max() < spec.mod_rows
+    pos, rows = W.layout_for(W.spec_by_name("t2va"))
+    assert sorted(set(rows.tolist())) == [0, 1, 5]
+    # video t spans [512, 512 + 5/3 * 51]; audio frames sit at 512 + i
+    vid = rows == 0
+    assert pos[vid, 0].min() == 512.0 and pos[vid, 0].max() == pytest.approx(597.0)
+    assert pos[rows == 5, 0].max() == 767.0
+    pos, rows = W.layout_for(W.spec_by_name("edit"))
+    assert sorted(set(rows.tolist())) == [0, 1]
+
+
+# ---------------------------------------------------------- whole block ----
+
+def _tiny_mmh3_spec(n=7):
+    return W.BlockSpec("tiny", "mmh3", "f32", n=n, D=16, H=2, hd=8, F=12, slots=2, rank=3,
+                       grid=9, rope="split_half", rope_axes=(2, 2, 4), rope_theta=100.0)
+
+
+def _brute_mmh3(spec, x, rows, pos, sigmas, w):
+    """Scalar loops, written independently of the oracle's array code."""
+    D, H, hd, F = spec.D, spec.H, spec.hd, spec.F
+    n = len(x)
+    T, E = spec.tags, 6
+    G = spec.grid
+    mods = {}
+    for s, sg in enumerate(sigmas):
+        t = 1.0 - max(sg, 1e-6)
+        p = min(max(t, 0.0), 1.0) * (G - 1)
+        i0 = min(int(math.floor(p)), G - 2)
+        f = p - i0
+        c = [w["adaln_table"][i0][k] * (1 - f) + w["adaln_table"][i0 + 1][k] * f
+             for k in range(spec.rank)]
+        for tag in range(T):
+            for e in range(E):
+                for d in range(D):
+                    j = ((s * T + tag) * E + e) * D + d
+                    mods[(s * T + tag, e, d)] = w["adaln_bias"][j] + sum(
+                        w["adaln_basis"][j][k] * c[k] for k in range(spec.rank))
+
+    def rms(vec, g, eps):
+        ms = sum(v * v for v in vec) / len(vec)
+        inv = 1.0 / math.sqrt(ms + eps)
+        return [vec[i] * inv * g[i] for i in range(len(vec))]
+
+    def mv(W_, vec, r0, r1):
+        return [sum(W_[r][c] * vec[c] for c in range(len(vec))) for r in range(r0, r1)]
+
+    freqs = []
+    for a, d in enumerate(spec.rope_axes):
+        for m in range(d // 2):
+            freqs.append((a, spec.rope_theta ** (-2.0 * m / d)))
+    P = len(freqs)
+
+    def rope(vec, i):
+        out = list(vec)
+        for j, (a, om) in enumerate(freqs):
+            ang = pos[i][a] * om
+            c, s_ = math.cos(ang), math.sin(ang)
+            out[j] = vec[j] * c - vec[j + P] * s_
+            out[j + P] = vec[j] * s_ + vec[j + P] * c
+        return out
+
+    xn = []
+    for i in range(n):
+        r = rows[i]
+        z = rms(list(x[i]), w["norm1"], spec.eps)
+        xn.append([z[d] * (1 + mods[(r, 1, d)]) + mods[(r, 0, d)] for d in range(D)])
+    Q, K, V = [], [], []
+    for i in range(n):
+        qkv = mv(w["w_qkv"], xn[i], 0, 3 * D)
+        Q.append([rope(rms(qkv[h * hd:(h + 1) * hd], w["q_norm"], spec.qk_eps), i) for h in range(H)])
+        K.append([rope(rms(qkv[D + h * hd:D + (h + 1) * hd], w["k_norm"], spec.qk_eps), i) for h in range(H)])
+        V.append([qkv[2 * D + h * hd:2 * D + (h + 1) * hd] for h in range(H)])
+    out = np.zeros((n, D))
+    for i in range(n):
+        r = rows[i]
+        o = []
+        for h in range(H):
+            s = [sum(Q[i][h][d] * K[j][h][d] for d in range(hd)) / math.sqrt(hd) for j in range(n)]
+            mx = max(s)
+            e = [math.exp(v - mx) for v in s]
+            tot = sum(e)
+            o += [sum(e[j] * V[j][h][d] for j in range(n)) / tot for d in range(hd)]
+        proj = mv(w["w_out"], o, 0, D)
+        x1 = [x[i][d] + mods[(r, 2, d)] * proj[d] for d in range(D)]
+        z = rms(x1, w["norm2"], spec.eps)
+        h2 = [z[d] * (1 + mods[(r, 4, d)]) + mods[(r, 3, d)] for d in range(D)]
+        gu = mv(w["w_fc1"], h2, 0, 2 * F)
+        act = [gu[f] / (1 + math.exp(-gu[f])) * gu[F + f] for f in range(F)]
+        y = mv(w["w_fc2"], act, 0, D)
+        out[i] = [x1[d] + mods[(r, 5, d)] * y[d] for d in range(D)]
+    return out
+
+
+def _tiny_mmh3_inputs(seed=13, n=7):
+    spec = _tiny_mmh3_spec(n)
+    wl = W.make_custom_workload(spec, seed, sigmas=[0.37, 0.81])
+    w = {k: v.astype(np.float64) for k, v in wl.weights.items()}
+    # make the modulation visible: larger basis, table of unit scale
+    w["adaln_basis"] = w["adaln_basis"] * 10.0
+    for k in ("w_qkv", "w_out", "w_fc1", "w_fc2"):
+        w[k] = w[k] * 10.0
+    return spec, wl.x.astype(np.float64), wl.rows, wl.pos.astype(np.float64), [0.37, 0.81], w
+
+
+def test_mmh3_block_brute_force_tiny():
+    spec, x, rows, pos, sig, w = _tiny_mmh3_inputs()
+    got = O.mmh3_block(spec, x, rows, pos, sig, w)["out"]
+    want = _brute_mmh3(spec, x, rows, pos, sig, w)
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-11)
+    # the sampled-row form returns the same rows
+    sel = np.array([5, 0, 3])
+    np.testing.assert_allclose(O.mmh3_block(spec, x, rows, pos, sig, w, qrows=sel)["out"],
+                               got[sel], rtol=1e-12, atol=1e-12)
+
+
+def test_mmh3_block_permutation_equivariant():
+    spec, x, rows, pos, sig, w = _tiny_mmh3_inputs(14, n=9)
+    perm = np.random.default_rng(0).permutation(9)
+    a = O.mmh3_block(spec, x, rows, pos, sig, w)["out"]
+    b = O.mmh3_block(spec, x[perm], rows[perm], pos[perm], sig, w)["out"]
+    np.testing.assert_allclose(b, a[perm], rtol=1e-12, atol=1e-12)
+
+
+def test_mmh3_block_rope_translation_invariant():
+    spec, x, rows, pos, sig, w = _tiny_mmh3_inputs(15, n=9)
+    a = O.mmh3_block(spec, x, rows, pos, sig, w)
+    b = O.mmh3_block(spec, x, rows, pos + np.array([3.0, -7.5, 11.25]), sig, w)
+    np.testing.assert_allclose(b["o"], a["o"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(b["out"], a["out"], rtol=1e-11, atol=1e-12)
+
+
+def test_mmh3_block_zero_gates_identity():
+    spec, x, rows, pos, sig, w = _tiny_mmh3_inputs(16)
+    D, T, E = spec.D, spec.tags, 6
+    basis, bias = w["adaln_basis"].copy(), w["adaln_bias"].copy()
+    for r in range(spec.slots * T):
+        for e in (2, 5):
+            sl = slice((r * E + e) * D, (r * E + e + 1) * D)
+            basis[sl] = 0.0
+            bias[sl] = 0.0
+    w2 = dict(w, adaln_basis=basis, adaln_bias=bias)
+    out = O.mmh3_block(spec, x, rows, pos, sig, w2)["out"]
+    np.testing.assert_array_equal(out, x)
+
+
+def test_mmh3_block_scale_minus_one_kills_attention_branch():
+    spec, x, rows, pos, sig, w = _tiny_mmh3_inputs(17)
+    D, T, E = spec.D, spec.tags, 6
+    basis, bias = w["adaln_basis"].copy(), w["adaln_bias"].copy()
+    for r in range(spec.slots * T):
+        for e, val in ((0, 0.0), (1, -1.0)):
+            sl = slice((r * E + e) * D, (r * E + e + 1) * D)
+            basis[sl] = 0.0
+            bias[sl] = val
+    st = O.mmh3_block(spec, x, rows, pos, sig, dict(w, adaln_basis=basis, adaln_bias=bias))
+    np.testing.assert_array_equal(st["xn"], 0.0)
+    np.testing.assert_array_equal(st["x1"], x)
+
+
+def test_mmh3_equal_rows_modulated_identically():
+    spec, x, rows, pos, sig, w = _tiny_mmh3_inputs(18, n=6)
+    x = np.repeat(x[:1], 6, axis=0)
+    rows = np.array([1, 1, 4, 4, 1, 4], dtype=np.int32)
+    st = O.mmh3_block(spec, x, rows, pos, sig, w)
+    np.testing.assert_array_equal(st["xn"][0], st["xn"][1])
+    np.testing.assert_array_equal(st["xn"][2], st["xn"][3])
+    assert not np.array_equal(st["xn"][0], st["xn"][2])
+
+
+def test_mmh3_rejects_out_of_range_rows():
+    spec, x, rows, pos, sig, w = _tiny_mmh3_inputs(19)
+    rows = rows.copy()
+    rows[2] = 6
+    with pytest.raises(ValueError):
+        O.mmh3_block(spec, x, rows, pos, sig, w)
+
+
+def test_qk_norm_unit_rms_in_block():
+    spec, x, rows, pos, sig, w = _tiny_mmh3_inputs(20)
+    w = dict(w, q_norm=np.ones(spec.hd), k_norm=np.ones(spec.hd))
+    st = O.mmh3_block(spec, x, rows, pos, sig, w)
+    # RoPE preserves norms, so q and k keep the RMS sqrt(ms / (ms + eps)) ~ 1
+    rq = np.sqrt(np.mean(st["q"] ** 2, axis=-1))
+    assert np.all(np.abs(rq - 1.0) < 1e-3)
+
+
+def test_siglip_layer_matches_torch_composition():
+    import torch
+    import torch.nn.functional as Fn
+    spec = W.BlockSpec("tiny_siglip", "siglip", "f32", n=20, D=32, H=4, hd=8, F=48, eps=1e-6)
+    wl = W.make_custom_workload(spec, 21)
+    w = {k: torch.from_numpy(v.astype(np.float64)) for k, v in wl.weights.items()}
+    x = torch.from_numpy(wl.x.astype(np.float64))
+    D, H, hd = spec.D, spec.H, spec.hd
+    xn = Fn.layer_norm(x, (D,), w["ln1_w"], w["ln1_b"], 1e-6)
+    qkv = Fn.linear(xn, w["w_qkv"], w["b_qkv"])
+    q, k, v = (qkv[:, i * D:(i + 1) * D].reshape(-1, H, hd).transpose(0, 1) for i in range(3))
+    o = Fn.scaled_dot_product_attention(q, k, v).transpose(0, 1).reshape(-1, D)
+    x1 = x + Fn.linear(o, w["w_out"], w["b_out"])
+    h = Fn.gelu(Fn.linear(Fn.layer_norm(x1, (D,), w["ln2_w"], w["ln2_b"], 1e-6), w["w_fc1"], w["b_fc1"]),
+                approximate="tanh")
+    want = x1 + Fn.linear(h, w["w_fc2"], w["b_fc2"])
+    got = O.siglip_layer(spec, wl.x, {k: v.numpy() for k, v in w.items()})["out"]
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_timestep_embedding_closed_forms():
+    e = O.timestep_embedding(0.0, 256)
+    np.testing.assert_array_equal(e[:128], 1.0)
+    np.testing.assert_array_equal(e[128:], 0.0)
+    e = O.timestep_embedding(0.7, 256)
+    assert e[0] == pytest.approx(math.cos(0.7)) and e[128] == pytest.approx(math.sin(0.7))
+    # the last frequency is 10000^(-127/128)
+    assert e[255] == pytest.approx(math.sin(0.7 * 10000.0 ** (-127.0 / 128.0)), rel=1e-13)
+
+
+def _tiny_zimage():
+    spec = W.BlockSpec("tiny_z", "zimage", "f32", n=10, D=16, H=2, hd=8, F=12,
+                       rope="interleaved", rope_axes=(2, 2, 4), rope_theta=256.0,
+                       temb_freq=16, temb_hidden=24)
+    wl = W.make_custom_workload(spec, 22)
+    w = {k: v.astype(np.float64) for k, v in wl.weights.items()}
+    return spec, wl.x.astype(np.float64), wl.pos.astype(np.float64), w
+
+
+def test_zimage_zero_gates_identity():
+    spec, x, pos, w = _tiny_zimage()
+    D = spec.D
+    aw, ab = w["ada_w"].copy(), w["ada_b"].copy()
+    for c in (1, 3):  # gate_msa, gate_mlp -> tanh(0) = 0
+        aw[c * D:(c + 1) * D] = 0.0
+        ab[c * D:(c + 1) * D] = 0.0
+    out = O.zimage_block(spec, x, pos, 0.4, dict(w, ada_w=aw, ada_b=ab))["out"]
+    np.testing.assert_array_equal(out, x)
+
+
+def test_zimage_block_matches_torch_composition():
+    import torch
+    import torch.nn.functional as Fn
+    spec, x, pos, w = _tiny_zimage()
+    D, H, hd, F = spec.D, spec.H, spec.hd, spec.F
+    tw = {k: torch.from_numpy(v) for k, v in w.items()}
+    t = 0.3
+    half = spec.temb_freq // 2
+    f = torch.exp(-math.log(10000.0) * torch.arange(half, dtype=torch.float64) / half)
+    arg = t * spec.t_scale * f
+    emb = torch.cat([torch.cos(arg), torch.sin(arg)])
+    temb = Fn.linear(Fn.silu(Fn.linear(emb, tw["temb_w1"], tw["temb_b1"])), tw["temb_w2"], tw["temb_b2"])
+    m = Fn.linear(temb, tw["ada_w"], tw["ada_b"])
+    sc1, g1, sc2, g2 = (m[i * D:(i + 1) * D] for i in range(4))
+    xt = torch.from_numpy(x)
+    xn = Fn.rms_norm(xt, (D,), tw["norm1"], 1e-5) * (1 + sc1)
+    qkv = Fn.linear(xn, tw["w_qkv"])
+    q, k, v = (qkv[:, i * D:(i + 1) * D].reshape(-1, H, hd) for i in range(3))
+    q = Fn.rms_norm(q, (hd,), tw["q_norm"], 1e-5)
+    k = Fn.rms_norm(k, (hd,), tw["k_norm"], 1e-5)
+    # interleaved rotation through complex multiplication
+    ang = []
+    for a, d in enumerate(spec.rope_axes):
+        om = spec.rope_theta ** (-torch.arange(d // 2, dtype=torch.float64) * 2.0 / d)
+        ang.append(torch.from_numpy(pos[:, a:a + 1]) * om[None])
+    ang = torch.cat(ang, dim=1)[:, None, :]
+    rot = torch.polar(torch.ones_like(ang), ang)
+
+    def rope(z):
+        c = torch.view_as_complex(z.reshape(*z.shape[:-1], hd // 2, 2).contiguous()) * rot
+        return torch.view_as_real(c).reshape(z.shape)
+
+    q, k = rope(q), rope(k)
+    o = Fn.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1))
+    o = o.transpose(0, 1).reshape(-1, D)
+    x1 = xt + torch.tanh(g1) * Fn.rms_norm(Fn.linear(o, tw["w_out"]), (D,), tw["post_attn_norm"], 1e-5)
+    xf = Fn.rms_norm(x1, (D,), tw["norm2"], 1e-5) * (1 + sc2)
+    gu = Fn.linear(xf, tw["w_fc1"])
+    y2 = Fn.linear(Fn.silu(gu[:, :F]) * gu[:, F:], tw["w_fc2"])
+    want = x1 + torch.tanh(g2) * Fn.rms_norm(y2, (D,), tw["post_ffn_norm"], 1e-5)
+    got = O.zimage_block(spec, x, pos, t, w)["out"]
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_rel_rms():
+    assert O.rel_rms(np.array([1.0, 2.0]), np.array([1.0, 2.0])) == 0.0
+    assert O.rel_rms(np.array([2.0, 0.0]), np.array([1.0, 0.0])) == 1.0

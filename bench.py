@@ -1,0 +1,166 @@
+"""Benchmark of one packed DiT block forward on one MI355X.
+
+A step is one dit_block_forward call (adaLN, pre-norms, QKV, qk-norm/RoPE,
+attention, out projection, SwiGLU FFN) over the text-to-audio+video packing:
+512 text + 512 audio + 24576 video tokens, D=2688, 21 heads x 128, SwiGLU
+10752, two timestep slots.  Inputs are seeded synthetic tensors already resident
+in HBM.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "packed DiT block tokens/s + attention TFLOP/s (% MFMA peak), 25.6k tokens"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(spec, wl):
+    """The fp64 oracle on the same workload, on the host cores: two bounded
+    samples of query rows (K/V for all tokens are always computed), timed and
+    extrapolated linearly to the whole block."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    sig = O.resolve_sigmas(wl.slot_plan)
+    times = {}
+    for m in (8, 40):
+        rows = np.linspace(0, spec.n - 1, m).astype(np.int64)
+        t0 = time.perf_counter()
+        O.block(spec, wl.x, wl.rows, wl.pos, sig, wl.weights, qrows=rows)
+        times[m] = time.perf_counter() - t0
+        log(f"cpu oracle: {m} query rows in {times[m]:.2f} s")
+    per_row = max((times[40] - times[8]) / 32.0, 1e-9)
+    fixed = max(times[8] - 8 * per_row, 0.0)
+    full = fixed + per_row * spec.n
+    return {"value": spec.n / full, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"fp64 numpy oracle of the full {spec.n}-token block evaluated at 8 and 40 "
+                       f"query rows ({times[8]:.1f} s, {times[40]:.1f} s; K/V of all tokens in both); "
+                       f"block time extrapolated linearly in query rows to {full:.0f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="t2va")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the block is "
+              "measured at its single-GPU shape", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from packed_sequence_diffusion_amd import dit
+    from synth import workloads as W
+    from synth.device import to_device
+
+    spec = W.spec_by_name(args.workload)
+    t0 = time.perf_counter()
+    wl = W.make_workload(spec)
+    dev = to_device(wl)
+    cfg = dit.make_config(spec)
+    blk = dit.Block(cfg, dev.weights)
+    sig = dit.resolve_sigmas(wl.slot_plan)
+    out = torch.empty_like(dev.x)
+    ws = blk.workspace(spec.n)
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t0:.1f} s; workspace {ws.numel() / 2**30:.2f} GiB")
+
+    for _ in range(args.warmup):
+        blk.forward(dev.x, dev.rows, dev.pos, sig, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    dit.profile_begin(args.steps)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        blk.forward(dev.x, dev.rows, dev.pos, sig, out=out, workspace=ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    phases = dit.profile_end()
+    total_ms = ev0.elapsed_time(ev1)
+    ms = total_ms / args.steps
+    calls = phases.pop("calls")
+    ph = {k: v / calls for k, v in phases.items()}
+    log("phases (ms/step): " + ", ".join(f"{k}={v:.3f}" for k, v in ph.items()))
+
+    attn_flops = spec.attn_flops()
+    gemm_flops = spec.gemm_flops()
+    attn_ms = ph["attention"]
+    gemm_ms = ph["qkv_gemm"] + ph["out_gemm"] + ph["fc1_gemm"] + ph["fc2_gemm"]
+    attn_tf = attn_flops / (attn_ms * 1e-3) / 1e12
+    gemm_tf = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    # bandwidth-bound pre-norm: read x fp32, write xn bf16 per element
+    norm_bytes = spec.n * spec.D * (4 + 2)
+    norm_gbs = norm_bytes / (ph["norm1"] * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": spec.n / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded normal inputs and weights; no checkpoint)",
+        "config": {
+            "workload": (f"{spec.name}: packed DiT block, {spec.n} tokens (512 text + 512 audio + "
+                         f"24576 video 16x32x48), D={spec.D}, {spec.H}x{spec.hd} heads, SwiGLU "
+                         f"{spec.F}, {spec.slots} timestep slots x 3 tags, rank-24 adaLN")
+            if spec.name == "t2va" else f"{spec.name}: n={spec.n} D={spec.D}",
+            "n": spec.n, "D": spec.D, "heads": spec.H, "head_dim": spec.hd, "ffn": spec.F,
+            "parallelism": "single GPU",
+        },
+        "attention_tflops": attn_tf,
+        "attention_frac_mfma_peak": attn_tf / PEAK_BF16_TFLOPS,
+        "gemm_tflops": gemm_tf,
+        "gemm_frac_mfma_peak": gemm_tf / PEAK_BF16_TFLOPS,
+        "norm1_gbs": norm_gbs,
+        "norm1_frac_hbm_peak": norm_gbs / PEAK_HBM_GBS,
+        "phases_ms": ph,
+        "roofline": {
+            "kernel": "k_attn_bf16<128> (attention)",
+            "bound": "mfma",
+            "achieved": attn_tf,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": attn_tf / PEAK_BF16_TFLOPS,
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(spec, wl)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

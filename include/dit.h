@@ -1,0 +1,238 @@
+/*
+ * dit.h - C ABI of the packed diffusion-transformer block library (libdit.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One call runs the forward pass of one DiT block over a packed token
+ * sequence: text, audio and video (or image) tokens share one sequence and are
+ * told apart only by a per-token modulation row.  Citation tags:
+ *
+ *   [MMH3]   docs.rs source page of cortiq-engine 0.5.72, src/mmh3.rs
+ *   [SIGLIP] docs.rs source page of ffai-argus 0.7.0, src/siglip.rs
+ *   [ZIMG]   ollama fork, x/imagegen/models/zimage/transformer.go
+ *
+ * Conventions for every entry point:
+ *   - Data pointers are DEVICE memory owned by the caller, except where an
+ *     argument is marked "host".  The library never allocates or frees device
+ *     memory: prepared weights and the workspace are caller buffers sized by
+ *     the *_size queries.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; nothing synchronizes inside the library.
+ *   - All arguments are validated on the host before anything is launched.
+ *     On failure nothing is written and a negative dit_status is returned; the
+ *     message is in dit_last_error() (thread-local).  Launch failures return
+ *     DIT_EHIP.  Device faults surface at the caller's next synchronization.
+ *   - n == 0 is valid and does nothing.
+ *   - There is no CPU fallback: every step runs in the library's HIP kernels.
+ *   - Supported shapes: hd in {64, 128}, D = H*hd, D % 128 == 0,
+ *     F % 128 == 0, D <= 4096, 1 <= slots <= 8, rank <= 64, grid >= 2;
+ *     pointers 16-byte aligned; tensors contiguous row-major.
+ */
+#ifndef DIT_H
+#define DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DIT_OK = 0,
+  DIT_EINVAL = -1,       /* NULL pointer where one is required, bad value   */
+  DIT_ESHAPE = -2,       /* inconsistent sizes                              */
+  DIT_EDTYPE = -3,       /* unknown dtype                                   */
+  DIT_EALIGN = -4,       /* pointer not 16-byte aligned                     */
+  DIT_EWORKSPACE = -5,   /* workspace or prepared buffer too small          */
+  DIT_EUNSUPPORTED = -6, /* shape outside the supported set                 */
+  DIT_EHIP = -7          /* a HIP launch failed                             */
+} dit_status;
+
+/* Block variant. */
+enum {
+  DIT_MMH3 = 0,   /* six-chunk adaLN (shift/scale/gate x2) from a rank-r timestep-curve
+                     basis, RMSNorm, qk-RMSNorm + 3-axis RoPE, SwiGLU ([MMH3] block_forward) */
+  DIT_SIGLIP = 1, /* pre-LayerNorm encoder layer with biases, GELU-tanh, no modulation and
+                     no RoPE; softmax scale folded into W_q, b_q ([SIGLIP] Layer::forward)    */
+  DIT_ZIMAGE = 2  /* four-chunk adaLN from a sinusoidal timestep MLP, tanh gates, sandwich
+                     RMSNorms, interleaved RoPE, SwiGLU ([ZIMG] TransformerBlock.Forward)     */
+};
+
+/* Arithmetic type of GEMM operands, attention inputs and the intermediates
+ * (the residual stream x, x1 and out are always fp32). */
+enum { DIT_F32 = 0, DIT_BF16 = 1 };
+
+/* RoPE pair layout. */
+enum {
+  DIT_ROPE_NONE = 0,
+  DIT_ROPE_SPLIT_HALF = 1,  /* pair (j, j + hd/2) ([MMH3] norm_rope_w)  */
+  DIT_ROPE_INTERLEAVED = 2  /* pair (2j, 2j + 1) ([ZIMG] applyRoPE3D)  */
+};
+
+typedef struct dit_config {
+  int32_t variant;       /* DIT_MMH3 / DIT_SIGLIP / DIT_ZIMAGE                         */
+  int32_t dtype;         /* DIT_F32 / DIT_BF16                                          */
+  int32_t D, H, hd, F;   /* hidden, heads, head dim (D = H*hd), FFN hidden              */
+  int32_t slots;         /* MMH3: timestep slots S                                      */
+  int32_t tags;          /* MMH3: modality tags T (3: video 0, text 1, audio 2)         */
+  int32_t rank;          /* MMH3: adaLN curve rank r (24)                               */
+  int32_t grid;          /* MMH3: adaLN table rows G (1025)                             */
+  int32_t rope;          /* DIT_ROPE_*                                                  */
+  int32_t rope_axes[3];  /* dims per position axis (t, h, w); sum = hd                  */
+  double rope_theta;     /* frequency base: axis a, pair m turns by pos * theta^(-2m/d_a) */
+  float eps;             /* block norm epsilon (RMSNorm or LayerNorm)                   */
+  float qk_eps;          /* qk-RMSNorm epsilon                                          */
+  int32_t temb_freq;     /* ZIMAGE: sinusoid width (256)                                */
+  int32_t temb_hidden;   /* ZIMAGE: timestep MLP hidden width (1024)                    */
+  float t_scale;         /* ZIMAGE: timestep multiplier before the sinusoid (1000)      */
+} dit_config;
+
+/* Raw weights, device pointers.  GEMM weights (w_*) are [out, in] row-major in
+ * the config's dtype (float or bfloat16); everything else is fp32.  Pointers a
+ * variant does not use may be NULL.
+ *   MMH3:   norm1, norm2 [D]; w_qkv [3D, D] (rows q | k | v); w_out [D, D];
+ *           q_norm, k_norm [hd]; w_fc1 [2F, D] (rows gate | up); w_fc2 [D, F];
+ *           adaln_basis [S*T*6*D, r] (slot-major: rows of slot s are
+ *           [s*T*6*D, (s+1)*T*6*D)); adaln_bias [S*T*6*D] (NULL = 0);
+ *           adaln_table [G, r].
+ *   SIGLIP: norm1/ln1_b, norm2/ln2_b [D] LayerNorm gain/bias; w_qkv [3D, D]
+ *           + b_qkv [3D]; w_out + b_out; w_fc1 [F, D] + b_fc1 [F];
+ *           w_fc2 [D, F] + b_fc2 [D].
+ *   ZIMAGE: norm1 (attention pre-norm), post_attn_norm, norm2 (FFN pre-norm),
+ *           post_ffn_norm [D]; w_qkv, w_out, q_norm, k_norm; w_fc1 [2F, D]
+ *           (rows W1 gate | W3 up); w_fc2 [D, F]; temb_w1 [Th, Tf] + temb_b1;
+ *           temb_w2 [Tf, Th] + temb_b2; ada_w [4D, Tf] + ada_b [4D]
+ *           (chunks scale_msa, gate_msa, scale_mlp, gate_mlp). */
+typedef struct dit_weights {
+  const float *norm1, *norm2, *ln1_b, *ln2_b, *post_attn_norm, *post_ffn_norm;
+  const void *w_qkv, *w_out, *w_fc1, *w_fc2;
+  const float *b_qkv, *b_out, *b_fc1, *b_fc2;
+  const float *q_norm, *k_norm;
+  const float *adaln_basis, *adaln_bias, *adaln_table;
+  const float *temb_w1, *temb_b1, *temb_w2, *temb_b2, *ada_w, *ada_b;
+} dit_weights;
+
+/* Byte offsets of the intermediates inside the workspace of dit_block_forward
+ * (for inspection after the call; `none` = SIZE_MAX when a variant has no such
+ * buffer).  ldn = n rounded up to 128.  act = the config's dtype.
+ *   mods  fp32 [R, E*D]   R = S*T (MMH3) or 1 (ZIMAGE), E = 6 or 4
+ *   rope  fp32 [n, hd/2, 2] (cos, sin) per token and pair
+ *   xn    act  [n, D]     pre-norm + modulate of the FFN half after the call
+ *                         (the attention half's is overwritten)
+ *   qkv   act  [n, 3D]    QKV projection (+ bias)
+ *   q, k  act  [H, ldn, hd]  after qk-norm and RoPE; q carries hd^-1/2
+ *   vt    act  [H, hd, ldn]  V transposed per head
+ *   o     act  [n, D]     attention output, head h at columns h*hd
+ *   x1    fp32 [n, D]     residual stream after the attention half
+ *   a     act  [n, F]     FFN activation (SwiGLU or GELU-tanh)
+ *   y     fp32 [n, D]     ZIMAGE: last projection before its sandwich norm (fc2's after the call) */
+typedef struct dit_ws_layout {
+  size_t mods, rope, xn, qkv, q, k, vt, o, x1, a, y, temb, total;
+  int32_t ldn;
+} dit_ws_layout;
+
+/* Checks a configuration; DIT_OK if the library supports it. */
+dit_status dit_validate_config(const dit_config* cfg);
+
+/* Bytes of the prepared-weights buffer for `cfg` (0 if cfg is invalid). */
+size_t dit_prepared_size(const dit_config* cfg);
+
+/* Copies the raw weights into `prepared` (device, `bytes` long) in the
+ * kernels' layout: SwiGLU fc1 rows interleaved in groups of 32 (gate group g,
+ * then up group g), SIGLIP W_q and b_q pre-multiplied by hd^-1/2
+ * ([SIGLIP] Layer::load, the scale fold).  `raw` may be freed after the
+ * stream has passed this call. */
+dit_status dit_prepare_weights(const dit_config* cfg, const dit_weights* raw, void* prepared,
+                               size_t bytes, void* stream);
+
+/* Workspace bytes needed by dit_block_forward for n tokens. */
+size_t dit_workspace_size(const dit_config* cfg, int32_t n);
+
+/* Fills `out` (host) with the workspace layout for n tokens. */
+dit_status dit_workspace_layout(const dit_config* cfg, int32_t n, dit_ws_layout* out);
+
+/* Modulation rows ([MMH3] Adaln::eval; [ZIMG] TimestepEmbedder + adaLN).
+ * sigmas (host, n_sigmas = S for MMH3, 1 for ZIMAGE):
+ *   MMH3:   slot s's sigma; t_s = 1 - max(sigma_s, 1e-6), grid coordinate
+ *           p = clamp(t_s, 0, 1)*(G-1) taken in fp64 on the host; row j of
+ *           the basis is evaluated at its own slot's interpolated coordinates.
+ *   ZIMAGE: sigmas[0] is the timestep t (multiplied by t_scale).
+ * mods_out: device fp32 [R, E*D], element (r, e, d) at (r*E + e)*D + d.
+ * temb_scratch: ZIMAGE only, device fp32 [temb_hidden + temb_freq] (else NULL). */
+dit_status dit_adaln_eval(const dit_config* cfg, const void* prepared, const double* sigmas,
+                          int32_t n_sigmas, float* mods_out, float* temb_scratch, void* stream);
+
+/* Modulation + segment gather + pre-norm + modulate of one half of the block:
+ * mods_out = dit_adaln_eval(...), then for every token i with r = rows[i]:
+ *   MMH3:   xn_i = RMSNorm(x_i; g, eps) * (1 + mods[r, scale]) + mods[r, shift]
+ *           (half 0: g = norm1, chunks shift 0 / scale 1; half 1: norm2, 3 / 4)
+ *   ZIMAGE: xn_i = RMSNorm(x_i; g, eps) * (1 + mods[0, scale]) (chunk 0 or 2)
+ *   SIGLIP: xn_i = LayerNorm(x_i; g, b, eps), mods unused (may be NULL)
+ * x: device fp32 [n, D]; rows: device int32 [n], each in [0, R) (unchecked on
+ * the device: an out-of-range row reads outside mods); NULL means row 0.
+ * xn_out: device [n, D] in the config's dtype. */
+dit_status dit_adaln_modulate(const dit_config* cfg, const void* prepared, const float* x,
+                              int32_t n, const int32_t* rows, const double* sigmas,
+                              int32_t n_sigmas, int32_t half, void* xn_out, float* mods_out,
+                              float* temb_scratch, void* stream);
+
+/* One block forward ([MMH3] block_forward + ffn_tail; [SIGLIP] Layer::forward;
+ * [ZIMG] TransformerBlock.Forward):
+ *   x:    device fp32 [n, D] residual stream in
+ *   rows: device int32 [n] modulation row per token (MMH3; NULL = row 0)
+ *   pos:  device fp32 [n, 3] (t, h, w) per token (needed unless rope = NONE)
+ *   sigmas: host, as dit_adaln_eval (ignored for SIGLIP)
+ *   out:  device fp32 [n, D]; may alias x (x is read only before out is written)
+ *   workspace: device, >= dit_workspace_size(cfg, n) bytes, 256-byte aligned */
+dit_status dit_block_forward(const dit_config* cfg, const void* prepared, const float* x,
+                             int32_t n, const int32_t* rows, const float* pos,
+                             const double* sigmas, int32_t n_sigmas, float* out,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/* Standalone full bidirectional attention over one packed sequence, per head
+ * ([MMH3] attention; online softmax with normalization deferred to the output,
+ * [SIGLIP] deferred normalisation):
+ *   q, k: device [H, ldn, hd]; vt: device [H, hd, ldn] (V transposed), all in
+ *   the config's dtype, rows/columns >= n ignored (keys are masked, but the
+ *   padding of vt must hold finite values);
+ *   o: device [n, H*hd] in the config's dtype;
+ *   score_scale: multiplier of q.k before the softmax (q is used as given).
+ * ldn must be a multiple of 128 and >= n. */
+dit_status dit_attention(const dit_config* cfg, const void* q, const void* k, const void* vt,
+                         int32_t n, int32_t ldn, float score_scale, void* o, void* stream);
+
+/* Per-phase timing of dit_block_forward ([MMH3] per-phase profiler: one
+ * stopwatch per phase, none overlapping).  dit_profile_begin(max_calls) arms
+ * hipEvents (created on the host; no device memory) for the next max_calls
+ * block calls on this thread; each call records DIT_NPHASES + 1 events on its
+ * stream, one before its first kernel and one after each phase.
+ * dit_profile_end() waits for the last recorded event, writes the summed
+ * milliseconds of every phase over the recorded calls into phase_ms (host,
+ * DIT_NPHASES doubles) and the number of recorded calls into *calls, and
+ * releases the events.  Phases: 0 adaLN + RoPE table, 1 pre-norm (attention),
+ * 2 QKV GEMM, 3 qk-norm/RoPE split, 4 attention, 5 out GEMM + residual,
+ * 6 pre-norm (FFN), 7 fc1 GEMM + activation, 8 fc2 GEMM + residual. */
+#define DIT_NPHASES 9
+dit_status dit_profile_begin(int32_t max_calls);
+dit_status dit_profile_end(double* phase_ms, int32_t* calls);
+const char* dit_phase_name(int32_t phase);
+
+/* sigma on the to_shift flow schedule at the same base-grid point as sigma on
+ * the from_shift schedule ([MMH3] time_shift_sigma); 12 -> 3 is s / (4 - 3s).
+ * Host function. */
+double dit_sigma_remap(double sigma, double from_shift, double to_shift);
+
+/* d sigma_to / d sigma_from of dit_sigma_remap ([MMH3] time_shift_slope). */
+double dit_sigma_remap_slope(double sigma, double from_shift, double to_shift);
+
+/* Message of the last failure on this thread ("" if none). */
+const char* dit_last_error(void);
+
+/* ABI version (increments on any change of this header). */
+int32_t dit_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_H */

@@ -1,0 +1,70 @@
+// Device-side helpers shared by the block's kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // bfloat16 storage
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+#define DIT_DEV __device__ __forceinline__
+
+DIT_DEV float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// float -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32).
+DIT_DEV bf16_t f2bf(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, h);
+}
+
+// Two floats -> two packed bfloat16 (low = a).
+DIT_DEV uint32_t pack2bf(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  static DIT_DEV float ld(const float* p) { return *p; }
+  static DIT_DEV void st(float* p, float v) { *p = v; }
+  // four consecutive elements
+  static DIT_DEV float4 ld4(const float* p) { return *(const float4*)p; }
+  static DIT_DEV void st4(float* p, float4 v) { *(float4*)p = v; }
+};
+template <> struct Elt<bf16_t> {
+  static DIT_DEV float ld(const bf16_t* p) { return bf2f(*p); }
+  static DIT_DEV void st(bf16_t* p, float v) { *p = f2bf(v); }
+  static DIT_DEV float4 ld4(const bf16_t* p) {
+    uint2 u = *(const uint2*)p;
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  }
+  static DIT_DEV void st4(bf16_t* p, float4 v) {
+    *(uint2*)p = make_uint2(pack2bf(v.x, v.y), pack2bf(v.z, v.w));
+  }
+};
+
+DIT_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+DIT_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+DIT_DEV float silu_f(float v) { return v / (1.0f + __expf(-v)); }
+
+// Tanh-form GELU; tanh(u) = 1 - 2 / (exp(2u) + 1).
+DIT_DEV float gelu_tanh_f(float v) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  float u = k0 * (v + 0.044715f * v * v * v);
+  float t = 1.0f - 2.0f / (__expf(2.0f * u) + 1.0f);
+  return 0.5f * v * (1.0f + t);
+}
+
+DIT_DEV float tanh_f(float u) { return 1.0f - 2.0f / (__expf(2.0f * u) + 1.0f); }

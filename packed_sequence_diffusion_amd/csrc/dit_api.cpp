@@ -1,0 +1,628 @@
+// C ABI of libdit.so: host-side validation, buffer layouts and the launch
+// sequence of one block on the caller's stream.  Validation touches no device
+// memory and makes no HIP call, so every refusal can be exercised without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "../../include/dit.h"
+#include "dit_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dit_status fail(dit_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+constexpr size_t kNone = SIZE_MAX;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t esize(const dit_config* c) { return c->dtype == DIT_BF16 ? 2 : 4; }
+int chunks(const dit_config* c) { return c->variant == DIT_MMH3 ? 6 : (c->variant == DIT_ZIMAGE ? 4 : 0); }
+int mod_rows(const dit_config* c) {
+  return c->variant == DIT_MMH3 ? c->slots * c->tags : (c->variant == DIT_ZIMAGE ? 1 : 0);
+}
+bool swiglu(const dit_config* c) { return c->variant != DIT_SIGLIP; }
+int fc1_rows(const dit_config* c) { return swiglu(c) ? 2 * c->F : c->F; }
+
+dit_status check_config(const dit_config* c) {
+  if (!c) return fail(DIT_EINVAL, "config is NULL");
+  if (c->variant < DIT_MMH3 || c->variant > DIT_ZIMAGE)
+    return fail(DIT_EINVAL, "unknown variant %d", c->variant);
+  if (c->dtype != DIT_F32 && c->dtype != DIT_BF16) return fail(DIT_EDTYPE, "unknown dtype %d", c->dtype);
+  if (c->hd != 64 && c->hd != 128) return fail(DIT_EUNSUPPORTED, "head dim %d not in {64, 128}", c->hd);
+  if (c->H <= 0 || c->D != c->H * c->hd) return fail(DIT_ESHAPE, "D=%d != H*hd=%d*%d", c->D, c->H, c->hd);
+  if (c->D % 128 || c->D > 4096) return fail(DIT_EUNSUPPORTED, "D=%d must be a multiple of 128 and <= 4096", c->D);
+  if (c->F <= 0 || c->F % 128) return fail(DIT_EUNSUPPORTED, "F=%d must be a positive multiple of 128", c->F);
+  if (!(c->eps >= 0.0f) || !(c->qk_eps >= 0.0f)) return fail(DIT_EINVAL, "eps must be >= 0");
+  if (c->rope < DIT_ROPE_NONE || c->rope > DIT_ROPE_INTERLEAVED) return fail(DIT_EINVAL, "unknown rope %d", c->rope);
+  if (c->rope != DIT_ROPE_NONE) {
+    int sum = 0;
+    for (int a = 0; a < 3; ++a) {
+      if (c->rope_axes[a] < 0 || c->rope_axes[a] % 2) return fail(DIT_EINVAL, "rope axis dims must be even and >= 0");
+      sum += c->rope_axes[a];
+    }
+    if (sum != c->hd) return fail(DIT_ESHAPE, "rope axis dims sum to %d, head dim is %d", sum, c->hd);
+    if (!(c->rope_theta > 0.0) || !isfinite(c->rope_theta)) return fail(DIT_EINVAL, "rope_theta must be > 0");
+  }
+  if (c->variant == DIT_MMH3) {
+    if (c->slots < 1 || c->slots > 8) return fail(DIT_EUNSUPPORTED, "slots=%d not in [1, 8]", c->slots);
+    if (c->tags < 1 || c->tags > 16) return fail(DIT_EINVAL, "tags=%d not in [1, 16]", c->tags);
+    if (c->rank < 1 || c->rank > 64) return fail(DIT_EUNSUPPORTED, "rank=%d not in [1, 64]", c->rank);
+    if (c->grid < 2) return fail(DIT_EINVAL, "grid=%d must be >= 2", c->grid);
+  }
+  if (c->variant == DIT_SIGLIP && c->rope != DIT_ROPE_NONE)
+    return fail(DIT_EUNSUPPORTED, "the SigLIP layer takes no RoPE");
+  if (c->variant == DIT_ZIMAGE) {
+    if (c->temb_freq < 2 || c->temb_freq % 2 || c->temb_hidden < 1)
+      return fail(DIT_EINVAL, "temb sizes freq=%d hidden=%d invalid", c->temb_freq, c->temb_hidden);
+  }
+  g_err[0] = 0;
+  return DIT_OK;
+}
+
+// ---------------------------------------------------------------- layouts ----
+struct PrepLayout {
+  size_t norm1 = kNone, norm2 = kNone, ln1_b = kNone, ln2_b = kNone, post_attn = kNone,
+         post_ffn = kNone, w_qkv = kNone, w_out = kNone, w_fc1 = kNone, w_fc2 = kNone,
+         b_qkv = kNone, b_out = kNone, b_fc1 = kNone, b_fc2 = kNone, q_norm = kNone,
+         k_norm = kNone, basis = kNone, abias = kNone, table = kNone, tw1 = kNone, tb1 = kNone,
+         tw2 = kNone, tb2 = kNone, aw = kNone, ab = kNone, total = 0;
+};
+
+PrepLayout prep_layout(const dit_config* c) {
+  PrepLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t D = c->D, F = c->F, es = esize(c);
+  L.w_qkv = take(3 * D * D * es);
+  L.w_out = take(D * D * es);
+  L.w_fc1 = take((size_t)fc1_rows(c) * D * es);
+  L.w_fc2 = take(D * F * es);
+  L.norm1 = take(D * 4);
+  L.norm2 = take(D * 4);
+  if (c->variant != DIT_SIGLIP) {
+    L.q_norm = take(c->hd * 4);
+    L.k_norm = take(c->hd * 4);
+  }
+  if (c->variant == DIT_SIGLIP) {
+    L.ln1_b = take(D * 4);
+    L.ln2_b = take(D * 4);
+    L.b_qkv = take(3 * D * 4);
+    L.b_out = take(D * 4);
+    L.b_fc1 = take(F * 4);
+    L.b_fc2 = take(D * 4);
+  }
+  if (c->variant == DIT_MMH3) {
+    size_t rows = (size_t)c->slots * c->tags * 6 * D;
+    L.basis = take(rows * c->rank * 4);
+    L.abias = take(rows * 4);
+    L.table = take((size_t)c->grid * c->rank * 4);
+  }
+  if (c->variant == DIT_ZIMAGE) {
+    L.post_attn = take(D * 4);
+    L.post_ffn = take(D * 4);
+    size_t tf = c->temb_freq, th = c->temb_hidden;
+    L.tw1 = take(th * tf * 4);
+    L.tb1 = take(th * 4);
+    L.tw2 = take(tf * th * 4);
+    L.tb2 = take(tf * 4);
+    L.aw = take(4 * D * tf * 4);
+    L.ab = take(4 * D * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+int ldn_of(int n) { return (n + 127) / 128 * 128; }
+
+dit_ws_layout ws_layout(const dit_config* c, int n) {
+  dit_ws_layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t D = c->D, F = c->F, es = esize(c);
+  const int ldn = ldn_of(n);
+  L.ldn = ldn;
+  L.mods = mod_rows(c) ? take((size_t)mod_rows(c) * chunks(c) * D * 4) : kNone;
+  L.temb = c->variant == DIT_ZIMAGE ? take((size_t)(c->temb_hidden + c->temb_freq) * 4) : kNone;
+  L.rope = c->rope != DIT_ROPE_NONE ? take((size_t)n * (c->hd / 2) * 8) : kNone;
+  L.xn = take((size_t)n * D * es);
+  L.qkv = take((size_t)n * 3 * D * es);
+  L.q = take((size_t)c->H * ldn * c->hd * es);
+  L.k = take((size_t)c->H * ldn * c->hd * es);
+  L.vt = take((size_t)c->H * ldn * c->hd * es);
+  L.o = take((size_t)n * D * es);
+  L.x1 = take((size_t)n * D * 4);
+  L.a = take((size_t)n * F * es);
+  L.y = c->variant == DIT_ZIMAGE ? take((size_t)n * D * 4) : kNone;
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return off == kNone ? nullptr : (T*)((char*)base + off);
+}
+template <typename T>
+const T* atc(const void* base, size_t off) {
+  return off == kNone ? nullptr : (const T*)((const char*)base + off);
+}
+
+dit_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DIT_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return DIT_OK;
+}
+
+#define DIT_TRY(expr)                          \
+  do {                                         \
+    dit_status st_ = (expr);                   \
+    if (st_ != DIT_OK) return st_;             \
+  } while (0)
+#define HIP_TRY(expr, what) DIT_TRY(hip_check((expr), what))
+
+dit_status check_sigmas(const dit_config* c, const double* sigmas, int n_sigmas) {
+  if (c->variant == DIT_SIGLIP) return DIT_OK;
+  int need = c->variant == DIT_MMH3 ? c->slots : 1;
+  if (!sigmas) return fail(DIT_EINVAL, "sigmas is NULL");
+  if (n_sigmas != need) return fail(DIT_ESHAPE, "n_sigmas=%d, the configuration needs %d", n_sigmas, need);
+  for (int i = 0; i < need; ++i)
+    if (!isfinite(sigmas[i])) return fail(DIT_EINVAL, "sigma %d is not finite", i);
+  return DIT_OK;
+}
+
+// Modulation rows into `mods` (device).  MMH3: slot timestep t = 1 -
+// max(sigma, 1e-6) and grid coordinate p = clamp(t, 0, 1) * (G - 1), i0 =
+// min(floor(p), G - 2), f = p - i0, all in fp64 ([MMH3] MiniMaxH3::forward and
+// Adaln::eval).
+dit_status launch_mods(const dit_config* c, const void* prep, const double* sigmas, float* mods,
+                       float* temb, hipStream_t s) {
+  PrepLayout P = prep_layout(c);
+  if (c->variant == DIT_MMH3) {
+    dit::SlotCoords sc;
+    memset(&sc, 0, sizeof(sc));
+    for (int i = 0; i < c->slots; ++i) {
+      double t = 1.0 - std::max(sigmas[i], 1e-6);
+      double p = std::min(std::max(t, 0.0), 1.0) * (double)(c->grid - 1);
+      int i0 = std::min((int)floor(p), c->grid - 2);
+      sc.i0[i] = i0;
+      sc.f[i] = (float)(p - (double)i0);
+    }
+    int per_slot = c->tags * 6 * c->D;
+    HIP_TRY(dit::adaln_interp(atc<float>(prep, P.basis), atc<float>(prep, P.abias),
+                              atc<float>(prep, P.table), c->rank, per_slot, c->slots, sc, mods, s),
+            "adaln_interp");
+  } else if (c->variant == DIT_ZIMAGE) {
+    HIP_TRY(dit::temb_mods(sigmas[0] * (double)c->t_scale, c->temb_freq, c->temb_hidden, 4 * c->D,
+                           atc<float>(prep, P.tw1), atc<float>(prep, P.tb1), atc<float>(prep, P.tw2),
+                           atc<float>(prep, P.tb2), atc<float>(prep, P.aw), atc<float>(prep, P.ab),
+                           temb, mods, s),
+            "temb_mods");
+  }
+  return DIT_OK;
+}
+
+// Pre-norm (+ modulate) of one half into xn.
+dit_status launch_prenorm(const dit_config* c, const void* prep, const float* x, int n,
+                          const int* rows, const float* mods, int half, void* xn, hipStream_t s) {
+  PrepLayout P = prep_layout(c);
+  const int D = c->D;
+  const bool bf = c->dtype == DIT_BF16;
+  const float* g = atc<float>(prep, half ? P.norm2 : P.norm1);
+  if (c->variant == DIT_MMH3) {
+    HIP_TRY(dit::norm_mod(dit::NORM_RMS, dit::MOD_SHIFT_SCALE, bf, x, n, D, g, nullptr, c->eps, mods,
+                          6 * D, rows, (half ? 3 : 0) * D, (half ? 4 : 1) * D, xn, s),
+            "norm_mod");
+  } else if (c->variant == DIT_ZIMAGE) {
+    HIP_TRY(dit::norm_mod(dit::NORM_RMS, dit::MOD_SCALE, bf, x, n, D, g, nullptr, c->eps, mods, 4 * D,
+                          nullptr, 0, (half ? 2 : 0) * D, xn, s),
+            "norm_mod");
+  } else {
+    HIP_TRY(dit::norm_mod(dit::NORM_LAYER, dit::MOD_NONE, bf, x, n, D, g,
+                          atc<float>(prep, half ? P.ln2_b : P.ln1_b), c->eps, nullptr, 0, nullptr, 0,
+                          0, xn, s),
+            "norm_mod");
+  }
+  return DIT_OK;
+}
+
+// Per-phase event timing (thread-local; see dit_profile_begin).
+struct Profiler {
+  bool on = false;
+  int max_calls = 0, used = 0;
+  std::vector<hipEvent_t> ev;
+};
+thread_local Profiler g_prof;
+
+struct PhaseMarks {
+  hipStream_t s;
+  hipEvent_t* ev = nullptr;
+  explicit PhaseMarks(hipStream_t st) : s(st) {
+    if (g_prof.on && g_prof.used < g_prof.max_calls) {
+      ev = &g_prof.ev[(size_t)g_prof.used * (DIT_NPHASES + 1)];
+      ++g_prof.used;
+      hipEventRecord(ev[0], s);
+    }
+  }
+  void mark(int phase) {
+    if (ev) hipEventRecord(ev[phase + 1], s);
+  }
+};
+
+const char* kPhaseNames[DIT_NPHASES] = {"adaln+rope", "norm1", "qkv_gemm", "qk_split", "attention",
+                                        "out_gemm", "norm2", "fc1_gemm", "fc2_gemm"};
+
+}  // namespace
+
+extern "C" {
+
+const char* dit_phase_name(int32_t phase) {
+  return (phase >= 0 && phase < DIT_NPHASES) ? kPhaseNames[phase] : "";
+}
+
+dit_status dit_profile_begin(int32_t max_calls) {
+  if (max_calls < 1 || max_calls > 100000) return fail(DIT_EINVAL, "max_calls=%d not in [1, 100000]", max_calls);
+  if (g_prof.on) return fail(DIT_EINVAL, "profiling already armed on this thread");
+  g_prof.ev.assign((size_t)max_calls * (DIT_NPHASES + 1), nullptr);
+  for (auto& e : g_prof.ev) {
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      for (auto& f : g_prof.ev)
+        if (f) hipEventDestroy(f);
+      g_prof.ev.clear();
+      return hip_check(err, "hipEventCreate");
+    }
+  }
+  g_prof.on = true;
+  g_prof.max_calls = max_calls;
+  g_prof.used = 0;
+  return DIT_OK;
+}
+
+dit_status dit_profile_end(double* phase_ms, int32_t* calls) {
+  if (!g_prof.on) return fail(DIT_EINVAL, "profiling is not armed");
+  if (!phase_ms || !calls) return fail(DIT_EINVAL, "phase_ms/calls is NULL");
+  dit_status st = DIT_OK;
+  for (int p = 0; p < DIT_NPHASES; ++p) phase_ms[p] = 0.0;
+  if (g_prof.used > 0) {
+    hipError_t e = hipEventSynchronize(g_prof.ev[(size_t)g_prof.used * (DIT_NPHASES + 1) - 1]);
+    if (e != hipSuccess) st = hip_check(e, "hipEventSynchronize");
+    for (int c = 0; c < g_prof.used && st == DIT_OK; ++c)
+      for (int p = 0; p < DIT_NPHASES; ++p) {
+        float ms = 0.0f;
+        hipError_t e2 = hipEventElapsedTime(&ms, g_prof.ev[(size_t)c * (DIT_NPHASES + 1) + p],
+                                            g_prof.ev[(size_t)c * (DIT_NPHASES + 1) + p + 1]);
+        if (e2 != hipSuccess) {
+          st = hip_check(e2, "hipEventElapsedTime");
+          break;
+        }
+        phase_ms[p] += ms;
+      }
+  }
+  *calls = g_prof.used;
+  for (auto& e : g_prof.ev) hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.on = false;
+  g_prof.used = g_prof.max_calls = 0;
+  return st;
+}
+
+
+int32_t dit_abi_version(void) { return 1; }
+
+const char* dit_last_error(void) { return g_err; }
+
+double dit_sigma_remap(double sigma, double from_shift, double to_shift) {
+  // Base-grid point of sigma on the from_shift schedule, then onto to_shift's
+  // ([MMH3] time_shift_sigma).
+  double base = sigma / (from_shift + sigma * (1.0 - from_shift));
+  return to_shift * base / (1.0 + (to_shift - 1.0) * base);
+}
+
+double dit_sigma_remap_slope(double sigma, double from_shift, double to_shift) {
+  double base = sigma / (from_shift + sigma * (1.0 - from_shift));
+  double a = 1.0 + (from_shift - 1.0) * base, b = 1.0 + (to_shift - 1.0) * base;
+  return (to_shift * a * a) / (from_shift * b * b);
+}
+
+dit_status dit_validate_config(const dit_config* cfg) { return check_config(cfg); }
+
+size_t dit_prepared_size(const dit_config* cfg) {
+  if (check_config(cfg) != DIT_OK) return 0;
+  return prep_layout(cfg).total;
+}
+
+size_t dit_workspace_size(const dit_config* cfg, int32_t n) {
+  if (check_config(cfg) != DIT_OK || n < 0) return 0;
+  return ws_layout(cfg, n).total;
+}
+
+dit_status dit_workspace_layout(const dit_config* cfg, int32_t n, dit_ws_layout* out) {
+  DIT_TRY(check_config(cfg));
+  if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
+  if (!out) return fail(DIT_EINVAL, "out is NULL");
+  *out = ws_layout(cfg, n);
+  return DIT_OK;
+}
+
+dit_status dit_prepare_weights(const dit_config* c, const dit_weights* w, void* prepared,
+                               size_t bytes, void* stream) {
+  DIT_TRY(check_config(c));
+  if (!w) return fail(DIT_EINVAL, "weights is NULL");
+  if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
+  if ((uintptr_t)prepared % kAlign) return fail(DIT_EALIGN, "prepared must be 256-byte aligned");
+  PrepLayout P = prep_layout(c);
+  if (bytes < P.total) return fail(DIT_EWORKSPACE, "prepared buffer %zu < %zu bytes", bytes, P.total);
+  struct Need {
+    const void* p;
+    const char* name;
+  };
+  Need common[] = {{w->w_qkv, "w_qkv"}, {w->w_out, "w_out"}, {w->w_fc1, "w_fc1"},
+                   {w->w_fc2, "w_fc2"}, {w->norm1, "norm1"}, {w->norm2, "norm2"}};
+  for (auto& q : common) {
+    if (!q.p) return fail(DIT_EINVAL, "weight %s is NULL", q.name);
+    if (!aligned16(q.p)) return fail(DIT_EALIGN, "weight %s is not 16-byte aligned", q.name);
+  }
+  if (c->variant != DIT_SIGLIP && (!w->q_norm || !w->k_norm)) return fail(DIT_EINVAL, "q_norm/k_norm are NULL");
+  if (c->variant == DIT_MMH3 && (!w->adaln_basis || !w->adaln_table))
+    return fail(DIT_EINVAL, "adaln_basis/adaln_table are NULL");
+  if (c->variant == DIT_SIGLIP && (!w->ln1_b || !w->ln2_b))
+    return fail(DIT_EINVAL, "SigLIP LayerNorm biases are NULL");
+  if (c->variant == DIT_ZIMAGE &&
+      (!w->post_attn_norm || !w->post_ffn_norm || !w->temb_w1 || !w->temb_w2 || !w->ada_w))
+    return fail(DIT_EINVAL, "Z-Image norms or timestep weights are NULL");
+
+  hipStream_t s = (hipStream_t)stream;
+  const int D = c->D, F = c->F, dt = c->dtype;
+  // [SIGLIP] Layer::load folds hd^-1/2 into W_q and b_q.
+  const bool fold = c->variant == DIT_SIGLIP;
+  const float qs = fold ? (float)(1.0 / sqrt((double)c->hd)) : 1.0f;
+  HIP_TRY(dit::prep_matrix(dt, w->w_qkv, at<char>(prepared, P.w_qkv), 3 * D, D, 0, fold ? D : 0, qs, s), "prep w_qkv");
+  HIP_TRY(dit::prep_matrix(dt, w->w_out, at<char>(prepared, P.w_out), D, D, 0, 0, 1.0f, s), "prep w_out");
+  HIP_TRY(dit::prep_matrix(dt, w->w_fc1, at<char>(prepared, P.w_fc1), fc1_rows(c), D,
+                           swiglu(c) ? F : 0, 0, 1.0f, s), "prep w_fc1");
+  HIP_TRY(dit::prep_matrix(dt, w->w_fc2, at<char>(prepared, P.w_fc2), D, F, 0, 0, 1.0f, s), "prep w_fc2");
+  auto vec = [&](const float* src, size_t off, int n, int scale_n = 0, float sc = 1.0f) {
+    return dit::prep_vector(src, at<float>(prepared, off), n, scale_n, sc, s);
+  };
+  HIP_TRY(vec(w->norm1, P.norm1, D), "prep norm1");
+  HIP_TRY(vec(w->norm2, P.norm2, D), "prep norm2");
+  if (c->variant != DIT_SIGLIP) {
+    HIP_TRY(vec(w->q_norm, P.q_norm, c->hd), "prep q_norm");
+    HIP_TRY(vec(w->k_norm, P.k_norm, c->hd), "prep k_norm");
+  }
+  if (c->variant == DIT_SIGLIP) {
+    HIP_TRY(vec(w->ln1_b, P.ln1_b, D), "prep ln1_b");
+    HIP_TRY(vec(w->ln2_b, P.ln2_b, D), "prep ln2_b");
+    HIP_TRY(vec(w->b_qkv, P.b_qkv, 3 * D, D, qs), "prep b_qkv");
+    HIP_TRY(vec(w->b_out, P.b_out, D), "prep b_out");
+    HIP_TRY(vec(w->b_fc1, P.b_fc1, F), "prep b_fc1");
+    HIP_TRY(vec(w->b_fc2, P.b_fc2, D), "prep b_fc2");
+  }
+  if (c->variant == DIT_MMH3) {
+    int rows = c->slots * c->tags * 6 * D;
+    HIP_TRY(dit::prep_matrix(dit::F32, w->adaln_basis, at<char>(prepared, P.basis), rows, c->rank, 0, 0, 1.0f, s),
+            "prep adaln_basis");
+    HIP_TRY(vec(w->adaln_bias, P.abias, rows), "prep adaln_bias");
+    HIP_TRY(dit::prep_matrix(dit::F32, w->adaln_table, at<char>(prepared, P.table), c->grid, c->rank, 0, 0, 1.0f, s),
+            "prep adaln_table");
+  }
+  if (c->variant == DIT_ZIMAGE) {
+    const int tf = c->temb_freq, th = c->temb_hidden;
+    HIP_TRY(vec(w->post_attn_norm, P.post_attn, D), "prep post_attn_norm");
+    HIP_TRY(vec(w->post_ffn_norm, P.post_ffn, D), "prep post_ffn_norm");
+    HIP_TRY(dit::prep_matrix(dit::F32, w->temb_w1, at<char>(prepared, P.tw1), th, tf, 0, 0, 1.0f, s), "prep temb_w1");
+    HIP_TRY(vec(w->temb_b1, P.tb1, th), "prep temb_b1");
+    HIP_TRY(dit::prep_matrix(dit::F32, w->temb_w2, at<char>(prepared, P.tw2), tf, th, 0, 0, 1.0f, s), "prep temb_w2");
+    HIP_TRY(vec(w->temb_b2, P.tb2, tf), "prep temb_b2");
+    HIP_TRY(dit::prep_matrix(dit::F32, w->ada_w, at<char>(prepared, P.aw), 4 * D, tf, 0, 0, 1.0f, s), "prep ada_w");
+    HIP_TRY(vec(w->ada_b, P.ab, 4 * D), "prep ada_b");
+  }
+  return DIT_OK;
+}
+
+dit_status dit_adaln_eval(const dit_config* c, const void* prepared, const double* sigmas,
+                          int32_t n_sigmas, float* mods_out, float* temb_scratch, void* stream) {
+  DIT_TRY(check_config(c));
+  if (c->variant == DIT_SIGLIP) return fail(DIT_EUNSUPPORTED, "the SigLIP layer has no modulation");
+  if (!prepared || !mods_out) return fail(DIT_EINVAL, "prepared/mods_out is NULL");
+  if (c->variant == DIT_ZIMAGE && !temb_scratch) return fail(DIT_EINVAL, "temb_scratch is NULL");
+  DIT_TRY(check_sigmas(c, sigmas, n_sigmas));
+  return launch_mods(c, prepared, sigmas, mods_out, temb_scratch, (hipStream_t)stream);
+}
+
+dit_status dit_adaln_modulate(const dit_config* c, const void* prepared, const float* x, int32_t n,
+                              const int32_t* rows, const double* sigmas, int32_t n_sigmas,
+                              int32_t half, void* xn_out, float* mods_out, float* temb_scratch,
+                              void* stream) {
+  DIT_TRY(check_config(c));
+  if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
+  if (half != 0 && half != 1) return fail(DIT_EINVAL, "half=%d not in {0, 1}", half);
+  if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
+  if (c->variant != DIT_SIGLIP) {
+    if (!mods_out) return fail(DIT_EINVAL, "mods_out is NULL");
+    if (c->variant == DIT_ZIMAGE && !temb_scratch) return fail(DIT_EINVAL, "temb_scratch is NULL");
+    DIT_TRY(check_sigmas(c, sigmas, n_sigmas));
+  }
+  if (n == 0) return DIT_OK;
+  if (!x || !xn_out) return fail(DIT_EINVAL, "x/xn_out is NULL");
+  if (!aligned16(x) || !aligned16(xn_out)) return fail(DIT_EALIGN, "x/xn_out not 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (c->variant != DIT_SIGLIP) DIT_TRY(launch_mods(c, prepared, sigmas, mods_out, temb_scratch, s));
+  return launch_prenorm(c, prepared, x, n, rows, mods_out, half, xn_out, s);
+}
+
+dit_status dit_attention(const dit_config* c, const void* q, const void* k, const void* vt,
+                         int32_t n, int32_t ldn, float score_scale, void* o, void* stream) {
+  DIT_TRY(check_config(c));
+  if (n < 0 || ldn < n || ldn % 128) return fail(DIT_ESHAPE, "need 0 <= n <= ldn, ldn %% 128 == 0 (n=%d ldn=%d)", n, ldn);
+  if (n == 0) return DIT_OK;
+  if (!q || !k || !vt || !o) return fail(DIT_EINVAL, "q/k/vt/o is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
+    return fail(DIT_EALIGN, "q/k/vt/o not 16-byte aligned");
+  if (!isfinite(score_scale)) return fail(DIT_EINVAL, "score_scale not finite");
+  const float log2e = 1.4426950408889634f;
+  HIP_TRY(dit::attention(c->dtype, c->hd, q, k, vt, n, ldn, c->H, score_scale * log2e, o, (hipStream_t)stream),
+          "attention");
+  return DIT_OK;
+}
+
+dit_status dit_block_forward(const dit_config* c, const void* prepared, const float* x, int32_t n,
+                             const int32_t* rows, const float* pos, const double* sigmas,
+                             int32_t n_sigmas, float* out, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  DIT_TRY(check_config(c));
+  if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
+  if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
+  DIT_TRY(check_sigmas(c, sigmas, n_sigmas));
+  if (n == 0) return DIT_OK;
+  if (!x || !out) return fail(DIT_EINVAL, "x/out is NULL");
+  if (!aligned16(x) || !aligned16(out)) return fail(DIT_EALIGN, "x/out not 16-byte aligned");
+  if (c->rope != DIT_ROPE_NONE && !pos) return fail(DIT_EINVAL, "pos is NULL but the block applies RoPE");
+  if (!workspace) return fail(DIT_EINVAL, "workspace is NULL");
+  if ((uintptr_t)workspace % kAlign) return fail(DIT_EALIGN, "workspace must be 256-byte aligned");
+  dit_ws_layout L = ws_layout(c, n);
+  if (ws_bytes < L.total) return fail(DIT_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  PrepLayout P = prep_layout(c);
+  const int D = c->D, F = c->F, H = c->H, hd = c->hd, dt = c->dtype;
+  const bool bf = dt == DIT_BF16;
+  const int ldn = L.ldn;
+  float* mods = at<float>(workspace, L.mods);
+  void* xn = at<char>(workspace, L.xn);
+  void* qkv = at<char>(workspace, L.qkv);
+  void* q = at<char>(workspace, L.q);
+  void* k = at<char>(workspace, L.k);
+  void* vt = at<char>(workspace, L.vt);
+  void* o = at<char>(workspace, L.o);
+  float* x1 = at<float>(workspace, L.x1);
+  void* a = at<char>(workspace, L.a);
+  float* y = at<float>(workspace, L.y);
+  float* cs = at<float>(workspace, L.rope);
+
+  PhaseMarks pm(s);
+  // a1: modulation rows; RoPE table
+  if (c->variant != DIT_SIGLIP) DIT_TRY(launch_mods(c, prepared, sigmas, mods, at<float>(workspace, L.temb), s));
+  if (c->rope != DIT_ROPE_NONE)
+    HIP_TRY(dit::rope_table(pos, n, hd / 2, c->rope_axes, c->rope_theta, cs, s), "rope_table");
+  pm.mark(0);
+  // a2: pre-norm + modulate
+  DIT_TRY(launch_prenorm(c, prepared, x, n, rows, mods, 0, xn, s));
+  pm.mark(1);
+  // a3: QKV projection (+ bias)
+  {
+    dit::Epi ep;
+    ep.out = qkv;
+    ep.ldc = 3 * D;
+    ep.bias = atc<float>(prepared, P.b_qkv);
+    HIP_TRY(dit::gemm(dt, dit::EPI_STORE, bf, xn, D, atc<char>(prepared, P.w_qkv), D, n, 3 * D, D, ep, s), "qkv gemm");
+  }
+  pm.mark(2);
+  // a4: qk-norm + RoPE + scale fold, head-major q, k and transposed v
+  {
+    const bool qkn = c->variant != DIT_SIGLIP;
+    float q_scale = c->variant == DIT_SIGLIP ? 1.0f : (float)(1.0 / sqrt((double)hd));
+    HIP_TRY(dit::qk_split(dt, hd, qkv, n, ldn, H, qkn ? atc<float>(prepared, P.q_norm) : nullptr,
+                          qkn ? atc<float>(prepared, P.k_norm) : nullptr, c->qk_eps, cs, c->rope,
+                          q_scale, q, k, vt, s),
+            "qk_split");
+  }
+  pm.mark(3);
+  // a5: attention (q carries hd^-1/2; the kernel works in base 2)
+  HIP_TRY(dit::attention(dt, hd, q, k, vt, n, ldn, H, 1.4426950408889634f, o, s), "attention");
+  pm.mark(4);
+  // a6: out projection + residual
+  if (c->variant == DIT_ZIMAGE) {
+    dit::Epi ep;
+    ep.out = y;
+    ep.ldc = D;
+    HIP_TRY(dit::gemm(dt, dit::EPI_STORE, false, o, D, atc<char>(prepared, P.w_out), D, n, D, D, ep, s), "out gemm");
+    // x1 = x + tanh(gate_msa) RMSNorm(y); xn = RMSNorm(x1) (1 + scale_mlp)
+    HIP_TRY(dit::sandwich(x, y, n, D, atc<float>(prepared, P.post_attn), mods + 1 * D, c->eps, x1,
+                          atc<float>(prepared, P.norm2), mods + 2 * D, bf, xn, s),
+            "sandwich attn");
+    pm.mark(5);
+    pm.mark(6);
+  } else {
+    dit::Epi ep;
+    ep.out = x1;
+    ep.ldc = D;
+    ep.resid = x;
+    ep.ldr = D;
+    ep.bias = atc<float>(prepared, P.b_out);
+    if (c->variant == DIT_MMH3) {
+      ep.mods = mods;
+      ep.mstride = 6 * D;
+      ep.goff = 2 * D;
+      ep.rows = rows;
+    }
+    HIP_TRY(dit::gemm(dt, dit::EPI_GATED_RES, false, o, D, atc<char>(prepared, P.w_out), D, n, D, D, ep, s),
+            "out gemm");
+    pm.mark(5);
+    // a7: FFN pre-norm + modulate
+    DIT_TRY(launch_prenorm(c, prepared, x1, n, rows, mods, 1, xn, s));
+    pm.mark(6);
+  }
+  // a8: fc1 + activation
+  {
+    dit::Epi ep;
+    ep.out = a;
+    ep.ldc = F;
+    ep.bias = atc<float>(prepared, P.b_fc1);
+    HIP_TRY(dit::gemm(dt, swiglu(c) ? dit::EPI_SWIGLU : dit::EPI_GELU, bf, xn, D, atc<char>(prepared, P.w_fc1), D, n,
+                      fc1_rows(c), D, ep, s),
+            "fc1 gemm");
+  }
+  pm.mark(7);
+  // a9: fc2 + residual
+  if (c->variant == DIT_ZIMAGE) {
+    dit::Epi ep;
+    ep.out = y;
+    ep.ldc = D;
+    HIP_TRY(dit::gemm(dt, dit::EPI_STORE, false, a, F, atc<char>(prepared, P.w_fc2), F, n, D, F, ep, s), "fc2 gemm");
+    HIP_TRY(dit::sandwich(x1, y, n, D, atc<float>(prepared, P.post_ffn), mods + 3 * D, c->eps, out, nullptr,
+                          nullptr, bf, nullptr, s),
+            "sandwich ffn");
+  } else {
+    dit::Epi ep;
+    ep.out = out;
+    ep.ldc = D;
+    ep.resid = x1;
+    ep.ldr = D;
+    ep.bias = atc<float>(prepared, P.b_fc2);
+    if (c->variant == DIT_MMH3) {
+      ep.mods = mods;
+      ep.mstride = 6 * D;
+      ep.goff = 5 * D;
+      ep.rows = rows;
+    }
+    HIP_TRY(dit::gemm(dt, dit::EPI_GATED_RES, false, a, F, atc<char>(prepared, P.w_fc2), F, n, D, F, ep, s),
+            "fc2 gemm");
+  }
+  pm.mark(8);
+  return DIT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Launchers of the block's HIP kernels (internal to libdit.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+enum Dtype { F32 = 0, BF16 = 1 };
+
+// ---- GEMM: C[M, N] = A[M, K] * B[N, K]^T with a fused epilogue ----------------
+enum EpiKind {
+  EPI_STORE = 0,      // out[r, c] = acc (+ bias[c])
+  EPI_GATED_RES = 1,  // out_f32[r, c] = resid[r, c] + gate(r, c) * (acc (+ bias[c])); gate = 1 without mods
+  EPI_SWIGLU = 2,     // columns interleaved in groups of 32 (gate g, up g): out[r, c'] = silu(g) * u
+  EPI_GELU = 3        // out[r, c] = gelu_tanh(acc + bias[c])
+};
+
+struct Epi {
+  void* out = nullptr;  // element type: fp32 for GATED_RES, else the GEMM's out type
+  int ldc = 0;
+  const float* bias = nullptr;   // [N] (GELU, STORE, GATED_RES) or null
+  const float* resid = nullptr;  // GATED_RES: fp32 [M, ldr]
+  int ldr = 0;
+  const float* mods = nullptr;  // GATED_RES: gate = mods[rows[r] * mstride + goff + c]
+  int mstride = 0;
+  int goff = 0;
+  const int* rows = nullptr;  // null = row 0
+};
+
+hipError_t gemm(int dtype, int epi, bool out_bf16, const void* A, int lda, const void* B, int ldb,
+                int M, int N, int K, const Epi& ep, hipStream_t s);
+
+// ---- modulation --------------------------------------------------------------------
+struct SlotCoords {
+  int i0[8];
+  float f[8];
+};
+hipError_t adaln_interp(const float* basis, const float* bias, const float* table, int rank,
+                        int per_slot, int slots, const SlotCoords& sc, float* mods, hipStream_t s);
+// Z-Image: sinusoid(t) -> L1 + SiLU -> L2 -> adaLN linear; scratch [hidden + freq].
+hipError_t temb_mods(double t_scaled, int freq, int hidden, int out_dim, const float* w1,
+                     const float* b1, const float* w2, const float* b2, const float* wa,
+                     const float* ba, float* scratch, float* mods, hipStream_t s);
+
+// ---- row kernels --------------------------------------------------------------------
+enum NormKind { NORM_RMS = 0, NORM_LAYER = 1 };
+enum ModKind { MOD_NONE = 0, MOD_SHIFT_SCALE = 1, MOD_SCALE = 2 };
+hipError_t norm_mod(int norm, int mod, bool out_bf16, const float* x, int n, int D, const float* g,
+                    const float* beta, float eps, const float* mods, int mstride, const int* rows,
+                    int shift_off, int scale_off, void* y, hipStream_t s);
+
+// x1 = x + tanh(gate) * RMSNorm(y; g_post); optionally xf = RMSNorm(x1; g_next) * (1 + scale).
+hipError_t sandwich(const float* x, const float* y, int n, int D, const float* g_post,
+                    const float* gate, float eps, float* x1, const float* g_next,
+                    const float* scale, bool xf_bf16, void* xf, hipStream_t s);
+
+// cos/sin per token and rotation pair, from fp64 angles.
+hipError_t rope_table(const float* pos, int n, int P, const int axes[3], double theta, float* cs,
+                      hipStream_t s);
+
+// qkv [n, 3D] -> q, k [H, ldn, hd] (qk-norm, RoPE, q scaled), vt [H, hd, ldn]; rows >= n zero.
+hipError_t qk_split(int dtype, int hd, const void* qkv, int n, int ldn, int H, const float* qn,
+                    const float* kn, float eps, const float* cs, int rope_mode, float q_scale,
+                    void* q, void* k, void* vt, hipStream_t s);
+
+hipError_t attention(int dtype, int hd, const void* q, const void* k, const void* vt, int n,
+                     int ldn, int H, float scale_log2, void* o, hipStream_t s);
+
+// ---- weight preparation ---------------------------------------------------------------
+// dst[r, :] = src[perm(r), :] * (r < scale_rows ? scale : 1); perm = SwiGLU group interleave
+// when swiglu_F > 0.
+hipError_t prep_matrix(int dtype, const void* src, void* dst, int rows, int cols, int swiglu_F,
+                       int scale_rows, float scale, hipStream_t s);
+hipError_t prep_vector(const float* src, float* dst, int n, int scale_n, float scale,
+                       hipStream_t s);
+
+}  // namespace dit

@@ -1,0 +1,258 @@
+// Full bidirectional attention over the packed sequence, per head, without
+// ever forming the score plane ([MMH3] attention: every token attends to every
+// token; softmax normalisation deferred to the output as in [SIGLIP]'s
+// deferred normalisation).
+//
+// bf16 path (flash-style, MFMA): a workgroup owns 128 queries of one head, four
+// waves of 32.  Each wave keeps its queries' Q fragment in registers and walks
+// the keys in tiles of 64 staged through LDS (double-buffered):
+//   S^T = K Q^T     (v_mfma_f32_32x32x16_bf16, A = K rows, B = Q^T)
+//   online softmax in base 2 (max, rescale, exp2), P in bf16
+//   O^T += V^T P^T  (A = V^T rows from the transposed V panel, B = P^T)
+// Because S^T's accumulator layout gives every lane one query column, the
+// softmax statistics are per lane and P lands in registers exactly in the
+// B-operand layout of the second product once the rows of the K tile are loaded
+// in a fixed permuted order (bits 2 and 3 of the row index swapped).
+//
+// fp32 path: a plain per-query loop (one thread per query), for the fp32
+// configuration.
+#include <math.h>
+
+#include "dev_common.h"
+#include "dit_kernels.h"
+
+namespace dit {
+
+// Row permutation of a 32-key block: swap bits 2 and 3.
+DIT_DEV int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+template <int HD>
+__global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16_t* __restrict__ Q,
+                                                      const bf16_t* __restrict__ Kp,
+                                                      const bf16_t* __restrict__ Vt, int n,
+                                                      int ldn, float scale_log2,
+                                                      bf16_t* __restrict__ O) {
+  constexpr int KT = 64;        // keys per tile
+  constexpr int NC = HD / 16;   // MFMA k-steps over the head dim
+  constexpr int ND = HD / 32;   // 32-row blocks of O^T
+  constexpr int KCH = HD / 8;   // 16-byte chunks per K row
+  constexpr int KPT = KT * KCH / 256;  // K chunks per thread per tile
+  constexpr int VPT = HD * (KT / 8) / 256;
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * HD];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[2][HD * KT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int h = blockIdx.y;
+  const int H = gridDim.y;
+  const int q0 = blockIdx.x * 128 + wave * 32;
+  const bf16_t* Qh = Q + (size_t)h * ldn * HD;
+  const bf16_t* Kh = Kp + (size_t)h * ldn * HD;
+  const bf16_t* Vh = Vt + (size_t)h * HD * ldn;
+
+  bf16x8_t qf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    qf[c] = *(const bf16x8_t*)(Qh + (size_t)(q0 + l32) * HD + 16 * c + 8 * half);
+
+  uint4 rk[KPT], rv[VPT];
+  // K tile [KT][HD]: chunk XOR row%16 (HD=128) or row%8 (HD=64); V^T tile
+  // [HD][KT]: chunk XOR row%8.
+#define KOFF(row, ch) ((row) * HD + ((((ch) ^ ((row) & (KCH - 1) & 15))) << 3))
+#define VOFF(row, ch) ((row) * KT + ((((ch) ^ ((row) & 7))) << 3))
+#define ATT_GLOAD(k0)                                                              \
+  do {                                                                             \
+    _Pragma("unroll") for (int i = 0; i < KPT; ++i) {                              \
+      int c_ = tid + 256 * i, row_ = c_ / KCH, ch_ = c_ % KCH;                     \
+      rk[i] = *(const uint4*)(Kh + (size_t)((k0) + row_) * HD + ch_ * 8);          \
+    }                                                                              \
+    _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                              \
+      int c_ = tid + 256 * i, row_ = c_ / (KT / 8), ch_ = c_ % (KT / 8);           \
+      rv[i] = *(const uint4*)(Vh + (size_t)row_ * ldn + (k0) + ch_ * 8);           \
+    }                                                                              \
+  } while (0)
+#define ATT_SSTORE(b)                                                              \
+  do {                                                                             \
+    _Pragma("unroll") for (int i = 0; i < KPT; ++i) {                              \
+      int c_ = tid + 256 * i, row_ = c_ / KCH, ch_ = c_ % KCH;                     \
+      *(uint4*)(&sK[b][KOFF(row_, ch_)]) = rk[i];                                  \
+    }                                                                              \
+    _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                              \
+      int c_ = tid + 256 * i, row_ = c_ / (KT / 8), ch_ = c_ % (KT / 8);           \
+      *(uint4*)(&sV[b][VOFF(row_, ch_)]) = rv[i];                                  \
+    }                                                                              \
+  } while (0)
+
+  f32x16_t oacc[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[d][v] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  const int ntiles = (n + KT - 1) / KT;
+  ATT_GLOAD(0);
+  ATT_SSTORE(0);
+  __syncthreads();
+  const int krow = key_perm(l32);
+  for (int t = 0; t < ntiles; ++t) {
+    const int b = t & 1;
+    if (t + 1 < ntiles) ATT_GLOAD((t + 1) * KT);
+
+    f32x16_t s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kb][v] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        bf16x8_t a = *(const bf16x8_t*)(&sK[b][KOFF(kb * 32 + krow, 2 * c + half)]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+      }
+    }
+    // accumulator value v of block kb is key kb*32 + 16*(v/8) + 8*half + v%8
+    if ((t + 1) * KT > n) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          int key = t * KT + kb * 32 + 16 * (v >> 3) + 8 * half + (v & 7);
+          if (key >= n) s[kb][v] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float alpha = exp2f(m_run - m_new);
+    float ls = 0.0f;
+    bf16x8_t p[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float pv = exp2f(fmaf(s[kb][8 * cc + e], scale_log2, -m_new));
+          ls += pv;
+          p[kb][cc][e] = (__bf16)pv;
+        }
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          bf16x8_t a = *(const bf16x8_t*)(&sV[b][VOFF(d * 32 + l32, 4 * kb + 2 * cc + half)]);
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kb][cc], oacc[d], 0, 0, 0);
+        }
+    if (t + 1 < ntiles) ATT_SSTORE(b ^ 1);
+    __syncthreads();
+  }
+
+  const float lt = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / lt;
+  const int qi = q0 + l32;
+  if (qi < n) {
+    bf16_t* orow = O + (size_t)qi * (H * HD) + h * HD;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        int col = d * 32 + 8 * g + 4 * half;
+        *(uint2*)(orow + col) =
+            make_uint2(pack2bf(oacc[d][4 * g + 0] * inv, oacc[d][4 * g + 1] * inv),
+                       pack2bf(oacc[d][4 * g + 2] * inv, oacc[d][4 * g + 3] * inv));
+      }
+  }
+}
+
+// fp32: one thread per query, keys in LDS tiles of 32, online softmax in base 2.
+template <int HD>
+__global__ __launch_bounds__(128) void k_attn_f32(const float* __restrict__ Q,
+                                                  const float* __restrict__ Kp,
+                                                  const float* __restrict__ Vt, int n, int ldn,
+                                                  float scale_log2, float* __restrict__ O) {
+  __shared__ float sk[32][HD + 1];
+  __shared__ float sv[32][HD + 1];
+  const int h = blockIdx.y, H = gridDim.y;
+  const int qi = blockIdx.x * 128 + threadIdx.x;
+  const float* qr = Q + ((size_t)h * ldn + qi) * HD;
+  float q[HD], acc[HD];
+#pragma unroll
+  for (int d = 0; d < HD; ++d) {
+    q[d] = qr[d];
+    acc[d] = 0.0f;
+  }
+  float m = -INFINITY, l = 0.0f;
+  for (int k0 = 0; k0 < n; k0 += 32) {
+    for (int e = threadIdx.x; e < 32 * HD; e += 128) {
+      int j = e / HD, d = e % HD;
+      sk[j][d] = Kp[((size_t)h * ldn + k0 + j) * HD + d];
+      int d2 = e / 32, j2 = e % 32;
+      sv[j2][d2] = Vt[((size_t)h * HD + d2) * ldn + k0 + j2];
+    }
+    __syncthreads();
+    const int kn = min(32, n - k0);
+    float sc[32];
+    float mx = m;
+    for (int j = 0; j < kn; ++j) {
+      float s = 0.0f;
+#pragma unroll
+      for (int d = 0; d < HD; ++d) s = fmaf(q[d], sk[j][d], s);
+      sc[j] = s * scale_log2;
+      mx = fmaxf(mx, sc[j]);
+    }
+    const float alpha = exp2f(m - mx);
+    l *= alpha;
+#pragma unroll
+    for (int d = 0; d < HD; ++d) acc[d] *= alpha;
+    for (int j = 0; j < kn; ++j) {
+      float p = exp2f(sc[j] - mx);
+      l += p;
+#pragma unroll
+      for (int d = 0; d < HD; ++d) acc[d] = fmaf(p, sv[j][d], acc[d]);
+    }
+    m = mx;
+    __syncthreads();
+  }
+  if (qi < n) {
+    float inv = 1.0f / l;
+    float* orow = O + (size_t)qi * (H * HD) + h * HD;
+#pragma unroll
+    for (int d = 0; d < HD; ++d) orow[d] = acc[d] * inv;
+  }
+}
+
+hipError_t attention(int dtype, int hd, const void* q, const void* k, const void* vt, int n,
+                     int ldn, int H, float scale_log2, void* o, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid((n + 127) / 128, H);
+  if (dtype == BF16) {
+    if (hd == 128)
+      k_attn_bf16<128><<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt,
+                                            n, ldn, scale_log2, (bf16_t*)o);
+    else
+      k_attn_bf16<64><<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt,
+                                           n, ldn, scale_log2, (bf16_t*)o);
+  } else {
+    if (hd == 128)
+      k_attn_f32<128><<<grid, 128, 0, s>>>((const float*)q, (const float*)k, (const float*)vt, n,
+                                           ldn, scale_log2, (float*)o);
+    else
+      k_attn_f32<64><<<grid, 128, 0, s>>>((const float*)q, (const float*)k, (const float*)vt, n,
+                                          ldn, scale_log2, (float*)o);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dit

@@ -1,0 +1,495 @@
+// Bandwidth-bound kernels of the block: adaLN interpolation, pre-norm +
+// modulate, sandwich residual, RoPE table, qk-norm/RoPE head split, weight prep.
+//
+// Citation tags: [MMH3] docs.rs source page of cortiq-engine 0.5.72,
+// src/mmh3.rs; [SIGLIP] ffai-argus 0.7.0, src/siglip.rs; [ZIMG] ollama's
+// zimage transformer.go.
+#include "dev_common.h"
+#include "dit_kernels.h"
+
+namespace dit {
+
+// ------------------------------------------------------------------------------
+// adaLN: mods[j] = bias[j] + sum_k basis[j, k] * c_s[k], s = j / per_slot,
+// c_s = table[i0_s] + f_s * (table[i0_s + 1] - table[i0_s])   ([MMH3] Adaln::eval)
+// One thread per flat element j; the basis row is read as rank/4 float4.
+// ------------------------------------------------------------------------------
+template <int RANK4>
+__global__ __launch_bounds__(256) void k_adaln_interp(const float* __restrict__ basis,
+                                                      const float* __restrict__ bias,
+                                                      const float* __restrict__ table,
+                                                      int rank, int per_slot, int total,
+                                                      SlotCoords sc, float* __restrict__ mods) {
+  int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= total) return;
+  int s = j / per_slot;
+  const float* t0 = table + (size_t)sc.i0[s] * rank;
+  const float* t1 = t0 + rank;
+  float f = sc.f[s];
+  float acc = bias ? bias[j] : 0.0f;
+  if (RANK4 > 0) {
+    const float4* b4 = (const float4*)(basis + (size_t)j * rank);
+    const float4* a4 = (const float4*)t0;
+    const float4* c4 = (const float4*)t1;
+#pragma unroll
+    for (int q = 0; q < RANK4; ++q) {
+      float4 b = b4[q], a = a4[q], c = c4[q];
+      acc += b.x * (a.x + f * (c.x - a.x));
+      acc += b.y * (a.y + f * (c.y - a.y));
+      acc += b.z * (a.z + f * (c.z - a.z));
+      acc += b.w * (a.w + f * (c.w - a.w));
+    }
+  } else {
+    const float* b = basis + (size_t)j * rank;
+    for (int k = 0; k < rank; ++k) acc += b[k] * (t0[k] + f * (t1[k] - t0[k]));
+  }
+  mods[j] = acc;
+}
+
+hipError_t adaln_interp(const float* basis, const float* bias, const float* table, int rank,
+                        int per_slot, int slots, const SlotCoords& sc, float* mods,
+                        hipStream_t s) {
+  int total = per_slot * slots;
+  dim3 grid((total + 255) / 256);
+  if (rank == 24)
+    k_adaln_interp<6><<<grid, 256, 0, s>>>(basis, bias, table, rank, per_slot, total, sc, mods);
+  else
+    k_adaln_interp<0><<<grid, 256, 0, s>>>(basis, bias, table, rank, per_slot, total, sc, mods);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------
+// Z-Image timestep embedding and adaLN ([ZIMG] TimestepEmbedder.Forward and
+// TransformerBlock.Forward): e = [cos(t f_i) | sin(t f_i)], f_i =
+// exp(-ln(10000) i / half); h = silu(W1 e + b1); temb = W2 h + b2;
+// mods = Wa temb + ba.  One thread per output of each dense layer.
+// ------------------------------------------------------------------------------
+__global__ void k_temb_l1(double t, int freq, int hidden, const float* __restrict__ w1,
+                          const float* __restrict__ b1, float* __restrict__ h) {
+  int o = blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= hidden) return;
+  int half = freq / 2;
+  const float* w = w1 + (size_t)o * freq;
+  double acc = 0.0;
+  for (int i = 0; i < half; ++i) {
+    double f = exp(-log(10000.0) * (double)i / (double)half);
+    double a = t * f;
+    acc += (double)w[i] * cos(a) + (double)w[half + i] * sin(a);
+  }
+  float v = (float)acc + (b1 ? b1[o] : 0.0f);
+  h[o] = v / (1.0f + expf(-v));
+}
+
+__global__ void k_dense(const float* __restrict__ x, int in, int out, const float* __restrict__ w,
+                        const float* __restrict__ b, float* __restrict__ y) {
+  int o = blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= out) return;
+  const float* wr = w + (size_t)o * in;
+  float acc = 0.0f;
+  for (int i = 0; i < in; ++i) acc += wr[i] * x[i];
+  y[o] = acc + (b ? b[o] : 0.0f);
+}
+
+hipError_t temb_mods(double t_scaled, int freq, int hidden, int out_dim, const float* w1,
+                     const float* b1, const float* w2, const float* b2, const float* wa,
+                     const float* ba, float* scratch, float* mods, hipStream_t s) {
+  float* h = scratch;
+  float* temb = scratch + hidden;
+  k_temb_l1<<<(hidden + 255) / 256, 256, 0, s>>>(t_scaled, freq, hidden, w1, b1, h);
+  k_dense<<<(freq + 255) / 256, 256, 0, s>>>(h, hidden, freq, w2, b2, temb);
+  k_dense<<<(out_dim + 255) / 256, 256, 0, s>>>(temb, freq, out_dim, wa, ba, mods);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------
+// Pre-norm + modulate, one wave per token row, the row held in registers
+// ([MMH3] norm_rows + modulate; [SIGLIP] layer_norm; [ZIMG] RMSNorm * (1 + scale)).
+//   RMS:   y = x / sqrt(mean(x^2) + eps) * g
+//   LAYER: y = (x - mean) / sqrt(var + eps) * g + beta   (two passes in registers)
+//   then y * (1 + mods[r, scale]) (+ mods[r, shift]).
+// ------------------------------------------------------------------------------
+constexpr int kMaxChunks = 16;  // D <= 4096: 1024 float4 per row, 16 per lane
+
+template <int NORM, int MOD, typename OutT>
+__global__ __launch_bounds__(256) void k_norm_mod(const float* __restrict__ x, int n, int D,
+                                                  const float* __restrict__ g,
+                                                  const float* __restrict__ beta, float eps,
+                                                  const float* __restrict__ mods, int mstride,
+                                                  const int* __restrict__ rows, int shift_off,
+                                                  int scale_off, OutT* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const int nc = D >> 2;
+  const float4* xr = (const float4*)(x + (size_t)row * D);
+  float4 v[kMaxChunks];
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    int i = lane + 64 * c;
+    if (i < nc) {
+      v[c] = xr[i];
+      s += (NORM == NORM_RMS) ? (v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w)
+                              : (v[c].x + v[c].y + v[c].z + v[c].w);
+    }
+  }
+  s = wave_sum(s);
+  float mean = 0.0f, inv;
+  if (NORM == NORM_RMS) {
+    inv = 1.0f / sqrtf(s / (float)D + eps);
+  } else {
+    mean = s / (float)D;
+    float q = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      int i = lane + 64 * c;
+      if (i < nc) {
+        float a = v[c].x - mean, b = v[c].y - mean, cc = v[c].z - mean, d = v[c].w - mean;
+        q += a * a + b * b + cc * cc + d * d;
+      }
+    }
+    q = wave_sum(q);
+    inv = 1.0f / sqrtf(q / (float)D + eps);
+  }
+  const float* mrow = nullptr;
+  if (MOD != MOD_NONE) mrow = mods + (size_t)(rows ? rows[row] : 0) * mstride;
+  const float4* g4 = (const float4*)g;
+  OutT* yr = y + (size_t)row * D;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    int i = lane + 64 * c;
+    if (i < nc) {
+      float4 gg = g4[i];
+      float4 o;
+      o.x = (v[c].x - mean) * inv * gg.x;
+      o.y = (v[c].y - mean) * inv * gg.y;
+      o.z = (v[c].z - mean) * inv * gg.z;
+      o.w = (v[c].w - mean) * inv * gg.w;
+      if (NORM == NORM_LAYER) {
+        float4 bb = ((const float4*)beta)[i];
+        o.x += bb.x; o.y += bb.y; o.z += bb.z; o.w += bb.w;
+      }
+      if (MOD != MOD_NONE) {
+        float4 sc = ((const float4*)(mrow + scale_off))[i];
+        o.x *= 1.0f + sc.x; o.y *= 1.0f + sc.y; o.z *= 1.0f + sc.z; o.w *= 1.0f + sc.w;
+        if (MOD == MOD_SHIFT_SCALE) {
+          float4 sh = ((const float4*)(mrow + shift_off))[i];
+          o.x += sh.x; o.y += sh.y; o.z += sh.z; o.w += sh.w;
+        }
+      }
+      Elt<OutT>::st4(yr + 4 * i, o);
+    }
+  }
+}
+
+template <int NORM, int MOD>
+static void launch_norm_mod(bool out_bf16, const float* x, int n, int D, const float* g,
+                            const float* beta, float eps, const float* mods, int mstride,
+                            const int* rows, int so, int sc, void* y, hipStream_t s) {
+  dim3 grid((n + 3) / 4);
+  if (out_bf16)
+    k_norm_mod<NORM, MOD, bf16_t><<<grid, 256, 0, s>>>(x, n, D, g, beta, eps, mods, mstride, rows,
+                                                        so, sc, (bf16_t*)y);
+  else
+    k_norm_mod<NORM, MOD, float><<<grid, 256, 0, s>>>(x, n, D, g, beta, eps, mods, mstride, rows,
+                                                       so, sc, (float*)y);
+}
+
+hipError_t norm_mod(int norm, int mod, bool out_bf16, const float* x, int n, int D, const float* g,
+                    const float* beta, float eps, const float* mods, int mstride, const int* rows,
+                    int shift_off, int scale_off, void* y, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+#define NM(N_, M_) launch_norm_mod<N_, M_>(out_bf16, x, n, D, g, beta, eps, mods, mstride, rows, shift_off, scale_off, y, s)
+  if (norm == NORM_RMS) {
+    if (mod == MOD_NONE) NM(NORM_RMS, MOD_NONE);
+    else if (mod == MOD_SHIFT_SCALE) NM(NORM_RMS, MOD_SHIFT_SCALE);
+    else NM(NORM_RMS, MOD_SCALE);
+  } else {
+    if (mod == MOD_NONE) NM(NORM_LAYER, MOD_NONE);
+    else if (mod == MOD_SHIFT_SCALE) NM(NORM_LAYER, MOD_SHIFT_SCALE);
+    else NM(NORM_LAYER, MOD_SCALE);
+  }
+#undef NM
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------
+// Sandwich residual ([ZIMG] TransformerBlock.Forward):
+//   x1 = x + tanh(gate) * RMSNorm(y; g_post), and when g_next is given
+//   xf = RMSNorm(x1; g_next) * (1 + scale) for the next half.
+// ------------------------------------------------------------------------------
+template <typename OutT>
+__global__ __launch_bounds__(256) void k_sandwich(const float* __restrict__ x,
+                                                  const float* __restrict__ y, int n, int D,
+                                                  const float* __restrict__ g_post,
+                                                  const float* __restrict__ gate, float eps,
+                                                  float* __restrict__ x1,
+                                                  const float* __restrict__ g_next,
+                                                  const float* __restrict__ scale,
+                                                  OutT* __restrict__ xf) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const int nc = D >> 2;
+  const float4* yr = (const float4*)(y + (size_t)row * D);
+  const float4* xr = (const float4*)(x + (size_t)row * D);
+  float4 v[kMaxChunks];
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    int i = lane + 64 * c;
+    if (i < nc) {
+      v[c] = yr[i];
+      s += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+    }
+  }
+  float inv = 1.0f / sqrtf(wave_sum(s) / (float)D + eps);
+  float s2 = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    int i = lane + 64 * c;
+    if (i < nc) {
+      float4 xx = xr[i], gp = ((const float4*)g_post)[i], gt = ((const float4*)gate)[i];
+      float4 o;
+      o.x = xx.x + tanh_f(gt.x) * (v[c].x * inv * gp.x);
+      o.y = xx.y + tanh_f(gt.y) * (v[c].y * inv * gp.y);
+      o.z = xx.z + tanh_f(gt.z) * (v[c].z * inv * gp.z);
+      o.w = xx.w + tanh_f(gt.w) * (v[c].w * inv * gp.w);
+      ((float4*)(x1 + (size_t)row * D))[i] = o;
+      v[c] = o;
+      s2 += o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+    }
+  }
+  if (g_next == nullptr) return;
+  float inv2 = 1.0f / sqrtf(wave_sum(s2) / (float)D + eps);
+  OutT* fr = xf + (size_t)row * D;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    int i = lane + 64 * c;
+    if (i < nc) {
+      float4 gn = ((const float4*)g_next)[i], sc = ((const float4*)scale)[i];
+      float4 o;
+      o.x = v[c].x * inv2 * gn.x * (1.0f + sc.x);
+      o.y = v[c].y * inv2 * gn.y * (1.0f + sc.y);
+      o.z = v[c].z * inv2 * gn.z * (1.0f + sc.z);
+      o.w = v[c].w * inv2 * gn.w * (1.0f + sc.w);
+      Elt<OutT>::st4(fr + 4 * i, o);
+    }
+  }
+}
+
+hipError_t sandwich(const float* x, const float* y, int n, int D, const float* g_post,
+                    const float* gate, float eps, float* x1, const float* g_next,
+                    const float* scale, bool xf_bf16, void* xf, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid((n + 3) / 4);
+  if (xf_bf16)
+    k_sandwich<bf16_t><<<grid, 256, 0, s>>>(x, y, n, D, g_post, gate, eps, x1, g_next, scale,
+                                             (bf16_t*)xf);
+  else
+    k_sandwich<float><<<grid, 256, 0, s>>>(x, y, n, D, g_post, gate, eps, x1, g_next, scale,
+                                            (float*)xf);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------
+// RoPE table: angle (i, j) = pos[i, a] * theta^(-2m/d_a) for pair j = (axis a,
+// frequency m), axes concatenated t, h, w ([MMH3] rope_angles; per-axis
+// frequencies as [ZIMG] prepareRoPE3D).  Angles and their cos/sin are taken in
+// fp64 and stored as fp32 (cos, sin).
+// ------------------------------------------------------------------------------
+__global__ void k_rope_table(const float* __restrict__ pos, int n, int P, int d0, int d1, int d2,
+                             double theta, float2* __restrict__ cs) {
+  int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n * P) return;
+  int i = idx / P, j = idx - i * P;
+  int a, m, d;
+  if (j < d0 / 2) {
+    a = 0; m = j; d = d0;
+  } else if (j < d0 / 2 + d1 / 2) {
+    a = 1; m = j - d0 / 2; d = d1;
+  } else {
+    a = 2; m = j - d0 / 2 - d1 / 2; d = d2;
+  }
+  double omega = pow(theta, -2.0 * (double)m / (double)d);
+  double ang = (double)pos[(size_t)i * 3 + a] * omega;
+  double sn, cn;
+  sincos(ang, &sn, &cn);
+  cs[idx] = make_float2((float)cn, (float)sn);
+}
+
+hipError_t rope_table(const float* pos, int n, int P, const int axes[3], double theta, float* cs,
+                      hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int total = n * P;
+  k_rope_table<<<(total + 255) / 256, 256, 0, s>>>(pos, n, P, axes[0], axes[1], axes[2], theta,
+                                                    (float2*)cs);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------
+// Head split of the fused qkv panel with qk-RMSNorm and RoPE on q and k
+// ([MMH3] norm_rope_w; qk-norm before rotary as [ENC] rms_norm_heads).
+// One wave per (token, head, q|k); lane p owns rotation pair p.  q is scaled by
+// q_scale (the softmax's hd^-1/2) after the rotation.  Tokens in [n, ldn) are
+// written as zeros so attention reads finite padding.
+// ------------------------------------------------------------------------------
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void k_qk_split(const T* __restrict__ qkv, int n, int ldn, int H,
+                                                  const float* __restrict__ qn,
+                                                  const float* __restrict__ kn, float eps,
+                                                  const float2* __restrict__ cs, int rope_mode,
+                                                  float q_scale, T* __restrict__ q_out,
+                                                  T* __restrict__ k_out) {
+  constexpr int P = HD / 2;
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int h = blockIdx.y, which = blockIdx.z;
+  if (tok >= ldn) return;
+  const int D = H * HD;
+  T* dst = (which ? k_out : q_out) + ((size_t)h * ldn + tok) * HD;
+  const bool act = lane < P;
+  int ia, ib;
+  if (rope_mode == 2) {
+    ia = 2 * lane; ib = 2 * lane + 1;
+  } else {
+    ia = lane; ib = lane + P;
+  }
+  if (tok >= n) {
+    if (act) {
+      Elt<T>::st(dst + ia, 0.0f);
+      Elt<T>::st(dst + ib, 0.0f);
+    }
+    return;
+  }
+  const T* src = qkv + (size_t)tok * 3 * D + which * D + h * HD;
+  float a = 0.0f, b = 0.0f;
+  if (act) {
+    a = Elt<T>::ld(src + ia);
+    b = Elt<T>::ld(src + ib);
+  }
+  const float* g = which ? kn : qn;
+  if (g) {
+    float ss = wave_sum(a * a + b * b);
+    float inv = 1.0f / sqrtf(ss / (float)HD + eps);
+    if (act) {
+      a = a * inv * g[ia];
+      b = b * inv * g[ib];
+    }
+  }
+  if (act && rope_mode != 0) {
+    float2 c = cs[(size_t)tok * P + lane];
+    float ra = a * c.x - b * c.y;
+    float rb = a * c.y + b * c.x;
+    a = ra;
+    b = rb;
+  }
+  if (which == 0) {
+    a *= q_scale;
+    b *= q_scale;
+  }
+  if (act) {
+    Elt<T>::st(dst + ia, a);
+    Elt<T>::st(dst + ib, b);
+  }
+}
+
+// V part of the panel, transposed per head: vt[h, d, tok], zeros for tok >= n.
+template <typename T>
+__global__ __launch_bounds__(256) void k_v_transpose(const T* __restrict__ qkv, int n, int ldn,
+                                                     int H, int HD, T* __restrict__ vt) {
+  __shared__ float tile[64][65];
+  const int t0 = blockIdx.x * 64, d0 = blockIdx.y * 64, h = blockIdx.z;
+  const int D = H * HD;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    int tok = t0 + r;
+    float v = 0.0f;
+    if (tok < n) v = Elt<T>::ld(qkv + (size_t)tok * 3 * D + 2 * D + h * HD + d0 + tx);
+    tile[r][tx] = v;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    int d = d0 + r;
+    int tok = t0 + tx;
+    if (tok < ldn) Elt<T>::st(vt + ((size_t)h * HD + d) * ldn + tok, tile[tx][r]);
+  }
+}
+
+template <typename T>
+static void launch_split(int hd, const void* qkv, int n, int ldn, int H, const float* qn,
+                         const float* kn, float eps, const float* cs, int rope_mode,
+                         float q_scale, void* q, void* k, void* vt, hipStream_t s) {
+  dim3 g1((ldn + 3) / 4, H, 2);
+  if (hd == 128)
+    k_qk_split<T, 128><<<g1, 256, 0, s>>>((const T*)qkv, n, ldn, H, qn, kn, eps,
+                                          (const float2*)cs, rope_mode, q_scale, (T*)q, (T*)k);
+  else
+    k_qk_split<T, 64><<<g1, 256, 0, s>>>((const T*)qkv, n, ldn, H, qn, kn, eps,
+                                         (const float2*)cs, rope_mode, q_scale, (T*)q, (T*)k);
+  dim3 g2(ldn / 64, hd / 64, H);
+  k_v_transpose<T><<<g2, 256, 0, s>>>((const T*)qkv, n, ldn, H, hd, (T*)vt);
+}
+
+hipError_t qk_split(int dtype, int hd, const void* qkv, int n, int ldn, int H, const float* qn,
+                    const float* kn, float eps, const float* cs, int rope_mode, float q_scale,
+                    void* q, void* k, void* vt, hipStream_t s) {
+  if (ldn <= 0) return hipSuccess;
+  if (dtype == BF16)
+    launch_split<bf16_t>(hd, qkv, n, ldn, H, qn, kn, eps, cs, rope_mode, q_scale, q, k, vt, s);
+  else
+    launch_split<float>(hd, qkv, n, ldn, H, qn, kn, eps, cs, rope_mode, q_scale, q, k, vt, s);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------
+// Weight preparation: row permutation (SwiGLU group interleave) and scaling.
+// Prepared row r of fc1 (N = 2F rows): group g = r / 64, j = r % 64;
+// j < 32 -> gate row 32 g + j, else up row F + 32 g + (j - 32).
+// ------------------------------------------------------------------------------
+template <typename T>
+__global__ void k_prep_matrix(const T* __restrict__ src, T* __restrict__ dst, int rows, int cols,
+                              int swiglu_F, int scale_rows, float scale) {
+  size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t total = (size_t)rows * cols;
+  if (idx >= total) return;
+  int r = (int)(idx / cols), c = (int)(idx - (size_t)r * cols);
+  int sr = r;
+  if (swiglu_F > 0) {
+    int g = r >> 6, j = r & 63;
+    sr = (j < 32) ? (32 * g + j) : (swiglu_F + 32 * g + (j - 32));
+  }
+  float v = Elt<T>::ld(src + (size_t)sr * cols + c);
+  if (r < scale_rows) v *= scale;
+  Elt<T>::st(dst + idx, v);
+}
+
+hipError_t prep_matrix(int dtype, const void* src, void* dst, int rows, int cols, int swiglu_F,
+                       int scale_rows, float scale, hipStream_t s) {
+  size_t total = (size_t)rows * cols;
+  dim3 grid((unsigned)((total + 255) / 256));
+  if (dtype == BF16)
+    k_prep_matrix<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)src, (bf16_t*)dst, rows, cols,
+                                                swiglu_F, scale_rows, scale);
+  else
+    k_prep_matrix<float><<<grid, 256, 0, s>>>((const float*)src, (float*)dst, rows, cols,
+                                               swiglu_F, scale_rows, scale);
+  return hipGetLastError();
+}
+
+__global__ void k_prep_vector(const float* __restrict__ src, float* __restrict__ dst, int n,
+                              int scale_n, float scale) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float v = src ? src[i] : 0.0f;
+  dst[i] = (i < scale_n) ? v * scale : v;
+}
+
+hipError_t prep_vector(const float* src, float* dst, int n, int scale_n, float scale,
+                       hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_prep_vector<<<(n + 255) / 256, 256, 0, s>>>(src, dst, n, scale_n, scale);
+  return hipGetLastError();
+}
+
+}  // namespace dit

@@ -1,0 +1,253 @@
+"""ctypes binding of libdit.so (the C ABI declared in include/dit.h).
+
+Argument marshalling only: every step of the block runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  If the
+library has not been built, importing this module raises: there is no CPU
+fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_double, c_float, c_int32, c_size_t, c_void_p
+from typing import Dict, List, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdit.so")
+
+MMH3, SIGLIP, ZIMAGE = 0, 1, 2
+F32, BF16 = 0, 1
+ROPE_NONE, ROPE_SPLIT_HALF, ROPE_INTERLEAVED = 0, 1, 2
+NPHASES = 9
+
+_VARIANTS = {"mmh3": MMH3, "siglip": SIGLIP, "zimage": ZIMAGE}
+_DTYPES = {"f32": F32, "bf16": BF16}
+_ROPES = {"none": ROPE_NONE, "split_half": ROPE_SPLIT_HALF, "interleaved": ROPE_INTERLEAVED}
+
+STATUS = {0: "DIT_OK", -1: "DIT_EINVAL", -2: "DIT_ESHAPE", -3: "DIT_EDTYPE", -4: "DIT_EALIGN",
+          -5: "DIT_EWORKSPACE", -6: "DIT_EUNSUPPORTED", -7: "DIT_EHIP"}
+
+
+class DitConfig(ctypes.Structure):
+    _fields_ = [("variant", c_int32), ("dtype", c_int32), ("D", c_int32), ("H", c_int32),
+                ("hd", c_int32), ("F", c_int32), ("slots", c_int32), ("tags", c_int32),
+                ("rank", c_int32), ("grid", c_int32), ("rope", c_int32),
+                ("rope_axes", c_int32 * 3), ("rope_theta", c_double), ("eps", c_float),
+                ("qk_eps", c_float), ("temb_freq", c_int32), ("temb_hidden", c_int32),
+                ("t_scale", c_float)]
+
+
+WEIGHT_FIELDS = ["norm1", "norm2", "ln1_b", "ln2_b", "post_attn_norm", "post_ffn_norm",
+                 "w_qkv", "w_out", "w_fc1", "w_fc2", "b_qkv", "b_out", "b_fc1", "b_fc2",
+                 "q_norm", "k_norm", "adaln_basis", "adaln_bias", "adaln_table",
+                 "temb_w1", "temb_b1", "temb_w2", "temb_b2", "ada_w", "ada_b"]
+
+
+class DitWeights(ctypes.Structure):
+    _fields_ = [(f, c_void_p) for f in WEIGHT_FIELDS]
+
+
+class DitWsLayout(ctypes.Structure):
+    _fields_ = [(f, c_size_t) for f in ("mods", "rope", "xn", "qkv", "q", "k", "vt", "o", "x1",
+                                         "a", "y", "temb", "total")] + [("ldn", c_int32)]
+
+
+NONE_OFFSET = (1 << (8 * ctypes.sizeof(c_size_t))) - 1
+
+
+class DitError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run packed_sequence_diffusion_amd.build "
+                          "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = POINTER
+    sig = {
+        "dit_abi_version": (c_int32, []),
+        "dit_last_error": (ctypes.c_char_p, []),
+        "dit_sigma_remap": (c_double, [c_double, c_double, c_double]),
+        "dit_sigma_remap_slope": (c_double, [c_double, c_double, c_double]),
+        "dit_validate_config": (c_int32, [P(DitConfig)]),
+        "dit_prepared_size": (c_size_t, [P(DitConfig)]),
+        "dit_prepare_weights": (c_int32, [P(DitConfig), P(DitWeights), c_void_p, c_size_t, c_void_p]),
+        "dit_workspace_size": (c_size_t, [P(DitConfig), c_int32]),
+        "dit_workspace_layout": (c_int32, [P(DitConfig), c_int32, P(DitWsLayout)]),
+        "dit_adaln_eval": (c_int32, [P(DitConfig), c_void_p, P(c_double), c_int32, c_void_p,
+                                     c_void_p, c_void_p]),
+        "dit_adaln_modulate": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_int32, c_void_p,
+                                         P(c_double), c_int32, c_int32, c_void_p, c_void_p,
+                                         c_void_p, c_void_p]),
+        "dit_block_forward": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_int32, c_void_p,
+                                        c_void_p, P(c_double), c_int32, c_void_p, c_void_p,
+                                        c_size_t, c_void_p]),
+        "dit_attention": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_void_p, c_int32, c_int32,
+                                    c_float, c_void_p, c_void_p]),
+        "dit_profile_begin": (c_int32, [c_int32]),
+        "dit_profile_end": (c_int32, [P(c_double), P(c_int32)]),
+        "dit_phase_name": (ctypes.c_char_p, [c_int32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise DitError(status, lib.dit_last_error().decode())
+
+
+def last_error() -> str:
+    return lib.dit_last_error().decode()
+
+
+def sigma_remap(sigma: float, from_shift: float, to_shift: float) -> float:
+    return lib.dit_sigma_remap(sigma, from_shift, to_shift)
+
+
+def sigma_remap_slope(sigma: float, from_shift: float, to_shift: float) -> float:
+    return lib.dit_sigma_remap_slope(sigma, from_shift, to_shift)
+
+
+def resolve_sigmas(plan: Sequence[tuple]) -> List[float]:
+    """Slot sigmas from a slot plan; remapped slots go through the library's
+    dit_sigma_remap."""
+    out: List[float] = []
+    for item in plan:
+        if item[0] == "value":
+            out.append(float(item[1]))
+        else:
+            _, src, a, b = item
+            out.append(sigma_remap(out[src], a, b))
+    return out
+
+
+def make_config(spec) -> DitConfig:
+    """DitConfig from any object with the block-shape attributes (variant,
+    dtype, D, H, hd, F, slots, tags, rank, grid, rope, rope_axes, rope_theta,
+    eps, qk_eps, temb_freq, temb_hidden, t_scale)."""
+    c = DitConfig()
+    c.variant = _VARIANTS[spec.variant] if isinstance(spec.variant, str) else int(spec.variant)
+    c.dtype = _DTYPES[spec.dtype] if isinstance(spec.dtype, str) else int(spec.dtype)
+    c.D, c.H, c.hd, c.F = spec.D, spec.H, spec.hd, spec.F
+    c.slots, c.tags, c.rank, c.grid = spec.slots, spec.tags, spec.rank, spec.grid
+    c.rope = _ROPES[spec.rope] if isinstance(spec.rope, str) else int(spec.rope)
+    for i in range(3):
+        c.rope_axes[i] = spec.rope_axes[i]
+    c.rope_theta = spec.rope_theta
+    c.eps, c.qk_eps = spec.eps, spec.qk_eps
+    c.temb_freq, c.temb_hidden, c.t_scale = spec.temb_freq, spec.temb_hidden, spec.t_scale
+    return c
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dbl(vals: Sequence[float]):
+    arr = (c_double * max(len(vals), 1))(*vals)
+    return arr, len(vals)
+
+
+def validate(cfg: DitConfig) -> None:
+    _check(lib.dit_validate_config(ctypes.byref(cfg)))
+
+
+def workspace_layout(cfg: DitConfig, n: int) -> DitWsLayout:
+    L = DitWsLayout()
+    _check(lib.dit_workspace_layout(ctypes.byref(cfg), n, ctypes.byref(L)))
+    return L
+
+
+class Block:
+    """Prepared weights of one block on the current GPU.
+
+    ``weights``: dict of device tensors named as in ``DitWeights`` (GEMM
+    weights in the config's dtype, everything else fp32, all contiguous)."""
+
+    def __init__(self, cfg: DitConfig, weights: Dict[str, "object"], stream=None):
+        import torch
+        validate(cfg)
+        self.cfg = cfg
+        w = DitWeights()
+        for f in WEIGHT_FIELDS:
+            t = weights.get(f)
+            if t is not None and not t.is_contiguous():
+                raise ValueError(f"weight {f} must be contiguous")
+            setattr(w, f, _ptr(t))
+        nbytes = lib.dit_prepared_size(ctypes.byref(cfg))
+        self.prepared = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        _check(lib.dit_prepare_weights(ctypes.byref(cfg), ctypes.byref(w), self.prepared.data_ptr(),
+                                       nbytes, _stream(stream)))
+        self._ws = None
+
+    def workspace(self, n: int):
+        import torch
+        need = lib.dit_workspace_size(ctypes.byref(self.cfg), n)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        return self._ws
+
+    def forward(self, x, rows, pos, sigmas: Sequence[float], out=None, workspace=None,
+                stream=None):
+        import torch
+        n = int(x.shape[0])
+        if out is None:
+            out = torch.empty_like(x)
+        ws = self.workspace(n) if workspace is None else workspace
+        sg, ns = _dbl(sigmas)
+        _check(lib.dit_block_forward(ctypes.byref(self.cfg), self.prepared.data_ptr(), _ptr(x), n,
+                                     _ptr(rows), _ptr(pos), sg, ns, _ptr(out), ws.data_ptr(),
+                                     ws.numel(), _stream(stream)))
+        return out
+
+    def adaln_modulate(self, x, rows, sigmas: Sequence[float], half: int, xn_out, mods_out=None,
+                       temb_scratch=None, stream=None):
+        n = int(x.shape[0])
+        sg, ns = _dbl(sigmas)
+        _check(lib.dit_adaln_modulate(ctypes.byref(self.cfg), self.prepared.data_ptr(), _ptr(x), n,
+                                      _ptr(rows), sg, ns, half, _ptr(xn_out), _ptr(mods_out),
+                                      _ptr(temb_scratch), _stream(stream)))
+        return xn_out
+
+    def adaln_eval(self, sigmas: Sequence[float], mods_out, temb_scratch=None, stream=None):
+        sg, ns = _dbl(sigmas)
+        _check(lib.dit_adaln_eval(ctypes.byref(self.cfg), self.prepared.data_ptr(), sg, ns,
+                                  _ptr(mods_out), _ptr(temb_scratch), _stream(stream)))
+        return mods_out
+
+
+def attention(cfg: DitConfig, q, k, vt, n: int, ldn: int, score_scale: float, o, stream=None):
+    _check(lib.dit_attention(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(vt), n, ldn, score_scale,
+                             _ptr(o), _stream(stream)))
+    return o
+
+
+def profile_begin(max_calls: int) -> None:
+    _check(lib.dit_profile_begin(max_calls))
+
+
+def profile_end() -> Dict[str, float]:
+    """Summed ms per phase over the recorded calls (plus "calls")."""
+    ms = (c_double * NPHASES)()
+    calls = c_int32(0)
+    _check(lib.dit_profile_end(ms, ctypes.byref(calls)))
+    out = {lib.dit_phase_name(i).decode(): ms[i] for i in range(NPHASES)}
+    out["calls"] = calls.value
+    return out

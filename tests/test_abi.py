@@ -1,0 +1,151 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, and refuses bad arguments on the host before any launch (no
+GPU call is made: every case fails validation)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from synth import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit.h")
+LIB = os.path.join(ROOT, "packed_sequence_diffusion_amd", "libdit.so")
+
+
+@pytest.fixture(scope="module")
+def dit():
+    if not os.path.exists(LIB):
+        from packed_sequence_diffusion_amd import build
+        build.build()
+    from packed_sequence_diffusion_amd import dit as d
+    return d
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(dit_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_header_functions_exported(dit):
+    names = declared_functions()
+    assert len(names) >= 15
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (dit_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(dit.lib, n)
+
+
+def test_abi_version(dit):
+    assert dit.lib.dit_abi_version() == 1
+
+
+def test_sigma_remap_printed_points(dit):
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "sigma_remap.json")))
+    for s in g["involution_points"]:
+        a = dit.sigma_remap(s, 12.0, 3.0)
+        assert abs(dit.sigma_remap(a, 3.0, 12.0) - s) < g["involution_tol"]
+        assert abs(a - s / (4.0 - 3.0 * s)) < 1e-14
+    h = g["slope_step"]
+    for s in g["slope_points"]:
+        num = (dit.sigma_remap(s + h, 12.0, 3.0) - dit.sigma_remap(s - h, 12.0, 3.0)) / (2 * h)
+        assert abs(num - dit.sigma_remap_slope(s, 12.0, 3.0)) < g["slope_tol"]
+
+
+def test_configs_validate(dit):
+    for spec in W.SPECS:
+        dit.validate(dit.make_config(spec))
+        assert dit.lib.dit_prepared_size(ctypes.byref(dit.make_config(spec))) > 0
+
+
+def _cfg(dit, **kw):
+    spec = W.spec_by_name("t2va")
+    c = dit.make_config(spec)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("hd", 96, -6), ("D", 2560, -2), ("dtype", 7, -3), ("variant", 9, -1), ("slots", 0, -6),
+    ("slots", 9, -6), ("F", 100, -6), ("rank", 0, -6), ("grid", 1, -1), ("rope", 5, -1),
+])
+def test_config_refusals(dit, field, value, status):
+    c = _cfg(dit, **{field: value})
+    assert dit.lib.dit_validate_config(ctypes.byref(c)) == status
+    assert dit.last_error()
+    assert dit.lib.dit_prepared_size(ctypes.byref(c)) == 0
+
+
+def test_rope_axes_must_sum_to_head_dim(dit):
+    c = _cfg(dit)
+    c.rope_axes[0] = 30
+    assert dit.lib.dit_validate_config(ctypes.byref(c)) == -2
+
+
+def test_workspace_layout_monotone(dit):
+    c = _cfg(dit)
+    L = dit.workspace_layout(c, 25600)
+    assert L.ldn == 25600
+    offs = [L.mods, L.rope, L.xn, L.qkv, L.q, L.k, L.vt, L.o, L.x1, L.a]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert L.y == dit.NONE_OFFSET
+    assert dit.lib.dit_workspace_size(ctypes.byref(c), 25600) == L.total
+    assert dit.workspace_layout(c, 333).ldn == 384
+
+
+def _fwd(dit, c, x=16, n=10, rows=16, pos=16, sig=(0.5, 0.2), out=16, ws=256, wsb=1 << 40,
+         prep=256):
+    arr = (ctypes.c_double * 2)(*sig)
+    return dit.lib.dit_block_forward(ctypes.byref(c), prep, x, n, rows, pos, arr, len(sig), out,
+                                     ws, wsb, None)
+
+
+def test_block_forward_refusals(dit):
+    c = _cfg(dit)
+    assert _fwd(dit, c, n=-1) == -2
+    assert _fwd(dit, c, prep=None) == -1
+    assert _fwd(dit, c, sig=(0.5,)) == -2
+    assert _fwd(dit, c, sig=(float("nan"), 0.2)) == -1
+    assert _fwd(dit, c, x=None) == -1
+    assert _fwd(dit, c, x=8) == -4
+    assert _fwd(dit, c, pos=None) == -1
+    assert _fwd(dit, c, ws=None) == -1
+    assert _fwd(dit, c, ws=128) == -4
+    assert _fwd(dit, c, wsb=1024) == -5
+    assert "workspace" in dit.last_error()
+    # n == 0 is a valid no-op: returns before touching anything
+    assert _fwd(dit, c, n=0, x=None, out=None, ws=None) == 0
+
+
+def test_prepare_refusals(dit):
+    c = _cfg(dit)
+    w = dit.DitWeights()
+    assert dit.lib.dit_prepare_weights(ctypes.byref(c), ctypes.byref(w), 256, 1 << 40, None) == -1
+    need = dit.lib.dit_prepared_size(ctypes.byref(c))
+    assert dit.lib.dit_prepare_weights(ctypes.byref(c), ctypes.byref(w), 256, need - 1, None) == -5
+    assert dit.lib.dit_prepare_weights(ctypes.byref(c), ctypes.byref(w), 16, need, None) == -4
+
+
+def test_attention_refusals(dit):
+    c = _cfg(dit)
+    L = dit.lib.dit_attention
+    assert L(ctypes.byref(c), 16, 16, 16, 100, 100, 1.0, 16, None) == -2  # ldn % 128
+    assert L(ctypes.byref(c), 16, 16, 16, 300, 256, 1.0, 16, None) == -2  # ldn < n
+    assert L(ctypes.byref(c), None, 16, 16, 10, 128, 1.0, 16, None) == -1
+    assert L(ctypes.byref(c), 16, 16, 16, 0, 128, 1.0, 16, None) == 0
+
+
+def test_profile_arming(dit):
+    ms = (ctypes.c_double * dit.NPHASES)()
+    calls = ctypes.c_int32(0)
+    assert dit.lib.dit_profile_end(ms, ctypes.byref(calls)) == -1
+    assert dit.lib.dit_profile_begin(0) == -1
+    assert [dit.lib.dit_phase_name(i).decode() for i in range(dit.NPHASES)][4] == "attention"

@@ -115,15 +115,18 @@ def test_small_ragged(dit, variant, dtype, n, D, hd, F):
     _check(spec.name, spec, wl, dit)
 
 
-@pytest.mark.parametrize("gain", [4.0, 8.0])
-def test_peaky_attention(dit, gain):
-    """qk-norm gains scaled up make the softmax peaky: exercises the online
-    max rescaling across key tiles."""
+def test_peakier_block_attention(dit):
+    """qk-norm gains x2: logits with std ~4 instead of ~1 through the whole
+    block.  (Much larger gains make the logits' own bf16 input rounding -- the
+    q and k panels are bf16 -- the dominant error: a relative rounding of
+    2^-9 on q and k moves a logit of size s by ~s * 2^-8.  The attention
+    kernel's handling of peaky rows is checked on exactly representable
+    inputs in test_standalone_attention.)"""
     spec = _small("mmh3", "bf16", 450, 256, 128, 256)
     wl = W.make_custom_workload(spec, 77)
-    wl.weights["q_norm"] = wl.weights["q_norm"] * np.float32(gain)
-    wl.weights["k_norm"] = wl.weights["k_norm"] * np.float32(gain)
-    st = _check(f"peaky-x{gain}", spec, wl, dit)
+    wl.weights["q_norm"] = wl.weights["q_norm"] * np.float32(2.0)
+    wl.weights["k_norm"] = wl.weights["k_norm"] * np.float32(2.0)
+    st = _check("peakier-x2", spec, wl, dit)
     assert np.all(np.isfinite(st["o"]))
 
 
@@ -181,16 +184,20 @@ def test_zero_gates_identity(dit):
     assert torch.equal(out.cpu(), torch.from_numpy(wl.x))
 
 
-def test_standalone_attention_extremes(dit):
-    """dit_attention on raw q/k/v with scores spanning [-90, 90] and a ragged n."""
+@pytest.mark.parametrize("hd,n,qnorm", [(128, 300, 90.0), (128, 1000, 8.0), (128, 777, 30.0),
+                                         (64, 515, 40.0), (64, 64, 5.0)])
+def test_standalone_attention(dit, hd, n, qnorm):
+    """dit_attention on raw bf16 q/k/v (the same bf16 values on both sides),
+    |q| = qnorm and unit-norm k, so logits span [-qnorm, qnorm]: peaky rows,
+    several key tiles and a ragged tail."""
     import torch
-    H, hd, n = 3, 128, 300
-    ldn = 384
-    rng = np.random.default_rng(11)
+    H = 3 if hd == 128 else 4  # H * hd a multiple of 128
+    ldn = (n + 127) // 128 * 128
+    rng = np.random.default_rng(11 + n)
     q = rng.standard_normal((H, n, hd)).astype(np.float32)
     k = rng.standard_normal((H, n, hd)).astype(np.float32)
     v = rng.standard_normal((H, n, hd)).astype(np.float32)
-    q *= 90.0 / np.sqrt(np.sum(q * q, axis=-1, keepdims=True))  # |q.k| up to ~90 |k|
+    q *= qnorm / np.sqrt(np.sum(q * q, axis=-1, keepdims=True))
     k /= np.sqrt(np.sum(k * k, axis=-1, keepdims=True))
     from synth.workloads import bf16_round
     q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
@@ -211,5 +218,5 @@ def test_standalone_attention_extremes(dit):
     ref = O.attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), 1.0)
     ref = ref.transpose(1, 0, 2).reshape(n, H * hd)
     err = O.rel_rms(o.float().cpu().numpy(), ref)
-    log(f"[case] attention-extremes: rel_rms={err:.2e}")
+    log(f"[case] attention hd={hd} n={n} |q|={qnorm}: rel_rms={err:.2e}")
     assert err <= 1e-2

@@ -8,6 +8,9 @@ typedef uint16_t bf16_t;  // bfloat16 storage
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+// Native 16-byte vector for register staging of tiles (HIP's uint4 is a
+// class with a union, which keeps arrays of it out of registers).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 #define DIT_DEV __device__ __forceinline__
 

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16_t* __restrict__
   for (int c = 0; c < NC; ++c)
     qf[c] = *(const bf16x8_t*)(Qh + (size_t)(q0 + l32) * HD + 16 * c + 8 * half);
 
-  uint4 rk[KPT], rv[VPT];
+  u32x4_t rk[KPT], rv[VPT];
   // K tile [KT][HD]: chunk XOR row%16 (HD=128) or row%8 (HD=64); V^T tile
   // [HD][KT]: chunk XOR row%8.
 #define KOFF(row, ch) ((row) * HD + ((((ch) ^ ((row) & (KCH - 1) & 15))) << 3))
@@ -64,22 +64,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16_t* __restrict__
   do {                                                                             \
     _Pragma("unroll") for (int i = 0; i < KPT; ++i) {                              \
       int c_ = tid + 256 * i, row_ = c_ / KCH, ch_ = c_ % KCH;                     \
-      rk[i] = *(const uint4*)(Kh + (size_t)((k0) + row_) * HD + ch_ * 8);          \
+      rk[i] = *(const u32x4_t*)(Kh + (size_t)((k0) + row_) * HD + ch_ * 8);          \
     }                                                                              \
     _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                              \
       int c_ = tid + 256 * i, row_ = c_ / (KT / 8), ch_ = c_ % (KT / 8);           \
-      rv[i] = *(const uint4*)(Vh + (size_t)row_ * ldn + (k0) + ch_ * 8);           \
+      rv[i] = *(const u32x4_t*)(Vh + (size_t)row_ * ldn + (k0) + ch_ * 8);           \
     }                                                                              \
   } while (0)
 #define ATT_SSTORE(b)                                                              \
   do {                                                                             \
     _Pragma("unroll") for (int i = 0; i < KPT; ++i) {                              \
       int c_ = tid + 256 * i, row_ = c_ / KCH, ch_ = c_ % KCH;                     \
-      *(uint4*)(&sK[b][KOFF(row_, ch_)]) = rk[i];                                  \
+      *(u32x4_t*)(&sK[b][KOFF(row_, ch_)]) = rk[i];                                  \
     }                                                                              \
     _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                              \
       int c_ = tid + 256 * i, row_ = c_ / (KT / 8), ch_ = c_ % (KT / 8);           \
-      *(uint4*)(&sV[b][VOFF(row_, ch_)]) = rv[i];                                  \
+      *(u32x4_t*)(&sV[b][VOFF(row_, ch_)]) = rv[i];                                  \
     }                                                                              \
   } while (0)
 
@@ -93,11 +93,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16_t* __restrict__
   const int ntiles = (n + KT - 1) / KT;
   ATT_GLOAD(0);
   ATT_SSTORE(0);
+  ATT_GLOAD(min(1, ntiles - 1) * KT);
   __syncthreads();
   const int krow = key_perm(l32);
   for (int t = 0; t < ntiles; ++t) {
     const int b = t & 1;
-    if (t + 1 < ntiles) ATT_GLOAD((t + 1) * KT);
 
     f32x16_t s[2];
 #pragma unroll
@@ -155,7 +155,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16_t* __restrict__
           bf16x8_t a = *(const bf16x8_t*)(&sV[b][VOFF(d * 32 + l32, 4 * kb + 2 * cc + half)]);
           oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kb][cc], oacc[d], 0, 0, 0);
         }
-    if (t + 1 < ntiles) ATT_SSTORE(b ^ 1);
+    // Unconditional (see the GEMM): tile t+1 to LDS, then the loads of t+2.
+    ATT_SSTORE(b ^ 1);
+    ATT_GLOAD(min(t + 2, ntiles - 1) * KT);
     __syncthreads();
   }
 

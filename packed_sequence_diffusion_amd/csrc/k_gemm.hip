@@ -3,7 +3,7 @@
 // plain/bias store, gated residual ([MMH3] residual), SwiGLU pairing ([MMH3]
 // ffn_tail) and bias + GELU-tanh ([SIGLIP] GeluBiasOp).
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 on LDS-staged 256x128x64 tiles; four
+// bf16 path: v_mfma_f32_32x32x16_bf16 on LDS-staged 256x256x64 tiles; eight
 // waves, each owning a 64x128 strip of the tile (2x4 MFMA blocks of 32x32).
 // fp32 path: a plain LDS-tiled FMA kernel (64x64 tiles), used by the fp32
 // block configuration.
@@ -36,97 +36,122 @@ DIT_DEV void epi_swiglu(const Epi& ep, int row, int ocol, float g, float u) {
 }
 
 // ---------------------------------------------------------------- bf16 MFMA ----
-constexpr int GBM = 256, GBN = 128, GBK = 64;
+// 256x256x64 workgroup tile, 512 threads = 8 waves as 4 (M) x 2 (N); each wave
+// owns a 64x128 strip (2x4 blocks of 32x32, 128 fp32 accumulators per lane).
+// The next K tile is loaded into registers one full MFMA section ahead of its
+// LDS store (the loads of tile k+2 are issued right after tile k+1 is stored),
+// so global latency hides behind a whole tile of MFMAs.  A partial last N tile
+// (N % 256 == 128) clamps its B rows and masks its stores.
+constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int GWM = 4, GWN = 2;                 // wave grid
+constexpr int GTM = GBM / GWM, GTN = GBN / GWN;  // 64 x 128 per wave
+constexpr int GMI = GTM / 32, GNI = GTN / 32;
+constexpr int GNT = 64 * GWM * GWN;             // 512 threads
+constexpr int GCPR = GBK / 8;                   // 16-byte chunks per tile row
+constexpr int GAL = GBM * GCPR / GNT, GBL = GBN * GCPR / GNT;
 
-// LDS element offset of 16-byte chunk `ch` (0..7) of row `r` in a [rows][64]
-// bf16 tile; the chunk index is XOR-swizzled with the row so that 8
-// consecutive rows reading the same logical chunk hit 8 different bank groups.
-DIT_DEV int swz64(int r, int ch) { return r * GBK + ((ch ^ (r & 7)) << 3); }
+// LDS element offset of 16-byte chunk `ch` of row `r` in a [rows][64] bf16
+// tile.  The chunk index is XOR-ed with (r / 2) % 8: the 16 rows that one
+// quarter-wave's ds_read_b128 touches then cover all 64 banks exactly once.
+DIT_DEV int swz64(int r, int ch) { return r * GBK + ((ch ^ ((r >> 1) & 7)) << 3); }
 
 template <int EPI, typename OutT>
-__global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ A, int lda,
+__global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A, int lda,
                                                    const bf16_t* __restrict__ B, int ldb, int M,
                                                    int N, int K, Epi ep) {
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (GBM + GBN) * GBK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ntn = N / GBN;
+  const int wm = wave / GWN, wn = wave % GWN;
+  const int ntn = (N + GBN - 1) / GBN;
   const int tm = blockIdx.x / ntn, tn = blockIdx.x - tm * ntn;
   const int m0 = tm * GBM, n0 = tn * GBN;
-  const int lrow = tid >> 3, lch = tid & 7;
 
-  uint4 ra[8], rb[4];
-#define GEMM_GLOAD(k0)                                                              \
-  do {                                                                              \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                 \
-      int gr = min(m0 + lrow + 32 * i, M - 1);                                      \
-      ra[i] = *(const uint4*)(A + (size_t)gr * lda + (k0) + lch * 8);               \
-    }                                                                               \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) rb[i] =                           \
-        *(const uint4*)(B + (size_t)(n0 + lrow + 32 * i) * ldb + (k0) + lch * 8);   \
+  u32x4_t ra[GAL], rb[GBL];
+#define GEMM_GLOAD(k0)                                                                   \
+  do {                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < GAL; ++i) {                                    \
+      const int c_ = tid + GNT * i, r_ = c_ / GCPR, ch_ = c_ % GCPR;                     \
+      ra[i] = *(const u32x4_t*)(A + (size_t)min(m0 + r_, M - 1) * lda + (k0) + ch_ * 8); \
+    }                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < GBL; ++i) {                                    \
+      const int c_ = tid + GNT * i, r_ = c_ / GCPR, ch_ = c_ % GCPR;                     \
+      rb[i] = *(const u32x4_t*)(B + (size_t)min(n0 + r_, N - 1) * ldb + (k0) + ch_ * 8); \
+    }                                                                                    \
   } while (0)
-#define GEMM_SSTORE(buf)                                                            \
-  do {                                                                              \
-    bf16_t* As_ = smem + (buf) * (GBM + GBN) * GBK;                                 \
-    bf16_t* Bs_ = As_ + GBM * GBK;                                                  \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                   \
-        *(uint4*)(As_ + swz64(lrow + 32 * i, lch)) = ra[i];                         \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                   \
-        *(uint4*)(Bs_ + swz64(lrow + 32 * i, lch)) = rb[i];                         \
+#define GEMM_SSTORE(buf)                                                                 \
+  do {                                                                                   \
+    bf16_t* As_ = smem + (buf) * (GBM + GBN) * GBK;                                      \
+    bf16_t* Bs_ = As_ + GBM * GBK;                                                       \
+    _Pragma("unroll") for (int i = 0; i < GAL; ++i) {                                    \
+      const int c_ = tid + GNT * i;                                                      \
+      *(u32x4_t*)(As_ + swz64(c_ / GCPR, c_ % GCPR)) = ra[i];                            \
+    }                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < GBL; ++i) {                                    \
+      const int c_ = tid + GNT * i;                                                      \
+      *(u32x4_t*)(Bs_ + swz64(c_ / GCPR, c_ % GCPR)) = rb[i];                            \
+    }                                                                                    \
   } while (0)
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[GMI][GNI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < GMI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < GNI; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int nk = K / GBK;
   GEMM_GLOAD(0);
   GEMM_SSTORE(0);
+  GEMM_GLOAD(min(1, nk - 1) * GBK);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) GEMM_GLOAD((kt + 1) * GBK);
-    const bf16_t* As = smem + buf * (GBM + GBN) * GBK;
+    const bf16_t* As = smem + (kt & 1) * (GBM + GBN) * GBK;
     const bf16_t* Bs = As + GBM * GBK;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < GBK / 16; ++s) {
       const int ch = 2 * s + (lane >> 5);
-      bf16x8_t a[2], b[4];
+      bf16x8_t a[GMI], b[GNI];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        a[mi] = *(const bf16x8_t*)(As + swz64(wave * 64 + mi * 32 + (lane & 31), ch));
+      for (int mi = 0; mi < GMI; ++mi)
+        a[mi] = *(const bf16x8_t*)(As + swz64(wm * GTM + mi * 32 + (lane & 31), ch));
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        b[ni] = *(const bf16x8_t*)(Bs + swz64(ni * 32 + (lane & 31), ch));
+      for (int ni = 0; ni < GNI; ++ni)
+        b[ni] = *(const bf16x8_t*)(Bs + swz64(wn * GTN + ni * 32 + (lane & 31), ch));
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < GMI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+        for (int ni = 0; ni < GNI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
     }
-    if (kt + 1 < nk) GEMM_SSTORE(buf ^ 1);
+    // Unconditional: on the last two iterations these re-load the last tile
+    // and fill the buffer nobody reads again, which keeps the staging
+    // registers out of control flow (they stay in VGPRs).
+    GEMM_SSTORE((kt + 1) & 1);
+    GEMM_GLOAD(min(kt + 2, nk - 1) * GBK);
     __syncthreads();
   }
+#undef GEMM_GLOAD
+#undef GEMM_SSTORE
 
   // C layout of a 32x32 block: lane holds column (lane & 31) and rows
   // 8*(v/4) + 4*(lane/32) + v%4 for v = 0..15.
   const int cl = lane & 31, rh = (lane >> 5) * 4;
+  const int cbase = n0 + wn * GTN;
+  if (cbase >= N) return;  // the masked half of a partial last N tile
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+  for (int mi = 0; mi < GMI; ++mi) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int row = m0 + wave * 64 + mi * 32 + (v >> 2) * 8 + rh + (v & 3);
+      const int row = m0 + wm * GTM + mi * 32 + (v >> 2) * 8 + rh + (v & 3);
       if (row >= M) continue;
       if (EPI == EPI_SWIGLU) {
 #pragma unroll
-        for (int ni = 0; ni < 4; ni += 2)
-          epi_swiglu<OutT>(ep, row, (n0 + ni * 32) / 2 + cl, acc[mi][ni][v], acc[mi][ni + 1][v]);
+        for (int ni = 0; ni < GNI; ni += 2)
+          epi_swiglu<OutT>(ep, row, (cbase + ni * 32) / 2 + cl, acc[mi][ni][v], acc[mi][ni + 1][v]);
       } else {
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) epi_one<EPI, OutT>(ep, row, n0 + ni * 32 + cl, acc[mi][ni][v]);
+        for (int ni = 0; ni < GNI; ++ni) epi_one<EPI, OutT>(ep, row, cbase + ni * 32 + cl, acc[mi][ni][v]);
       }
     }
   }
@@ -184,12 +209,12 @@ template <int EPI>
 static hipError_t launch_gemm(int dtype, bool out_bf16, const void* A, int lda, const void* B,
                               int ldb, int M, int N, int K, const Epi& ep, hipStream_t s) {
   if (dtype == BF16) {
-    dim3 grid(((M + GBM - 1) / GBM) * (N / GBN));
+    dim3 grid(((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN));
     if (out_bf16 || EPI == EPI_GATED_RES)
-      k_gemm_bf16<EPI, bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)A, lda, (const bf16_t*)B, ldb,
+      k_gemm_bf16<EPI, bf16_t><<<grid, GNT, 0, s>>>((const bf16_t*)A, lda, (const bf16_t*)B, ldb,
                                                      M, N, K, ep);
     else
-      k_gemm_bf16<EPI, float><<<grid, 256, 0, s>>>((const bf16_t*)A, lda, (const bf16_t*)B, ldb,
+      k_gemm_bf16<EPI, float><<<grid, GNT, 0, s>>>((const bf16_t*)A, lda, (const bf16_t*)B, ldb,
                                                     M, N, K, ep);
   } else {
     dim3 grid(((M + 63) / 64) * (N / 64));

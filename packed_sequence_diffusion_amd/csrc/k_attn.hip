@@ -38,8 +38,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16_t* __restrict__
   constexpr int KCH = HD / 8;   // 16-byte chunks per K row
   constexpr int KPT = KT * KCH / 256;  // K chunks per thread per tile
   constexpr int VPT = HD * (KT / 8) / 256;
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * HD];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[2][HD * KT];
+  // LDS rows are padded by one 16-byte chunk: the 16 rows one quarter-wave
+  // reads at the same chunk then start in 16 different bank groups, and each
+  // lane's addresses for the different chunks differ by constants (immediate
+  // offsets of ds_read_b128 rather than one address register per chunk).
+  constexpr int KLD = HD + 8, VLD = KT + 8;
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * KLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[2][HD * VLD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
@@ -56,30 +61,28 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16_t* __restrict__
     qf[c] = *(const bf16x8_t*)(Qh + (size_t)(q0 + l32) * HD + 16 * c + 8 * half);
 
   u32x4_t rk[KPT], rv[VPT];
-  // K tile [KT][HD]: chunk XOR row%16 (HD=128) or row%8 (HD=64); V^T tile
-  // [HD][KT]: chunk XOR row%8.
-#define KOFF(row, ch) ((row) * HD + ((((ch) ^ ((row) & (KCH - 1) & 15))) << 3))
-#define VOFF(row, ch) ((row) * KT + ((((ch) ^ ((row) & 7))) << 3))
+#define KOFF(row, ch) ((row) * KLD + ((ch) << 3))
+#define VOFF(row, ch) ((row) * VLD + ((ch) << 3))
 #define ATT_GLOAD(k0)                                                              \
   do {                                                                             \
     _Pragma("unroll") for (int i = 0; i < KPT; ++i) {                              \
       int c_ = tid + 256 * i, row_ = c_ / KCH, ch_ = c_ % KCH;                     \
-      rk[i] = *(const u32x4_t*)(Kh + (size_t)((k0) + row_) * HD + ch_ * 8);          \
+      rk[i] = *(const u32x4_t*)(Kh + (size_t)((k0) + row_) * HD + ch_ * 8);        \
     }                                                                              \
     _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                              \
       int c_ = tid + 256 * i, row_ = c_ / (KT / 8), ch_ = c_ % (KT / 8);           \
-      rv[i] = *(const u32x4_t*)(Vh + (size_t)row_ * ldn + (k0) + ch_ * 8);           \
+      rv[i] = *(const u32x4_t*)(Vh + (size_t)row_ * ldn + (k0) + ch_ * 8);         \
     }                                                                              \
   } while (0)
 #define ATT_SSTORE(b)                                                              \
   do {                                                                             \
     _Pragma("unroll") for (int i = 0; i < KPT; ++i) {                              \
       int c_ = tid + 256 * i, row_ = c_ / KCH, ch_ = c_ % KCH;                     \
-      *(u32x4_t*)(&sK[b][KOFF(row_, ch_)]) = rk[i];                                  \
+      *(u32x4_t*)(&sK[b][KOFF(row_, ch_)]) = rk[i];                                \
     }                                                                              \
     _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                              \
       int c_ = tid + 256 * i, row_ = c_ / (KT / 8), ch_ = c_ % (KT / 8);           \
-      *(u32x4_t*)(&sV[b][VOFF(row_, ch_)]) = rv[i];                                  \
+      *(u32x4_t*)(&sV[b][VOFF(row_, ch_)]) = rv[i];                                \
     }                                                                              \
   } while (0)
 
@@ -88,78 +91,86 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16_t* __restrict__
   for (int d = 0; d < ND; ++d)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[d][v] = 0.0f;
+  // Base-2 running maximum actually used for the exponentials.  It is only
+  // raised when a tile's maximum exceeds it by more than kLazy (O and the row
+  // sum are then rescaled); otherwise p = 2^(s*c - m) <= 2^kLazy, harmless in
+  // the fp32 sums and in bf16, and the final normalization is unchanged.
+  constexpr float kLazy = 8.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int ntiles = (n + KT - 1) / KT;
+  const int nfull = n / KT;  // tiles whose 64 keys are all valid
   ATT_GLOAD(0);
   ATT_SSTORE(0);
   ATT_GLOAD(min(1, ntiles - 1) * KT);
   __syncthreads();
   const int krow = key_perm(l32);
-  for (int t = 0; t < ntiles; ++t) {
-    const int b = t & 1;
 
-    f32x16_t s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        bf16x8_t a = *(const bf16x8_t*)(&sK[b][KOFF(kb * 32 + krow, 2 * c + half)]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
-      }
-    }
-    // accumulator value v of block kb is key kb*32 + 16*(v/8) + 8*half + v%8
-    if ((t + 1) * KT > n) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          int key = t * KT + kb * 32 + 16 * (v >> 3) + 8 * half + (v & 7);
-          if (key >= n) s[kb][v] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = exp2f(m_run - m_new);
-    float ls = 0.0f;
-    bf16x8_t p[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float pv = exp2f(fmaf(s[kb][8 * cc + e], scale_log2, -m_new));
-          ls += pv;
-          p[kb][cc][e] = (__bf16)pv;
-        }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          bf16x8_t a = *(const bf16x8_t*)(&sV[b][VOFF(d * 32 + l32, 4 * kb + 2 * cc + half)]);
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kb][cc], oacc[d], 0, 0, 0);
-        }
+#define ATT_TILE(MASKED)                                                                   \
+  do {                                                                                     \
+    f32x16_t s_[2];                                                                        \
+    _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                                     \
+      _Pragma("unroll") for (int v = 0; v < 16; ++v) s_[kb][v] = 0.0f;                    \
+      _Pragma("unroll") for (int c = 0; c < NC; ++c) {                                     \
+        bf16x8_t a_ = *(const bf16x8_t*)(&sK[b][KOFF(kb * 32 + krow, 2 * c + half)]);    \
+        s_[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_, qf[c], s_[kb], 0, 0, 0);     \
+      }                                                                                    \
+    }                                                                                      \
+    /* value v of block kb is key kb*32 + 16*(v/8) + 8*half + v%8 of the tile */           \
+    if (MASKED) {                                                                          \
+      _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                     \
+      _Pragma("unroll") for (int v = 0; v < 16; ++v) {                                     \
+        const int key = t * KT + kb * 32 + 16 * (v >> 3) + 8 * half + (v & 7);            \
+        if (key >= n) s_[kb][v] = -INFINITY;                                               \
+      }                                                                                    \
+    }                                                                                      \
+    float mx_ = -INFINITY;                                                                 \
+    _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                       \
+    _Pragma("unroll") for (int v = 0; v < 16; ++v) mx_ = fmaxf(mx_, s_[kb][v]);           \
+    mx_ = fmaxf(mx_, __shfl_xor(mx_, 32, 64)) * scale_log2;                                \
+    const bool need_ = mx_ > m_run + kLazy;                                                \
+    if (__ballot(need_)) {                                                                 \
+      const float m_new_ = need_ ? mx_ : m_run;                                            \
+      const float alpha_ = __builtin_amdgcn_exp2f(m_run - m_new_);                         \
+      m_run = m_new_;                                                                      \
+      l_run *= alpha_;                                                                     \
+      _Pragma("unroll") for (int d = 0; d < ND; ++d)                                       \
+      _Pragma("unroll") for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha_;                 \
+    }                                                                                      \
+    bf16x8_t p_[2][2];                                                                     \
+    _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                       \
+    _Pragma("unroll") for (int cc = 0; cc < 2; ++cc)                                       \
+    _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                        \
+      const float pv_ = __builtin_amdgcn_exp2f(fmaf(s_[kb][8 * cc + e], scale_log2, -m_run)); \
+      l_run += pv_;                                                                        \
+      p_[kb][cc][e] = (__bf16)pv_;                                                         \
+    }                                                                                      \
+    _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                       \
+    _Pragma("unroll") for (int cc = 0; cc < 2; ++cc)                                       \
+    _Pragma("unroll") for (int d = 0; d < ND; ++d) {                                       \
+      bf16x8_t a_ = *(const bf16x8_t*)(&sV[b][VOFF(d * 32 + l32, 4 * kb + 2 * cc + half)]); \
+      oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_, p_[kb][cc], oacc[d], 0, 0, 0); \
+    }                                                                                      \
+  } while (0)
+
+  // Full tiles in the loop, the ragged last tile (if any) after it.
+  for (int t = 0; t < nfull; ++t) {
+    const int b = t & 1;
+    ATT_TILE(false);
     // Unconditional (see the GEMM): tile t+1 to LDS, then the loads of t+2.
     ATT_SSTORE(b ^ 1);
     ATT_GLOAD(min(t + 2, ntiles - 1) * KT);
     __syncthreads();
   }
+  if (nfull < ntiles) {
+    const int t = nfull, b = t & 1;
+    ATT_TILE(true);
+  }
+#undef ATT_TILE
+#undef ATT_GLOAD
+#undef ATT_SSTORE
+#undef KOFF
+#undef VOFF
 
   const float lt = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / lt;

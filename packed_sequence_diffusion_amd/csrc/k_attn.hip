@@ -3,7 +3,7 @@
 // token; softmax normalisation deferred to the output as in [SIGLIP]'s
 // deferred normalisation).
 //
-// bf16 path (flash-style, MFMA): a workgroup owns 128 queries of one head, four
+// bf16 path (flash-style, MFMA): a workgroup owns 256 queries of one head, eight
 // waves of 32.  Each wave keeps its queries' Q fragment in registers and walks
 // the keys in tiles of 64 staged through LDS (double-buffered):
 //   S^T = K Q^T     (v_mfma_f32_32x32x16_bf16, A = K rows, B = Q^T)
@@ -26,8 +26,12 @@ namespace dit {
 // Row permutation of a 32-key block: swap bits 2 and 3.
 DIT_DEV int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+constexpr int kAttnWaves = 8;  // 8 waves x 32 queries per workgroup
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kAttnRows = 32 * kAttnWaves;
+
 template <int HD>
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16_t* __restrict__ Q,
+__global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __restrict__ Q,
                                                       const bf16_t* __restrict__ Kp,
                                                       const bf16_t* __restrict__ Vt, int n,
                                                       int ldn, float scale_log2,
@@ -36,8 +40,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16_t* __restrict__
   constexpr int NC = HD / 16;   // MFMA k-steps over the head dim
   constexpr int ND = HD / 32;   // 32-row blocks of O^T
   constexpr int KCH = HD / 8;   // 16-byte chunks per K row
-  constexpr int KPT = KT * KCH / 256;  // K chunks per thread per tile
-  constexpr int VPT = HD * (KT / 8) / 256;
+  constexpr int KPT = KT * KCH / kAttnThreads;  // K chunks per thread per tile
+  constexpr int VPT = HD * (KT / 8) / kAttnThreads;
   // LDS rows are padded by one 16-byte chunk: the 16 rows one quarter-wave
   // reads at the same chunk then start in 16 different bank groups, and each
   // lane's addresses for the different chunks differ by constants (immediate
@@ -50,7 +54,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16_t* __restrict__
   const int half = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.y;
   const int H = gridDim.y;
-  const int q0 = blockIdx.x * 128 + wave * 32;
+  const int q0 = blockIdx.x * kAttnRows + wave * 32;
   const bf16_t* Qh = Q + (size_t)h * ldn * HD;
   const bf16_t* Kh = Kp + (size_t)h * ldn * HD;
   const bf16_t* Vh = Vt + (size_t)h * HD * ldn;
@@ -58,7 +62,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16_t* __restrict__
   bf16x8_t qf[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
-    qf[c] = *(const bf16x8_t*)(Qh + (size_t)(q0 + l32) * HD + 16 * c + 8 * half);
+    qf[c] = *(const bf16x8_t*)(Qh + (size_t)min(q0 + l32, ldn - 1) * HD + 16 * c + 8 * half);
 
   u32x4_t rk[KPT], rv[VPT];
 #define KOFF(row, ch) ((row) * KLD + ((ch) << 3))
@@ -66,22 +70,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16_t* __restrict__
 #define ATT_GLOAD(k0)                                                              \
   do {                                                                             \
     _Pragma("unroll") for (int i = 0; i < KPT; ++i) {                              \
-      int c_ = tid + 256 * i, row_ = c_ / KCH, ch_ = c_ % KCH;                     \
+      int c_ = tid + kAttnThreads * i, row_ = c_ / KCH, ch_ = c_ % KCH;                     \
       rk[i] = *(const u32x4_t*)(Kh + (size_t)((k0) + row_) * HD + ch_ * 8);        \
     }                                                                              \
     _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                              \
-      int c_ = tid + 256 * i, row_ = c_ / (KT / 8), ch_ = c_ % (KT / 8);           \
+      int c_ = tid + kAttnThreads * i, row_ = c_ / (KT / 8), ch_ = c_ % (KT / 8);           \
       rv[i] = *(const u32x4_t*)(Vh + (size_t)row_ * ldn + (k0) + ch_ * 8);         \
     }                                                                              \
   } while (0)
 #define ATT_SSTORE(b)                                                              \
   do {                                                                             \
     _Pragma("unroll") for (int i = 0; i < KPT; ++i) {                              \
-      int c_ = tid + 256 * i, row_ = c_ / KCH, ch_ = c_ % KCH;                     \
+      int c_ = tid + kAttnThreads * i, row_ = c_ / KCH, ch_ = c_ % KCH;                     \
       *(u32x4_t*)(&sK[b][KOFF(row_, ch_)]) = rk[i];                                \
     }                                                                              \
     _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                              \
-      int c_ = tid + 256 * i, row_ = c_ / (KT / 8), ch_ = c_ % (KT / 8);           \
+      int c_ = tid + kAttnThreads * i, row_ = c_ / (KT / 8), ch_ = c_ % (KT / 8);           \
       *(u32x4_t*)(&sV[b][VOFF(row_, ch_)]) = rv[i];                                \
     }                                                                              \
   } while (0)
@@ -249,15 +253,16 @@ __global__ __launch_bounds__(128) void k_attn_f32(const float* __restrict__ Q,
 hipError_t attention(int dtype, int hd, const void* q, const void* k, const void* vt, int n,
                      int ldn, int H, float scale_log2, void* o, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  dim3 grid((n + 127) / 128, H);
   if (dtype == BF16) {
+    dim3 grid((n + kAttnRows - 1) / kAttnRows, H);
     if (hd == 128)
-      k_attn_bf16<128><<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt,
+      k_attn_bf16<128><<<grid, kAttnThreads, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt,
                                             n, ldn, scale_log2, (bf16_t*)o);
     else
-      k_attn_bf16<64><<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt,
+      k_attn_bf16<64><<<grid, kAttnThreads, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt,
                                            n, ldn, scale_log2, (bf16_t*)o);
   } else {
+    dim3 grid((n + 127) / 128, H);
     if (hd == 128)
       k_attn_f32<128><<<grid, 128, 0, s>>>((const float*)q, (const float*)k, (const float*)vt, n,
                                            ldn, scale_log2, (float*)o);

@@ -18,12 +18,6 @@ DIT_DEV void epi_one(const Epi& ep, int row, int col, float v) {
   if (EPI == EPI_STORE) {
     if (ep.bias) v += ep.bias[col];
     Elt<OutT>::st((OutT*)ep.out + (size_t)row * ep.ldc + col, v);
-  } else if (EPI == EPI_GATED_RES) {
-    if (ep.bias) v += ep.bias[col];
-    float gate = 1.0f;
-    if (ep.mods) gate = ep.mods[(size_t)(ep.rows ? ep.rows[row] : 0) * ep.mstride + ep.goff + col];
-    float* o = (float*)ep.out + (size_t)row * ep.ldc + col;
-    *o = ep.resid[(size_t)row * ep.ldr + col] + gate * v;
   } else if (EPI == EPI_GELU) {
     if (ep.bias) v += ep.bias[col];
     Elt<OutT>::st((OutT*)ep.out + (size_t)row * ep.ldc + col, gelu_tanh_f(v));
@@ -33,6 +27,39 @@ DIT_DEV void epi_one(const Epi& ep, int row, int col, float v) {
 template <typename OutT>
 DIT_DEV void epi_swiglu(const Epi& ep, int row, int ocol, float g, float u) {
   Elt<OutT>::st((OutT*)ep.out + (size_t)row * ep.ldc + ocol, silu_f(g) * u);
+}
+
+// Gated residual for NV accumulator rows of one lane: out = resid + gate * (acc
+// + bias).  All loads are issued before any store (the residual, the gates
+// and the output never overlap within one GEMM), so the epilogue pays one
+// memory latency instead of one per element.
+template <int NR, int NC>
+DIT_DEV void epi_gated_rows(const Epi& ep, const int (&row)[NR], int M, int cbase, int cl,
+                            const float (&acc)[NR][NC]) {
+  const float* __restrict__ resid = ep.resid;
+  float* __restrict__ out = (float*)ep.out;
+  float rv[NR][NC], gv[NR][NC], bv[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) bv[j] = ep.bias ? ep.bias[cbase + 32 * j + cl] : 0.0f;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int r = min(row[i], M - 1);
+    const float* rr = resid + (size_t)r * ep.ldr + cbase + cl;
+    const float* gr = ep.mods ? ep.mods + (size_t)(ep.rows ? ep.rows[r] : 0) * ep.mstride + ep.goff + cbase + cl
+                              : nullptr;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      rv[i][j] = rr[32 * j];
+      gv[i][j] = gr ? gr[32 * j] : 1.0f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    if (row[i] >= M) continue;
+    float* orow = out + (size_t)row[i] * ep.ldc + cbase + cl;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) orow[32 * j] = rv[i][j] + gv[i][j] * (acc[i][j] + bv[j]);
+  }
 }
 
 // ---------------------------------------------------------------- bf16 MFMA ----
@@ -139,6 +166,24 @@ __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A,
   const int cl = lane & 31, rh = (lane >> 5) * 4;
   const int cbase = n0 + wn * GTN;
   if (cbase >= N) return;  // the masked half of a partial last N tile
+  if (EPI == EPI_GATED_RES) {
+#pragma unroll
+    for (int mi = 0; mi < GMI; ++mi)
+#pragma unroll
+      for (int vh = 0; vh < 2; ++vh) {
+        int rows8[8];
+        float a8[8][GNI];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int v = vh * 8 + i;
+          rows8[i] = m0 + wm * GTM + mi * 32 + (v >> 2) * 8 + rh + (v & 3);
+#pragma unroll
+          for (int ni = 0; ni < GNI; ++ni) a8[i][ni] = acc[mi][ni][v];
+        }
+        epi_gated_rows<8, GNI>(ep, rows8, M, cbase, cl, a8);
+      }
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < GMI; ++mi) {
 #pragma unroll
@@ -198,6 +243,14 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
     if (EPI == EPI_SWIGLU) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) epi_swiglu<OutT>(ep, row, n0 / 2 + tx + 16 * j, acc[i][j], acc[i][j + 2]);
+    } else if (EPI == EPI_GATED_RES) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + tx + 16 * j;
+        float v = acc[i][j] + (ep.bias ? ep.bias[col] : 0.0f);
+        float gate = ep.mods ? ep.mods[(size_t)(ep.rows ? ep.rows[row] : 0) * ep.mstride + ep.goff + col] : 1.0f;
+        ((float*)ep.out)[(size_t)row * ep.ldc + col] = ep.resid[(size_t)row * ep.ldr + col] + gate * v;
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) epi_one<EPI, OutT>(ep, row, n0 + tx + 16 * j, acc[i][j]);

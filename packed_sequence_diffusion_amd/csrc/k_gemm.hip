@@ -76,6 +76,7 @@ constexpr int GMI = GTM / 32, GNI = GTN / 32;
 constexpr int GNT = 64 * GWM * GWN;             // 512 threads
 constexpr int GCPR = GBK / 8;                   // 16-byte chunks per tile row
 constexpr int GAL = GBM * GCPR / GNT, GBL = GBN * GCPR / GNT;
+constexpr int kGroupM = 4;  // tile rows per rasterization group
 
 // LDS element offset of 16-byte chunk `ch` of row `r` in a [rows][64] bf16
 // tile.  The chunk index is XOR-ed with (r / 2) % 8: the 16 rows that one
@@ -89,8 +90,18 @@ __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A,
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (GBM + GBN) * GBK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / GWN, wn = wave % GWN;
-  const int ntn = (N + GBN - 1) / GBN;
-  const int tm = blockIdx.x / ntn, tn = blockIdx.x - tm * ntn;
+  // Tile order.  Workgroup i is dispatched to XCD i % 8 and each XCD has its
+  // own L2, so every XCD gets a contiguous chunk of the tile sequence, and the
+  // sequence runs through groups of kGroupM tile rows with the row index
+  // fastest: the workgroups resident on one XCD then share both A row panels
+  // and B column panels in its L2.
+  const int ntn = (N + GBN - 1) / GBN, ntm = (M + GBM - 1) / GBM;
+  const int total = ntn * ntm, chunk = (total + 7) / 8;
+  const int L = (blockIdx.x % 8) * chunk + blockIdx.x / 8;
+  if (L >= total) return;
+  const int gsz = kGroupM * ntn, g = L / gsz, gr = L - g * gsz;
+  const int gm = min(kGroupM, ntm - g * kGroupM);
+  const int tm = g * kGroupM + gr % gm, tn = gr / gm;
   const int m0 = tm * GBM, n0 = tn * GBN;
 
   u32x4_t ra[GAL], rb[GBL];
@@ -156,6 +167,31 @@ __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A,
     // registers out of control flow (they stay in VGPRs).
     GEMM_SSTORE((kt + 1) & 1);
     GEMM_GLOAD(min(kt + 2, nk - 1) * GBK);
+    // Issue order of the iteration: the first step's fragment reads, then
+    // every MFMA of steps 0..2 followed by one fragment read of the next step,
+    // and the last step's MFMAs each followed by one LDS store and one global
+    // load of the staged tile, so neither burst leaves the matrix pipe idle.
+    {
+      constexpr int NR = GMI + GNI, NM = GMI * GNI, NS = GBK / 16, NL = GAL + GBL;
+      static_assert(NM >= NR && NM >= NL, "schedule pattern");
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // ds_read
+#pragma unroll
+      for (int st = 0; st < NS - 1; ++st) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // ds_read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // ds_write
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM - NL, 0);
+    }
     __syncthreads();
   }
 #undef GEMM_GLOAD
@@ -262,7 +298,8 @@ template <int EPI>
 static hipError_t launch_gemm(int dtype, bool out_bf16, const void* A, int lda, const void* B,
                               int ldb, int M, int N, int K, const Epi& ep, hipStream_t s) {
   if (dtype == BF16) {
-    dim3 grid(((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN));
+    const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+    dim3 grid((tiles + 7) / 8 * 8);  // a whole number of rounds over the 8 XCDs
     if (out_bf16 || EPI == EPI_GATED_RES)
       k_gemm_bf16<EPI, bf16_t><<<grid, GNT, 0, s>>>((const bf16_t*)A, lda, (const bf16_t*)B, ldb,
                                                      M, N, K, ep);

@@ -41,20 +41,45 @@ def cpu_baseline(spec, wl):
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
     sig = O.resolve_sigmas(wl.slot_plan)
+    m1, m2 = 64, 1088
     times = {}
-    for m in (8, 40):
+    for m in (m1, m2):
         rows = np.linspace(0, spec.n - 1, m).astype(np.int64)
         t0 = time.perf_counter()
         O.block(spec, wl.x, wl.rows, wl.pos, sig, wl.weights, qrows=rows)
         times[m] = time.perf_counter() - t0
         log(f"cpu oracle: {m} query rows in {times[m]:.2f} s")
-    per_row = max((times[40] - times[8]) / 32.0, 1e-9)
-    fixed = max(times[8] - 8 * per_row, 0.0)
+    per_row = max((times[m2] - times[m1]) / (m2 - m1), 1e-9)
+    fixed = max(times[m1] - m1 * per_row, 0.0)
     full = fixed + per_row * spec.n
     return {"value": spec.n / full, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"fp64 numpy oracle of the full {spec.n}-token block evaluated at 8 and 40 "
-                       f"query rows ({times[8]:.1f} s, {times[40]:.1f} s; K/V of all tokens in both); "
-                       f"block time extrapolated linearly in query rows to {full:.0f} s")}
+            "sample": (f"fp64 numpy oracle of the full {spec.n}-token block evaluated at {m1} and "
+                       f"{m2} query rows ({times[m1]:.1f} s, {times[m2]:.1f} s; xn, K and V of all "
+                       f"tokens in both); block time extrapolated linearly in query rows to "
+                       f"{full:.0f} s")}
+
+
+def measured_traffic(kernel_sources):
+    """HBM bytes per attention dispatch from the committed counter summary, if
+    it was taken on the current kernel sources (sha256 match), else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attention_t2va_hbm_traffic.md")
+    try:
+        txt = open(path).read()
+        block = txt.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(block)
+    except (OSError, IndexError, ValueError):
+        return None
+    for rel in kernel_sources:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["sources_sha256"].get(rel):
+                return None
+    return rec["traffic_bytes"]
+
+
+ATTN_SOURCES = ("packed_sequence_diffusion_amd/csrc/k_attn.hip",
+                "packed_sequence_diffusion_amd/csrc/dev_common.h",
+                "packed_sequence_diffusion_amd/csrc/dit_kernels.h")
 
 
 def main():
@@ -165,7 +190,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": attn_tf / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic(ATTN_SOURCES) if spec.name == "t2va" else None,
         },
     }
     if not args.no_cpu_baseline:

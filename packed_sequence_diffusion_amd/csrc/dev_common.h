@@ -60,6 +60,19 @@ DIT_DEV float wave_max(float v) {
   return v;
 }
 
+// max / sum of a value and its copy in the other 32-lane half of the wave
+// (lane l and lane l ^ 32), with gfx950's v_permlane32_swap: swapping the
+// upper half of one copy with the lower half of another leaves, in every lane,
+// the pair {x[l], x[l ^ 32]}.
+DIT_DEV float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+DIT_DEV float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 DIT_DEV float silu_f(float v) { return v / (1.0f + __expf(-v)); }
 
 // Tanh-form GELU; tanh(u) = 1 - 2 / (exp(2u) + 1).

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
     float mx_ = -INFINITY;                                                                 \
     _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                       \
     _Pragma("unroll") for (int v = 0; v < 16; ++v) mx_ = fmaxf(mx_, s_[kb][v]);           \
-    mx_ = fmaxf(mx_, __shfl_xor(mx_, 32, 64)) * scale_log2;                                \
+    mx_ = half_swap_max(mx_) * scale_log2;                                                 \
     const bool need_ = mx_ > m_run + kLazy;                                                \
     if (__ballot(need_)) {                                                                 \
       const float m_new_ = need_ ? mx_ : m_run;                                            \
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
 #undef KOFF
 #undef VOFF
 
-  const float lt = l_run + __shfl_xor(l_run, 32, 64);
+  const float lt = half_swap_sum(l_run);
   const float inv = 1.0f / lt;
   const int qi = q0 + l32;
   if (qi < n) {

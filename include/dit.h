@@ -119,7 +119,8 @@ typedef struct dit_weights {
  *   rope  fp32 [n, hd/2, 2] (cos, sin) per token and pair
  *   xn    act  [n, D]     pre-norm + modulate of the FFN half after the call
  *                         (the attention half's is overwritten)
- *   qkv   act  [n, 3D]    QKV projection (+ bias)
+ *   qkv   act  [n, 3D]    QKV projection (+ bias); fp32 configurations only (the bf16
+ *                         QKV GEMM writes q, k and vt directly from its epilogue)
  *   q, k  act  [H, ldn, hd]  after qk-norm and RoPE; q carries hd^-1/2
  *   vt    act  [H, hd, ldn]  V transposed per head
  *   o     act  [n, D]     attention output, head h at columns h*hd
@@ -210,7 +211,8 @@ dit_status dit_attention(const dit_config* cfg, const void* q, const void* k, co
  * milliseconds of every phase over the recorded calls into phase_ms (host,
  * DIT_NPHASES doubles) and the number of recorded calls into *calls, and
  * releases the events.  Phases: 0 adaLN + RoPE table, 1 pre-norm (attention),
- * 2 QKV GEMM, 3 qk-norm/RoPE split, 4 attention, 5 out GEMM + residual,
+ * 2 QKV GEMM (with qk-norm, RoPE and the head split for bf16), 3 qk-norm/RoPE split
+ * (fp32 only; empty for bf16), 4 attention, 5 out GEMM + residual,
  * 6 pre-norm (FFN), 7 fc1 GEMM + activation, 8 fc2 GEMM + residual. */
 #define DIT_NPHASES 9
 dit_status dit_profile_begin(int32_t max_calls);

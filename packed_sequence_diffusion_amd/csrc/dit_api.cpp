@@ -149,7 +149,8 @@ dit_ws_layout ws_layout(const dit_config* c, int n) {
   L.temb = c->variant == DIT_ZIMAGE ? take((size_t)(c->temb_hidden + c->temb_freq) * 4) : kNone;
   L.rope = c->rope != DIT_ROPE_NONE ? take((size_t)n * (c->hd / 2) * 8) : kNone;
   L.xn = take((size_t)n * D * es);
-  L.qkv = take((size_t)n * 3 * D * es);
+  // the bf16 QKV GEMM writes q, k and v^T directly; only the fp32 path stages qkv
+  L.qkv = c->dtype == DIT_F32 ? take((size_t)n * 3 * D * es) : kNone;
   L.q = take((size_t)c->H * ldn * c->hd * es);
   L.k = take((size_t)c->H * ldn * c->hd * es);
   L.vt = take((size_t)c->H * ldn * c->hd * es);
@@ -531,23 +532,40 @@ dit_status dit_block_forward(const dit_config* c, const void* prepared, const fl
   // a2: pre-norm + modulate
   DIT_TRY(launch_prenorm(c, prepared, x, n, rows, mods, 0, xn, s));
   pm.mark(1);
-  // a3: QKV projection (+ bias)
-  {
-    dit::Epi ep;
-    ep.out = qkv;
-    ep.ldc = 3 * D;
-    ep.bias = atc<float>(prepared, P.b_qkv);
-    HIP_TRY(dit::gemm(dt, dit::EPI_STORE, bf, xn, D, atc<char>(prepared, P.w_qkv), D, n, 3 * D, D, ep, s), "qkv gemm");
-  }
-  pm.mark(2);
-  // a4: qk-norm + RoPE + scale fold, head-major q, k and transposed v
+  // a3 + a4: QKV projection (+ bias), qk-norm, RoPE and the hd^-1/2 fold into q,
+  // head-major q and k and transposed v (fused into the GEMM epilogue for bf16)
   {
     const bool qkn = c->variant != DIT_SIGLIP;
-    float q_scale = c->variant == DIT_SIGLIP ? 1.0f : (float)(1.0 / sqrt((double)hd));
-    HIP_TRY(dit::qk_split(dt, hd, qkv, n, ldn, H, qkn ? atc<float>(prepared, P.q_norm) : nullptr,
-                          qkn ? atc<float>(prepared, P.k_norm) : nullptr, c->qk_eps, cs, c->rope,
-                          q_scale, q, k, vt, s),
-            "qk_split");
+    const float q_scale = c->variant == DIT_SIGLIP ? 1.0f : (float)(1.0 / sqrt((double)hd));
+    const float* qn = qkn ? atc<float>(prepared, P.q_norm) : nullptr;
+    const float* kn = qkn ? atc<float>(prepared, P.k_norm) : nullptr;
+    dit::Epi ep;
+    ep.bias = atc<float>(prepared, P.b_qkv);
+    if (bf) {
+      ep.ldc = D;
+      ep.hd = hd;
+      ep.ldn = ldn;
+      ep.qn = qn;
+      ep.kn = kn;
+      ep.qk_eps = c->qk_eps;
+      ep.cs = cs;
+      ep.rope = c->rope;
+      ep.q_scale = q_scale;
+      ep.q = q;
+      ep.k = k;
+      ep.vt = vt;
+      HIP_TRY(dit::gemm(dt, dit::EPI_QKV, true, xn, D, atc<char>(prepared, P.w_qkv), D, n, 3 * D, D, ep, s),
+              "qkv gemm");
+      pm.mark(2);
+    } else {
+      ep.out = qkv;
+      ep.ldc = 3 * D;
+      HIP_TRY(dit::gemm(dt, dit::EPI_STORE, false, xn, D, atc<char>(prepared, P.w_qkv), D, n, 3 * D, D, ep, s),
+              "qkv gemm");
+      pm.mark(2);
+      HIP_TRY(dit::qk_split(dt, hd, qkv, n, ldn, H, qn, kn, c->qk_eps, cs, c->rope, q_scale, q, k, vt, s),
+              "qk_split");
+    }
   }
   pm.mark(3);
   // a5: attention (q carries hd^-1/2; the kernel works in base 2)

@@ -13,7 +13,10 @@ enum EpiKind {
   EPI_STORE = 0,      // out[r, c] = acc (+ bias[c])
   EPI_GATED_RES = 1,  // out_f32[r, c] = resid[r, c] + gate(r, c) * (acc (+ bias[c])); gate = 1 without mods
   EPI_SWIGLU = 2,     // columns interleaved in groups of 32 (gate g, up g): out[r, c'] = silu(g) * u
-  EPI_GELU = 3        // out[r, c] = gelu_tanh(acc + bias[c])
+  EPI_GELU = 3,       // out[r, c] = gelu_tanh(acc + bias[c])
+  EPI_QKV = 4         // bf16 QKV head split: (+ bias), qk-RMSNorm, RoPE and the q scale on
+                      // q and k, written head-major [H, ldn, hd]; v written transposed
+                      // [H, hd, ldn]; rows in [M, ldn) written as zeros
 };
 
 struct Epi {
@@ -26,6 +29,17 @@ struct Epi {
   int mstride = 0;
   int goff = 0;
   const int* rows = nullptr;  // null = row 0
+  // EPI_QKV (ldc holds D = H * hd)
+  int hd = 0, ldn = 0;
+  const float* qn = nullptr;  // q_norm / k_norm gains [hd], null = no qk-norm
+  const float* kn = nullptr;
+  float qk_eps = 0.0f;
+  const float* cs = nullptr;  // RoPE (cos, sin) [M, hd/2, 2]
+  int rope = 0;               // 0 none, 1 split-half, 2 interleaved
+  float q_scale = 1.0f;
+  void* q = nullptr;
+  void* k = nullptr;
+  void* vt = nullptr;
 };
 
 hipError_t gemm(int dtype, int epi, bool out_bf16, const void* A, int lda, const void* B, int ldb,

@@ -83,6 +83,140 @@ constexpr int kGroupM = 4;  // tile rows per rasterization group
 // quarter-wave's ds_read_b128 touches then cover all 64 banks exactly once.
 DIT_DEV int swz64(int r, int ch) { return r * GBK + ((ch ^ ((r >> 1) & 7)) << 3); }
 
+// QKV epilogue of one wave's 64 x 128 strip, which covers whole heads (128
+// columns = one head of 128 or two of 64; strips start on head boundaries).
+// Per token and head ([MMH3] norm_rope_w; qk-norm before rotary as [ENC]
+// rms_norm_heads): q and k are RMS-normalized with the shared [hd] gain,
+// rotated pairwise by the token's angles, q is scaled by q_scale (the
+// softmax's hd^-1/2) and both are written head-major; v goes out transposed
+// per head (keys contiguous) for the attention kernel's second product.
+// Rows are finished one at a time so that only the accumulators stay live.
+template <int HD, int ROPE>
+DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rbase, int c0,
+                         int which, int lane) {
+  constexpr int P = HD / 2;
+  const int cl = lane & 31, rh = (lane >> 5) * 4;
+  const int ldn = ep.ldn;
+  const float* g = which ? ep.kn : ep.qn;
+  const float qs = which == 0 ? ep.q_scale : 1.0f;
+  bf16_t* dst = (bf16_t*)(which ? ep.k : ep.q);
+  const float2* cs = (const float2*)ep.cs;
+  float gv[GNI];
+#pragma unroll
+  for (int ni = 0; ni < GNI; ++ni) gv[ni] = g ? g[(32 * ni + cl) & (HD - 1)] : 1.0f;
+  const bool even = (cl & 1) == 0;
+#pragma unroll
+  for (int mi = 0; mi < GMI; ++mi)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = rbase + mi * 32 + (v >> 2) * 8 + rh + (v & 3);
+      float x[GNI];
+#pragma unroll
+      for (int ni = 0; ni < GNI; ++ni) x[ni] = acc[mi][ni][v];
+      if (g) {
+        // blocks 0..3 are one head (HD = 128) or two (HD = 64: 0-1 and 2-3); the
+        // other 31 lanes of this half-wave hold the rest of the row's columns
+        float s0 = (HD == 128) ? (x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3])
+                               : x[0] * x[0] + x[1] * x[1];
+        float s1 = (HD == 128) ? 0.0f : x[2] * x[2] + x[3] * x[3];
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+          s0 += __shfl_xor(s0, o, 64);
+          if (HD != 128) s1 += __shfl_xor(s1, o, 64);
+        }
+        const float i0 = 1.0f / sqrtf(s0 * (1.0f / HD) + ep.qk_eps);
+        const float i1 = (HD == 128) ? i0 : 1.0f / sqrtf(s1 * (1.0f / HD) + ep.qk_eps);
+#pragma unroll
+        for (int ni = 0; ni < GNI; ++ni) x[ni] *= ((HD == 128 || ni < 2) ? i0 : i1) * gv[ni];
+      }
+      if (ROPE != 0) {
+        const float2* csr = cs + (size_t)min(row, M - 1) * P;
+        if (ROPE == 1) {  // split-half: pair (d, d + P) is in this lane, blocks ni, ni + P/32
+          if (HD == 128) {
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+              const float2 c = csr[32 * ni + cl];
+              const float a = x[ni], b = x[ni + 2];
+              x[ni] = a * c.x - b * c.y;
+              x[ni + 2] = a * c.y + b * c.x;
+            }
+          } else {
+            const float2 c = csr[cl];
+#pragma unroll
+            for (int ni = 0; ni < GNI; ni += 2) {
+              const float a = x[ni], b = x[ni + 1];
+              x[ni] = a * c.x - b * c.y;
+              x[ni + 1] = a * c.y + b * c.x;
+            }
+          }
+        } else {  // interleaved: pair (2i, 2i + 1) is in lanes cl and cl ^ 1
+#pragma unroll
+          for (int ni = 0; ni < GNI; ++ni) {
+            const float oth = __shfl_xor(x[ni], 1, 64);
+            const float2 c = csr[((32 * ni + cl) & (HD - 1)) >> 1];
+            const float xe = even ? x[ni] : oth, xo = even ? oth : x[ni];
+            x[ni] = even ? (xe * c.x - xo * c.y) : (xe * c.y + xo * c.x);
+          }
+        }
+      }
+      if (row < ldn) {
+        const bool valid = row < M;
+#pragma unroll
+        for (int ni = 0; ni < GNI; ++ni) {
+          const int col = c0 + 32 * ni + cl;
+          const int h = col / HD, d = col - h * HD;
+          dst[((size_t)h * ldn + row) * HD + d] = f2bf(valid ? x[ni] * qs : 0.0f);
+        }
+      }
+    }
+}
+
+DIT_DEV void epi_qkv(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rbase, int cbase,
+                     int lane) {
+  const int cl = lane & 31, rh = (lane >> 5) * 4;
+  const int D = ep.ldc, ldn = ep.ldn;
+  const int which = cbase / D;       // 0 q, 1 k, 2 v
+  const int c0 = cbase - which * D;  // first column of the strip inside its q/k/v block
+  if (ep.bias) {
+#pragma unroll
+    for (int ni = 0; ni < GNI; ++ni) {
+      const float b = ep.bias[cbase + 32 * ni + cl];
+#pragma unroll
+      for (int mi = 0; mi < GMI; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mi][ni][v] += b;
+    }
+  }
+  if (which == 2) {
+    // v^T [H, hd, ldn]: a lane holds 4 consecutive rows of one column per (mi, ni, v/4)
+    bf16_t* vt = (bf16_t*)ep.vt;
+#pragma unroll
+    for (int mi = 0; mi < GMI; ++mi)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        const int row0 = rbase + mi * 32 + vq * 8 + rh;
+        if (row0 >= ldn) continue;  // ldn is a multiple of 128: all four rows in or out
+#pragma unroll
+        for (int ni = 0; ni < GNI; ++ni) {
+          const int col = c0 + 32 * ni + cl;  // h * hd + d
+          float e[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) e[j] = (row0 + j < M) ? acc[mi][ni][vq * 4 + j] : 0.0f;
+          *(uint2*)(vt + (size_t)col * ldn + row0) = make_uint2(pack2bf(e[0], e[1]), pack2bf(e[2], e[3]));
+        }
+      }
+    return;
+  }
+  switch (ep.hd * 4 + ep.rope) {
+    case 128 * 4 + 0: epi_qk_rows<128, 0>(ep, acc, M, rbase, c0, which, lane); break;
+    case 128 * 4 + 1: epi_qk_rows<128, 1>(ep, acc, M, rbase, c0, which, lane); break;
+    case 128 * 4 + 2: epi_qk_rows<128, 2>(ep, acc, M, rbase, c0, which, lane); break;
+    case 64 * 4 + 0: epi_qk_rows<64, 0>(ep, acc, M, rbase, c0, which, lane); break;
+    case 64 * 4 + 1: epi_qk_rows<64, 1>(ep, acc, M, rbase, c0, which, lane); break;
+    default: epi_qk_rows<64, 2>(ep, acc, M, rbase, c0, which, lane); break;
+  }
+}
+
 template <int EPI, typename OutT>
 __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A, int lda,
                                                    const bf16_t* __restrict__ B, int ldb, int M,
@@ -202,6 +336,10 @@ __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A,
   const int cl = lane & 31, rh = (lane >> 5) * 4;
   const int cbase = n0 + wn * GTN;
   if (cbase >= N) return;  // the masked half of a partial last N tile
+  if (EPI == EPI_QKV) {
+    epi_qkv(ep, acc, M, m0 + wm * GTM, cbase, lane);
+    return;
+  }
   if (EPI == EPI_GATED_RES) {
 #pragma unroll
     for (int mi = 0; mi < GMI; ++mi)
@@ -300,16 +438,25 @@ static hipError_t launch_gemm(int dtype, bool out_bf16, const void* A, int lda, 
   if (dtype == BF16) {
     const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
     dim3 grid((tiles + 7) / 8 * 8);  // a whole number of rounds over the 8 XCDs
-    if (out_bf16 || EPI == EPI_GATED_RES)
+    if constexpr (EPI == EPI_QKV || EPI == EPI_GATED_RES) {
       k_gemm_bf16<EPI, bf16_t><<<grid, GNT, 0, s>>>((const bf16_t*)A, lda, (const bf16_t*)B, ldb,
                                                      M, N, K, ep);
-    else
-      k_gemm_bf16<EPI, float><<<grid, GNT, 0, s>>>((const bf16_t*)A, lda, (const bf16_t*)B, ldb,
-                                                    M, N, K, ep);
+    } else {
+      if (out_bf16)
+        k_gemm_bf16<EPI, bf16_t><<<grid, GNT, 0, s>>>((const bf16_t*)A, lda, (const bf16_t*)B,
+                                                       ldb, M, N, K, ep);
+      else
+        k_gemm_bf16<EPI, float><<<grid, GNT, 0, s>>>((const bf16_t*)A, lda, (const bf16_t*)B, ldb,
+                                                      M, N, K, ep);
+    }
   } else {
-    dim3 grid(((M + 63) / 64) * (N / 64));
-    k_gemm_f32<EPI, float><<<grid, 256, 0, s>>>((const float*)A, lda, (const float*)B, ldb, M, N,
-                                                 K, ep);
+    if constexpr (EPI == EPI_QKV) {
+      return hipErrorInvalidValue;
+    } else {
+      dim3 grid(((M + 63) / 64) * (N / 64));
+      k_gemm_f32<EPI, float><<<grid, 256, 0, s>>>((const float*)A, lda, (const float*)B, ldb, M,
+                                                   N, K, ep);
+    }
   }
   return hipGetLastError();
 }
@@ -322,6 +469,9 @@ hipError_t gemm(int dtype, int epi, bool out_bf16, const void* A, int lda, const
     case EPI_GATED_RES: return launch_gemm<EPI_GATED_RES>(dtype, out_bf16, A, lda, B, ldb, M, N, K, ep, s);
     case EPI_SWIGLU: return launch_gemm<EPI_SWIGLU>(dtype, out_bf16, A, lda, B, ldb, M, N, K, ep, s);
     case EPI_GELU: return launch_gemm<EPI_GELU>(dtype, out_bf16, A, lda, B, ldb, M, N, K, ep, s);
+    case EPI_QKV:
+      if (dtype != BF16) return hipErrorInvalidValue;
+      return launch_gemm<EPI_QKV>(dtype, true, A, lda, B, ldb, M, N, K, ep, s);
   }
   return hipErrorInvalidValue;
 }

@@ -94,9 +94,14 @@ def test_workspace_layout_monotone(dit):
     c = _cfg(dit)
     L = dit.workspace_layout(c, 25600)
     assert L.ldn == 25600
-    offs = [L.mods, L.rope, L.xn, L.qkv, L.q, L.k, L.vt, L.o, L.x1, L.a]
+    offs = [L.mods, L.rope, L.xn, L.q, L.k, L.vt, L.o, L.x1, L.a]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert L.y == dit.NONE_OFFSET
+    # the bf16 QKV GEMM writes q, k and v^T directly: no staged qkv panel
+    assert L.qkv == dit.NONE_OFFSET
+    toy = dit.make_config(W.spec_by_name("toy"))
+    Lt = dit.workspace_layout(toy, 256)
+    assert Lt.qkv != dit.NONE_OFFSET and Lt.qkv % 256 == 0
     assert dit.lib.dit_workspace_size(ctypes.byref(c), 25600) == L.total
     assert dit.workspace_layout(c, 333).ldn == 384
 

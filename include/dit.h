@@ -121,14 +121,16 @@ typedef struct dit_weights {
  *                         (the attention half's is overwritten)
  *   qkv   act  [n, 3D]    QKV projection (+ bias); fp32 configurations only (the bf16
  *                         QKV GEMM writes q, k and vt directly from its epilogue)
- *   q, k  act  [H, ldn, hd]  after qk-norm and RoPE; q carries hd^-1/2
+ *   q, k  act  [H, ldn, hd]  after qk-norm and RoPE; q carries log2(e) * hd^-1/2
  *   vt    act  [H, hd, ldn]  V transposed per head
  *   o     act  [n, D]     attention output, head h at columns h*hd
  *   x1    fp32 [n, D]     residual stream after the attention half
  *   a     act  [n, F]     FFN activation (SwiGLU or GELU-tanh)
- *   y     fp32 [n, D]     ZIMAGE: last projection before its sandwich norm (fc2's after the call) */
+ *   y     fp32 [n, D]     ZIMAGE: last projection before its sandwich norm (fc2's after the call)
+ *   part  fp32            bf16 only: key-range partials of the attention's split last round
+ *                         (256 slots x 256 queries x (hd + 2) floats) */
 typedef struct dit_ws_layout {
-  size_t mods, rope, xn, qkv, q, k, vt, o, x1, a, y, temb, total;
+  size_t mods, rope, xn, qkv, q, k, vt, o, x1, a, y, temb, part, total;
   int32_t ldn;
 } dit_ws_layout;
 

@@ -158,6 +158,7 @@ dit_ws_layout ws_layout(const dit_config* c, int n) {
   L.x1 = take((size_t)n * D * 4);
   L.a = take((size_t)n * F * es);
   L.y = c->variant == DIT_ZIMAGE ? take((size_t)n * D * 4) : kNone;
+  L.part = c->dtype == DIT_BF16 ? take(dit::attention_part_bytes(c->hd)) : kNone;
   L.total = off;
   return L;
 }
@@ -330,7 +331,7 @@ dit_status dit_profile_end(double* phase_ms, int32_t* calls) {
 }
 
 
-int32_t dit_abi_version(void) { return 1; }
+int32_t dit_abi_version(void) { return 2; }
 
 const char* dit_last_error(void) { return g_err; }
 
@@ -484,7 +485,8 @@ dit_status dit_attention(const dit_config* c, const void* q, const void* k, cons
     return fail(DIT_EALIGN, "q/k/vt/o not 16-byte aligned");
   if (!isfinite(score_scale)) return fail(DIT_EINVAL, "score_scale not finite");
   const float log2e = 1.4426950408889634f;
-  HIP_TRY(dit::attention(c->dtype, c->hd, q, k, vt, n, ldn, c->H, score_scale * log2e, o, (hipStream_t)stream),
+  HIP_TRY(dit::attention(c->dtype, c->hd, q, k, vt, n, ldn, c->H, score_scale * log2e, o, nullptr,
+                         (hipStream_t)stream),
           "attention");
   return DIT_OK;
 }
@@ -532,11 +534,15 @@ dit_status dit_block_forward(const dit_config* c, const void* prepared, const fl
   // a2: pre-norm + modulate
   DIT_TRY(launch_prenorm(c, prepared, x, n, rows, mods, 0, xn, s));
   pm.mark(1);
-  // a3 + a4: QKV projection (+ bias), qk-norm, RoPE and the hd^-1/2 fold into q,
+  // a3 + a4: QKV projection (+ bias), qk-norm, RoPE and the score-scale fold into q,
   // head-major q and k and transposed v (fused into the GEMM epilogue for bf16)
   {
     const bool qkn = c->variant != DIT_SIGLIP;
-    const float q_scale = c->variant == DIT_SIGLIP ? 1.0f : (float)(1.0 / sqrt((double)hd));
+    // q carries the whole base-2 score scale, log2(e) * hd^-1/2 (SigLIP's
+    // hd^-1/2 is already in W_q), so the attention kernel runs with scale 1.
+    const double kLog2e = 1.4426950408889634;
+    const float q_scale =
+        (float)(kLog2e * (c->variant == DIT_SIGLIP ? 1.0 : 1.0 / sqrt((double)hd)));
     const float* qn = qkn ? atc<float>(prepared, P.q_norm) : nullptr;
     const float* kn = qkn ? atc<float>(prepared, P.k_norm) : nullptr;
     dit::Epi ep;
@@ -568,8 +574,9 @@ dit_status dit_block_forward(const dit_config* c, const void* prepared, const fl
     }
   }
   pm.mark(3);
-  // a5: attention (q carries hd^-1/2; the kernel works in base 2)
-  HIP_TRY(dit::attention(dt, hd, q, k, vt, n, ldn, H, 1.4426950408889634f, o, s), "attention");
+  // a5: attention (q carries log2(e) hd^-1/2; the kernel works in base 2)
+  HIP_TRY(dit::attention(dt, hd, q, k, vt, n, ldn, H, 1.0f, o, bf ? at<float>(workspace, L.part) : nullptr, s),
+          "attention");
   pm.mark(4);
   // a6: out projection + residual
   if (c->variant == DIT_ZIMAGE) {

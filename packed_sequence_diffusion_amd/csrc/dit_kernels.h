@@ -78,8 +78,16 @@ hipError_t qk_split(int dtype, int hd, const void* qkv, int n, int ldn, int H, c
                     const float* kn, float eps, const float* cs, int rope_mode, float q_scale,
                     void* q, void* k, void* vt, hipStream_t s);
 
+// Attention over all n keys per head; q carries the base-2 score scale times
+// scale_log2.  bf16: `part` (attention_part_bytes(hd), may be null) holds the
+// key-range partials of the grid's last, split round; null disables the split.
+constexpr int kAttnMaxSlots = 256;  // split workgroups in the last round, at most
+constexpr int kAttnQueryRows = 256; // queries per workgroup
+inline size_t attention_part_bytes(int hd) {
+  return (size_t)kAttnMaxSlots * kAttnQueryRows * (size_t)(hd + 2) * sizeof(float);
+}
 hipError_t attention(int dtype, int hd, const void* q, const void* k, const void* vt, int n,
-                     int ldn, int H, float scale_log2, void* o, hipStream_t s);
+                     int ldn, int H, float scale_log2, void* o, float* part, hipStream_t s);
 
 // ---- weight preparation ---------------------------------------------------------------
 // dst[r, :] = src[perm(r), :] * (r < scale_rows ? scale : 1); perm = SwiGLU group interleave

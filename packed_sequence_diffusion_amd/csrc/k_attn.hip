@@ -13,6 +13,10 @@
 // softmax statistics are per lane and P lands in registers exactly in the
 // B-operand layout of the second product once the rows of the K tile are loaded
 // in a fixed permuted order (bits 2 and 3 of the row index swapped).
+// When q already carries the whole base-2 score scale (UNIT), the running
+// maximum is subtracted by the first MFMA of each score block (its
+// accumulator input is a register block holding -m), so the exponent needs no
+// per-score VALU instruction besides v_exp itself.
 //
 // fp32 path: a plain per-query loop (one thread per query), for the fp32
 // configuration.
@@ -29,13 +33,20 @@ DIT_DEV int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1)
 constexpr int kAttnWaves = 8;  // 8 waves x 32 queries per workgroup
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kAttnRows = 32 * kAttnWaves;
+static_assert(kAttnRows == kAttnQueryRows, "partial-buffer rows");
 
-template <int HD>
+// Work units are (head, block of 256 queries), head-major.  Units below
+// `whole` take every key and write O.  The remaining units (the last, partial
+// round of the grid) are each split into `nsplit` consecutive key ranges, one
+// workgroup per range, which write unnormalized partial results (O, running
+// maximum, row sum) for k_attn_merge to combine.
+template <int HD, bool UNIT>
 __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __restrict__ Q,
                                                       const bf16_t* __restrict__ Kp,
                                                       const bf16_t* __restrict__ Vt, int n,
-                                                      int ldn, float scale_log2,
-                                                      bf16_t* __restrict__ O) {
+                                                      int ldn, int H, float scale_log2,
+                                                      bf16_t* __restrict__ O, int whole,
+                                                      int nsplit, float* __restrict__ part) {
   constexpr int KT = 64;        // keys per tile
   constexpr int NC = HD / 16;   // MFMA k-steps over the head dim
   constexpr int ND = HD / 32;   // 32-row blocks of O^T
@@ -52,9 +63,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int h = blockIdx.y;
-  const int H = gridDim.y;
-  const int q0 = blockIdx.x * kAttnRows + wave * 32;
+  const int qblocks = (n + kAttnRows - 1) / kAttnRows;
+  const int ntiles = (n + KT - 1) / KT;
+  const int w = blockIdx.x;
+  const bool split = w >= whole;
+  const int u = split ? whole + (w - whole) / nsplit : w;
+  const int j = split ? (w - whole) % nsplit : 0;
+  const int ns = split ? nsplit : 1;
+  const int h = u / qblocks;
+  const int q0 = (u - h * qblocks) * kAttnRows + wave * 32;
+  // key tiles [t_lo, t_hi) of this workgroup
+  const int t_lo = j * ntiles / ns, t_hi = (j + 1) * ntiles / ns;
   const bf16_t* Qh = Q + (size_t)h * ldn * HD;
   const bf16_t* Kh = Kp + (size_t)h * ldn * HD;
   const bf16_t* Vh = Vt + (size_t)h * HD * ldn;
@@ -101,12 +120,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
   // the fp32 sums and in bf16, and the final normalization is unchanged.
   constexpr float kLazy = 8.0f;
   float m_run = -INFINITY, l_run = 0.0f;
+  // Scores are kept relative to cm (base 2): t = s * scale_log2 - cm.  cm is
+  // 0 until the first tile has set m_run, then equal to m_run.  With UNIT the
+  // subtraction happens in the MFMA through cneg = {-cm, ...}.
+  float cm = 0.0f;
+  f32x16_t cneg;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) cneg[v] = 0.0f;
 
-  const int ntiles = (n + KT - 1) / KT;
-  const int nfull = n / KT;  // tiles whose 64 keys are all valid
-  ATT_GLOAD(0);
-  ATT_SSTORE(0);
-  ATT_GLOAD(min(1, ntiles - 1) * KT);
+  const int t_full = min(t_hi, n / KT);  // tiles below t_full have 64 valid keys
+  ATT_GLOAD(t_lo * KT);
+  ATT_SSTORE(t_lo & 1);
+  ATT_GLOAD(min(t_lo + 1, t_hi - 1) * KT);
   __syncthreads();
   const int krow = key_perm(l32);
 
@@ -114,10 +139,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
   do {                                                                                     \
     f32x16_t s_[2];                                                                        \
     _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                                     \
-      _Pragma("unroll") for (int v = 0; v < 16; ++v) s_[kb][v] = 0.0f;                    \
       _Pragma("unroll") for (int c = 0; c < NC; ++c) {                                     \
         bf16x8_t a_ = *(const bf16x8_t*)(&sK[b][KOFF(kb * 32 + krow, 2 * c + half)]);    \
-        s_[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_, qf[c], s_[kb], 0, 0, 0);     \
+        s_[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_, qf[c], c == 0 ? cneg : s_[kb], \
+                                                         0, 0, 0);                         \
+      }                                                                                    \
+      if (!UNIT) {                                                                         \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v)                                     \
+          s_[kb][v] = fmaf(s_[kb][v], scale_log2, -cm);                                    \
       }                                                                                    \
     }                                                                                      \
     /* value v of block kb is key kb*32 + 16*(v/8) + 8*half + v%8 of the tile */           \
@@ -131,21 +160,28 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
     float mx_ = -INFINITY;                                                                 \
     _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                       \
     _Pragma("unroll") for (int v = 0; v < 16; ++v) mx_ = fmaxf(mx_, s_[kb][v]);           \
-    mx_ = half_swap_max(mx_) * scale_log2;                                                 \
-    const bool need_ = mx_ > m_run + kLazy;                                                \
+    mx_ = half_swap_max(mx_);                                                              \
+    const bool need_ = cm + mx_ > m_run + kLazy;                                           \
     if (__ballot(need_)) {                                                                 \
-      const float m_new_ = need_ ? mx_ : m_run;                                            \
+      const float m_new_ = need_ ? cm + mx_ : m_run;                                       \
       const float alpha_ = __builtin_amdgcn_exp2f(m_run - m_new_);                         \
+      const float delta_ = m_new_ - cm;                                                    \
       m_run = m_new_;                                                                      \
+      cm = m_new_;                                                                         \
       l_run *= alpha_;                                                                     \
       _Pragma("unroll") for (int d = 0; d < ND; ++d)                                       \
       _Pragma("unroll") for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha_;                 \
+      _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                     \
+      _Pragma("unroll") for (int v = 0; v < 16; ++v) s_[kb][v] -= delta_;                  \
+      if (UNIT) {                                                                          \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) cneg[v] = -cm;                      \
+      }                                                                                    \
     }                                                                                      \
     bf16x8_t p_[2][2];                                                                     \
     _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                       \
     _Pragma("unroll") for (int cc = 0; cc < 2; ++cc)                                       \
     _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                        \
-      const float pv_ = __builtin_amdgcn_exp2f(fmaf(s_[kb][8 * cc + e], scale_log2, -m_run)); \
+      const float pv_ = __builtin_amdgcn_exp2f(s_[kb][8 * cc + e]);                        \
       l_run += pv_;                                                                        \
       p_[kb][cc][e] = (__bf16)pv_;                                                         \
     }                                                                                      \
@@ -158,16 +194,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
   } while (0)
 
   // Full tiles in the loop, the ragged last tile (if any) after it.
-  for (int t = 0; t < nfull; ++t) {
+  for (int t = t_lo; t < t_full; ++t) {
     const int b = t & 1;
     ATT_TILE(false);
     // Unconditional (see the GEMM): tile t+1 to LDS, then the loads of t+2.
     ATT_SSTORE(b ^ 1);
-    ATT_GLOAD(min(t + 2, ntiles - 1) * KT);
+    ATT_GLOAD(min(t + 2, t_hi - 1) * KT);
     __syncthreads();
   }
-  if (nfull < ntiles) {
-    const int t = nfull, b = t & 1;
+  if (t_full < t_hi) {
+    const int t = t_full, b = t & 1;
     ATT_TILE(true);
   }
 #undef ATT_TILE
@@ -177,8 +213,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
 #undef VOFF
 
   const float lt = half_swap_sum(l_run);
-  const float inv = 1.0f / lt;
   const int qi = q0 + l32;
+  if (split) {
+    // partial slot (unit, range): O^T unnormalized fp32 [256][HD], then (m, l)
+    const size_t slot = (size_t)(u - whole) * nsplit + j;
+    const int ql = wave * 32 + l32;
+    float* po = part + (slot * kAttnRows + ql) * HD;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(float4*)(po + d * 32 + 8 * g + 4 * half) =
+            make_float4(oacc[d][4 * g], oacc[d][4 * g + 1], oacc[d][4 * g + 2], oacc[d][4 * g + 3]);
+    if (half == 0) {
+      float* pml = part + (size_t)kAttnMaxSlots * kAttnRows * HD + (slot * kAttnRows + ql) * 2;
+      *(float2*)pml = make_float2(m_run, lt);
+    }
+    return;
+  }
+  const float inv = 1.0f / lt;
   if (qi < n) {
     bf16_t* orow = O + (size_t)qi * (H * HD) + h * HD;
 #pragma unroll
@@ -250,17 +303,91 @@ __global__ __launch_bounds__(128) void k_attn_f32(const float* __restrict__ Q,
   }
 }
 
+// Combines the key-range partials of the split units: per query,
+// M = max m_j, O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j.  One wave per
+// query row, lanes over the head dimension.
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part, int n, int H,
+                                                    int whole, int nsplit, int nunits,
+                                                    bf16_t* __restrict__ O) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);  // (split unit, query) row
+  if (r >= nunits * kAttnRows) return;
+  const int us = r / kAttnRows, ql = r % kAttnRows;
+  const int u = whole + us;
+  const int qblocks = (n + kAttnRows - 1) / kAttnRows;
+  const int h = u / qblocks;
+  const int qi = (u - h * qblocks) * kAttnRows + ql;
+  if (qi >= n) return;
+  const float* pml = part + (size_t)kAttnMaxSlots * kAttnRows * HD;
+  float M = -INFINITY;
+  for (int j = 0; j < nsplit; ++j)
+    M = fmaxf(M, pml[(((size_t)us * nsplit + j) * kAttnRows + ql) * 2]);
+  constexpr int PER = HD / 64;
+  float acc[PER] = {};
+  float L = 0.0f;
+  for (int j = 0; j < nsplit; ++j) {
+    const size_t slot = (size_t)us * nsplit + j;
+    const float2 ml = *(const float2*)(pml + (slot * kAttnRows + ql) * 2);
+    const float wgt = __builtin_amdgcn_exp2f(ml.x - M);
+    L += wgt * ml.y;
+    const float* po = part + (slot * kAttnRows + ql) * HD;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += wgt * po[lane * PER + e];
+  }
+  const float inv = 1.0f / L;
+  bf16_t* orow = O + (size_t)qi * (H * HD) + h * HD + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) orow[e] = f2bf(acc[e] * inv);
+}
+
+namespace {
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      c = 256;
+    cus[dev] = c;
+  }
+  return cus[dev];
+}
+}  // namespace
+
 hipError_t attention(int dtype, int hd, const void* q, const void* k, const void* vt, int n,
-                     int ldn, int H, float scale_log2, void* o, hipStream_t s) {
+                     int ldn, int H, float scale_log2, void* o, float* part, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (dtype == BF16) {
-    dim3 grid((n + kAttnRows - 1) / kAttnRows, H);
-    if (hd == 128)
-      k_attn_bf16<128><<<grid, kAttnThreads, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt,
-                                            n, ldn, scale_log2, (bf16_t*)o);
-    else
-      k_attn_bf16<64><<<grid, kAttnThreads, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt,
-                                           n, ldn, scale_log2, (bf16_t*)o);
+    const bf16_t *Qb = (const bf16_t*)q, *Kb = (const bf16_t*)k, *Vb = (const bf16_t*)vt;
+    bf16_t* Ob = (bf16_t*)o;
+    // One workgroup per CU at a time: units = H * qblocks run in rounds of
+    // `cus`.  A last round that would leave at least half the CUs idle is
+    // split along the keys so that it fills them.
+    const int units = H * ((n + kAttnRows - 1) / kAttnRows);
+    const int cus = min(device_cus(), kAttnMaxSlots);
+    const int tail = units % cus;
+    const int ntiles = (n + 63) / 64;
+    int nsplit = tail ? min(min(cus / tail, 8), ntiles) : 1;
+    if (!part || nsplit < 2) nsplit = 1;
+    const int whole = nsplit > 1 ? units - tail : units;
+    const int grid = whole + (units - whole) * nsplit;
+    const bool unit = scale_log2 == 1.0f;
+#define ATT_LAUNCH(HD_, U_) \
+  k_attn_bf16<HD_, U_><<<grid, kAttnThreads, 0, s>>>(Qb, Kb, Vb, n, ldn, H, scale_log2, Ob, whole, nsplit, part)
+    if (hd == 128 && unit) ATT_LAUNCH(128, true);
+    else if (hd == 128) ATT_LAUNCH(128, false);
+    else if (unit) ATT_LAUNCH(64, true);
+    else ATT_LAUNCH(64, false);
+#undef ATT_LAUNCH
+    if (nsplit > 1) {
+      const int rows = (units - whole) * kAttnRows;
+      if (hd == 128)
+        k_attn_merge<128><<<(rows + 3) / 4, 256, 0, s>>>(part, n, H, whole, nsplit, units - whole, Ob);
+      else
+        k_attn_merge<64><<<(rows + 3) / 4, 256, 0, s>>>(part, n, H, whole, nsplit, units - whole, Ob);
+    }
   } else {
     dim3 grid((n + 127) / 128, H);
     if (hd == 128)

@@ -88,7 +88,7 @@ DIT_DEV int swz64(int r, int ch) { return r * GBK + ((ch ^ ((r >> 1) & 7)) << 3)
 // Per token and head ([MMH3] norm_rope_w; qk-norm before rotary as [ENC]
 // rms_norm_heads): q and k are RMS-normalized with the shared [hd] gain,
 // rotated pairwise by the token's angles, q is scaled by q_scale (the
-// softmax's hd^-1/2) and both are written head-major; v goes out transposed
+// softmax's base-2 score scale) and both are written head-major; v goes out transposed
 // per head (keys contiguous) for the attention kernel's second product.
 // Rows are finished one at a time so that only the accumulators stay live.
 template <int HD, int ROPE>

@@ -62,42 +62,45 @@ hipError_t adaln_interp(const float* basis, const float* bias, const float* tabl
 // Z-Image timestep embedding and adaLN ([ZIMG] TimestepEmbedder.Forward and
 // TransformerBlock.Forward): e = [cos(t f_i) | sin(t f_i)], f_i =
 // exp(-ln(10000) i / half); h = silu(W1 e + b1); temb = W2 h + b2;
-// mods = Wa temb + ba.  One thread per output of each dense layer.
+// mods = Wa temb + ba.  The sinusoid is evaluated once, in fp64; each dense
+// layer gives one wave to each output, the lanes striding over the inputs so
+// that a wave reads its weight row contiguously.
 // ------------------------------------------------------------------------------
-__global__ void k_temb_l1(double t, int freq, int hidden, const float* __restrict__ w1,
-                          const float* __restrict__ b1, float* __restrict__ h) {
-  int o = blockIdx.x * blockDim.x + threadIdx.x;
-  if (o >= hidden) return;
-  int half = freq / 2;
-  const float* w = w1 + (size_t)o * freq;
-  double acc = 0.0;
-  for (int i = 0; i < half; ++i) {
-    double f = exp(-log(10000.0) * (double)i / (double)half);
-    double a = t * f;
-    acc += (double)w[i] * cos(a) + (double)w[half + i] * sin(a);
-  }
-  float v = (float)acc + (b1 ? b1[o] : 0.0f);
-  h[o] = v / (1.0f + expf(-v));
+__global__ void k_temb_sin(double t, int half, float* __restrict__ e) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= half) return;
+  double a = t * exp(-log(10000.0) * (double)i / (double)half);
+  e[i] = (float)cos(a);
+  e[half + i] = (float)sin(a);
 }
 
-__global__ void k_dense(const float* __restrict__ x, int in, int out, const float* __restrict__ w,
-                        const float* __restrict__ b, float* __restrict__ y) {
-  int o = blockIdx.x * blockDim.x + threadIdx.x;
+template <bool SILU>
+__global__ __launch_bounds__(256) void k_dense(const float* __restrict__ x, int in, int out,
+                                               const float* __restrict__ w,
+                                               const float* __restrict__ b,
+                                               float* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int o = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (o >= out) return;
   const float* wr = w + (size_t)o * in;
   float acc = 0.0f;
-  for (int i = 0; i < in; ++i) acc += wr[i] * x[i];
-  y[o] = acc + (b ? b[o] : 0.0f);
+  for (int i = lane; i < in; i += 64) acc += wr[i] * x[i];
+  acc = wave_sum(acc) + (b ? b[o] : 0.0f);
+  if (lane == 0) y[o] = SILU ? silu_f(acc) : acc;
 }
 
 hipError_t temb_mods(double t_scaled, int freq, int hidden, int out_dim, const float* w1,
                      const float* b1, const float* w2, const float* b2, const float* wa,
                      const float* ba, float* scratch, float* mods, hipStream_t s) {
+  // scratch: h [hidden] then one [freq] slot that holds the sinusoid e until
+  // the first layer has read it, then temb.
   float* h = scratch;
-  float* temb = scratch + hidden;
-  k_temb_l1<<<(hidden + 255) / 256, 256, 0, s>>>(t_scaled, freq, hidden, w1, b1, h);
-  k_dense<<<(freq + 255) / 256, 256, 0, s>>>(h, hidden, freq, w2, b2, temb);
-  k_dense<<<(out_dim + 255) / 256, 256, 0, s>>>(temb, freq, out_dim, wa, ba, mods);
+  float* et = scratch + hidden;
+  const int half = freq / 2;
+  k_temb_sin<<<(half + 127) / 128, 128, 0, s>>>(t_scaled, half, et);
+  k_dense<true><<<(hidden + 3) / 4, 256, 0, s>>>(et, freq, hidden, w1, b1, h);
+  k_dense<false><<<(freq + 3) / 4, 256, 0, s>>>(h, hidden, freq, w2, b2, et);
+  k_dense<false><<<(out_dim + 3) / 4, 256, 0, s>>>(et, freq, out_dim, wa, ba, mods);
   return hipGetLastError();
 }
 
@@ -331,7 +334,7 @@ hipError_t rope_table(const float* pos, int n, int P, const int axes[3], double 
 // Head split of the fused qkv panel with qk-RMSNorm and RoPE on q and k
 // ([MMH3] norm_rope_w; qk-norm before rotary as [ENC] rms_norm_heads).
 // One wave per (token, head, q|k); lane p owns rotation pair p.  q is scaled by
-// q_scale (the softmax's hd^-1/2) after the rotation.  Tokens in [n, ldn) are
+// q_scale (the softmax's base-2 score scale) after the rotation.  Tokens in [n, ldn) are
 // written as zeros so attention reads finite padding.
 // ------------------------------------------------------------------------------
 template <typename T, int HD>

@@ -50,7 +50,7 @@ class DitWeights(ctypes.Structure):
 
 class DitWsLayout(ctypes.Structure):
     _fields_ = [(f, c_size_t) for f in ("mods", "rope", "xn", "qkv", "q", "k", "vt", "o", "x1",
-                                         "a", "y", "temb", "total")] + [("ldn", c_int32)]
+                                         "a", "y", "temb", "part", "total")] + [("ldn", c_int32)]
 
 
 NONE_OFFSET = (1 << (8 * ctypes.sizeof(c_size_t))) - 1

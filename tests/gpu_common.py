@@ -67,7 +67,8 @@ def run_gpu(spec, wl, dit, out_alias=False):
     st["xn"] = f64(xn_a)
     if mods is not None:
         st["mods"] = f64(mods)
-    st["q"] = f64(ws_view(ws, L.q, ad, (H, ldn, hd))[:, :n]) * math.sqrt(hd)
+    # q carries log2(e) * hd^-1/2 (the attention kernel works in base 2)
+    st["q"] = f64(ws_view(ws, L.q, ad, (H, ldn, hd))[:, :n]) * (math.sqrt(hd) / math.log2(math.e))
     st["k"] = f64(ws_view(ws, L.k, ad, (H, ldn, hd))[:, :n])
     st["v"] = f64(ws_view(ws, L.vt, ad, (H, hd, ldn))[:, :, :n].transpose(1, 2))
     st["o"] = f64(ws_view(ws, L.o, ad, (n, D)))

@@ -43,7 +43,7 @@ def test_header_functions_exported(dit):
 
 
 def test_abi_version(dit):
-    assert dit.lib.dit_abi_version() == 1
+    assert dit.lib.dit_abi_version() == 2
 
 
 def test_sigma_remap_printed_points(dit):
@@ -94,7 +94,7 @@ def test_workspace_layout_monotone(dit):
     c = _cfg(dit)
     L = dit.workspace_layout(c, 25600)
     assert L.ldn == 25600
-    offs = [L.mods, L.rope, L.xn, L.q, L.k, L.vt, L.o, L.x1, L.a]
+    offs = [L.mods, L.rope, L.xn, L.q, L.k, L.vt, L.o, L.x1, L.a, L.part]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert L.y == dit.NONE_OFFSET
     # the bf16 QKV GEMM writes q, k and v^T directly: no staged qkv panel

@@ -145,6 +145,18 @@ def main():
     ph = {k: v / calls for k, v in phases.items()}
     log("phases (ms/step): " + ", ".join(f"{k}={v:.3f}" for k, v in ph.items()))
 
+    # practical HBM ceiling on this machine: a device copy of the residual stream
+    xc = torch.empty_like(dev.x)
+    xc.copy_(dev.x)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(20):
+        xc.copy_(dev.x)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * dev.x.numel() * 4 * 20 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del xc
+
     attn_flops = spec.attn_flops()
     gemm_flops = spec.gemm_flops()
     attn_ms = ph["attention"]
@@ -183,6 +195,8 @@ def main():
         "gemm_frac_mfma_peak": gemm_tf / PEAK_BF16_TFLOPS,
         "norm1_gbs": norm_gbs,
         "norm1_frac_hbm_peak": norm_gbs / PEAK_HBM_GBS,
+        "hbm_copy_gbs": copy_gbs,
+        "norm1_frac_of_copy": norm_gbs / copy_gbs,
         "phases_ms": ph,
         "roofline": {
             "kernel": "k_attn_bf16<128> (attention)",

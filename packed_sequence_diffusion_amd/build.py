@@ -61,7 +61,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    # --no-undefined: a symbol missing from the objects fails the link, not the first load
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,--no-undefined", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

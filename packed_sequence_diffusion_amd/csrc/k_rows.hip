@@ -110,10 +110,14 @@ hipError_t temb_mods(double t_scaled, int freq, int hidden, int out_dim, const f
 //   RMS:   y = x / sqrt(mean(x^2) + eps) * g
 //   LAYER: y = (x - mean) / sqrt(var + eps) * g + beta   (two passes in registers)
 //   then y * (1 + mods[r, scale]) (+ mods[r, shift]).
+// The multiplier G = g * (1 + scale) and the additive term B = beta + shift are
+// fetched (from L2: they are shared by every row with the same segment row)
+// right after the row's own loads, so their latency overlaps the HBM reads;
+// y = (x - mean) * inv * G + B.  NCH = float4 chunks per lane (D <= 256 * NCH).
 // ------------------------------------------------------------------------------
 constexpr int kMaxChunks = 16;  // D <= 4096: 1024 float4 per row, 16 per lane
 
-template <int NORM, int MOD, typename OutT>
+template <int NORM, int MOD, int NCH, typename OutT>
 __global__ __launch_bounds__(256) void k_norm_mod(const float* __restrict__ x, int n, int D,
                                                   const float* __restrict__ g,
                                                   const float* __restrict__ beta, float eps,
@@ -125,17 +129,39 @@ __global__ __launch_bounds__(256) void k_norm_mod(const float* __restrict__ x, i
   if (row >= n) return;
   const int nc = D >> 2;
   const float4* xr = (const float4*)(x + (size_t)row * D);
-  float4 v[kMaxChunks];
-  float s = 0.0f;
+  float4 v[NCH], G[NCH], B[NCH];
+  // loads clamp their chunk index (always in bounds); sums and stores skip the
+  // chunks beyond the row
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    int i = lane + 64 * c;
-    if (i < nc) {
-      v[c] = xr[i];
-      s += (NORM == NORM_RMS) ? (v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w)
-                              : (v[c].x + v[c].y + v[c].z + v[c].w);
+  for (int c = 0; c < NCH; ++c) v[c] = xr[min(lane + 64 * c, nc - 1)];
+  const float* mrow = nullptr;
+  if (MOD != MOD_NONE) mrow = mods + (size_t)(rows ? rows[row] : 0) * mstride;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i = min(lane + 64 * c, nc - 1);
+    G[c] = ((const float4*)g)[i];
+    B[c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (NORM == NORM_LAYER) B[c] = ((const float4*)beta)[i];
+    if (MOD != MOD_NONE) {
+      const float4 sc = ((const float4*)(mrow + scale_off))[i];
+      // (g x + beta)(1 + sc) + sh: G = g (1 + sc), B = beta (1 + sc) + sh
+      G[c] = make_float4(G[c].x * (1.0f + sc.x), G[c].y * (1.0f + sc.y), G[c].z * (1.0f + sc.z),
+                         G[c].w * (1.0f + sc.w));
+      if (NORM == NORM_LAYER)
+        B[c] = make_float4(B[c].x * (1.0f + sc.x), B[c].y * (1.0f + sc.y), B[c].z * (1.0f + sc.z),
+                           B[c].w * (1.0f + sc.w));
+      if (MOD == MOD_SHIFT_SCALE) {
+        const float4 sh = ((const float4*)(mrow + shift_off))[i];
+        B[c] = make_float4(B[c].x + sh.x, B[c].y + sh.y, B[c].z + sh.z, B[c].w + sh.w);
+      }
     }
   }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    if (lane + 64 * c < nc)
+      s += (NORM == NORM_RMS) ? (v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w)
+                              : (v[c].x + v[c].y + v[c].z + v[c].w);
   s = wave_sum(s);
   float mean = 0.0f, inv;
   if (NORM == NORM_RMS) {
@@ -144,58 +170,53 @@ __global__ __launch_bounds__(256) void k_norm_mod(const float* __restrict__ x, i
     mean = s / (float)D;
     float q = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      int i = lane + 64 * c;
-      if (i < nc) {
+    for (int c = 0; c < NCH; ++c)
+      if (lane + 64 * c < nc) {
         float a = v[c].x - mean, b = v[c].y - mean, cc = v[c].z - mean, d = v[c].w - mean;
         q += a * a + b * b + cc * cc + d * d;
       }
-    }
     q = wave_sum(q);
     inv = 1.0f / sqrtf(q / (float)D + eps);
   }
-  const float* mrow = nullptr;
-  if (MOD != MOD_NONE) mrow = mods + (size_t)(rows ? rows[row] : 0) * mstride;
-  const float4* g4 = (const float4*)g;
   OutT* yr = y + (size_t)row * D;
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    int i = lane + 64 * c;
+  for (int c = 0; c < NCH; ++c) {
+    const int i = lane + 64 * c;
     if (i < nc) {
-      float4 gg = g4[i];
       float4 o;
-      o.x = (v[c].x - mean) * inv * gg.x;
-      o.y = (v[c].y - mean) * inv * gg.y;
-      o.z = (v[c].z - mean) * inv * gg.z;
-      o.w = (v[c].w - mean) * inv * gg.w;
-      if (NORM == NORM_LAYER) {
-        float4 bb = ((const float4*)beta)[i];
-        o.x += bb.x; o.y += bb.y; o.z += bb.z; o.w += bb.w;
-      }
-      if (MOD != MOD_NONE) {
-        float4 sc = ((const float4*)(mrow + scale_off))[i];
-        o.x *= 1.0f + sc.x; o.y *= 1.0f + sc.y; o.z *= 1.0f + sc.z; o.w *= 1.0f + sc.w;
-        if (MOD == MOD_SHIFT_SCALE) {
-          float4 sh = ((const float4*)(mrow + shift_off))[i];
-          o.x += sh.x; o.y += sh.y; o.z += sh.z; o.w += sh.w;
-        }
-      }
+      o.x = (v[c].x - mean) * inv * G[c].x + B[c].x;
+      o.y = (v[c].y - mean) * inv * G[c].y + B[c].y;
+      o.z = (v[c].z - mean) * inv * G[c].z + B[c].z;
+      o.w = (v[c].w - mean) * inv * G[c].w + B[c].w;
       Elt<OutT>::st4(yr + 4 * i, o);
     }
   }
+}
+
+template <int NORM, int MOD, int NCH>
+static void launch_norm_mod(bool out_bf16, const float* x, int n, int D, const float* g,
+                            const float* beta, float eps, const float* mods, int mstride,
+                            const int* rows, int so, int sc, void* y, hipStream_t s) {
+  dim3 grid((n + 3) / 4);
+  if (out_bf16)
+    k_norm_mod<NORM, MOD, NCH, bf16_t><<<grid, 256, 0, s>>>(x, n, D, g, beta, eps, mods, mstride,
+                                                             rows, so, sc, (bf16_t*)y);
+  else
+    k_norm_mod<NORM, MOD, NCH, float><<<grid, 256, 0, s>>>(x, n, D, g, beta, eps, mods, mstride,
+                                                            rows, so, sc, (float*)y);
 }
 
 template <int NORM, int MOD>
 static void launch_norm_mod(bool out_bf16, const float* x, int n, int D, const float* g,
                             const float* beta, float eps, const float* mods, int mstride,
                             const int* rows, int so, int sc, void* y, hipStream_t s) {
-  dim3 grid((n + 3) / 4);
-  if (out_bf16)
-    k_norm_mod<NORM, MOD, bf16_t><<<grid, 256, 0, s>>>(x, n, D, g, beta, eps, mods, mstride, rows,
-                                                        so, sc, (bf16_t*)y);
-  else
-    k_norm_mod<NORM, MOD, float><<<grid, 256, 0, s>>>(x, n, D, g, beta, eps, mods, mstride, rows,
-                                                       so, sc, (float*)y);
+  const int per_lane = (D + 255) / 256;  // float4 chunks per lane
+#define NMC(C_) launch_norm_mod<NORM, MOD, C_>(out_bf16, x, n, D, g, beta, eps, mods, mstride, rows, so, sc, y, s)
+  if (per_lane <= 4) NMC(4);
+  else if (per_lane <= 8) NMC(8);
+  else if (per_lane <= 12) NMC(12);
+  else NMC(16);
+#undef NMC
 }
 
 hipError_t norm_mod(int norm, int mod, bool out_bf16, const float* x, int n, int D, const float* g,

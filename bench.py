@@ -29,7 +29,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(spec, wl):
+def cpu_baseline(spec, wl, seq_starts=None):
     """The fp64 oracle on the same workload, on the host cores: two bounded
     samples of query rows (K/V for all tokens are always computed), timed and
     extrapolated linearly to the whole block."""
@@ -46,7 +46,7 @@ def cpu_baseline(spec, wl):
     for m in (m1, m2):
         rows = np.linspace(0, spec.n - 1, m).astype(np.int64)
         t0 = time.perf_counter()
-        O.block(spec, wl.x, wl.rows, wl.pos, sig, wl.weights, qrows=rows)
+        O.block(spec, wl.x, wl.rows, wl.pos, sig, wl.weights, qrows=rows, seq_starts=seq_starts)
         times[m] = time.perf_counter() - t0
         log(f"cpu oracle: {m} query rows in {times[m]:.2f} s")
     per_row = max((times[m2] - times[m1]) / (m2 - m1), 1e-9)
@@ -89,6 +89,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="t2va")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seqs", type=int, default=1,
+                    help="pack the workload as this many independent samples of equal length "
+                         "(block-diagonal attention); 1 = one sequence")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times (the "
                          "calibration kernel for the HBM byte counters) and exit")
@@ -112,6 +115,9 @@ def main():
     from synth.device import to_device
 
     spec = W.spec_by_name(args.workload)
+    seq_starts = None
+    if args.seqs > 1:
+        seq_starts = [spec.n * i // args.seqs for i in range(args.seqs + 1)]
     t0 = time.perf_counter()
     wl = W.make_workload(spec)
     dev = to_device(wl)
@@ -124,7 +130,7 @@ def main():
     log(f"setup {time.perf_counter() - t0:.1f} s; workspace {ws.numel() / 2**30:.2f} GiB")
 
     for _ in range(args.warmup):
-        blk.forward(dev.x, dev.rows, dev.pos, sig, out=out, workspace=ws)
+        blk.forward(dev.x, dev.rows, dev.pos, sig, out=out, workspace=ws, seq_starts=seq_starts)
     torch.cuda.synchronize()
     log("warmup done")
 
@@ -135,7 +141,7 @@ def main():
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
-        blk.forward(dev.x, dev.rows, dev.pos, sig, out=out, workspace=ws)
+        blk.forward(dev.x, dev.rows, dev.pos, sig, out=out, workspace=ws, seq_starts=seq_starts)
     ev1.record(stream)
     torch.cuda.synchronize()
     phases = dit.profile_end()
@@ -158,6 +164,8 @@ def main():
     del xc
 
     attn_flops = spec.attn_flops()
+    if seq_starts is not None:  # block-diagonal: 4 * sum(len^2) * D
+        attn_flops = 4.0 * spec.D * sum((b - a) ** 2 for a, b in zip(seq_starts, seq_starts[1:]))
     gemm_flops = spec.gemm_flops()
     attn_ms = ph["attention"]
     gemm_ms = ph["qkv_gemm"] + ph["out_gemm"] + ph["fc1_gemm"] + ph["fc2_gemm"]
@@ -188,6 +196,7 @@ def main():
             if spec.name == "t2va" else f"{spec.name}: n={spec.n} D={spec.D}",
             "n": spec.n, "D": spec.D, "heads": spec.H, "head_dim": spec.hd, "ffn": spec.F,
             "parallelism": "single GPU",
+            "samples": args.seqs,
         },
         "attention_tflops": attn_tf,
         "attention_frac_mfma_peak": attn_tf / PEAK_BF16_TFLOPS,
@@ -205,11 +214,12 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": attn_tf / PEAK_BF16_TFLOPS,
-            "traffic": measured_traffic(ATTN_SOURCES) if spec.name == "t2va" else None,
+            "traffic": (measured_traffic(ATTN_SOURCES)
+                        if spec.name == "t2va" and seq_starts is None else None),
         },
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(spec, wl)
+        res["cpu_baseline"] = cpu_baseline(spec, wl, seq_starts)
     print(json.dumps(res), flush=True)
 
 

@@ -9,6 +9,7 @@
  *   [MMH3]   docs.rs source page of cortiq-engine 0.5.72, src/mmh3.rs
  *   [SIGLIP] docs.rs source page of ffai-argus 0.7.0, src/siglip.rs
  *   [ZIMG]   ollama fork, x/imagegen/models/zimage/transformer.go
+ *   [ENC]    docs.rs source page of inferencelayer 0.2.1, src/encoder_cpu.rs
  *
  * Conventions for every entry point:
  *   - Data pointers are DEVICE memory owned by the caller, except where an
@@ -192,6 +193,21 @@ dit_status dit_block_forward(const dit_config* cfg, const void* prepared, const 
                              const double* sigmas, int32_t n_sigmas, float* out,
                              void* workspace, size_t ws_bytes, void* stream);
 
+/* Several independent samples packed in one sequence ([ENC] attention_ragged
+ * over seq_starts: each query attends only to the keys of its own sample, so
+ * the packed call equals the samples run one by one; every other step of the
+ * block is per token).  seq_starts: HOST int32 [nseq + 1], seq_starts[0] = 0,
+ * non-decreasing (empty samples allowed), seq_starts[nseq] = n, 1 <= nseq <=
+ * DIT_MAX_SEQS; refused with DIT_ESHAPE otherwise.  Positions and rows are the
+ * caller's per token (a sample's positions are its own).  Arguments otherwise as
+ * dit_block_forward; nseq = 1 computes exactly what dit_block_forward does. */
+#define DIT_MAX_SEQS 64
+dit_status dit_block_forward_packed(const dit_config* cfg, const void* prepared, const float* x,
+                                    int32_t n, const int32_t* rows, const float* pos,
+                                    const double* sigmas, int32_t n_sigmas,
+                                    const int32_t* seq_starts, int32_t nseq, float* out,
+                                    void* workspace, size_t ws_bytes, void* stream);
+
 /* Standalone full bidirectional attention over one packed sequence, per head
  * ([MMH3] attention; online softmax with normalization deferred to the output,
  * [SIGLIP] deferred normalisation):
@@ -203,6 +219,13 @@ dit_status dit_block_forward(const dit_config* cfg, const void* prepared, const 
  * ldn must be a multiple of 128 and >= n. */
 dit_status dit_attention(const dit_config* cfg, const void* q, const void* k, const void* vt,
                          int32_t n, int32_t ldn, float score_scale, void* o, void* stream);
+
+/* dit_attention with the samples of seq_starts (host, as in
+ * dit_block_forward_packed): query i attends to the keys of its own sample. */
+dit_status dit_attention_packed(const dit_config* cfg, const void* q, const void* k,
+                                const void* vt, int32_t n, int32_t ldn,
+                                const int32_t* seq_starts, int32_t nseq, float score_scale,
+                                void* o, void* stream);
 
 /* Per-phase timing of dit_block_forward ([MMH3] per-phase profiler: one
  * stopwatch per phase, none overlapping).  dit_profile_begin(max_calls) arms

@@ -232,6 +232,36 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.n
     return out
 
 
+def sample_ranges(seq_starts: Sequence[int], n: int) -> List[tuple]:
+    """[(a, e)] token ranges of the packed samples; checks 0 = s_0 <= ... <= s_N = n."""
+    st = [int(v) for v in seq_starts]
+    if len(st) < 2 or st[0] != 0 or st[-1] != n or any(b < a for a, b in zip(st, st[1:])):
+        raise ValueError("seq_starts must rise from 0 to n")
+    return list(zip(st[:-1], st[1:]))
+
+
+def attention_packed(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                     qtok: np.ndarray, seq_starts: Sequence[int]) -> np.ndarray:
+    """Attention over independent samples packed in one sequence ([ENC]
+    ``attention_ragged``): query row r (token qtok[r]) of sample s attends only
+    to the keys of that sample, tokens [seq_starts[s], seq_starts[s+1]).
+
+    q [H, m, hd]; k, v [H, n, hd] over all tokens -> [H, m, hd]."""
+    qtok = np.asarray(qtok, dtype=np.int64)
+    out = np.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=F64)
+    for a, e in sample_ranges(seq_starts, k.shape[1]):
+        r = np.nonzero((qtok >= a) & (qtok < e))[0]
+        if r.size:
+            out[:, r] = attention(q[:, r], k[:, a:e], v[:, a:e], scale)
+    return out
+
+
+def _attend(q, k, v, scale, sel, seq_starts):
+    if seq_starts is None:
+        return attention(q, k, v, scale)
+    return attention_packed(q, k, v, scale, sel, seq_starts)
+
+
 def _heads(y: np.ndarray, H: int, hd: int) -> np.ndarray:
     """[m, H*hd] -> [H, m, hd] (head h is columns [h*hd, (h+1)*hd))."""
     return np.ascontiguousarray(y.reshape(y.shape[0], H, hd).transpose(1, 0, 2))
@@ -260,13 +290,15 @@ def _sel(qrows: Optional[np.ndarray], n: int) -> np.ndarray:
 
 def mmh3_block(spec, x: np.ndarray, rows: np.ndarray, pos: Optional[np.ndarray],
                sigmas: Sequence[float], w: Dict[str, np.ndarray],
-               qrows: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+               qrows: Optional[np.ndarray] = None,
+               seq_starts: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """One MiniMax-H3 block over the packed sequence.
 
     Stages (fp64): mods [R, 6D]; xn [n, D]; q, k, v [H, *, hd] (q and k after
     qk-norm and RoPE, q unscaled); o [m, D]; x1, xn2 [m, D]; a [m, F];
     out [m, D], where m indexes ``qrows`` (all tokens if None).  K and V always
-    cover every token, because every query attends to all of them."""
+    cover every token, because every query attends to all of them (to all of
+    its own sample's, when ``seq_starts`` packs several samples)."""
     D, H, hd, F = spec.D, spec.H, spec.hd, spec.F
     n = x.shape[0]
     x = np.asarray(x, F64)
@@ -293,7 +325,7 @@ def mmh3_block(spec, x: np.ndarray, rows: np.ndarray, pos: Optional[np.ndarray],
         k = rope_rotate(k, ang[None], spec.rope)
         q = rope_rotate(q, ang[sel][None], spec.rope)
 
-    o = _merge(attention(q, k, v, 1.0 / math.sqrt(hd)))
+    o = _merge(_attend(q, k, v, 1.0 / math.sqrt(hd), sel, seq_starts))
     rs = rows[sel]
     x1 = x[sel] + chunk(rs, 2) * _lin(o, w["w_out"])
 
@@ -311,7 +343,8 @@ def mmh3_block(spec, x: np.ndarray, rows: np.ndarray, pos: Optional[np.ndarray],
 
 
 def siglip_layer(spec, x: np.ndarray, w: Dict[str, np.ndarray],
-                 qrows: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                 qrows: Optional[np.ndarray] = None,
+                 seq_starts: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """Pre-LN encoder layer: LN1 -> qkv (+bias) -> attention (scores scaled by
     hd^-1/2) -> out (+bias) + residual -> LN2 -> fc1 (+bias) -> GELU-tanh ->
     fc2 (+bias) + residual.  Stages as in ``mmh3_block`` (no mods)."""
@@ -325,7 +358,7 @@ def siglip_layer(spec, x: np.ndarray, w: Dict[str, np.ndarray],
     k = _heads(_lin(xn, wk, bk), H, hd)
     v = _heads(_lin(xn, wv, bv), H, hd)
     q = _heads(_lin(xn[sel], wq, bq), H, hd)
-    o = _merge(attention(q, k, v, 1.0 / math.sqrt(hd)))
+    o = _merge(_attend(q, k, v, 1.0 / math.sqrt(hd), sel, seq_starts))
     x1 = x[sel] + _lin(o, w["w_out"], w["b_out"])
     xn2 = layer_norm(x1, w["ln2_w"], w["ln2_b"], spec.eps)
     a = gelu_tanh(_lin(xn2, w["w_fc1"], w["b_fc1"]))
@@ -358,7 +391,8 @@ def zimage_mods(spec, t: float, w: Dict[str, np.ndarray]) -> np.ndarray:
 
 
 def zimage_block(spec, x: np.ndarray, pos: np.ndarray, t: float, w: Dict[str, np.ndarray],
-                 qrows: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                 qrows: Optional[np.ndarray] = None,
+                 seq_starts: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """Modulated Z-Image block: x1 = x + tanh(gate_msa) * RMSNorm(Attn(RMSNorm(x)
     * (1 + scale_msa))); out = x1 + tanh(gate_mlp) * RMSNorm(W2(silu(W1 xf) *
     W3 xf)) with xf = RMSNorm(x1) * (1 + scale_mlp).  Interleaved RoPE.
@@ -378,7 +412,7 @@ def zimage_block(spec, x: np.ndarray, pos: np.ndarray, t: float, w: Dict[str, np
     v = _heads(_lin(xn, wv), H, hd)
     q = rope_rotate(rms_norm(_heads(_lin(xn[sel], wq), H, hd), w["q_norm"], spec.qk_eps),
                     ang[sel][None], spec.rope)
-    o = _merge(attention(q, k, v, 1.0 / math.sqrt(hd)))
+    o = _merge(_attend(q, k, v, 1.0 / math.sqrt(hd), sel, seq_starts))
     y = _lin(o, w["w_out"])
     x1 = x[sel] + np.tanh(g_msa) * rms_norm(y, w["post_attn_norm"], spec.eps)
     xn2 = modulate(rms_norm(x1, w["norm2"], spec.eps), None, sc_mlp)
@@ -390,15 +424,16 @@ def zimage_block(spec, x: np.ndarray, pos: np.ndarray, t: float, w: Dict[str, np
                 out=out)
 
 
-def block(spec, x, rows, pos, sigmas, w, qrows=None) -> Dict[str, np.ndarray]:
+def block(spec, x, rows, pos, sigmas, w, qrows=None, seq_starts=None) -> Dict[str, np.ndarray]:
     """Dispatch on the block variant.  ``sigmas``: slot sigmas (mmh3) or
-    [t] (zimage); ignored for siglip."""
+    [t] (zimage); ignored for siglip.  ``seq_starts``: packed samples (None =
+    one sequence)."""
     if spec.variant == "mmh3":
-        return mmh3_block(spec, x, rows, pos, sigmas, w, qrows)
+        return mmh3_block(spec, x, rows, pos, sigmas, w, qrows, seq_starts)
     if spec.variant == "siglip":
-        return siglip_layer(spec, x, w, qrows)
+        return siglip_layer(spec, x, w, qrows, seq_starts)
     if spec.variant == "zimage":
-        return zimage_block(spec, x, pos, sigmas[0], w, qrows)
+        return zimage_block(spec, x, pos, sigmas[0], w, qrows, seq_starts)
     raise ValueError(spec.variant)
 
 
@@ -414,7 +449,8 @@ def rel_rms(a: np.ndarray, ref: np.ndarray) -> float:
 __all__ = [
     "sigma_remap", "sigma_remap_slope", "resolve_sigmas", "mmh3_timestep",
     "adaln_coords", "adaln_mods", "rms_norm", "layer_norm", "modulate", "silu",
-    "gelu_tanh", "rope_angles", "rope_rotate", "attention", "mmh3_block",
+    "gelu_tanh", "rope_angles", "rope_rotate", "attention", "sample_ranges",
+    "attention_packed", "mmh3_block",
     "siglip_layer", "timestep_embedding", "zimage_mods", "zimage_block", "block",
     "rel_rms",
 ]

@@ -475,28 +475,60 @@ dit_status dit_adaln_modulate(const dit_config* c, const void* prepared, const f
   return launch_prenorm(c, prepared, x, n, rows, mods_out, half, xn_out, s);
 }
 
-dit_status dit_attention(const dit_config* c, const void* q, const void* k, const void* vt,
-                         int32_t n, int32_t ldn, float score_scale, void* o, void* stream) {
+// Host-side check of a packed-sample table: 1 <= nseq <= DIT_MAX_SEQS,
+// starts[0] = 0, non-decreasing, starts[nseq] = n.
+static dit_status check_seqs(const int32_t* seq_starts, int32_t nseq, int32_t n) {
+  if (!seq_starts) return fail(DIT_EINVAL, "seq_starts is NULL");
+  if (nseq < 1 || nseq > DIT_MAX_SEQS)
+    return fail(DIT_ESHAPE, "nseq=%d outside [1, %d]", nseq, DIT_MAX_SEQS);
+  if (seq_starts[0] != 0) return fail(DIT_ESHAPE, "seq_starts[0]=%d, must be 0", seq_starts[0]);
+  for (int i = 0; i < nseq; ++i)
+    if (seq_starts[i + 1] < seq_starts[i])
+      return fail(DIT_ESHAPE, "seq_starts decreases at %d (%d -> %d)", i, seq_starts[i], seq_starts[i + 1]);
+  if (seq_starts[nseq] != n)
+    return fail(DIT_ESHAPE, "seq_starts[nseq]=%d must equal n=%d", seq_starts[nseq], n);
+  return DIT_OK;
+}
+
+static dit_status attention_impl(const dit_config* c, const void* q, const void* k, const void* vt,
+                          int32_t n, int32_t ldn, const int32_t* seq_starts, int32_t nseq,
+                          float score_scale, void* o, void* stream) {
   DIT_TRY(check_config(c));
   if (n < 0 || ldn < n || ldn % 128) return fail(DIT_ESHAPE, "need 0 <= n <= ldn, ldn %% 128 == 0 (n=%d ldn=%d)", n, ldn);
+  if (seq_starts) DIT_TRY(check_seqs(seq_starts, nseq, n));
   if (n == 0) return DIT_OK;
   if (!q || !k || !vt || !o) return fail(DIT_EINVAL, "q/k/vt/o is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
     return fail(DIT_EALIGN, "q/k/vt/o not 16-byte aligned");
   if (!isfinite(score_scale)) return fail(DIT_EINVAL, "score_scale not finite");
   const float log2e = 1.4426950408889634f;
+  dit::SeqTable tab;
+  dit::make_seq_table(seq_starts, nseq, n, &tab);
   HIP_TRY(dit::attention(c->dtype, c->hd, q, k, vt, n, ldn, c->H, score_scale * log2e, o, nullptr,
-                         (hipStream_t)stream),
+                         tab, (hipStream_t)stream),
           "attention");
   return DIT_OK;
 }
 
-dit_status dit_block_forward(const dit_config* c, const void* prepared, const float* x, int32_t n,
-                             const int32_t* rows, const float* pos, const double* sigmas,
-                             int32_t n_sigmas, float* out, void* workspace, size_t ws_bytes,
-                             void* stream) {
+dit_status dit_attention(const dit_config* c, const void* q, const void* k, const void* vt,
+                         int32_t n, int32_t ldn, float score_scale, void* o, void* stream) {
+  return attention_impl(c, q, k, vt, n, ldn, nullptr, 0, score_scale, o, stream);
+}
+
+dit_status dit_attention_packed(const dit_config* c, const void* q, const void* k, const void* vt,
+                                int32_t n, int32_t ldn, const int32_t* seq_starts, int32_t nseq,
+                                float score_scale, void* o, void* stream) {
+  if (!seq_starts) return fail(DIT_EINVAL, "seq_starts is NULL");
+  return attention_impl(c, q, k, vt, n, ldn, seq_starts, nseq, score_scale, o, stream);
+}
+
+static dit_status block_forward_impl(const dit_config* c, const void* prepared, const float* x, int32_t n,
+                              const int32_t* rows, const float* pos, const double* sigmas,
+                              int32_t n_sigmas, const int32_t* seq_starts, int32_t nseq, float* out,
+                              void* workspace, size_t ws_bytes, void* stream) {
   DIT_TRY(check_config(c));
   if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
+  if (seq_starts) DIT_TRY(check_seqs(seq_starts, nseq, n));
   if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
   DIT_TRY(check_sigmas(c, sigmas, n_sigmas));
   if (n == 0) return DIT_OK;
@@ -575,8 +607,13 @@ dit_status dit_block_forward(const dit_config* c, const void* prepared, const fl
   }
   pm.mark(3);
   // a5: attention (q carries log2(e) hd^-1/2; the kernel works in base 2)
-  HIP_TRY(dit::attention(dt, hd, q, k, vt, n, ldn, H, 1.0f, o, bf ? at<float>(workspace, L.part) : nullptr, s),
-          "attention");
+  {
+    dit::SeqTable tab;
+    dit::make_seq_table(seq_starts, nseq, n, &tab);
+    HIP_TRY(dit::attention(dt, hd, q, k, vt, n, ldn, H, 1.0f, o,
+                           bf ? at<float>(workspace, L.part) : nullptr, tab, s),
+            "attention");
+  }
   pm.mark(4);
   // a6: out projection + residual
   if (c->variant == DIT_ZIMAGE) {
@@ -648,6 +685,24 @@ dit_status dit_block_forward(const dit_config* c, const void* prepared, const fl
   }
   pm.mark(8);
   return DIT_OK;
+}
+
+dit_status dit_block_forward(const dit_config* c, const void* prepared, const float* x, int32_t n,
+                             const int32_t* rows, const float* pos, const double* sigmas,
+                             int32_t n_sigmas, float* out, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  return block_forward_impl(c, prepared, x, n, rows, pos, sigmas, n_sigmas, nullptr, 0, out,
+                            workspace, ws_bytes, stream);
+}
+
+dit_status dit_block_forward_packed(const dit_config* c, const void* prepared, const float* x,
+                                    int32_t n, const int32_t* rows, const float* pos,
+                                    const double* sigmas, int32_t n_sigmas,
+                                    const int32_t* seq_starts, int32_t nseq, float* out,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  if (!seq_starts) return fail(DIT_EINVAL, "seq_starts is NULL");
+  return block_forward_impl(c, prepared, x, n, rows, pos, sigmas, n_sigmas, seq_starts, nseq, out,
+                            workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -86,8 +86,21 @@ constexpr int kAttnQueryRows = 256; // queries per workgroup
 inline size_t attention_part_bytes(int hd) {
   return (size_t)kAttnMaxSlots * kAttnQueryRows * (size_t)(hd + 2) * sizeof(float);
 }
+// Independent samples packed in one sequence: sample s is tokens
+// [start[s], start[s+1]) and its queries attend only to its own keys.
+// blk[s] = query blocks of kAttnQueryRows before sample s (blk[nseq] = total).
+// Passed by value to the kernels.
+constexpr int kMaxSeqs = 64;
+struct SeqTable {
+  int nseq;
+  int start[kMaxSeqs + 1];
+  int blk[kMaxSeqs + 1];
+};
+// Builds the table from host offsets (nullptr: one sequence of n tokens).
+void make_seq_table(const int* seq_starts, int nseq, int n, SeqTable* t);
 hipError_t attention(int dtype, int hd, const void* q, const void* k, const void* vt, int n,
-                     int ldn, int H, float scale_log2, void* o, float* part, hipStream_t s);
+                     int ldn, int H, float scale_log2, void* o, float* part, const SeqTable& seqs,
+                     hipStream_t s);
 
 // ---- weight preparation ---------------------------------------------------------------
 // dst[r, :] = src[perm(r), :] * (r < scale_rows ? scale : 1); perm = SwiGLU group interleave

@@ -35,18 +35,43 @@ constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kAttnRows = 32 * kAttnWaves;
 static_assert(kAttnRows == kAttnQueryRows, "partial-buffer rows");
 
-// Work units are (head, block of 256 queries), head-major.  Units below
-// `whole` take every key and write O.  The remaining units (the last, partial
-// round of the grid) are each split into `nsplit` consecutive key ranges, one
-// workgroup per range, which write unnormalized partial results (O, running
-// maximum, row sum) for k_attn_merge to combine.
+// Unit u -> head h, its sample's token range [ks, ke) and first query q0.  The
+// scan over the table is unrolled (constant indices: scalar kernel-argument
+// loads) and keeps the last sample whose first block is <= the unit's block.
+DIT_DEV void unit_of(const SeqTable& t, int u, int& h, int& ks, int& ke, int& q0) {
+  const int per_head = t.blk[t.nseq];
+  h = u / per_head;
+  const int b = u - h * per_head;
+  int b0 = 0;
+  ks = t.start[0];
+  ke = t.start[1];
+#pragma unroll
+  for (int i = 1; i < kMaxSeqs; ++i) {
+    if (i < t.nseq && b >= t.blk[i]) {
+      b0 = t.blk[i];
+      ks = t.start[i];
+      ke = t.start[i + 1];
+    }
+  }
+  q0 = ks + (b - b0) * kAttnRows;
+}
+
+// Work units are (head, block of 256 queries of one sample), head-major, the
+// query blocks of each sample starting at its first token.  A unit's queries
+// attend to the keys of their sample ([ENC] attention_ragged: a ragged batch
+// behaves as the sequences run alone); with one sample that is every key.
+// Units below `whole` take all of their keys and write O.  The remaining units
+// (the last, partial round of the grid) are each split into `nsplit`
+// consecutive key ranges, one workgroup per range, which write unnormalized
+// partial results (O, running maximum, row sum) for k_attn_merge to combine.
 template <int HD, bool UNIT>
 __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __restrict__ Q,
                                                       const bf16_t* __restrict__ Kp,
                                                       const bf16_t* __restrict__ Vt, int n,
                                                       int ldn, int H, float scale_log2,
                                                       bf16_t* __restrict__ O, int whole,
-                                                      int nsplit, float* __restrict__ part) {
+                                                      int nsplit, float* __restrict__ part,
+                                                      SeqTable seqs) {
   constexpr int KT = 64;        // keys per tile
   constexpr int NC = HD / 16;   // MFMA k-steps over the head dim
   constexpr int ND = HD / 32;   // 32-row blocks of O^T
@@ -63,17 +88,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int qblocks = (n + kAttnRows - 1) / kAttnRows;
-  const int ntiles = (n + KT - 1) / KT;
   const int w = blockIdx.x;
   const bool split = w >= whole;
   const int u = split ? whole + (w - whole) / nsplit : w;
   const int j = split ? (w - whole) % nsplit : 0;
   const int ns = split ? nsplit : 1;
-  const int h = u / qblocks;
-  const int q0 = (u - h * qblocks) * kAttnRows + wave * 32;
-  // key tiles [t_lo, t_hi) of this workgroup
-  const int t_lo = j * ntiles / ns, t_hi = (j + 1) * ntiles / ns;
+  int h, ks, ke, q0;
+  unit_of(seqs, u, h, ks, ke, q0);
+  q0 += wave * 32;
+  // key tiles [t_lo, t_hi) of this workgroup, out of the sample's [T0, T1)
+  const int T0 = ks / KT, T1 = (ke + KT - 1) / KT;
+  const int t_lo = T0 + j * (T1 - T0) / ns, t_hi = T0 + (j + 1) * (T1 - T0) / ns;
   const bf16_t* Qh = Q + (size_t)h * ldn * HD;
   const bf16_t* Kh = Kp + (size_t)h * ldn * HD;
   const bf16_t* Vh = Vt + (size_t)h * HD * ldn;
@@ -128,7 +153,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
 #pragma unroll
   for (int v = 0; v < 16; ++v) cneg[v] = 0.0f;
 
-  const int t_full = min(t_hi, n / KT);  // tiles below t_full have 64 valid keys
+  const int t_full = min(t_hi, ke / KT);  // tiles in [ceil(ks/KT), t_full) are all valid
   ATT_GLOAD(t_lo * KT);
   ATT_SSTORE(t_lo & 1);
   ATT_GLOAD(min(t_lo + 1, t_hi - 1) * KT);
@@ -154,7 +179,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
       _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                     \
       _Pragma("unroll") for (int v = 0; v < 16; ++v) {                                     \
         const int key = t * KT + kb * 32 + 16 * (v >> 3) + 8 * half + (v & 7);            \
-        if (key >= n) s_[kb][v] = -INFINITY;                                               \
+        if (key < ks || key >= ke) s_[kb][v] = -INFINITY;                                  \
       }                                                                                    \
     }                                                                                      \
     float mx_ = -INFINITY;                                                                 \
@@ -193,8 +218,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
     }                                                                                      \
   } while (0)
 
-  // Full tiles in the loop, the ragged last tile (if any) after it.
-  for (int t = t_lo; t < t_full; ++t) {
+  // A first tile that starts before the sample (masked), the full tiles in the
+  // loop, a ragged last tile (masked) after it.
+  int t = t_lo;
+  if (t * KT < ks) {
+    const int b = t & 1;
+    ATT_TILE(true);
+    ATT_SSTORE(b ^ 1);
+    ATT_GLOAD(min(t + 2, t_hi - 1) * KT);
+    __syncthreads();
+    ++t;
+  }
+  for (; t < t_full; ++t) {
     const int b = t & 1;
     ATT_TILE(false);
     // Unconditional (see the GEMM): tile t+1 to LDS, then the loads of t+2.
@@ -202,8 +237,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
     ATT_GLOAD(min(t + 2, t_hi - 1) * KT);
     __syncthreads();
   }
-  if (t_full < t_hi) {
-    const int t = t_full, b = t & 1;
+  if (t < t_hi) {
+    const int b = t & 1;
     ATT_TILE(true);
   }
 #undef ATT_TILE
@@ -232,7 +267,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
     return;
   }
   const float inv = 1.0f / lt;
-  if (qi < n) {
+  if (qi < ke) {
     bf16_t* orow = O + (size_t)qi * (H * HD) + h * HD;
 #pragma unroll
     for (int d = 0; d < ND; ++d)
@@ -246,16 +281,35 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
   }
 }
 
-// fp32: one thread per query, keys in LDS tiles of 32, online softmax in base 2.
+// Token i -> the token range [a, e) of its sample (unrolled scan, as unit_of).
+DIT_DEV void sample_of(const SeqTable& t, int i, int& a, int& e) {
+  a = t.start[0];
+  e = t.start[1];
+#pragma unroll
+  for (int s = 1; s < kMaxSeqs; ++s)
+    if (s < t.nseq && i >= t.start[s]) {
+      a = t.start[s];
+      e = t.start[s + 1];
+    }
+}
+
+// fp32: one thread per query, keys in LDS tiles of 32, online softmax in base
+// 2.  The block walks the keys of every sample its queries belong to; each
+// thread uses only its own sample's keys.
 template <int HD>
 __global__ __launch_bounds__(128) void k_attn_f32(const float* __restrict__ Q,
                                                   const float* __restrict__ Kp,
                                                   const float* __restrict__ Vt, int n, int ldn,
-                                                  float scale_log2, float* __restrict__ O) {
+                                                  float scale_log2, SeqTable seqs,
+                                                  float* __restrict__ O) {
   __shared__ float sk[32][HD + 1];
   __shared__ float sv[32][HD + 1];
   const int h = blockIdx.y, H = gridDim.y;
   const int qi = blockIdx.x * 128 + threadIdx.x;
+  int qs, qe, blo, bhi, t0, t1;
+  sample_of(seqs, min(qi, n - 1), qs, qe);
+  sample_of(seqs, blockIdx.x * 128, blo, t0);
+  sample_of(seqs, min(blockIdx.x * 128 + 127, n - 1), t1, bhi);
   const float* qr = Q + ((size_t)h * ldn + qi) * HD;
   float q[HD], acc[HD];
 #pragma unroll
@@ -264,7 +318,7 @@ __global__ __launch_bounds__(128) void k_attn_f32(const float* __restrict__ Q,
     acc[d] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f;
-  for (int k0 = 0; k0 < n; k0 += 32) {
+  for (int k0 = blo & ~31; k0 < bhi; k0 += 32) {
     for (int e = threadIdx.x; e < 32 * HD; e += 128) {
       int j = e / HD, d = e % HD;
       sk[j][d] = Kp[((size_t)h * ldn + k0 + j) * HD + d];
@@ -272,27 +326,29 @@ __global__ __launch_bounds__(128) void k_attn_f32(const float* __restrict__ Q,
       sv[j2][d2] = Vt[((size_t)h * HD + d2) * ldn + k0 + j2];
     }
     __syncthreads();
-    const int kn = min(32, n - k0);
-    float sc[32];
-    float mx = m;
-    for (int j = 0; j < kn; ++j) {
-      float s = 0.0f;
+    const int j0 = max(qs - k0, 0), j1 = min(qe - k0, 32);  // this query's keys in the tile
+    if (j1 > j0) {
+      float sc[32];
+      float mx = m;
+      for (int j = j0; j < j1; ++j) {
+        float s = 0.0f;
 #pragma unroll
-      for (int d = 0; d < HD; ++d) s = fmaf(q[d], sk[j][d], s);
-      sc[j] = s * scale_log2;
-      mx = fmaxf(mx, sc[j]);
+        for (int d = 0; d < HD; ++d) s = fmaf(q[d], sk[j][d], s);
+        sc[j] = s * scale_log2;
+        mx = fmaxf(mx, sc[j]);
+      }
+      const float alpha = exp2f(m - mx);  // m = -inf before the first key: alpha = 0
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < HD; ++d) acc[d] *= alpha;
+      for (int j = j0; j < j1; ++j) {
+        float p = exp2f(sc[j] - mx);
+        l += p;
+#pragma unroll
+        for (int d = 0; d < HD; ++d) acc[d] = fmaf(p, sv[j][d], acc[d]);
+      }
+      m = mx;
     }
-    const float alpha = exp2f(m - mx);
-    l *= alpha;
-#pragma unroll
-    for (int d = 0; d < HD; ++d) acc[d] *= alpha;
-    for (int j = 0; j < kn; ++j) {
-      float p = exp2f(sc[j] - mx);
-      l += p;
-#pragma unroll
-      for (int d = 0; d < HD; ++d) acc[d] = fmaf(p, sv[j][d], acc[d]);
-    }
-    m = mx;
     __syncthreads();
   }
   if (qi < n) {
@@ -307,18 +363,17 @@ __global__ __launch_bounds__(128) void k_attn_f32(const float* __restrict__ Q,
 // M = max m_j, O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j.  One wave per
 // query row, lanes over the head dimension.
 template <int HD>
-__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part, int n, int H,
+__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part, int H,
                                                     int whole, int nsplit, int nunits,
-                                                    bf16_t* __restrict__ O) {
+                                                    SeqTable seqs, bf16_t* __restrict__ O) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);  // (split unit, query) row
   if (r >= nunits * kAttnRows) return;
   const int us = r / kAttnRows, ql = r % kAttnRows;
-  const int u = whole + us;
-  const int qblocks = (n + kAttnRows - 1) / kAttnRows;
-  const int h = u / qblocks;
-  const int qi = (u - h * qblocks) * kAttnRows + ql;
-  if (qi >= n) return;
+  int h, ks, ke, q0;
+  unit_of(seqs, whole + us, h, ks, ke, q0);
+  const int qi = q0 + ql;
+  if (qi >= ke) return;
   const float* pml = part + (size_t)kAttnMaxSlots * kAttnRows * HD;
   float M = -INFINITY;
   for (int j = 0; j < nsplit; ++j)
@@ -356,26 +411,50 @@ int device_cus() {
 }
 }  // namespace
 
+void make_seq_table(const int* seq_starts, int nseq, int n, SeqTable* t) {
+  if (!seq_starts) {
+    t->nseq = 1;
+    t->start[0] = 0;
+    t->start[1] = n;
+    t->blk[0] = 0;
+    t->blk[1] = (n + kAttnRows - 1) / kAttnRows;
+    return;
+  }
+  t->nseq = nseq;
+  t->blk[0] = 0;
+  for (int i = 0; i <= nseq; ++i) t->start[i] = seq_starts[i];
+  for (int i = 0; i < nseq; ++i)
+    t->blk[i + 1] = t->blk[i] + (seq_starts[i + 1] - seq_starts[i] + kAttnRows - 1) / kAttnRows;
+}
+
 hipError_t attention(int dtype, int hd, const void* q, const void* k, const void* vt, int n,
-                     int ldn, int H, float scale_log2, void* o, float* part, hipStream_t s) {
+                     int ldn, int H, float scale_log2, void* o, float* part, const SeqTable& seqs,
+                     hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (dtype == BF16) {
     const bf16_t *Qb = (const bf16_t*)q, *Kb = (const bf16_t*)k, *Vb = (const bf16_t*)vt;
     bf16_t* Ob = (bf16_t*)o;
-    // One workgroup per CU at a time: units = H * qblocks run in rounds of
-    // `cus`.  A last round that would leave at least half the CUs idle is
-    // split along the keys so that it fills them.
-    const int units = H * ((n + kAttnRows - 1) / kAttnRows);
+    // One workgroup per CU at a time: units = H * query blocks run in rounds
+    // of `cus`.  A last round that would leave at least half the CUs idle is
+    // split along the keys so that it fills them (each range keeps at least
+    // one key tile of the shortest sample).
+    const int units = H * seqs.blk[seqs.nseq];
+    if (units == 0) return hipSuccess;
+    int min_tiles = 1 << 30;
+    for (int i = 0; i < seqs.nseq; ++i) {
+      const int a = seqs.start[i], e = seqs.start[i + 1];
+      if (e > a) min_tiles = min(min_tiles, (e + 63) / 64 - a / 64);
+    }
     const int cus = min(device_cus(), kAttnMaxSlots);
     const int tail = units % cus;
-    const int ntiles = (n + 63) / 64;
-    int nsplit = tail ? min(min(cus / tail, 8), ntiles) : 1;
+    int nsplit = tail ? min(min(cus / tail, 8), min_tiles) : 1;
     if (!part || nsplit < 2) nsplit = 1;
     const int whole = nsplit > 1 ? units - tail : units;
     const int grid = whole + (units - whole) * nsplit;
     const bool unit = scale_log2 == 1.0f;
-#define ATT_LAUNCH(HD_, U_) \
-  k_attn_bf16<HD_, U_><<<grid, kAttnThreads, 0, s>>>(Qb, Kb, Vb, n, ldn, H, scale_log2, Ob, whole, nsplit, part)
+#define ATT_LAUNCH(HD_, U_)                                                                      \
+  k_attn_bf16<HD_, U_><<<grid, kAttnThreads, 0, s>>>(Qb, Kb, Vb, n, ldn, H, scale_log2, Ob, whole, \
+                                                     nsplit, part, seqs)
     if (hd == 128 && unit) ATT_LAUNCH(128, true);
     else if (hd == 128) ATT_LAUNCH(128, false);
     else if (unit) ATT_LAUNCH(64, true);
@@ -384,18 +463,18 @@ hipError_t attention(int dtype, int hd, const void* q, const void* k, const void
     if (nsplit > 1) {
       const int rows = (units - whole) * kAttnRows;
       if (hd == 128)
-        k_attn_merge<128><<<(rows + 3) / 4, 256, 0, s>>>(part, n, H, whole, nsplit, units - whole, Ob);
+        k_attn_merge<128><<<(rows + 3) / 4, 256, 0, s>>>(part, H, whole, nsplit, units - whole, seqs, Ob);
       else
-        k_attn_merge<64><<<(rows + 3) / 4, 256, 0, s>>>(part, n, H, whole, nsplit, units - whole, Ob);
+        k_attn_merge<64><<<(rows + 3) / 4, 256, 0, s>>>(part, H, whole, nsplit, units - whole, seqs, Ob);
     }
   } else {
     dim3 grid((n + 127) / 128, H);
     if (hd == 128)
       k_attn_f32<128><<<grid, 128, 0, s>>>((const float*)q, (const float*)k, (const float*)vt, n,
-                                           ldn, scale_log2, (float*)o);
+                                           ldn, scale_log2, seqs, (float*)o);
     else
       k_attn_f32<64><<<grid, 128, 0, s>>>((const float*)q, (const float*)k, (const float*)vt, n,
-                                          ldn, scale_log2, (float*)o);
+                                          ldn, scale_log2, seqs, (float*)o);
   }
   return hipGetLastError();
 }

@@ -86,8 +86,15 @@ def _load() -> ctypes.CDLL:
         "dit_block_forward": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_int32, c_void_p,
                                         c_void_p, P(c_double), c_int32, c_void_p, c_void_p,
                                         c_size_t, c_void_p]),
+        "dit_block_forward_packed": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_int32,
+                                               c_void_p, c_void_p, P(c_double), c_int32,
+                                               P(c_int32), c_int32, c_void_p, c_void_p, c_size_t,
+                                               c_void_p]),
         "dit_attention": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                     c_float, c_void_p, c_void_p]),
+        "dit_attention_packed": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_void_p, c_int32,
+                                           c_int32, P(c_int32), c_int32, c_float, c_void_p,
+                                           c_void_p]),
         "dit_profile_begin": (c_int32, [c_int32]),
         "dit_profile_end": (c_int32, [P(c_double), P(c_int32)]),
         "dit_phase_name": (ctypes.c_char_p, [c_int32]),
@@ -165,6 +172,12 @@ def _dbl(vals: Sequence[float]):
     return arr, len(vals)
 
 
+def _starts(seq_starts: Sequence[int]):
+    vals = [int(v) for v in seq_starts]
+    arr = (c_int32 * max(len(vals), 1))(*vals)
+    return arr, len(vals) - 1
+
+
 def validate(cfg: DitConfig) -> None:
     _check(lib.dit_validate_config(ctypes.byref(cfg)))
 
@@ -205,16 +218,25 @@ class Block:
         return self._ws
 
     def forward(self, x, rows, pos, sigmas: Sequence[float], out=None, workspace=None,
-                stream=None):
+                stream=None, seq_starts: Optional[Sequence[int]] = None):
+        """One block forward; ``seq_starts`` (host ints, [0, ..., n]) packs
+        independent samples whose queries see only their own keys."""
         import torch
         n = int(x.shape[0])
         if out is None:
             out = torch.empty_like(x)
         ws = self.workspace(n) if workspace is None else workspace
         sg, ns = _dbl(sigmas)
-        _check(lib.dit_block_forward(ctypes.byref(self.cfg), self.prepared.data_ptr(), _ptr(x), n,
-                                     _ptr(rows), _ptr(pos), sg, ns, _ptr(out), ws.data_ptr(),
-                                     ws.numel(), _stream(stream)))
+        if seq_starts is None:
+            _check(lib.dit_block_forward(ctypes.byref(self.cfg), self.prepared.data_ptr(), _ptr(x),
+                                         n, _ptr(rows), _ptr(pos), sg, ns, _ptr(out),
+                                         ws.data_ptr(), ws.numel(), _stream(stream)))
+        else:
+            st, nseq = _starts(seq_starts)
+            _check(lib.dit_block_forward_packed(ctypes.byref(self.cfg), self.prepared.data_ptr(),
+                                                _ptr(x), n, _ptr(rows), _ptr(pos), sg, ns, st,
+                                                nseq, _ptr(out), ws.data_ptr(), ws.numel(),
+                                                _stream(stream)))
         return out
 
     def adaln_modulate(self, x, rows, sigmas: Sequence[float], half: int, xn_out, mods_out=None,
@@ -233,9 +255,15 @@ class Block:
         return mods_out
 
 
-def attention(cfg: DitConfig, q, k, vt, n: int, ldn: int, score_scale: float, o, stream=None):
-    _check(lib.dit_attention(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(vt), n, ldn, score_scale,
-                             _ptr(o), _stream(stream)))
+def attention(cfg: DitConfig, q, k, vt, n: int, ldn: int, score_scale: float, o, stream=None,
+              seq_starts: Optional[Sequence[int]] = None):
+    if seq_starts is None:
+        _check(lib.dit_attention(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(vt), n, ldn,
+                                 score_scale, _ptr(o), _stream(stream)))
+    else:
+        st, nseq = _starts(seq_starts)
+        _check(lib.dit_attention_packed(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(vt), n, ldn, st,
+                                        nseq, score_scale, _ptr(o), _stream(stream)))
     return o
 
 

@@ -31,9 +31,10 @@ def act_dtype(spec):
     return torch.bfloat16 if spec.dtype == "bf16" else torch.float32
 
 
-def run_gpu(spec, wl, dit, out_alias=False):
+def run_gpu(spec, wl, dit, out_alias=False, seq_starts=None):
     """Prepare + forward on the GPU; returns (out, stage dict of numpy fp64
-    arrays over ALL tokens, xn of the attention half, mods)."""
+    arrays over ALL tokens, xn of the attention half, mods).  ``seq_starts``
+    packs independent samples (dit_block_forward_packed)."""
     import torch
     dev = to_device(wl)
     cfg = dit.make_config(spec)
@@ -52,9 +53,9 @@ def run_gpu(spec, wl, dit, out_alias=False):
     blk.adaln_modulate(dev.x, dev.rows, sig, 0, xn_a, mods, temb)
     if out_alias:
         out = dev.x.clone()
-        blk.forward(out, dev.rows, dev.pos, sig, out=out)
+        blk.forward(out, dev.rows, dev.pos, sig, out=out, seq_starts=seq_starts)
     else:
-        out = blk.forward(dev.x, dev.rows, dev.pos, sig)
+        out = blk.forward(dev.x, dev.rows, dev.pos, sig, seq_starts=seq_starts)
     torch.cuda.synchronize()
     L = dit.workspace_layout(cfg, n)
     ws = blk._ws
@@ -86,11 +87,11 @@ def run_gpu(spec, wl, dit, out_alias=False):
     return out, st
 
 
-def compare(spec, wl, st, qrows=None, tol=None, skip=()):
+def compare(spec, wl, st, qrows=None, tol=None, skip=(), seq_starts=None):
     """Stage-by-stage rel-RMS vs the oracle; returns {stage: err}."""
     tol = TOL[spec.dtype] if tol is None else tol
     sig = O.resolve_sigmas(wl.slot_plan)
-    ref = O.block(spec, wl.x, wl.rows, wl.pos, sig, wl.weights, qrows)
+    ref = O.block(spec, wl.x, wl.rows, wl.pos, sig, wl.weights, qrows, seq_starts)
     n = wl.x.shape[0]
     sel = np.arange(n) if qrows is None else np.asarray(qrows)
     errs = {}

@@ -154,3 +154,27 @@ def test_profile_arming(dit):
     assert dit.lib.dit_profile_end(ms, ctypes.byref(calls)) == -1
     assert dit.lib.dit_profile_begin(0) == -1
     assert [dit.lib.dit_phase_name(i).decode() for i in range(dit.NPHASES)][4] == "attention"
+
+
+def test_packed_refusals(dit):
+    """Bad sample tables are refused on the host before any launch."""
+    c = _cfg(dit)
+    arr = (ctypes.c_double * 2)(0.5, 0.2)
+
+    def fwd(starts, nseq, n=10):
+        st = (ctypes.c_int32 * max(len(starts), 1))(*starts)
+        return dit.lib.dit_block_forward_packed(ctypes.byref(c), 256, 16, n, 16, 16, arr, 2, st,
+                                                nseq, 16, 256, 1 << 40, None)
+
+    assert fwd([0, 10], 0) == -2          # nseq < 1
+    assert fwd([0] * 66, 65) == -2        # nseq > DIT_MAX_SEQS
+    assert fwd([1, 10], 1) == -2          # must start at 0
+    assert fwd([0, 6, 4, 10], 3) == -2    # decreasing
+    assert fwd([0, 9], 1) == -2           # must end at n
+    assert "seq_starts" in dit.last_error()
+    assert dit.lib.dit_block_forward_packed(ctypes.byref(c), 256, 16, 10, 16, 16, arr, 2, None, 1,
+                                            16, 256, 1 << 40, None) == -1
+    A = dit.lib.dit_attention_packed
+    st = (ctypes.c_int32 * 3)(0, 5, 9)
+    assert A(ctypes.byref(c), 16, 16, 16, 10, 128, st, 2, 1.0, 16, None) == -2
+    assert A(ctypes.byref(c), 16, 16, 16, 10, 128, None, 1, 1.0, 16, None) == -1

@@ -32,11 +32,11 @@ def _sample_rows(n, k, seed=0):
     return np.sort(rows)
 
 
-def _check(name, spec, wl, dit, qrows=None, tol=None, alias=False):
+def _check(name, spec, wl, dit, qrows=None, tol=None, alias=False, seq_starts=None):
     log(f"[case] {name}: variant={spec.variant} dtype={spec.dtype} n={wl.x.shape[0]} D={spec.D} "
-        f"H={spec.H}x{spec.hd} F={spec.F}")
-    _, st = run_gpu(spec, wl, dit, out_alias=alias)
-    errs, bad, t = compare(spec, wl, st, qrows, tol)
+        f"H={spec.H}x{spec.hd} F={spec.F} seq_starts={seq_starts}")
+    _, st = run_gpu(spec, wl, dit, out_alias=alias, seq_starts=seq_starts)
+    errs, bad, t = compare(spec, wl, st, qrows, tol, seq_starts=seq_starts)
     log(f"[case] {name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert not bad, f"{name}: stages over {t}: {bad}"
     if "_pad_max" in st:
@@ -219,4 +219,86 @@ def test_standalone_attention(dit, hd, n, qnorm):
     ref = ref.transpose(1, 0, 2).reshape(n, H * hd)
     err = O.rel_rms(o.float().cpu().numpy(), ref)
     log(f"[case] attention hd={hd} n={n} |q|={qnorm}: rel_rms={err:.2e}")
+    assert err <= 1e-2
+
+
+# ---- independent samples packed in one sequence (block-diagonal attention) ----
+
+PACKED = [
+    ("mmh3", "bf16", 333, 256, 128, 384, [0, 100, 101, 333]),
+    ("mmh3", "bf16", 600, 256, 64, 256, [0, 64, 64, 320, 577, 600]),
+    ("mmh3", "f32", 130, 256, 64, 256, [0, 70, 130]),
+    ("siglip", "bf16", 300, 384, 64, 512, [0, 1, 150, 300]),
+    ("zimage", "bf16", 321, 256, 128, 384, [0, 257, 321]),
+    ("zimage", "f32", 90, 256, 64, 256, [0, 33, 90]),
+]
+
+
+@pytest.mark.parametrize("variant,dtype,n,D,hd,F,starts", PACKED)
+def test_packed_samples(dit, variant, dtype, n, D, hd, F, starts):
+    """Samples of ragged lengths (one token, an empty sample, boundaries off the
+    64-key tiles and the 256-query blocks): every token against the oracle's
+    per-sample attention."""
+    spec = _small(variant, dtype, n, D, hd, F, temb_hidden=64, temb_freq=32)
+    wl = W.make_custom_workload(spec, 2000 + n)
+    _check(spec.name + "-packed", spec, wl, dit, seq_starts=starts)
+
+
+def test_packed_t2va_sampled(dit):
+    """The t2va shape cut into four samples of 6400 tokens (units split along
+    the keys in the grid's last round), sampled rows of every sample."""
+    spec = W.spec_by_name("t2va")
+    wl = W.make_workload(spec)
+    starts = [0, 6400, 12800, 19200, 25600]
+    rows = np.unique(np.concatenate([_sample_rows(spec.n, SAMPLE, 7),
+                                     np.array([0, 6399, 6400, 12799, 19200, 25599])]))
+    _check("t2va-4-samples", spec, wl, dit, qrows=rows, seq_starts=starts)
+
+
+def test_packed_one_sample_equals_unpacked(dit):
+    """dit_block_forward_packed with one sample computes what
+    dit_block_forward computes, bit for bit."""
+    import torch
+    from synth.device import to_device
+    spec = _small("mmh3", "bf16", 333, 256, 128, 384)
+    wl = W.make_custom_workload(spec, 2333)
+    dev = to_device(wl)
+    blk = dit.Block(dit.make_config(spec), dev.weights)
+    sig = dit.resolve_sigmas(wl.slot_plan)
+    a = blk.forward(dev.x, dev.rows, dev.pos, sig)
+    b = blk.forward(dev.x, dev.rows, dev.pos, sig, seq_starts=[0, 333])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("hd,starts", [(128, [0, 300, 301, 777]), (64, [0, 129, 129, 515])])
+def test_standalone_attention_packed(dit, hd, starts):
+    """dit_attention_packed on exact bf16 inputs against the oracle's
+    per-sample attention."""
+    import torch
+    from synth.workloads import bf16_round
+    n = starts[-1]
+    H = 3 if hd == 128 else 4
+    ldn = (n + 127) // 128 * 128
+    rng = np.random.default_rng(31 + n)
+    q, k, v = (bf16_round(rng.standard_normal((H, n, hd)).astype(np.float32)) for _ in range(3))
+    spec = _small("mmh3", "bf16", n, H * hd, hd, 256)
+    cfg = dit.make_config(spec)
+
+    def pad(a):
+        out = np.zeros((H, ldn, hd), np.float32)
+        out[:, :n] = a
+        return out
+
+    qd = torch.from_numpy(pad(q)).to(torch.bfloat16).cuda()
+    kd = torch.from_numpy(pad(k)).to(torch.bfloat16).cuda()
+    vtd = torch.from_numpy(np.ascontiguousarray(pad(v).transpose(0, 2, 1))).to(torch.bfloat16).cuda()
+    o = torch.empty((n, H * hd), dtype=torch.bfloat16, device="cuda")
+    dit.attention(cfg, qd, kd, vtd, n, ldn, 0.125, o, seq_starts=starts)
+    torch.cuda.synchronize()
+    ref = O.attention_packed(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                             0.125, np.arange(n), starts)
+    ref = ref.transpose(1, 0, 2).reshape(n, H * hd)
+    err = O.rel_rms(o.float().cpu().numpy(), ref)
+    log(f"[case] packed attention hd={hd} starts={starts}: rel_rms={err:.2e}")
     assert err <= 1e-2

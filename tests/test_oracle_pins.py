@@ -303,6 +303,75 @@ def test_attention_extreme_scores_finite():
 
 # ---------------------------------------------------------------- layouts ----
 
+# -------------------------------------------------- packed samples (ragged) ----
+
+def _brute_masked_attention(q, k, v, scale, qtok, seq_starts):
+    """Scalar loops over every key with an explicit block-diagonal mask: key j
+    counts for query token i only when both lie in the same sample."""
+    H, m, hd = q.shape
+    n = k.shape[1]
+    sample = [None] * n
+    for s_, (a, e) in enumerate(zip(seq_starts[:-1], seq_starts[1:])):
+        for t in range(a, e):
+            sample[t] = s_
+    out = np.zeros((H, m, v.shape[2]))
+    for h in range(H):
+        for i in range(m):
+            keep = [j for j in range(n) if sample[j] == sample[qtok[i]]]
+            s = [scale * sum(q[h, i, d] * k[h, j, d] for d in range(hd)) for j in keep]
+            mx = max(s)
+            e = [math.exp(si - mx) for si in s]
+            tot = sum(e)
+            for d in range(v.shape[2]):
+                out[h, i, d] = sum(e[c] * v[h, j, d] for c, j in enumerate(keep)) / tot
+    return out
+
+
+def test_packed_attention_brute_force_tiny():
+    rng = np.random.default_rng(21)
+    starts = [0, 4, 5, 5, 13]  # lengths 4, 1, 0 (empty), 8
+    q = rng.standard_normal((2, 13, 6)) * 2
+    k = rng.standard_normal((2, 13, 6)) * 2
+    v = rng.standard_normal((2, 13, 6))
+    qtok = np.arange(13)
+    np.testing.assert_allclose(O.attention_packed(q, k, v, 0.4, qtok, starts),
+                               _brute_masked_attention(q, k, v, 0.4, qtok, starts),
+                               rtol=1e-12, atol=1e-13)
+    # a subset of query rows, out of order
+    sel = np.array([12, 4, 0, 7])
+    np.testing.assert_allclose(O.attention_packed(q[:, sel], k, v, 0.4, sel, starts),
+                               _brute_masked_attention(q[:, sel], k, v, 0.4, sel, starts),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_packed_attention_single_sample_is_full_attention():
+    rng = np.random.default_rng(22)
+    q, k, v = (rng.standard_normal((3, 17, 8)) for _ in range(3))
+    np.testing.assert_array_equal(O.attention_packed(q, k, v, 0.3, np.arange(17), [0, 17]),
+                                  O.attention(q, k, v, 0.3))
+
+
+def test_packed_attention_rejects_bad_starts():
+    q = np.zeros((1, 4, 2))
+    for bad in ([0, 5], [1, 4], [0, 3, 2, 4], [0]):
+        with pytest.raises(ValueError):
+            O.attention_packed(q, q, q, 1.0, np.arange(4), bad)
+
+
+def test_packed_block_equals_samples_run_alone():
+    """[ENC]: a ragged batch behaves exactly like its sequences run solo."""
+    spec, x, rows, pos, sig, w = _tiny_mmh3_inputs(16, n=12)
+    starts = [0, 5, 6, 12]
+    packed = O.mmh3_block(spec, x, rows, pos, sig, w, seq_starts=starts)
+    for a, e in zip(starts[:-1], starts[1:]):
+        alone = O.mmh3_block(spec, x[a:e], rows[a:e], pos[a:e], sig, w)
+        for name in ("o", "x1", "out"):
+            np.testing.assert_allclose(packed[name][a:e], alone[name], rtol=1e-12, atol=1e-12)
+    # and differs from attending across samples
+    full = O.mmh3_block(spec, x, rows, pos, sig, w)
+    assert np.abs(full["o"] - packed["o"]).max() > 1e-3
+
+
 def test_layout_t2va_printed():
     g = gold("layouts.json")
     lay = W.build_layout(*g["t2va_args"])

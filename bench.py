@@ -208,7 +208,7 @@ def main():
         "norm1_frac_of_copy": norm_gbs / copy_gbs,
         "phases_ms": ph,
         "roofline": {
-            "kernel": "k_attn_bf16<128> (attention)",
+            "kernel": "k_attn_bf16<128,true> (attention; + k_attn_merge)",
             "bound": "mfma",
             "achieved": attn_tf,
             "peak": PEAK_BF16_TFLOPS,

@@ -144,7 +144,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
   // sum are then rescaled); otherwise p = 2^(s*c - m) <= 2^kLazy, harmless in
   // the fp32 sums and in bf16, and the final normalization is unchanged.
   constexpr float kLazy = 8.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY;
+  // row sum in four partial sums (four short dependency chains instead of one)
+  float l4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   // Scores are kept relative to cm (base 2): t = s * scale_log2 - cm.  cm is
   // 0 until the first tile has set m_run, then equal to m_run.  With UNIT the
   // subtraction happens in the MFMA through cneg = {-cm, ...}.
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
       const float delta_ = m_new_ - cm;                                                    \
       m_run = m_new_;                                                                      \
       cm = m_new_;                                                                         \
-      l_run *= alpha_;                                                                     \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) l4[i] *= alpha_;                      \
       _Pragma("unroll") for (int d = 0; d < ND; ++d)                                       \
       _Pragma("unroll") for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha_;                 \
       _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                     \
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
     _Pragma("unroll") for (int cc = 0; cc < 2; ++cc)                                       \
     _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                        \
       const float pv_ = __builtin_amdgcn_exp2f(s_[kb][8 * cc + e]);                        \
-      l_run += pv_;                                                                        \
+      l4[e & 3] += pv_;                                                                    \
       p_[kb][cc][e] = (__bf16)pv_;                                                         \
     }                                                                                      \
     _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                       \
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
 #undef KOFF
 #undef VOFF
 
-  const float lt = half_swap_sum(l_run);
+  const float lt = half_swap_sum((l4[0] + l4[1]) + (l4[2] + l4[3]));
   const int qi = q0 + l32;
   if (split) {
     // partial slot (unit, range): O^T unnormalized fp32 [256][HD], then (m, l)

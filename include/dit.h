@@ -55,8 +55,12 @@ enum {
                      basis, RMSNorm, qk-RMSNorm + 3-axis RoPE, SwiGLU ([MMH3] block_forward) */
   DIT_SIGLIP = 1, /* pre-LayerNorm encoder layer with biases, GELU-tanh, no modulation and
                      no RoPE; softmax scale folded into W_q, b_q ([SIGLIP] Layer::forward)    */
-  DIT_ZIMAGE = 2  /* four-chunk adaLN from a sinusoidal timestep MLP, tanh gates, sandwich
+  DIT_ZIMAGE = 2, /* four-chunk adaLN from a sinusoidal timestep MLP, tanh gates, sandwich
                      RMSNorms, interleaved RoPE, SwiGLU ([ZIMG] TransformerBlock.Forward)     */
+  DIT_REFINER = 3 /* the MMH3 block without modulation, as its token refiner runs it
+                     ([MMH3] refine_text: block_forward with no mods): RMSNorm pre-norms,
+                     qk-RMSNorm, plain residuals, SwiGLU; RoPE as configured (the
+                     refiner itself is unrotated: rope = NONE); no sigmas          */
 };
 
 /* Arithmetic type of GEMM operands, attention inputs and the intermediates
@@ -116,7 +120,7 @@ typedef struct dit_weights {
 /* Byte offsets of the intermediates inside the workspace of dit_block_forward
  * (for inspection after the call; `none` = SIZE_MAX when a variant has no such
  * buffer).  ldn = n rounded up to 128.  act = the config's dtype.
- *   mods  fp32 [R, E*D]   R = S*T (MMH3) or 1 (ZIMAGE), E = 6 or 4
+ *   mods  fp32 [R, E*D]   R = S*T (MMH3) or 1 (ZIMAGE), E = 6 or 4 (none: SIGLIP, REFINER)
  *   rope  fp32 [n, hd/2, 2] (cos, sin) per token and pair
  *   xn    act  [n, D]     pre-norm + modulate of the FFN half after the call
  *                         (the attention half's is overwritten)
@@ -172,6 +176,7 @@ dit_status dit_adaln_eval(const dit_config* cfg, const void* prepared, const dou
  *           (half 0: g = norm1, chunks shift 0 / scale 1; half 1: norm2, 3 / 4)
  *   ZIMAGE: xn_i = RMSNorm(x_i; g, eps) * (1 + mods[0, scale]) (chunk 0 or 2)
  *   SIGLIP: xn_i = LayerNorm(x_i; g, b, eps), mods unused (may be NULL)
+ *   REFINER: xn_i = RMSNorm(x_i; g, eps), mods unused (may be NULL)
  * x: device fp32 [n, D]; rows: device int32 [n], each in [0, R) (unchecked on
  * the device: an out-of-range row reads outside mods); NULL means row 0.
  * xn_out: device [n, D] in the config's dtype. */
@@ -185,7 +190,7 @@ dit_status dit_adaln_modulate(const dit_config* cfg, const void* prepared, const
  *   x:    device fp32 [n, D] residual stream in
  *   rows: device int32 [n] modulation row per token (MMH3; NULL = row 0)
  *   pos:  device fp32 [n, 3] (t, h, w) per token (needed unless rope = NONE)
- *   sigmas: host, as dit_adaln_eval (ignored for SIGLIP)
+ *   sigmas: host, as dit_adaln_eval (ignored for SIGLIP and REFINER)
  *   out:  device fp32 [n, D]; may alias x (x is read only before out is written)
  *   workspace: device, >= dit_workspace_size(cfg, n) bytes, 256-byte aligned */
 dit_status dit_block_forward(const dit_config* cfg, const void* prepared, const float* x,

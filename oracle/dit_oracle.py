@@ -338,6 +338,41 @@ def mmh3_block(spec, x: np.ndarray, rows: np.ndarray, pos: Optional[np.ndarray],
 
 
 # ---------------------------------------------------------------------------
+# Token refiner: the MiniMax-H3 block without modulation ([MMH3] ``refine_text``
+# runs ``block_forward`` with no modulation buffer: ``norm_rows`` without
+# ``modulate``, ``residual`` without a gate)
+# ---------------------------------------------------------------------------
+
+
+def refiner_block(spec, x: np.ndarray, pos: Optional[np.ndarray], w: Dict[str, np.ndarray],
+                  qrows: Optional[np.ndarray] = None,
+                  seq_starts: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """xn = RMSNorm(x; norm1); q, k with qk-norm (RoPE only if the spec has
+    one; the refiner itself is unrotated); x1 = x + W_out o; xn2 =
+    RMSNorm(x1; norm2); out = x1 + W2 (silu(g) * u).  Stages as mmh3_block."""
+    D, H, hd, F = spec.D, spec.H, spec.hd, spec.F
+    n = x.shape[0]
+    x = np.asarray(x, F64)
+    sel = _sel(qrows, n)
+    xn = rms_norm(x, w["norm1"], spec.eps)
+    wq, wk, wv = (w["w_qkv"][i * D:(i + 1) * D] for i in range(3))
+    k = rms_norm(_heads(_lin(xn, wk), H, hd), w["k_norm"], spec.qk_eps)
+    v = _heads(_lin(xn, wv), H, hd)
+    q = rms_norm(_heads(_lin(xn[sel], wq), H, hd), w["q_norm"], spec.qk_eps)
+    if spec.rope != "none":
+        ang = rope_angles(pos, spec.rope_axes, spec.rope_theta)
+        k = rope_rotate(k, ang[None], spec.rope)
+        q = rope_rotate(q, ang[sel][None], spec.rope)
+    o = _merge(_attend(q, k, v, 1.0 / math.sqrt(hd), sel, seq_starts))
+    x1 = x[sel] + _lin(o, w["w_out"])
+    xn2 = rms_norm(x1, w["norm2"], spec.eps)
+    gu = _lin(xn2, w["w_fc1"])
+    a = silu(gu[:, :F]) * gu[:, F:]
+    out = x1 + _lin(a, w["w_fc2"])
+    return dict(xn=xn, q=q, k=k, v=v, o=o, x1=x1, xn2=xn2, a=a, out=out)
+
+
+# ---------------------------------------------------------------------------
 # SigLIP encoder layer ([SIGLIP] ``Layer::forward``, ``finish_attention``)
 # ---------------------------------------------------------------------------
 
@@ -426,7 +461,7 @@ def zimage_block(spec, x: np.ndarray, pos: np.ndarray, t: float, w: Dict[str, np
 
 def block(spec, x, rows, pos, sigmas, w, qrows=None, seq_starts=None) -> Dict[str, np.ndarray]:
     """Dispatch on the block variant.  ``sigmas``: slot sigmas (mmh3) or
-    [t] (zimage); ignored for siglip.  ``seq_starts``: packed samples (None =
+    [t] (zimage); ignored for siglip and refiner.  ``seq_starts``: packed samples (None =
     one sequence)."""
     if spec.variant == "mmh3":
         return mmh3_block(spec, x, rows, pos, sigmas, w, qrows, seq_starts)
@@ -434,6 +469,8 @@ def block(spec, x, rows, pos, sigmas, w, qrows=None, seq_starts=None) -> Dict[st
         return siglip_layer(spec, x, w, qrows, seq_starts)
     if spec.variant == "zimage":
         return zimage_block(spec, x, pos, sigmas[0], w, qrows, seq_starts)
+    if spec.variant == "refiner":
+        return refiner_block(spec, x, pos, w, qrows, seq_starts)
     raise ValueError(spec.variant)
 
 
@@ -450,7 +487,7 @@ __all__ = [
     "sigma_remap", "sigma_remap_slope", "resolve_sigmas", "mmh3_timestep",
     "adaln_coords", "adaln_mods", "rms_norm", "layer_norm", "modulate", "silu",
     "gelu_tanh", "rope_angles", "rope_rotate", "attention", "sample_ranges",
-    "attention_packed", "mmh3_block",
+    "attention_packed", "mmh3_block", "refiner_block",
     "siglip_layer", "timestep_embedding", "zimage_mods", "zimage_block", "block",
     "rel_rms",
 ]

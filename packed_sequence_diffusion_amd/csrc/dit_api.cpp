@@ -37,11 +37,13 @@ int mod_rows(const dit_config* c) {
   return c->variant == DIT_MMH3 ? c->slots * c->tags : (c->variant == DIT_ZIMAGE ? 1 : 0);
 }
 bool swiglu(const dit_config* c) { return c->variant != DIT_SIGLIP; }
+// modulated variants (adaLN rows, sigmas)
+bool has_mods(const dit_config* c) { return c->variant == DIT_MMH3 || c->variant == DIT_ZIMAGE; }
 int fc1_rows(const dit_config* c) { return swiglu(c) ? 2 * c->F : c->F; }
 
 dit_status check_config(const dit_config* c) {
   if (!c) return fail(DIT_EINVAL, "config is NULL");
-  if (c->variant < DIT_MMH3 || c->variant > DIT_ZIMAGE)
+  if (c->variant < DIT_MMH3 || c->variant > DIT_REFINER)
     return fail(DIT_EINVAL, "unknown variant %d", c->variant);
   if (c->dtype != DIT_F32 && c->dtype != DIT_BF16) return fail(DIT_EDTYPE, "unknown dtype %d", c->dtype);
   if (c->hd != 64 && c->hd != 128) return fail(DIT_EUNSUPPORTED, "head dim %d not in {64, 128}", c->hd);
@@ -185,7 +187,7 @@ dit_status hip_check(hipError_t e, const char* what) {
 #define HIP_TRY(expr, what) DIT_TRY(hip_check((expr), what))
 
 dit_status check_sigmas(const dit_config* c, const double* sigmas, int n_sigmas) {
-  if (c->variant == DIT_SIGLIP) return DIT_OK;
+  if (!has_mods(c)) return DIT_OK;
   int need = c->variant == DIT_MMH3 ? c->slots : 1;
   if (!sigmas) return fail(DIT_EINVAL, "sigmas is NULL");
   if (n_sigmas != need) return fail(DIT_ESHAPE, "n_sigmas=%d, the configuration needs %d", n_sigmas, need);
@@ -239,6 +241,10 @@ dit_status launch_prenorm(const dit_config* c, const void* prep, const float* x,
   } else if (c->variant == DIT_ZIMAGE) {
     HIP_TRY(dit::norm_mod(dit::NORM_RMS, dit::MOD_SCALE, bf, x, n, D, g, nullptr, c->eps, mods, 4 * D,
                           nullptr, 0, (half ? 2 : 0) * D, xn, s),
+            "norm_mod");
+  } else if (c->variant == DIT_REFINER) {
+    HIP_TRY(dit::norm_mod(dit::NORM_RMS, dit::MOD_NONE, bf, x, n, D, g, nullptr, c->eps, nullptr, 0,
+                          nullptr, 0, 0, xn, s),
             "norm_mod");
   } else {
     HIP_TRY(dit::norm_mod(dit::NORM_LAYER, dit::MOD_NONE, bf, x, n, D, g,
@@ -447,7 +453,7 @@ dit_status dit_prepare_weights(const dit_config* c, const dit_weights* w, void* 
 dit_status dit_adaln_eval(const dit_config* c, const void* prepared, const double* sigmas,
                           int32_t n_sigmas, float* mods_out, float* temb_scratch, void* stream) {
   DIT_TRY(check_config(c));
-  if (c->variant == DIT_SIGLIP) return fail(DIT_EUNSUPPORTED, "the SigLIP layer has no modulation");
+  if (!has_mods(c)) return fail(DIT_EUNSUPPORTED, "variant %d has no modulation", c->variant);
   if (!prepared || !mods_out) return fail(DIT_EINVAL, "prepared/mods_out is NULL");
   if (c->variant == DIT_ZIMAGE && !temb_scratch) return fail(DIT_EINVAL, "temb_scratch is NULL");
   DIT_TRY(check_sigmas(c, sigmas, n_sigmas));
@@ -462,7 +468,7 @@ dit_status dit_adaln_modulate(const dit_config* c, const void* prepared, const f
   if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
   if (half != 0 && half != 1) return fail(DIT_EINVAL, "half=%d not in {0, 1}", half);
   if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
-  if (c->variant != DIT_SIGLIP) {
+  if (has_mods(c)) {
     if (!mods_out) return fail(DIT_EINVAL, "mods_out is NULL");
     if (c->variant == DIT_ZIMAGE && !temb_scratch) return fail(DIT_EINVAL, "temb_scratch is NULL");
     DIT_TRY(check_sigmas(c, sigmas, n_sigmas));
@@ -471,7 +477,7 @@ dit_status dit_adaln_modulate(const dit_config* c, const void* prepared, const f
   if (!x || !xn_out) return fail(DIT_EINVAL, "x/xn_out is NULL");
   if (!aligned16(x) || !aligned16(xn_out)) return fail(DIT_EALIGN, "x/xn_out not 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  if (c->variant != DIT_SIGLIP) DIT_TRY(launch_mods(c, prepared, sigmas, mods_out, temb_scratch, s));
+  if (has_mods(c)) DIT_TRY(launch_mods(c, prepared, sigmas, mods_out, temb_scratch, s));
   return launch_prenorm(c, prepared, x, n, rows, mods_out, half, xn_out, s);
 }
 
@@ -559,7 +565,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
 
   PhaseMarks pm(s);
   // a1: modulation rows; RoPE table
-  if (c->variant != DIT_SIGLIP) DIT_TRY(launch_mods(c, prepared, sigmas, mods, at<float>(workspace, L.temb), s));
+  if (has_mods(c)) DIT_TRY(launch_mods(c, prepared, sigmas, mods, at<float>(workspace, L.temb), s));
   if (c->rope != DIT_ROPE_NONE)
     HIP_TRY(dit::rope_table(pos, n, hd / 2, c->rope_axes, c->rope_theta, cs, s), "rope_table");
   pm.mark(0);

@@ -16,12 +16,12 @@ from typing import Dict, List, Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdit.so")
 
-MMH3, SIGLIP, ZIMAGE = 0, 1, 2
+MMH3, SIGLIP, ZIMAGE, REFINER = 0, 1, 2, 3
 F32, BF16 = 0, 1
 ROPE_NONE, ROPE_SPLIT_HALF, ROPE_INTERLEAVED = 0, 1, 2
 NPHASES = 9
 
-_VARIANTS = {"mmh3": MMH3, "siglip": SIGLIP, "zimage": ZIMAGE}
+_VARIANTS = {"mmh3": MMH3, "siglip": SIGLIP, "zimage": ZIMAGE, "refiner": REFINER}
 _DTYPES = {"f32": F32, "bf16": BF16}
 _ROPES = {"none": ROPE_NONE, "split_half": ROPE_SPLIT_HALF, "interleaved": ROPE_INTERLEAVED}
 

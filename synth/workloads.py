@@ -32,8 +32,9 @@ class BlockSpec:
 
     variant: "mmh3" (six-chunk adaLN from a rank-r timestep-curve basis,
     [MMH3] ``block_forward``), "siglip" (pre-LayerNorm encoder layer,
-    [SIGLIP] ``Layer::forward``) or "zimage" (four-chunk tanh-gated
-    sandwich-norm block, [ZIMG] ``TransformerBlock.Forward``).
+    [SIGLIP] ``Layer::forward``), "zimage" (four-chunk tanh-gated
+    sandwich-norm block, [ZIMG] ``TransformerBlock.Forward``) or "refiner"
+    (the mmh3 block without modulation, [MMH3] ``refine_text``).
     """
 
     name: str
@@ -59,7 +60,7 @@ class BlockSpec:
 
     @property
     def chunks(self) -> int:
-        return {"mmh3": 6, "zimage": 4, "siglip": 0}[self.variant]
+        return {"mmh3": 6, "zimage": 4, "siglip": 0, "refiner": 0}[self.variant]
 
     @property
     def mod_rows(self) -> int:
@@ -266,6 +267,13 @@ def weight_shapes(spec: BlockSpec) -> List[Tuple[str, Tuple[int, ...], str]]:
             ("adaln_basis", (R, spec.rank), "vec"), ("adaln_bias", (R,), "vec"),
             ("adaln_table", (spec.grid, spec.rank), "table"),
         ]
+    if spec.variant == "refiner":
+        return [
+            ("norm1", (D,), "gain"), ("norm2", (D,), "gain"),
+            ("w_qkv", (3 * D, D), "lin"), ("w_out", (D, D), "lin"),
+            ("q_norm", (hd,), "gain"), ("k_norm", (hd,), "gain"),
+            ("w_fc1", (2 * F, D), "lin"), ("w_fc2", (D, F), "lin"),
+        ]
     if spec.variant == "siglip":
         return [
             ("ln1_w", (D,), "gain"), ("ln1_b", (D,), "vec"),
@@ -409,7 +417,7 @@ def make_custom_workload(spec: BlockSpec, seed: int, pos: Optional[np.ndarray] =
     if not sigmas:
         sigmas = [float(v) for v in rng.uniform(0.0, 1.0, size=max(spec.slots, 1))]
     plan = [("value", float(s)) for s in sigmas]
-    if spec.variant == "siglip":
+    if spec.variant in ("siglip", "refiner"):
         plan = []
     return Workload(spec, x, rows, None if pos is None else np.asarray(pos, np.float32),
                     plan, make_weights(spec, seed + 1), seed)

@@ -46,7 +46,7 @@ def run_gpu(spec, wl, dit, out_alias=False, seq_starts=None):
     xn_a = torch.empty((n, spec.D), dtype=ad, device="cuda")
     mods = None
     temb = None
-    if spec.variant != "siglip":
+    if spec.variant in ("mmh3", "zimage"):
         mods = torch.empty((spec.mod_rows, spec.chunks * spec.D), dtype=torch.float32, device="cuda")
         if spec.variant == "zimage":
             temb = torch.empty(spec.temb_hidden + spec.temb_freq, dtype=torch.float32, device="cuda")

@@ -88,7 +88,8 @@ def test_t2va_random_rows_sampled(dit):
 def _small(variant, dtype, n, D, hd, F, slots=2, rope=None, axes=None, theta=1e4, **kw):
     H = D // hd
     if rope is None:
-        rope = {"mmh3": "split_half", "zimage": "interleaved", "siglip": "none"}[variant]
+        rope = {"mmh3": "split_half", "zimage": "interleaved", "siglip": "none",
+                "refiner": "none"}[variant]
     if axes is None:
         axes = (0, 0, 0) if rope == "none" else ((hd // 4, hd // 8 * 3, hd // 8 * 3) if hd == 128 else (16, 24, 24))
     return W.BlockSpec(f"small-{variant}-{dtype}-{n}", variant, dtype, n=n, D=D, H=H, hd=hd, F=F,
@@ -105,6 +106,8 @@ SMALL = [
     ("siglip", "f32", 65, 256, 64, 256),
     ("zimage", "bf16", 321, 256, 128, 384),
     ("zimage", "f32", 90, 256, 64, 256),
+    ("refiner", "bf16", 333, 256, 128, 384),
+    ("refiner", "f32", 77, 256, 64, 256),
 ]
 
 
@@ -231,6 +234,7 @@ PACKED = [
     ("siglip", "bf16", 300, 384, 64, 512, [0, 1, 150, 300]),
     ("zimage", "bf16", 321, 256, 128, 384, [0, 257, 321]),
     ("zimage", "f32", 90, 256, 64, 256, [0, 33, 90]),
+    ("refiner", "bf16", 333, 256, 128, 384, [0, 200, 333]),
 ]
 
 

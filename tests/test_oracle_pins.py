@@ -358,6 +358,27 @@ def test_packed_attention_rejects_bad_starts():
             O.attention_packed(q, q, q, 1.0, np.arange(4), bad)
 
 
+def test_refiner_is_the_mmh3_block_with_neutral_modulation():
+    """The unmodulated block equals the (brute-force pinned) MMH3 block whose
+    adaLN rows are shift 0, scale 0, gate 1 in both halves: zero basis, bias
+    holding those values."""
+    spec, x, rows, pos, sig, w = _tiny_mmh3_inputs(17, n=11)
+    D = spec.D
+    neutral = np.zeros(6 * D)
+    neutral[2 * D:3 * D] = 1.0
+    neutral[5 * D:6 * D] = 1.0
+    wn = dict(w)
+    wn["adaln_basis"] = np.zeros_like(w["adaln_basis"])
+    wn["adaln_bias"] = np.tile(neutral, spec.slots * spec.tags)
+    for rope, p in (("none", None), ("split_half", pos)):
+        mspec = W.small_spec(spec, rope=rope)
+        rspec = W.small_spec(mspec, variant="refiner")
+        want = O.mmh3_block(mspec, x, rows, p, sig, wn)
+        got = O.refiner_block(rspec, x, p, w)
+        for name in ("xn", "o", "x1", "a", "out"):
+            np.testing.assert_allclose(got[name], want[name], rtol=1e-13, atol=1e-13)
+
+
 def test_packed_block_equals_samples_run_alone():
     """[ENC]: a ragged batch behaves exactly like its sequences run solo."""
     spec, x, rows, pos, sig, w = _tiny_mmh3_inputs(16, n=12)

@@ -213,6 +213,20 @@ dit_status dit_block_forward_packed(const dit_config* cfg, const void* prepared,
                                     const int32_t* seq_starts, int32_t nseq, float* out,
                                     void* workspace, size_t ws_bytes, void* stream);
 
+/* dit_block_forward with the modulation rows supplied instead of evaluated
+ * (MMH3 and ZIMAGE; refused with DIT_EUNSUPPORTED for the others): for rows
+ * from another source, e.g. a full-rank adaLN map, or one basis shared by
+ * every timestep as [MMH3] Adaln::eval evaluates it, or rows evaluated once and
+ * reused across calls.
+ *   mods: device fp32 [R, E*D] in dit_adaln_eval's layout (read only);
+ *   seq_starts/nseq: as dit_block_forward_packed, or NULL for one sequence.
+ * With mods from dit_adaln_eval(sigmas) this computes exactly what
+ * dit_block_forward(sigmas) computes. */
+dit_status dit_block_forward_mods(const dit_config* cfg, const void* prepared, const float* x,
+                                  int32_t n, const int32_t* rows, const float* pos,
+                                  const float* mods, const int32_t* seq_starts, int32_t nseq,
+                                  float* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* Standalone full bidirectional attention over one packed sequence, per head
  * ([MMH3] attention; online softmax with normalization deferred to the output,
  * [SIGLIP] deferred normalisation):

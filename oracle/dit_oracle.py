@@ -291,8 +291,10 @@ def _sel(qrows: Optional[np.ndarray], n: int) -> np.ndarray:
 def mmh3_block(spec, x: np.ndarray, rows: np.ndarray, pos: Optional[np.ndarray],
                sigmas: Sequence[float], w: Dict[str, np.ndarray],
                qrows: Optional[np.ndarray] = None,
-               seq_starts: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
-    """One MiniMax-H3 block over the packed sequence.
+               seq_starts: Optional[Sequence[int]] = None,
+               mods: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """One MiniMax-H3 block over the packed sequence.  ``mods`` [R, 6D], if
+    given, replaces the rows evaluated from the basis (``sigmas`` unused).
 
     Stages (fp64): mods [R, 6D]; xn [n, D]; q, k, v [H, *, hd] (q and k after
     qk-norm and RoPE, q unscaled); o [m, D]; x1, xn2 [m, D]; a [m, F];
@@ -306,9 +308,11 @@ def mmh3_block(spec, x: np.ndarray, rows: np.ndarray, pos: Optional[np.ndarray],
     R = spec.slots * spec.tags
     if rows.size and (rows.min() < 0 or rows.max() >= R):
         raise ValueError("modulation row out of range")
-    ts = [mmh3_timestep(s) for s in sigmas]
-    mods = adaln_mods(w["adaln_basis"], w.get("adaln_bias"), w["adaln_table"], ts,
-                      spec.tags, 6, D)
+    if mods is None:
+        ts = [mmh3_timestep(s) for s in sigmas]
+        mods = adaln_mods(w["adaln_basis"], w.get("adaln_bias"), w["adaln_table"], ts,
+                          spec.tags, 6, D)
+    mods = np.asarray(mods, F64)
     chunk = lambda r, e: mods[r, e * D:(e + 1) * D]  # noqa: E731
 
     # pre-norm + modulate (chunks 0 shift, 1 scale)
@@ -427,7 +431,8 @@ def zimage_mods(spec, t: float, w: Dict[str, np.ndarray]) -> np.ndarray:
 
 def zimage_block(spec, x: np.ndarray, pos: np.ndarray, t: float, w: Dict[str, np.ndarray],
                  qrows: Optional[np.ndarray] = None,
-                 seq_starts: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+                 seq_starts: Optional[Sequence[int]] = None,
+                 mods: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Modulated Z-Image block: x1 = x + tanh(gate_msa) * RMSNorm(Attn(RMSNorm(x)
     * (1 + scale_msa))); out = x1 + tanh(gate_mlp) * RMSNorm(W2(silu(W1 xf) *
     W3 xf)) with xf = RMSNorm(x1) * (1 + scale_mlp).  Interleaved RoPE.
@@ -437,7 +442,7 @@ def zimage_block(spec, x: np.ndarray, pos: np.ndarray, t: float, w: Dict[str, np
     n = x.shape[0]
     x = np.asarray(x, F64)
     sel = _sel(qrows, n)
-    mods = zimage_mods(spec, t, w)
+    mods = zimage_mods(spec, t, w) if mods is None else np.asarray(mods, F64)
     sc_msa, g_msa, sc_mlp, g_mlp = (mods[0, i * D:(i + 1) * D] for i in range(4))
     xn = modulate(rms_norm(x, w["norm1"], spec.eps), None, sc_msa)
     wq, wk, wv = (w["w_qkv"][i * D:(i + 1) * D] for i in range(3))
@@ -459,16 +464,17 @@ def zimage_block(spec, x: np.ndarray, pos: np.ndarray, t: float, w: Dict[str, np
                 out=out)
 
 
-def block(spec, x, rows, pos, sigmas, w, qrows=None, seq_starts=None) -> Dict[str, np.ndarray]:
+def block(spec, x, rows, pos, sigmas, w, qrows=None, seq_starts=None,
+          mods=None) -> Dict[str, np.ndarray]:
     """Dispatch on the block variant.  ``sigmas``: slot sigmas (mmh3) or
     [t] (zimage); ignored for siglip and refiner.  ``seq_starts``: packed samples (None =
-    one sequence)."""
+    one sequence).  ``mods``: modulation rows replacing the evaluated ones."""
     if spec.variant == "mmh3":
-        return mmh3_block(spec, x, rows, pos, sigmas, w, qrows, seq_starts)
+        return mmh3_block(spec, x, rows, pos, sigmas, w, qrows, seq_starts, mods)
     if spec.variant == "siglip":
         return siglip_layer(spec, x, w, qrows, seq_starts)
     if spec.variant == "zimage":
-        return zimage_block(spec, x, pos, sigmas[0], w, qrows, seq_starts)
+        return zimage_block(spec, x, pos, sigmas[0] if sigmas else None, w, qrows, seq_starts, mods)
     if spec.variant == "refiner":
         return refiner_block(spec, x, pos, w, qrows, seq_starts)
     raise ValueError(spec.variant)

@@ -528,15 +528,22 @@ dit_status dit_attention_packed(const dit_config* c, const void* q, const void* 
   return attention_impl(c, q, k, vt, n, ldn, seq_starts, nseq, score_scale, o, stream);
 }
 
+// mods_in: modulation rows supplied by the caller (skips their evaluation).
 static dit_status block_forward_impl(const dit_config* c, const void* prepared, const float* x, int32_t n,
                               const int32_t* rows, const float* pos, const double* sigmas,
-                              int32_t n_sigmas, const int32_t* seq_starts, int32_t nseq, float* out,
-                              void* workspace, size_t ws_bytes, void* stream) {
+                              int32_t n_sigmas, const float* mods_in, const int32_t* seq_starts,
+                              int32_t nseq, float* out, void* workspace, size_t ws_bytes,
+                              void* stream) {
   DIT_TRY(check_config(c));
   if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
   if (seq_starts) DIT_TRY(check_seqs(seq_starts, nseq, n));
   if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
-  DIT_TRY(check_sigmas(c, sigmas, n_sigmas));
+  if (mods_in) {
+    if (!has_mods(c)) return fail(DIT_EUNSUPPORTED, "variant %d has no modulation", c->variant);
+    if (!aligned16(mods_in)) return fail(DIT_EALIGN, "mods not 16-byte aligned");
+  } else {
+    DIT_TRY(check_sigmas(c, sigmas, n_sigmas));
+  }
   if (n == 0) return DIT_OK;
   if (!x || !out) return fail(DIT_EINVAL, "x/out is NULL");
   if (!aligned16(x) || !aligned16(out)) return fail(DIT_EALIGN, "x/out not 16-byte aligned");
@@ -551,7 +558,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
   const int D = c->D, F = c->F, H = c->H, hd = c->hd, dt = c->dtype;
   const bool bf = dt == DIT_BF16;
   const int ldn = L.ldn;
-  float* mods = at<float>(workspace, L.mods);
+  const float* mods = mods_in ? mods_in : at<float>(workspace, L.mods);
   void* xn = at<char>(workspace, L.xn);
   void* qkv = at<char>(workspace, L.qkv);
   void* q = at<char>(workspace, L.q);
@@ -565,7 +572,8 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
 
   PhaseMarks pm(s);
   // a1: modulation rows; RoPE table
-  if (has_mods(c)) DIT_TRY(launch_mods(c, prepared, sigmas, mods, at<float>(workspace, L.temb), s));
+  if (has_mods(c) && !mods_in)
+    DIT_TRY(launch_mods(c, prepared, sigmas, at<float>(workspace, L.mods), at<float>(workspace, L.temb), s));
   if (c->rope != DIT_ROPE_NONE)
     HIP_TRY(dit::rope_table(pos, n, hd / 2, c->rope_axes, c->rope_theta, cs, s), "rope_table");
   pm.mark(0);
@@ -697,8 +705,8 @@ dit_status dit_block_forward(const dit_config* c, const void* prepared, const fl
                              const int32_t* rows, const float* pos, const double* sigmas,
                              int32_t n_sigmas, float* out, void* workspace, size_t ws_bytes,
                              void* stream) {
-  return block_forward_impl(c, prepared, x, n, rows, pos, sigmas, n_sigmas, nullptr, 0, out,
-                            workspace, ws_bytes, stream);
+  return block_forward_impl(c, prepared, x, n, rows, pos, sigmas, n_sigmas, nullptr, nullptr, 0,
+                            out, workspace, ws_bytes, stream);
 }
 
 dit_status dit_block_forward_packed(const dit_config* c, const void* prepared, const float* x,
@@ -707,7 +715,16 @@ dit_status dit_block_forward_packed(const dit_config* c, const void* prepared, c
                                     const int32_t* seq_starts, int32_t nseq, float* out,
                                     void* workspace, size_t ws_bytes, void* stream) {
   if (!seq_starts) return fail(DIT_EINVAL, "seq_starts is NULL");
-  return block_forward_impl(c, prepared, x, n, rows, pos, sigmas, n_sigmas, seq_starts, nseq, out,
+  return block_forward_impl(c, prepared, x, n, rows, pos, sigmas, n_sigmas, nullptr, seq_starts,
+                            nseq, out, workspace, ws_bytes, stream);
+}
+
+dit_status dit_block_forward_mods(const dit_config* c, const void* prepared, const float* x,
+                                  int32_t n, const int32_t* rows, const float* pos,
+                                  const float* mods, const int32_t* seq_starts, int32_t nseq,
+                                  float* out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!mods) return fail(DIT_EINVAL, "mods is NULL");
+  return block_forward_impl(c, prepared, x, n, rows, pos, nullptr, 0, mods, seq_starts, nseq, out,
                             workspace, ws_bytes, stream);
 }
 

@@ -90,6 +90,9 @@ def _load() -> ctypes.CDLL:
                                                c_void_p, c_void_p, P(c_double), c_int32,
                                                P(c_int32), c_int32, c_void_p, c_void_p, c_size_t,
                                                c_void_p]),
+        "dit_block_forward_mods": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_int32, c_void_p,
+                                             c_void_p, c_void_p, P(c_int32), c_int32, c_void_p,
+                                             c_void_p, c_size_t, c_void_p]),
         "dit_attention": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                     c_float, c_void_p, c_void_p]),
         "dit_attention_packed": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_void_p, c_int32,
@@ -237,6 +240,24 @@ class Block:
                                                 _ptr(x), n, _ptr(rows), _ptr(pos), sg, ns, st,
                                                 nseq, _ptr(out), ws.data_ptr(), ws.numel(),
                                                 _stream(stream)))
+        return out
+
+    def forward_mods(self, x, rows, pos, mods, out=None, workspace=None, stream=None,
+                     seq_starts: Optional[Sequence[int]] = None):
+        """Block forward with caller-supplied modulation rows ``mods`` (device
+        fp32 [R, E*D])."""
+        import torch
+        n = int(x.shape[0])
+        if out is None:
+            out = torch.empty_like(x)
+        ws = self.workspace(n) if workspace is None else workspace
+        if seq_starts is None:
+            st, nseq = None, 0
+        else:
+            st, nseq = _starts(seq_starts)
+        _check(lib.dit_block_forward_mods(ctypes.byref(self.cfg), self.prepared.data_ptr(), _ptr(x),
+                                          n, _ptr(rows), _ptr(pos), _ptr(mods), st, nseq, _ptr(out),
+                                          ws.data_ptr(), ws.numel(), _stream(stream)))
         return out
 
     def adaln_modulate(self, x, rows, sigmas: Sequence[float], half: int, xn_out, mods_out=None,

@@ -31,10 +31,11 @@ def act_dtype(spec):
     return torch.bfloat16 if spec.dtype == "bf16" else torch.float32
 
 
-def run_gpu(spec, wl, dit, out_alias=False, seq_starts=None):
+def run_gpu(spec, wl, dit, out_alias=False, seq_starts=None, mods_in=None):
     """Prepare + forward on the GPU; returns (out, stage dict of numpy fp64
     arrays over ALL tokens, xn of the attention half, mods).  ``seq_starts``
-    packs independent samples (dit_block_forward_packed)."""
+    packs independent samples (dit_block_forward_packed); ``mods_in`` (numpy
+    [R, E*D]) runs dit_block_forward_mods with those modulation rows."""
     import torch
     dev = to_device(wl)
     cfg = dit.make_config(spec)
@@ -51,7 +52,10 @@ def run_gpu(spec, wl, dit, out_alias=False, seq_starts=None):
         if spec.variant == "zimage":
             temb = torch.empty(spec.temb_hidden + spec.temb_freq, dtype=torch.float32, device="cuda")
     blk.adaln_modulate(dev.x, dev.rows, sig, 0, xn_a, mods, temb)
-    if out_alias:
+    if mods_in is not None:
+        md = torch.from_numpy(np.ascontiguousarray(mods_in, dtype=np.float32)).cuda()
+        out = blk.forward_mods(dev.x, dev.rows, dev.pos, md, seq_starts=seq_starts)
+    elif out_alias:
         out = dev.x.clone()
         blk.forward(out, dev.rows, dev.pos, sig, out=out, seq_starts=seq_starts)
     else:
@@ -87,11 +91,11 @@ def run_gpu(spec, wl, dit, out_alias=False, seq_starts=None):
     return out, st
 
 
-def compare(spec, wl, st, qrows=None, tol=None, skip=(), seq_starts=None):
+def compare(spec, wl, st, qrows=None, tol=None, skip=(), seq_starts=None, mods=None):
     """Stage-by-stage rel-RMS vs the oracle; returns {stage: err}."""
     tol = TOL[spec.dtype] if tol is None else tol
     sig = O.resolve_sigmas(wl.slot_plan)
-    ref = O.block(spec, wl.x, wl.rows, wl.pos, sig, wl.weights, qrows, seq_starts)
+    ref = O.block(spec, wl.x, wl.rows, wl.pos, sig, wl.weights, qrows, seq_starts, mods)
     n = wl.x.shape[0]
     sel = np.arange(n) if qrows is None else np.asarray(qrows)
     errs = {}

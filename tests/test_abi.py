@@ -178,3 +178,14 @@ def test_packed_refusals(dit):
     st = (ctypes.c_int32 * 3)(0, 5, 9)
     assert A(ctypes.byref(c), 16, 16, 16, 10, 128, st, 2, 1.0, 16, None) == -2
     assert A(ctypes.byref(c), 16, 16, 16, 10, 128, None, 1, 1.0, 16, None) == -1
+
+
+def test_given_mods_refusals(dit):
+    c = _cfg(dit)
+    F = dit.lib.dit_block_forward_mods
+    assert F(ctypes.byref(c), 256, 16, 10, 16, 16, None, None, 0, 16, 256, 1 << 40, None) == -1
+    assert F(ctypes.byref(c), 256, 16, 10, 16, 16, 8, None, 0, 16, 256, 1 << 40, None) == -4
+    sig = dit.make_config(W.spec_by_name("siglip"))
+    assert F(ctypes.byref(sig), 256, 16, 10, 16, 16, 256, None, 0, 16, 256, 1 << 40, None) == -6
+    st = (ctypes.c_int32 * 2)(0, 9)
+    assert F(ctypes.byref(c), 256, 16, 10, 16, 16, 256, st, 1, 16, 256, 1 << 40, None) == -2

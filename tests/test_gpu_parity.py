@@ -306,3 +306,45 @@ def test_standalone_attention_packed(dit, hd, starts):
     err = O.rel_rms(o.float().cpu().numpy(), ref)
     log(f"[case] packed attention hd={hd} starts={starts}: rel_rms={err:.2e}")
     assert err <= 1e-2
+
+
+# ---- caller-supplied modulation rows (dit_block_forward_mods) ----
+
+@pytest.mark.parametrize("variant,dtype,n,starts", [("mmh3", "bf16", 333, None),
+                                                    ("mmh3", "f32", 130, [0, 50, 130]),
+                                                    ("zimage", "bf16", 321, None)])
+def test_block_forward_given_mods(dit, variant, dtype, n, starts):
+    """Random modulation rows (N(0, 0.3): visible shifts, scales and gates)
+    supplied by the caller, against the oracle given the same rows; the
+    workspace's mods region is not used (the stage is skipped)."""
+    hd = 128 if variant == "zimage" or dtype == "bf16" else 64
+    spec = _small(variant, dtype, n, 256, hd, 384 if dtype == "bf16" else 256,
+                  temb_hidden=64, temb_freq=32)
+    wl = W.make_custom_workload(spec, 3000 + n)
+    rng = np.random.default_rng(n)
+    mods = (0.3 * rng.standard_normal((spec.mod_rows, spec.chunks * spec.D))).astype(np.float32)
+    name = f"{spec.name}-given-mods"
+    log(f"[case] {name} seq_starts={starts}")
+    _, st = run_gpu(spec, wl, dit, seq_starts=starts, mods_in=mods)
+    errs, bad, t = compare(spec, wl, st, None, None, skip=("mods", "xn"), seq_starts=starts,
+                           mods=mods.astype(np.float64))
+    log(f"[case] {name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert not bad, f"{name}: stages over {t}: {bad}"
+
+
+def test_given_mods_from_adaln_eval_equal_forward(dit):
+    """Rows from dit_adaln_eval fed to dit_block_forward_mods reproduce
+    dit_block_forward bit for bit."""
+    import torch
+    from synth.device import to_device
+    spec = _small("mmh3", "bf16", 333, 256, 128, 384)
+    wl = W.make_custom_workload(spec, 3333)
+    dev = to_device(wl)
+    blk = dit.Block(dit.make_config(spec), dev.weights)
+    sig = dit.resolve_sigmas(wl.slot_plan)
+    mods = torch.empty((spec.mod_rows, 6 * spec.D), dtype=torch.float32, device="cuda")
+    blk.adaln_eval(sig, mods)
+    a = blk.forward(dev.x, dev.rows, dev.pos, sig)
+    b = blk.forward_mods(dev.x, dev.rows, dev.pos, mods)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -57,10 +57,14 @@ enum {
                      no RoPE; softmax scale folded into W_q, b_q ([SIGLIP] Layer::forward)    */
   DIT_ZIMAGE = 2, /* four-chunk adaLN from a sinusoidal timestep MLP, tanh gates, sandwich
                      RMSNorms, interleaved RoPE, SwiGLU ([ZIMG] TransformerBlock.Forward)     */
-  DIT_REFINER = 3 /* the MMH3 block without modulation, as its token refiner runs it
+  DIT_REFINER = 3, /* the MMH3 block without modulation, as its token refiner runs it
                      ([MMH3] refine_text: block_forward with no mods): RMSNorm pre-norms,
                      qk-RMSNorm, plain residuals, SwiGLU; RoPE as configured (the
                      refiner itself is unrotated: rope = NONE); no sigmas          */
+  DIT_FINAL = 4    /* the MMH3 output head, not a block: RMSNorm, a single-modality
+                     adaLN of two chunks (shift, scale) per timestep slot, a linear
+                     head and the sign flip (tags = 1, F = output width; run by
+                     dit_final_forward) ([MMH3] MiniMaxH3::forward, heads)        */
 };
 
 /* Arithmetic type of GEMM operands, attention inputs and the intermediates
@@ -75,9 +79,10 @@ enum {
 };
 
 typedef struct dit_config {
-  int32_t variant;       /* DIT_MMH3 / DIT_SIGLIP / DIT_ZIMAGE                         */
+  int32_t variant;       /* DIT_MMH3 / DIT_SIGLIP / DIT_ZIMAGE / DIT_REFINER / DIT_FINAL */
   int32_t dtype;         /* DIT_F32 / DIT_BF16                                          */
-  int32_t D, H, hd, F;   /* hidden, heads, head dim (D = H*hd), FFN hidden              */
+  int32_t D, H, hd, F;   /* hidden, heads, head dim (D = H*hd), FFN hidden (FINAL: output
+                            width, a multiple of 32 for bf16 and of 64 for fp32)         */
   int32_t slots;         /* MMH3: timestep slots S                                      */
   int32_t tags;          /* MMH3: modality tags T (3: video 0, text 1, audio 2)         */
   int32_t rank;          /* MMH3: adaLN curve rank r (24)                               */
@@ -107,7 +112,11 @@ typedef struct dit_config {
  *           post_ffn_norm [D]; w_qkv, w_out, q_norm, k_norm; w_fc1 [2F, D]
  *           (rows W1 gate | W3 up); w_fc2 [D, F]; temb_w1 [Th, Tf] + temb_b1;
  *           temb_w2 [Tf, Th] + temb_b2; ada_w [4D, Tf] + ada_b [4D]
- *           (chunks scale_msa, gate_msa, scale_mlp, gate_mlp). */
+ *           (chunks scale_msa, gate_msa, scale_mlp, gate_mlp).
+ *   REFINER: as MMH3 without the adaLN tensors.
+ *   FINAL:  norm1 [D] final RMSNorm gain; w_fc1 [F, D] head weight + b_fc1 [F]
+ *           (NULL = 0); adaln_basis [S*2*D, r] (chunk 0 shift, 1 scale per
+ *           slot), adaln_bias [S*2*D] (NULL = 0), adaln_table [G, r]. */
 typedef struct dit_weights {
   const float *norm1, *norm2, *ln1_b, *ln2_b, *post_attn_norm, *post_ffn_norm;
   const void *w_qkv, *w_out, *w_fc1, *w_fc2;
@@ -226,6 +235,37 @@ dit_status dit_block_forward_mods(const dit_config* cfg, const void* prepared, c
                                   int32_t n, const int32_t* rows, const float* pos,
                                   const float* mods, const int32_t* seq_starts, int32_t nseq,
                                   float* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Output head of the MMH3 model (config variant DIT_FINAL; [MMH3]
+ * MiniMaxH3::forward, "heads"): with the rows m = dit_adaln_eval(sigmas)
+ * [S, 2D] of the head's own rank-r basis,
+ *   out_i = -(W (RMSNorm(h_i; g, eps) * (1 + m[r, D:2D]) + m[r, 0:D]) + b)
+ * for r = rows[i] (the token's timestep slot; NULL = 0).  h: device fp32
+ * [n, D]; out: device fp32 [n, F]; workspace: dit_workspace_size(cfg, n). */
+dit_status dit_final_forward(const dit_config* cfg, const void* prepared, const float* h,
+                             int32_t n, const int32_t* rows, const double* sigmas,
+                             int32_t n_sigmas, float* out, void* workspace, size_t ws_bytes,
+                             void* stream);
+
+/* out[m, nout] = alpha * (a[m, k] . w[nout, k]^T + bias), the embedding and
+ * head projections around the blocks, on the block GEMM kernels.  a and w in
+ * dtype (row-major, lda >= k), bias fp32 [nout] or NULL, out fp32 [m, nout].
+ * bf16: k % 64 == 0, nout % 32 == 0; fp32: k % 16 == 0, nout % 64 == 0;
+ * 16-byte aligned pointers; refused with DIT_EUNSUPPORTED / DIT_EALIGN. */
+dit_status dit_linear(int32_t dtype, const void* a, int32_t lda, int32_t m, int32_t k,
+                      const void* w, int32_t nout, const float* bias, float alpha, float* out,
+                      void* stream);
+
+/* A stack of n_blocks blocks of one configuration, in order, each with its own
+ * prepared weights (prepared[i], device): out = block_{L-1}(... block_0(x)),
+ * all blocks with the same rows, positions, sigmas and packed-sample table
+ * (seq_starts may be NULL).  The intermediate residual stream lives in out
+ * (out may alias x); workspace as for one block. */
+dit_status dit_stack_forward(const dit_config* cfg, const void* const* prepared, int32_t n_blocks,
+                             const float* x, int32_t n, const int32_t* rows, const float* pos,
+                             const double* sigmas, int32_t n_sigmas, const int32_t* seq_starts,
+                             int32_t nseq, float* out, void* workspace, size_t ws_bytes,
+                             void* stream);
 
 /* Standalone full bidirectional attention over one packed sequence, per head
  * ([MMH3] attention; online softmax with normalization deferred to the output,

@@ -377,6 +377,45 @@ def refiner_block(spec, x: np.ndarray, pos: Optional[np.ndarray], w: Dict[str, n
 
 
 # ---------------------------------------------------------------------------
+# Output head ([MMH3] ``MiniMaxH3::forward``, "heads": ``final_adaln.eval``, the
+# final ``rms_norm_into``, the shift/scale of the token's timestep row, the
+# head projection and the sign flip)
+# ---------------------------------------------------------------------------
+
+
+def linear(a: np.ndarray, w: np.ndarray, b: Optional[np.ndarray] = None,
+           alpha: float = 1.0) -> np.ndarray:
+    """alpha * (a @ W^T + b), W stored [out, in] (the embedding and head
+    projections)."""
+    return alpha * _lin(a, w, b)
+
+
+def final_layer(spec, h: np.ndarray, rows: Optional[np.ndarray], sigmas: Sequence[float],
+                w: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+    """mods [S, 2D] = rank-r adaLN of the head (one modality: chunk 0 shift,
+    chunk 1 scale per timestep slot); hn = RMSNorm(h; g) * (1 + scale_r) +
+    shift_r with r the token's slot; out = -(W hn + b)."""
+    D = spec.D
+    h = np.asarray(h, F64)
+    rows = np.zeros(h.shape[0], np.int64) if rows is None else np.asarray(rows, np.int64)
+    ts = [mmh3_timestep(s) for s in sigmas]
+    mods = adaln_mods(w["adaln_basis"], w.get("adaln_bias"), w["adaln_table"], ts, spec.tags, 2, D)
+    hn = modulate(rms_norm(h, w["norm1"], spec.eps), mods[rows, 0:D], mods[rows, D:2 * D])
+    out = -_lin(hn, w["w_fc1"], w.get("b_fc1"))
+    return dict(mods=mods, xn=hn, out=out)
+
+
+def stack(spec, x, rows, pos, sigmas, ws: Sequence[Dict[str, np.ndarray]], qrows=None,
+          seq_starts=None) -> np.ndarray:
+    """Blocks in order, each with its own weights; returns out of the last
+    (all rows: every block needs all tokens of the previous one)."""
+    h = np.asarray(x, F64)
+    for w in ws:
+        h = block(spec, h, rows, pos, sigmas, w, None, seq_starts)["out"]
+    return h if qrows is None else h[np.asarray(qrows)]
+
+
+# ---------------------------------------------------------------------------
 # SigLIP encoder layer ([SIGLIP] ``Layer::forward``, ``finish_attention``)
 # ---------------------------------------------------------------------------
 
@@ -493,7 +532,7 @@ __all__ = [
     "sigma_remap", "sigma_remap_slope", "resolve_sigmas", "mmh3_timestep",
     "adaln_coords", "adaln_mods", "rms_norm", "layer_norm", "modulate", "silu",
     "gelu_tanh", "rope_angles", "rope_rotate", "attention", "sample_ranges",
-    "attention_packed", "mmh3_block", "refiner_block",
+    "attention_packed", "mmh3_block", "refiner_block", "linear", "final_layer", "stack",
     "siglip_layer", "timestep_embedding", "zimage_mods", "zimage_block", "block",
     "rel_rms",
 ]

@@ -32,27 +32,42 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t esize(const dit_config* c) { return c->dtype == DIT_BF16 ? 2 : 4; }
-int chunks(const dit_config* c) { return c->variant == DIT_MMH3 ? 6 : (c->variant == DIT_ZIMAGE ? 4 : 0); }
+int chunks(const dit_config* c) {
+  switch (c->variant) {
+    case DIT_MMH3: return 6;
+    case DIT_ZIMAGE: return 4;
+    case DIT_FINAL: return 2;
+    default: return 0;
+  }
+}
+// rank-r basis variants: modulation rows from the interpolated timestep table
+bool basis_mods(const dit_config* c) { return c->variant == DIT_MMH3 || c->variant == DIT_FINAL; }
 int mod_rows(const dit_config* c) {
-  return c->variant == DIT_MMH3 ? c->slots * c->tags : (c->variant == DIT_ZIMAGE ? 1 : 0);
+  return basis_mods(c) ? c->slots * c->tags : (c->variant == DIT_ZIMAGE ? 1 : 0);
 }
 bool swiglu(const dit_config* c) { return c->variant != DIT_SIGLIP; }
 // modulated variants (adaLN rows, sigmas)
-bool has_mods(const dit_config* c) { return c->variant == DIT_MMH3 || c->variant == DIT_ZIMAGE; }
+bool has_mods(const dit_config* c) { return basis_mods(c) || c->variant == DIT_ZIMAGE; }
 int fc1_rows(const dit_config* c) { return swiglu(c) ? 2 * c->F : c->F; }
 
 dit_status check_config(const dit_config* c) {
   if (!c) return fail(DIT_EINVAL, "config is NULL");
-  if (c->variant < DIT_MMH3 || c->variant > DIT_REFINER)
+  if (c->variant < DIT_MMH3 || c->variant > DIT_FINAL)
     return fail(DIT_EINVAL, "unknown variant %d", c->variant);
   if (c->dtype != DIT_F32 && c->dtype != DIT_BF16) return fail(DIT_EDTYPE, "unknown dtype %d", c->dtype);
   if (c->hd != 64 && c->hd != 128) return fail(DIT_EUNSUPPORTED, "head dim %d not in {64, 128}", c->hd);
   if (c->H <= 0 || c->D != c->H * c->hd) return fail(DIT_ESHAPE, "D=%d != H*hd=%d*%d", c->D, c->H, c->hd);
   if (c->D % 128 || c->D > 4096) return fail(DIT_EUNSUPPORTED, "D=%d must be a multiple of 128 and <= 4096", c->D);
-  if (c->F <= 0 || c->F % 128) return fail(DIT_EUNSUPPORTED, "F=%d must be a positive multiple of 128", c->F);
+  if (c->variant == DIT_FINAL) {
+    const int fm = c->dtype == DIT_BF16 ? 32 : 64;
+    if (c->F <= 0 || c->F % fm) return fail(DIT_EUNSUPPORTED, "output width F=%d must be a positive multiple of %d", c->F, fm);
+    if (c->tags != 1) return fail(DIT_EINVAL, "the final layer has one modality (tags=%d)", c->tags);
+  } else if (c->F <= 0 || c->F % 128) {
+    return fail(DIT_EUNSUPPORTED, "F=%d must be a positive multiple of 128", c->F);
+  }
   if (!(c->eps >= 0.0f) || !(c->qk_eps >= 0.0f)) return fail(DIT_EINVAL, "eps must be >= 0");
   if (c->rope < DIT_ROPE_NONE || c->rope > DIT_ROPE_INTERLEAVED) return fail(DIT_EINVAL, "unknown rope %d", c->rope);
-  if (c->rope != DIT_ROPE_NONE) {
+  if (c->rope != DIT_ROPE_NONE && c->variant != DIT_FINAL) {
     int sum = 0;
     for (int a = 0; a < 3; ++a) {
       if (c->rope_axes[a] < 0 || c->rope_axes[a] % 2) return fail(DIT_EINVAL, "rope axis dims must be even and >= 0");
@@ -61,7 +76,7 @@ dit_status check_config(const dit_config* c) {
     if (sum != c->hd) return fail(DIT_ESHAPE, "rope axis dims sum to %d, head dim is %d", sum, c->hd);
     if (!(c->rope_theta > 0.0) || !isfinite(c->rope_theta)) return fail(DIT_EINVAL, "rope_theta must be > 0");
   }
-  if (c->variant == DIT_MMH3) {
+  if (basis_mods(c)) {
     if (c->slots < 1 || c->slots > 8) return fail(DIT_EUNSUPPORTED, "slots=%d not in [1, 8]", c->slots);
     if (c->tags < 1 || c->tags > 16) return fail(DIT_EINVAL, "tags=%d not in [1, 16]", c->tags);
     if (c->rank < 1 || c->rank > 64) return fail(DIT_EUNSUPPORTED, "rank=%d not in [1, 64]", c->rank);
@@ -95,6 +110,17 @@ PrepLayout prep_layout(const dit_config* c) {
     return o;
   };
   const size_t D = c->D, F = c->F, es = esize(c);
+  if (c->variant == DIT_FINAL) {
+    L.w_fc1 = take(F * D * es);
+    L.norm1 = take(D * 4);
+    L.b_fc1 = take(F * 4);
+    size_t rows = (size_t)c->slots * c->tags * 2 * D;
+    L.basis = take(rows * c->rank * 4);
+    L.abias = take(rows * 4);
+    L.table = take((size_t)c->grid * c->rank * 4);
+    L.total = off;
+    return L;
+  }
   L.w_qkv = take(3 * D * D * es);
   L.w_out = take(D * D * es);
   L.w_fc1 = take((size_t)fc1_rows(c) * D * es);
@@ -148,6 +174,12 @@ dit_ws_layout ws_layout(const dit_config* c, int n) {
   const int ldn = ldn_of(n);
   L.ldn = ldn;
   L.mods = mod_rows(c) ? take((size_t)mod_rows(c) * chunks(c) * D * 4) : kNone;
+  if (c->variant == DIT_FINAL) {  // the head: modulation rows and the normalized rows only
+    L.rope = L.qkv = L.q = L.k = L.vt = L.o = L.x1 = L.a = L.y = L.temb = L.part = kNone;
+    L.xn = take((size_t)n * D * es);
+    L.total = off;
+    return L;
+  }
   L.temb = c->variant == DIT_ZIMAGE ? take((size_t)(c->temb_hidden + c->temb_freq) * 4) : kNone;
   L.rope = c->rope != DIT_ROPE_NONE ? take((size_t)n * (c->hd / 2) * 8) : kNone;
   L.xn = take((size_t)n * D * es);
@@ -188,7 +220,7 @@ dit_status hip_check(hipError_t e, const char* what) {
 
 dit_status check_sigmas(const dit_config* c, const double* sigmas, int n_sigmas) {
   if (!has_mods(c)) return DIT_OK;
-  int need = c->variant == DIT_MMH3 ? c->slots : 1;
+  int need = basis_mods(c) ? c->slots : 1;
   if (!sigmas) return fail(DIT_EINVAL, "sigmas is NULL");
   if (n_sigmas != need) return fail(DIT_ESHAPE, "n_sigmas=%d, the configuration needs %d", n_sigmas, need);
   for (int i = 0; i < need; ++i)
@@ -203,7 +235,7 @@ dit_status check_sigmas(const dit_config* c, const double* sigmas, int n_sigmas)
 dit_status launch_mods(const dit_config* c, const void* prep, const double* sigmas, float* mods,
                        float* temb, hipStream_t s) {
   PrepLayout P = prep_layout(c);
-  if (c->variant == DIT_MMH3) {
+  if (basis_mods(c)) {
     dit::SlotCoords sc;
     memset(&sc, 0, sizeof(sc));
     for (int i = 0; i < c->slots; ++i) {
@@ -213,7 +245,7 @@ dit_status launch_mods(const dit_config* c, const void* prep, const double* sigm
       sc.i0[i] = i0;
       sc.f[i] = (float)(p - (double)i0);
     }
-    int per_slot = c->tags * 6 * c->D;
+    int per_slot = c->tags * chunks(c) * c->D;
     HIP_TRY(dit::adaln_interp(atc<float>(prep, P.basis), atc<float>(prep, P.abias),
                               atc<float>(prep, P.table), c->rank, per_slot, c->slots, sc, mods, s),
             "adaln_interp");
@@ -241,6 +273,10 @@ dit_status launch_prenorm(const dit_config* c, const void* prep, const float* x,
   } else if (c->variant == DIT_ZIMAGE) {
     HIP_TRY(dit::norm_mod(dit::NORM_RMS, dit::MOD_SCALE, bf, x, n, D, g, nullptr, c->eps, mods, 4 * D,
                           nullptr, 0, (half ? 2 : 0) * D, xn, s),
+            "norm_mod");
+  } else if (c->variant == DIT_FINAL) {  // shift chunk 0, scale chunk 1 of the token's slot
+    HIP_TRY(dit::norm_mod(dit::NORM_RMS, dit::MOD_SHIFT_SCALE, bf, x, n, D, g, nullptr, c->eps, mods,
+                          2 * D, rows, 0, D, xn, s),
             "norm_mod");
   } else if (c->variant == DIT_REFINER) {
     HIP_TRY(dit::norm_mod(dit::NORM_RMS, dit::MOD_NONE, bf, x, n, D, g, nullptr, c->eps, nullptr, 0,
@@ -386,6 +422,25 @@ dit_status dit_prepare_weights(const dit_config* c, const dit_weights* w, void* 
     const void* p;
     const char* name;
   };
+  hipStream_t s = (hipStream_t)stream;
+  if (c->variant == DIT_FINAL) {
+    Need need[] = {{w->norm1, "norm1"}, {w->w_fc1, "w_fc1 (head)"}, {w->adaln_basis, "adaln_basis"},
+                   {w->adaln_table, "adaln_table"}};
+    for (auto& q : need) {
+      if (!q.p) return fail(DIT_EINVAL, "weight %s is NULL", q.name);
+      if (!aligned16(q.p)) return fail(DIT_EALIGN, "weight %s is not 16-byte aligned", q.name);
+    }
+    const int D = c->D, F = c->F, rows = c->slots * c->tags * 2 * D;
+    HIP_TRY(dit::prep_matrix(c->dtype, w->w_fc1, at<char>(prepared, P.w_fc1), F, D, 0, 0, 1.0f, s), "prep head");
+    HIP_TRY(dit::prep_vector(w->norm1, at<float>(prepared, P.norm1), D, 0, 1.0f, s), "prep norm1");
+    HIP_TRY(dit::prep_vector(w->b_fc1, at<float>(prepared, P.b_fc1), F, 0, 1.0f, s), "prep head bias");
+    HIP_TRY(dit::prep_matrix(dit::F32, w->adaln_basis, at<char>(prepared, P.basis), rows, c->rank, 0, 0, 1.0f, s),
+            "prep adaln_basis");
+    HIP_TRY(dit::prep_vector(w->adaln_bias, at<float>(prepared, P.abias), rows, 0, 1.0f, s), "prep adaln_bias");
+    HIP_TRY(dit::prep_matrix(dit::F32, w->adaln_table, at<char>(prepared, P.table), c->grid, c->rank, 0, 0, 1.0f, s),
+            "prep adaln_table");
+    return DIT_OK;
+  }
   Need common[] = {{w->w_qkv, "w_qkv"}, {w->w_out, "w_out"}, {w->w_fc1, "w_fc1"},
                    {w->w_fc2, "w_fc2"}, {w->norm1, "norm1"}, {w->norm2, "norm2"}};
   for (auto& q : common) {
@@ -401,7 +456,6 @@ dit_status dit_prepare_weights(const dit_config* c, const dit_weights* w, void* 
       (!w->post_attn_norm || !w->post_ffn_norm || !w->temb_w1 || !w->temb_w2 || !w->ada_w))
     return fail(DIT_EINVAL, "Z-Image norms or timestep weights are NULL");
 
-  hipStream_t s = (hipStream_t)stream;
   const int D = c->D, F = c->F, dt = c->dtype;
   // [SIGLIP] Layer::load folds hd^-1/2 into W_q and b_q.
   const bool fold = c->variant == DIT_SIGLIP;
@@ -535,6 +589,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
                               int32_t nseq, float* out, void* workspace, size_t ws_bytes,
                               void* stream) {
   DIT_TRY(check_config(c));
+  if (c->variant == DIT_FINAL) return fail(DIT_EUNSUPPORTED, "DIT_FINAL is run by dit_final_forward");
   if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
   if (seq_starts) DIT_TRY(check_seqs(seq_starts, nseq, n));
   if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
@@ -717,6 +772,76 @@ dit_status dit_block_forward_packed(const dit_config* c, const void* prepared, c
   if (!seq_starts) return fail(DIT_EINVAL, "seq_starts is NULL");
   return block_forward_impl(c, prepared, x, n, rows, pos, sigmas, n_sigmas, nullptr, seq_starts,
                             nseq, out, workspace, ws_bytes, stream);
+}
+
+dit_status dit_final_forward(const dit_config* c, const void* prepared, const float* h, int32_t n,
+                             const int32_t* rows, const double* sigmas, int32_t n_sigmas, float* out,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  DIT_TRY(check_config(c));
+  if (c->variant != DIT_FINAL) return fail(DIT_EINVAL, "dit_final_forward needs a DIT_FINAL config");
+  if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
+  if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
+  DIT_TRY(check_sigmas(c, sigmas, n_sigmas));
+  if (n == 0) return DIT_OK;
+  if (!h || !out) return fail(DIT_EINVAL, "h/out is NULL");
+  if (!aligned16(h) || !aligned16(out)) return fail(DIT_EALIGN, "h/out not 16-byte aligned");
+  if (!workspace) return fail(DIT_EINVAL, "workspace is NULL");
+  if ((uintptr_t)workspace % kAlign) return fail(DIT_EALIGN, "workspace must be 256-byte aligned");
+  dit_ws_layout L = ws_layout(c, n);
+  if (ws_bytes < L.total) return fail(DIT_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  hipStream_t s = (hipStream_t)stream;
+  PrepLayout P = prep_layout(c);
+  float* mods = at<float>(workspace, L.mods);
+  void* xn = at<char>(workspace, L.xn);
+  DIT_TRY(launch_mods(c, prepared, sigmas, mods, nullptr, s));
+  DIT_TRY(launch_prenorm(c, prepared, h, n, rows, mods, 0, xn, s));
+  dit::Epi ep;
+  ep.out = out;
+  ep.ldc = c->F;
+  ep.bias = atc<float>(prepared, P.b_fc1);
+  ep.alpha = -1.0f;  // the head predicts toward the data: the velocity is its negative
+  HIP_TRY(dit::gemm(c->dtype, dit::EPI_STORE, false, xn, c->D, atc<char>(prepared, P.w_fc1), c->D, n,
+                    c->F, c->D, ep, s),
+          "head gemm");
+  return DIT_OK;
+}
+
+dit_status dit_linear(int32_t dtype, const void* a, int32_t lda, int32_t m, int32_t k, const void* w,
+                      int32_t nout, const float* bias, float alpha, float* out, void* stream) {
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return fail(DIT_EDTYPE, "unknown dtype %d", dtype);
+  if (m < 0 || k <= 0 || nout <= 0 || lda < k) return fail(DIT_ESHAPE, "m=%d k=%d nout=%d lda=%d", m, k, nout, lda);
+  const bool bf = dtype == DIT_BF16;
+  if (k % (bf ? 64 : 16) || nout % (bf ? 32 : 64))
+    return fail(DIT_EUNSUPPORTED, "k=%d / nout=%d: need k %% %d == 0 and nout %% %d == 0", k, nout,
+                bf ? 64 : 16, bf ? 32 : 64);
+  if (lda % (bf ? 8 : 4)) return fail(DIT_EALIGN, "lda=%d must keep rows 16-byte aligned", lda);
+  if (!isfinite(alpha)) return fail(DIT_EINVAL, "alpha not finite");
+  if (m == 0) return DIT_OK;
+  if (!a || !w || !out) return fail(DIT_EINVAL, "a/w/out is NULL");
+  if (!aligned16(a) || !aligned16(w) || !aligned16(out)) return fail(DIT_EALIGN, "a/w/out not 16-byte aligned");
+  dit::Epi ep;
+  ep.out = out;
+  ep.ldc = nout;
+  ep.bias = bias;
+  ep.alpha = alpha;
+  HIP_TRY(dit::gemm(dtype, dit::EPI_STORE, false, a, lda, w, k, m, nout, k, ep, (hipStream_t)stream),
+          "linear");
+  return DIT_OK;
+}
+
+dit_status dit_stack_forward(const dit_config* c, const void* const* prepared, int32_t n_blocks,
+                             const float* x, int32_t n, const int32_t* rows, const float* pos,
+                             const double* sigmas, int32_t n_sigmas, const int32_t* seq_starts,
+                             int32_t nseq, float* out, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  if (n_blocks < 1) return fail(DIT_ESHAPE, "n_blocks=%d < 1", n_blocks);
+  if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
+  for (int i = 0; i < n_blocks; ++i)
+    if (!prepared[i]) return fail(DIT_EINVAL, "prepared[%d] is NULL", i);
+  for (int i = 0; i < n_blocks; ++i)
+    DIT_TRY(block_forward_impl(c, prepared[i], i == 0 ? x : out, n, rows, pos, sigmas, n_sigmas,
+                               nullptr, seq_starts, nseq, out, workspace, ws_bytes, stream));
+  return DIT_OK;
 }
 
 dit_status dit_block_forward_mods(const dit_config* c, const void* prepared, const float* x,

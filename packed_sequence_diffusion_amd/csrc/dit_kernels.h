@@ -23,6 +23,7 @@ struct Epi {
   void* out = nullptr;  // element type: fp32 for GATED_RES, else the GEMM's out type
   int ldc = 0;
   const float* bias = nullptr;   // [N] (GELU, STORE, GATED_RES) or null
+  float alpha = 1.0f;            // STORE: out = alpha * (acc + bias)
   const float* resid = nullptr;  // GATED_RES: fp32 [M, ldr]
   int ldr = 0;
   const float* mods = nullptr;  // GATED_RES: gate = mods[rows[r] * mstride + goff + c]

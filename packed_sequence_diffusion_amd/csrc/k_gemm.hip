@@ -17,7 +17,7 @@ template <int EPI, typename OutT>
 DIT_DEV void epi_one(const Epi& ep, int row, int col, float v) {
   if (EPI == EPI_STORE) {
     if (ep.bias) v += ep.bias[col];
-    Elt<OutT>::st((OutT*)ep.out + (size_t)row * ep.ldc + col, v);
+    Elt<OutT>::st((OutT*)ep.out + (size_t)row * ep.ldc + col, ep.alpha * v);
   } else if (EPI == EPI_GELU) {
     if (ep.bias) v += ep.bias[col];
     Elt<OutT>::st((OutT*)ep.out + (size_t)row * ep.ldc + col, gelu_tanh_f(v));
@@ -68,7 +68,8 @@ DIT_DEV void epi_gated_rows(const Epi& ep, const int (&row)[NR], int M, int cbas
 // The next K tile is loaded into registers one full MFMA section ahead of its
 // LDS store (the loads of tile k+2 are issued right after tile k+1 is stored),
 // so global latency hides behind a whole tile of MFMAs.  A partial last N tile
-// (N % 256 == 128) clamps its B rows and masks its stores.
+// (N % 256 != 0, N % 32 == 0) clamps its B rows and masks its stores (per
+// 128-column wave strip, and per 32-column block in the plain-store epilogue).
 constexpr int GBM = 256, GBN = 256, GBK = 64;
 constexpr int GWM = 4, GWN = 2;                 // wave grid
 constexpr int GTM = GBM / GWM, GTN = GBN / GWN;  // 64 x 128 per wave
@@ -370,7 +371,9 @@ __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A,
           epi_swiglu<OutT>(ep, row, (cbase + ni * 32) / 2 + cl, acc[mi][ni][v], acc[mi][ni + 1][v]);
       } else {
 #pragma unroll
-        for (int ni = 0; ni < GNI; ++ni) epi_one<EPI, OutT>(ep, row, cbase + ni * 32 + cl, acc[mi][ni][v]);
+        for (int ni = 0; ni < GNI; ++ni)
+          if (cbase + ni * 32 < N)  // N % 32 == 0: whole 32-column blocks in or out
+            epi_one<EPI, OutT>(ep, row, cbase + ni * 32 + cl, acc[mi][ni][v]);
       }
     }
   }

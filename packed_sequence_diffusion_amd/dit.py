@@ -16,12 +16,12 @@ from typing import Dict, List, Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdit.so")
 
-MMH3, SIGLIP, ZIMAGE, REFINER = 0, 1, 2, 3
+MMH3, SIGLIP, ZIMAGE, REFINER, FINAL = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 ROPE_NONE, ROPE_SPLIT_HALF, ROPE_INTERLEAVED = 0, 1, 2
 NPHASES = 9
 
-_VARIANTS = {"mmh3": MMH3, "siglip": SIGLIP, "zimage": ZIMAGE, "refiner": REFINER}
+_VARIANTS = {"mmh3": MMH3, "siglip": SIGLIP, "zimage": ZIMAGE, "refiner": REFINER, "final": FINAL}
 _DTYPES = {"f32": F32, "bf16": BF16}
 _ROPES = {"none": ROPE_NONE, "split_half": ROPE_SPLIT_HALF, "interleaved": ROPE_INTERLEAVED}
 
@@ -93,6 +93,14 @@ def _load() -> ctypes.CDLL:
         "dit_block_forward_mods": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_int32, c_void_p,
                                              c_void_p, c_void_p, P(c_int32), c_int32, c_void_p,
                                              c_void_p, c_size_t, c_void_p]),
+        "dit_final_forward": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_int32, c_void_p,
+                                        P(c_double), c_int32, c_void_p, c_void_p, c_size_t,
+                                        c_void_p]),
+        "dit_linear": (c_int32, [c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_int32,
+                                 c_void_p, c_float, c_void_p, c_void_p]),
+        "dit_stack_forward": (c_int32, [P(DitConfig), P(c_void_p), c_int32, c_void_p, c_int32,
+                                        c_void_p, c_void_p, P(c_double), c_int32, P(c_int32),
+                                        c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
         "dit_attention": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                     c_float, c_void_p, c_void_p]),
         "dit_attention_packed": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_void_p, c_int32,
@@ -299,4 +307,51 @@ def profile_end() -> Dict[str, float]:
     _check(lib.dit_profile_end(ms, ctypes.byref(calls)))
     out = {lib.dit_phase_name(i).decode(): ms[i] for i in range(NPHASES)}
     out["calls"] = calls.value
+    return out
+
+
+def final_forward(blk: "Block", h, rows, sigmas: Sequence[float], out=None, workspace=None,
+                  stream=None):
+    """Output head (a Block prepared with a DIT_FINAL config): out = -(W
+    modulate(RMSNorm(h)) + b), fp32 [n, F]."""
+    import torch
+    n = int(h.shape[0])
+    if out is None:
+        out = torch.empty((n, blk.cfg.F), dtype=torch.float32, device=h.device)
+    ws = blk.workspace(n) if workspace is None else workspace
+    sg, ns = _dbl(sigmas)
+    _check(lib.dit_final_forward(ctypes.byref(blk.cfg), blk.prepared.data_ptr(), _ptr(h), n,
+                                 _ptr(rows), sg, ns, _ptr(out), ws.data_ptr(), ws.numel(),
+                                 _stream(stream)))
+    return out
+
+
+def linear(a, w, bias=None, alpha: float = 1.0, out=None, stream=None):
+    """out = alpha * (a @ w^T + bias) in fp32 on the block GEMM kernels; a and w
+    share a dtype (bfloat16 or float32)."""
+    import torch
+    m, k = int(a.shape[0]), int(a.shape[1])
+    nout = int(w.shape[0])
+    dtype = BF16 if a.dtype == torch.bfloat16 else F32
+    if out is None:
+        out = torch.empty((m, nout), dtype=torch.float32, device=a.device)
+    _check(lib.dit_linear(dtype, _ptr(a), int(a.stride(0)), m, k, _ptr(w), nout, _ptr(bias),
+                          alpha, _ptr(out), _stream(stream)))
+    return out
+
+
+def stack_forward(blocks: Sequence["Block"], x, rows, pos, sigmas: Sequence[float], out=None,
+                  workspace=None, stream=None, seq_starts: Optional[Sequence[int]] = None):
+    """Blocks of one configuration in order: out = blocks[-1](...blocks[0](x))."""
+    import torch
+    n = int(x.shape[0])
+    if out is None:
+        out = torch.empty_like(x)
+    ws = blocks[0].workspace(n) if workspace is None else workspace
+    preps = (c_void_p * len(blocks))(*[b.prepared.data_ptr() for b in blocks])
+    sg, ns = _dbl(sigmas)
+    st, nseq = (None, 0) if seq_starts is None else _starts(seq_starts)
+    _check(lib.dit_stack_forward(ctypes.byref(blocks[0].cfg), preps, len(blocks), _ptr(x), n,
+                                 _ptr(rows), _ptr(pos), sg, ns, st, nseq, _ptr(out),
+                                 ws.data_ptr(), ws.numel(), _stream(stream)))
     return out

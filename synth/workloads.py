@@ -60,11 +60,11 @@ class BlockSpec:
 
     @property
     def chunks(self) -> int:
-        return {"mmh3": 6, "zimage": 4, "siglip": 0, "refiner": 0}[self.variant]
+        return {"mmh3": 6, "zimage": 4, "siglip": 0, "refiner": 0, "final": 2}[self.variant]
 
     @property
     def mod_rows(self) -> int:
-        if self.variant == "mmh3":
+        if self.variant in ("mmh3", "final"):
             return self.slots * self.tags
         if self.variant == "zimage":
             return 1
@@ -264,6 +264,13 @@ def weight_shapes(spec: BlockSpec) -> List[Tuple[str, Tuple[int, ...], str]]:
             ("w_qkv", (3 * D, D), "lin"), ("w_out", (D, D), "lin"),
             ("q_norm", (hd,), "gain"), ("k_norm", (hd,), "gain"),
             ("w_fc1", (2 * F, D), "lin"), ("w_fc2", (D, F), "lin"),
+            ("adaln_basis", (R, spec.rank), "vec"), ("adaln_bias", (R,), "vec"),
+            ("adaln_table", (spec.grid, spec.rank), "table"),
+        ]
+    if spec.variant == "final":  # output head: F = output width, tags = 1
+        R = spec.slots * spec.tags * 2 * D
+        return [
+            ("norm1", (D,), "gain"), ("w_fc1", (F, D), "lin"), ("b_fc1", (F,), "vec"),
             ("adaln_basis", (R, spec.rank), "vec"), ("adaln_bias", (R,), "vec"),
             ("adaln_table", (spec.grid, spec.rank), "table"),
         ]

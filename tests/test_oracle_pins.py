@@ -379,6 +379,41 @@ def test_refiner_is_the_mmh3_block_with_neutral_modulation():
             np.testing.assert_allclose(got[name], want[name], rtol=1e-13, atol=1e-13)
 
 
+def test_final_layer_matches_torch_composition():
+    """The head against torch fp64: table lerp at the slot timesteps,
+    basis map, rms_norm, shift/scale of the token's slot, linear, negation."""
+    import torch
+    import torch.nn.functional as Fn
+    spec = W.BlockSpec("head", "final", "f32", n=9, D=16, H=2, hd=8, F=12, slots=2, tags=1,
+                       rank=3, grid=9)
+    wl = W.make_custom_workload(spec, 51, sigmas=[0.3, 0.85])
+    w = {k: v.astype(np.float64) for k, v in wl.weights.items()}
+    got = O.final_layer(spec, wl.x, wl.rows, [0.3, 0.85], w)["out"]
+    tw = {k: torch.from_numpy(v) for k, v in w.items()}
+    rows_per_slot = 2 * spec.D
+    mods = []
+    for s_, sig in enumerate([0.3, 0.85]):
+        t = 1.0 - max(sig, 1e-6)
+        p = min(max(t, 0.0), 1.0) * (spec.grid - 1)
+        i0 = min(int(math.floor(p)), spec.grid - 2)
+        c = tw["adaln_table"][i0] + (p - i0) * (tw["adaln_table"][i0 + 1] - tw["adaln_table"][i0])
+        blk = slice(s_ * rows_per_slot, (s_ + 1) * rows_per_slot)
+        mods.append(tw["adaln_basis"][blk] @ c + tw["adaln_bias"][blk])
+    mods = torch.stack(mods)
+    r = torch.from_numpy(wl.rows.astype(np.int64))
+    hn = Fn.rms_norm(torch.from_numpy(wl.x.astype(np.float64)), (spec.D,), tw["norm1"], spec.eps)
+    hn = hn * (1 + mods[r, spec.D:]) + mods[r, :spec.D]
+    want = -Fn.linear(hn, tw["w_fc1"], tw["b_fc1"])
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_stack_is_sequential_blocks():
+    spec, x, rows, pos, sig, w = _tiny_mmh3_inputs(18, n=8)
+    w2 = {k: v * (1.1 if k.startswith("w_") else 1.0) for k, v in w.items()}
+    a = O.mmh3_block(spec, O.mmh3_block(spec, x, rows, pos, sig, w)["out"], rows, pos, sig, w2)["out"]
+    np.testing.assert_array_equal(O.stack(spec, x, rows, pos, sig, [w, w2]), a)
+
+
 def test_packed_block_equals_samples_run_alone():
     """[ENC]: a ragged batch behaves exactly like its sequences run solo."""
     spec, x, rows, pos, sig, w = _tiny_mmh3_inputs(16, n=12)

@@ -92,6 +92,11 @@ def main():
     ap.add_argument("--seqs", type=int, default=1,
                     help="pack the workload as this many independent samples of equal length "
                          "(block-diagonal attention); 1 = one sequence")
+    ap.add_argument("--blocks", type=int, default=1,
+                    help="a stack of this many blocks with their own weights per step "
+                         "(dit_stack_forward); value stays tokens/s per block")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times (the "
                          "calibration kernel for the HBM byte counters) and exit")
@@ -123,30 +128,60 @@ def main():
     dev = to_device(wl)
     cfg = dit.make_config(spec)
     blk = dit.Block(cfg, dev.weights)
+    blocks = [blk]
+    for i in range(1, args.blocks):  # further blocks: same shape, their own seeded weights
+        blocks.append(dit.Block(cfg, to_device(W.make_custom_workload(
+            spec, 0xD17200 + i)).weights))
     sig = dit.resolve_sigmas(wl.slot_plan)
     out = torch.empty_like(dev.x)
     ws = blk.workspace(spec.n)
     torch.cuda.synchronize()
-    log(f"setup {time.perf_counter() - t0:.1f} s; workspace {ws.numel() / 2**30:.2f} GiB")
+    log(f"setup {time.perf_counter() - t0:.1f} s; workspace {ws.numel() / 2**30:.2f} GiB; "
+        f"{len(blocks)} block(s)")
+
+    def step():
+        if len(blocks) == 1:
+            blk.forward(dev.x, dev.rows, dev.pos, sig, out=out, workspace=ws, seq_starts=seq_starts)
+        else:
+            dit.stack_forward(blocks, dev.x, dev.rows, dev.pos, sig, out=out, workspace=ws,
+                              seq_starts=seq_starts)
+
+    stream = torch.cuda.current_stream()
+    run = step
+    if args.graph:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                step()
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        run = graph.replay
 
     for _ in range(args.warmup):
-        blk.forward(dev.x, dev.rows, dev.pos, sig, out=out, workspace=ws, seq_starts=seq_starts)
+        run()
     torch.cuda.synchronize()
     log("warmup done")
 
-    stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    dit.profile_begin(args.steps)
+    if not args.graph:
+        dit.profile_begin(args.steps * len(blocks))
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
-        blk.forward(dev.x, dev.rows, dev.pos, sig, out=out, workspace=ws, seq_starts=seq_starts)
+        run()
     ev1.record(stream)
     torch.cuda.synchronize()
+    if args.graph:  # phase split from an eager pass of the same steps
+        dit.profile_begin(args.steps * len(blocks))
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
     phases = dit.profile_end()
     total_ms = ev0.elapsed_time(ev1)
-    ms = total_ms / args.steps
+    ms = total_ms / args.steps / len(blocks)  # per block
     calls = phases.pop("calls")
     ph = {k: v / calls for k, v in phases.items()}
     log("phases (ms/step): " + ", ".join(f"{k}={v:.3f}" for k, v in ph.items()))
@@ -197,6 +232,8 @@ def main():
             "n": spec.n, "D": spec.D, "heads": spec.H, "head_dim": spec.hd, "ffn": spec.F,
             "parallelism": "single GPU",
             "samples": args.seqs,
+            "blocks_per_step": args.blocks,
+            "hip_graph": bool(args.graph),
         },
         "attention_tflops": attn_tf,
         "attention_frac_mfma_peak": attn_tf / PEAK_BF16_TFLOPS,

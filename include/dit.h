@@ -308,6 +308,23 @@ const char* dit_phase_name(int32_t phase);
  * Host function. */
 double dit_sigma_remap(double sigma, double from_shift, double to_shift);
 
+/* The timestep slots of one MMH3 evaluation ([MMH3] MiniMaxH3::forward): the
+ * video stream at t_v = 1 - max(sigma_v, 1e-6), the audio stream at t_a =
+ * 1 - dit_sigma_remap(max(sigma_v, 1e-6), shift_video, shift_audio), condition
+ * frames and reference images (has_cond) at t_c = max(t_v, cond_aug),
+ * reference audio (has_ref_audio) at t_ca = max(t_a, cond_aug_audio).  The
+ * distinct values, sorted ascending, are the slots (so the order is part of
+ * the contract).  Writes slot_sigmas[s] = 1 - t_s, the sigmas that the block
+ * entry points take (they evaluate slot s at 1 - max(sigma, 1e-6): a slot at
+ * t = 1 exactly is evaluated at 1 - 1e-6), and slot_of = {video, audio, cond,
+ * ref audio} slot indices (-1 when absent).  A token's modulation row is then
+ * slot * 3 + tag (video 0, text 1, audio 2; condition frames and reference
+ * images take the video tag, reference audio the audio tag).  Host function;
+ * returns the slot count (1..4), or DIT_EINVAL for non-finite input. */
+int32_t dit_mmh3_slots(double sigma_v, double shift_video, double shift_audio, double cond_aug,
+                       double cond_aug_audio, int32_t has_cond, int32_t has_ref_audio,
+                       double slot_sigmas[4], int32_t slot_of[4]);
+
 /* d sigma_to / d sigma_from of dit_sigma_remap ([MMH3] time_shift_slope). */
 double dit_sigma_remap_slope(double sigma, double from_shift, double to_shift);
 

@@ -79,6 +79,48 @@ def resolve_sigmas(plan: Sequence[tuple]) -> List[float]:
     return out
 
 
+def mmh3_slots(sigma_v: float, shift_video: float, shift_audio: float, cond_aug: float,
+               cond_aug_audio: float, has_cond: bool, has_ref_audio: bool):
+    """Timestep slots of one evaluation ([MMH3] ``MiniMaxH3::forward``): video
+    at 1 - max(sigma_v, 1e-6), audio at 1 - remap of that sigma, condition
+    frames / reference images at max(t_v, cond_aug), reference audio at
+    max(t_a, cond_aug_audio); distinct values ascending.  Returns (slot
+    timesteps, {stream: slot index or -1})."""
+    sv = max(sigma_v, 1e-6)
+    tv = 1.0 - sv
+    ta = 1.0 - sigma_remap(sv, shift_video, shift_audio)
+    ts = [tv, ta]
+    tc = max(tv, cond_aug)
+    tca = max(ta, cond_aug_audio)
+    if has_cond:
+        ts.append(tc)
+    if has_ref_audio:
+        ts.append(tca)
+    ts = sorted(set(ts))
+    slot = {"video": ts.index(tv), "audio": ts.index(ta),
+            "cond": ts.index(tc) if has_cond else -1,
+            "ref_audio": ts.index(tca) if has_ref_audio else -1}
+    return ts, slot
+
+
+def mmh3_token_rows(segments, slot, tags: int = 3) -> np.ndarray:
+    """Per-token modulation row slot * tags + tag from (kind, start, stop)
+    segments ([MMH3] ``MiniMaxH3::forward``): text at the video slot with the
+    text tag; video, condition frames and reference images with the video tag
+    (the latter two at the condition slot); audio and reference audio with the
+    audio tag."""
+    video, text, audio = 0, 1, 2
+    of = {"text": (slot["video"], text), "video": (slot["video"], video),
+          "audio": (slot["audio"], audio), "cond": (slot["cond"], video),
+          "ref_image": (slot["cond"], video), "ref_audio": (slot["ref_audio"], audio)}
+    n = max(b for _, _, b in segments)
+    rows = np.empty(n, dtype=np.int64)
+    for kind, a, b in segments:
+        s, t = of[kind]
+        rows[a:b] = s * tags + t
+    return rows
+
+
 def mmh3_timestep(sigma: float) -> float:
     """Slot timestep t = 1 - max(sigma, 1e-6) ([MMH3] ``MiniMaxH3::forward``)."""
     return 1.0 - max(sigma, 1e-6)
@@ -529,7 +571,8 @@ def rel_rms(a: np.ndarray, ref: np.ndarray) -> float:
 
 
 __all__ = [
-    "sigma_remap", "sigma_remap_slope", "resolve_sigmas", "mmh3_timestep",
+    "sigma_remap", "sigma_remap_slope", "resolve_sigmas", "mmh3_timestep", "mmh3_slots",
+    "mmh3_token_rows",
     "adaln_coords", "adaln_mods", "rms_norm", "layer_norm", "modulate", "silu",
     "gelu_tanh", "rope_angles", "rope_rotate", "attention", "sample_ranges",
     "attention_packed", "mmh3_block", "refiner_block", "linear", "final_layer", "stack",

@@ -384,6 +384,32 @@ double dit_sigma_remap(double sigma, double from_shift, double to_shift) {
   return to_shift * base / (1.0 + (to_shift - 1.0) * base);
 }
 
+int32_t dit_mmh3_slots(double sigma_v, double shift_video, double shift_audio, double cond_aug,
+                       double cond_aug_audio, int32_t has_cond, int32_t has_ref_audio,
+                       double slot_sigmas[4], int32_t slot_of[4]) {
+  if (!slot_sigmas || !slot_of) return fail(DIT_EINVAL, "slot_sigmas/slot_of is NULL");
+  if (!isfinite(sigma_v) || !isfinite(shift_video) || !isfinite(shift_audio) || !isfinite(cond_aug) ||
+      !isfinite(cond_aug_audio))
+    return fail(DIT_EINVAL, "non-finite slot input");
+  const double sv = std::max(sigma_v, 1e-6);
+  const double tv = 1.0 - sv;
+  const double ta = 1.0 - dit_sigma_remap(sv, shift_video, shift_audio);
+  double t[4] = {tv, ta, 0.0, 0.0};
+  int nt = 2;
+  const double tc = std::max(tv, cond_aug), tca = std::max(ta, cond_aug_audio);
+  if (has_cond) t[nt++] = tc;
+  if (has_ref_audio) t[nt++] = tca;
+  std::sort(t, t + nt);
+  nt = (int)(std::unique(t, t + nt) - t);
+  auto slot = [&](double v) { return (int32_t)(std::find(t, t + nt, v) - t); };
+  for (int i = 0; i < 4; ++i) slot_sigmas[i] = i < nt ? 1.0 - t[i] : 0.0;
+  slot_of[0] = slot(tv);
+  slot_of[1] = slot(ta);
+  slot_of[2] = has_cond ? slot(tc) : -1;
+  slot_of[3] = has_ref_audio ? slot(tca) : -1;
+  return nt;
+}
+
 double dit_sigma_remap_slope(double sigma, double from_shift, double to_shift) {
   double base = sigma / (from_shift + sigma * (1.0 - from_shift));
   double a = 1.0 + (from_shift - 1.0) * base, b = 1.0 + (to_shift - 1.0) * base;

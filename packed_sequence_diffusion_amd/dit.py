@@ -73,6 +73,8 @@ def _load() -> ctypes.CDLL:
         "dit_last_error": (ctypes.c_char_p, []),
         "dit_sigma_remap": (c_double, [c_double, c_double, c_double]),
         "dit_sigma_remap_slope": (c_double, [c_double, c_double, c_double]),
+        "dit_mmh3_slots": (c_int32, [c_double, c_double, c_double, c_double, c_double, c_int32,
+                                     c_int32, P(c_double), P(c_int32)]),
         "dit_validate_config": (c_int32, [P(DitConfig)]),
         "dit_prepared_size": (c_size_t, [P(DitConfig)]),
         "dit_prepare_weights": (c_int32, [P(DitConfig), P(DitWeights), c_void_p, c_size_t, c_void_p]),
@@ -135,6 +137,20 @@ def sigma_remap(sigma: float, from_shift: float, to_shift: float) -> float:
 
 def sigma_remap_slope(sigma: float, from_shift: float, to_shift: float) -> float:
     return lib.dit_sigma_remap_slope(sigma, from_shift, to_shift)
+
+
+def mmh3_slots(sigma_v: float, shift_video: float = 12.0, shift_audio: float = 3.0,
+               cond_aug: float = 0.999, cond_aug_audio: float = 1.0, has_cond: bool = False,
+               has_ref_audio: bool = False):
+    """(slot sigmas, {"video", "audio", "cond", "ref_audio"} -> slot or -1)
+    through dit_mmh3_slots."""
+    sg = (c_double * 4)()
+    so = (c_int32 * 4)()
+    k = lib.dit_mmh3_slots(sigma_v, shift_video, shift_audio, cond_aug, cond_aug_audio,
+                           int(has_cond), int(has_ref_audio), sg, so)
+    if k < 0:
+        raise DitError(k, lib.dit_last_error().decode())
+    return [sg[i] for i in range(k)], dict(zip(("video", "audio", "cond", "ref_audio"), so))
 
 
 def resolve_sigmas(plan: Sequence[tuple]) -> List[float]:

@@ -189,3 +189,20 @@ def test_given_mods_refusals(dit):
     assert F(ctypes.byref(sig), 256, 16, 10, 16, 16, 256, None, 0, 16, 256, 1 << 40, None) == -6
     st = (ctypes.c_int32 * 2)(0, 9)
     assert F(ctypes.byref(c), 256, 16, 10, 16, 16, 256, st, 1, 16, 256, 1 << 40, None) == -2
+
+
+def test_mmh3_slots_match_the_oracle(dit):
+    """The host slot planner against the oracle's, over random and edge sigmas
+    and every combination of condition streams."""
+    import numpy as np
+    import oracle as O
+    rng = np.random.default_rng(5)
+    for sv in [0.0, 1e-9, 1e-6, 0.001, 0.5, 0.999, 1.0] + list(rng.uniform(0, 1, 20)):
+        for hc in (False, True):
+            for hr in (False, True):
+                sig, slot = dit.mmh3_slots(float(sv), has_cond=hc, has_ref_audio=hr)
+                ts, oslot = O.mmh3_slots(float(sv), 12.0, 3.0, 0.999, 1.0, hc, hr)
+                assert slot == oslot
+                np.testing.assert_allclose([1.0 - s for s in sig], ts, rtol=0, atol=1e-15)
+    assert dit.lib.dit_mmh3_slots(float("nan"), 12.0, 3.0, 0.999, 1.0, 0, 0,
+                                  (ctypes.c_double * 4)(), (ctypes.c_int32 * 4)()) == -1

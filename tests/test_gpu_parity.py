@@ -348,3 +348,34 @@ def test_given_mods_from_adaln_eval_equal_forward(dit):
     b = blk.forward_mods(dev.x, dev.rows, dev.pos, mods)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ---- conditioning frames: a third timestep slot from the slot planner ----
+
+def test_keyframe_conditioning_slots(dit):
+    """A first-frame keyframe (condition rows at max(t_v, 0.999)) plus text,
+    stereo audio and three video frames: the library's slot planner gives the
+    slot sigmas and the streams' slots, the token rows are placed from the
+    layout; the oracle plans its own slots and rows from the page's rules."""
+    sigma_v = 0.37
+    lay = W.build_layout(32, 3, 16, 16, 24, keyframes=[(0, 3)])
+    sig, slot = dit.mmh3_slots(sigma_v, has_cond=True)
+    assert len(sig) == 3 and slot["cond"] == 2
+    rows = W._rows_for(lay, {"text": (slot["video"], W.TAG_TEXT), "cond": (slot["cond"], W.TAG_VIDEO),
+                             "audio": (slot["audio"], W.TAG_AUDIO),
+                             "video": (slot["video"], W.TAG_VIDEO)}, 3)
+    n = lay.seq_len
+    spec = W.BlockSpec("keyframe", "mmh3", "bf16", n=n, D=256, H=2, hd=128, F=384, slots=3,
+                       rope="split_half", rope_axes=(32, 48, 48))
+    wl = W.make_custom_workload(spec, 4000, pos=lay.pos.astype(np.float32), rows=rows, sigmas=sig)
+    ts, oslot = O.mmh3_slots(sigma_v, 12.0, 3.0, 0.999, 1.0, True, False)
+    orows = O.mmh3_token_rows(lay.segments, oslot)
+    assert np.array_equal(orows, rows)
+    # the oracle side runs on its own plan (same values to rounding)
+    owl = dataclasses.replace(wl, slot_plan=[("value", 1.0 - t) for t in ts],
+                              rows=orows.astype(np.int32))
+    log(f"[case] keyframe-3-slots: n={n} library sigmas={sig} oracle t={ts}")
+    _, st = run_gpu(spec, wl, dit)
+    errs, bad, t = compare(spec, owl, st)
+    log("[case] keyframe-3-slots: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert not bad, f"keyframe-3-slots: stages over {t}: {bad}"

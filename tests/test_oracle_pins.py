@@ -52,6 +52,30 @@ def test_remap_slope_finite_difference_printed_points():
         assert abs(O.sigma_remap_slope(s, 12.0, 3.0) - 4.0 / (4.0 - 3.0 * s) ** 2) < 1e-12
 
 
+def test_mmh3_slots_rules():
+    """The evaluation's timestep list, from the page's rules written out as
+    cases: ascending, deduplicated, conditions pinned near 1."""
+    # no conditions: audio is always later than video (sigma_a <= sigma_v)
+    ts, slot = O.mmh3_slots(0.5, 12.0, 3.0, 0.999, 1.0, False, False)
+    np.testing.assert_allclose(ts, [0.5, 1.0 - 0.2], rtol=0, atol=1e-15)
+    assert slot == {"video": 0, "audio": 1, "cond": -1, "ref_audio": -1}
+    # sigma_v = 1: both streams at t = 0 -> one slot
+    ts, slot = O.mmh3_slots(1.0, 12.0, 3.0, 0.999, 1.0, False, False)
+    assert ts == [0.0] and slot["video"] == slot["audio"] == 0
+    # keyframes at max(t_v, 0.999); reference audio at max(t_a, 1.0) = 1
+    ts, slot = O.mmh3_slots(0.6, 12.0, 3.0, 0.999, 1.0, True, True)
+    sa = 0.6 / (4.0 - 3.0 * 0.6)
+    np.testing.assert_allclose(ts, [0.4, 1.0 - sa, 0.999, 1.0], rtol=0, atol=1e-15)
+    assert slot == {"video": 0, "audio": 1, "cond": 2, "ref_audio": 3}
+    # sigma floor: t_v = 1 - 1e-6 is later than 0.999, so the condition rows
+    # share the video slot
+    ts, slot = O.mmh3_slots(0.0, 12.0, 3.0, 0.999, 1.0, True, False)
+    assert slot["cond"] == slot["video"] and len(ts) == 2
+    rows = O.mmh3_token_rows([("text", 0, 2), ("cond", 2, 3), ("audio", 3, 5), ("video", 5, 6)],
+                             {"video": 0, "audio": 1, "cond": 2, "ref_audio": -1})
+    assert rows.tolist() == [1, 1, 6, 5, 5, 0]
+
+
 def test_timestep_of_sigma():
     assert O.mmh3_timestep(0.3) == pytest.approx(0.7, abs=1e-15)
     assert O.mmh3_timestep(0.0) == 1.0 - 1e-6

@@ -256,6 +256,80 @@ dit_status dit_linear(int32_t dtype, const void* a, int32_t lda, int32_t m, int3
                       const void* w, int32_t nout, const float* bias, float alpha, float* out,
                       void* stream);
 
+/* Latent streams <-> token rows ([MMH3] patchify_video, unpatchify_video,
+ * pack_audio, unpack_audio).  video: device fp32 [C, T, H, W] (H, W even);
+ * rows [T*(H/2)*(W/2), 4C], row (t, h2, w2) holding the 2 x 2 patch at
+ * (2*h2, 2*w2) of frame t, column c*4 + p*2 + q = x[c, t, 2*h2 + p, 2*w2 + q].
+ * audio: device fp32 [C, 2, T]; rows [2T, C], row ch*T + t, column c =
+ * x[c, ch, t].  The packing side writes rows in `dtype` (the embedding GEMM's
+ * operand); the unpacking side reads fp32 rows (the head's output). */
+dit_status dit_patchify_video(int32_t dtype, const float* x, int32_t C, int32_t T, int32_t H,
+                              int32_t W, void* rows, void* stream);
+dit_status dit_unpatchify_video(const float* rows, int32_t C, int32_t T, int32_t H, int32_t W,
+                                float* x, void* stream);
+dit_status dit_pack_audio(int32_t dtype, const float* x, int32_t C, int32_t T, void* rows,
+                          void* stream);
+dit_status dit_unpack_audio(const float* rows, int32_t C, int32_t T, float* x, void* stream);
+
+/* One denoise evaluation of the MMH3 model ([MMH3] MiniMaxH3::forward):
+ * embed (video and condition frames through the video patch projection, audio
+ * through the audio one, refined text copied in), the timestep slots of
+ * dit_mmh3_slots and the token rows, the blocks in order, then the video and
+ * audio heads (dit_final_forward, negated) and the unpacking of their rows.
+ * Condition latents are taken as given (any noise augmentation is the
+ * caller's); the text span carries the text tag. */
+typedef enum {
+  DIT_SEG_TEXT = 0,
+  DIT_SEG_VIDEO = 1,  /* the noisy target, T*(H/2)*(W/2) rows */
+  DIT_SEG_AUDIO = 2,  /* 2*Ta rows */
+  DIT_SEG_COND = 3    /* one condition frame, (H/2)*(W/2) rows */
+} dit_segment_kind;
+
+typedef struct dit_segment {
+  int32_t kind, start, stop; /* rows [start, stop) of the packed sequence */
+} dit_segment;
+
+typedef struct dit_mmh3_model {
+  const dit_config* block;          /* DIT_MMH3; slots >= the slots of an evaluation (<= 3) */
+  const void* const* blocks;        /* n_blocks prepared block weights (host array)        */
+  int32_t n_blocks;
+  const dit_config* head_video;     /* DIT_FINAL, F = 4 * latent_c, same slots as block     */
+  const void* head_video_w;         /* prepared                                            */
+  const dit_config* head_audio;     /* DIT_FINAL, F = audio_c                               */
+  const void* head_audio_w;
+  int32_t latent_c, audio_c;        /* latent channels of the video and audio streams     */
+  const void* video_patch_w;        /* [D, 4*latent_c] in the block dtype                  */
+  const float* video_patch_b;       /* [D] or NULL                                          */
+  const void* audio_patch_w;        /* [D, audio_c] in the block dtype                     */
+  const float* audio_patch_b;       /* [D] or NULL                                          */
+  double shift_video, shift_audio;  /* flow shifts (12, 3)                                  */
+  double cond_aug, cond_aug_audio;  /* condition timesteps (0.999, 1)                       */
+} dit_mmh3_model;
+
+/* Workspace bytes of dit_mmh3_forward for these segments (0 if invalid). */
+size_t dit_mmh3_workspace_size(const dit_mmh3_model* m, const dit_segment* segs, int32_t nseg);
+
+/* segs: host, nseg entries covering [0, n) without gaps; one VIDEO, at most one
+ * AUDIO, one TEXT, any number of COND.  pos: device fp32 [n, 3].  text:
+ * device fp32 [text rows, D] (refined).  video: device fp32 [latent_c, T, H, W];
+ * audio: device fp32 [audio_c, 2, Ta] (NULL without an AUDIO segment).  cond:
+ * host array of device pointers, one fp32 [latent_c, 1, H, W] per COND segment
+ * in order.  Outputs (device fp32, same shapes as the inputs): the video and
+ * audio velocities.  The embedding GEMMs need a depth multiple of 64 (bf16) or
+ * 16 (fp32): latent_c % 16 == 0 and audio_c % 64 == 0 for bf16 blocks,
+ * latent_c % 4 == 0 and audio_c % 16 == 0 for fp32 blocks. */
+dit_status dit_mmh3_forward(const dit_mmh3_model* m, const dit_segment* segs, int32_t nseg,
+                            const float* pos, const float* text, const float* video, int32_t T,
+                            int32_t H, int32_t W, const float* audio, int32_t Ta,
+                            const float* const* cond, double sigma_v, float* video_out,
+                            float* audio_out, void* workspace, size_t ws_bytes, void* stream);
+
+/* RMSNorm of fp32 rows into fp32 rows: out_i = x_i / sqrt(mean(x_i^2) + eps) * g
+ * (e.g. the token refiner's final norm, [MMH3] refine_text).  D % 4 == 0,
+ * D <= 4096, 16-byte aligned pointers; out may alias x. */
+dit_status dit_rms_norm(const float* x, int32_t n, int32_t D, const float* g, float eps, float* out,
+                        void* stream);
+
 /* A stack of n_blocks blocks of one configuration, in order, each with its own
  * prepared weights (prepared[i], device): out = block_{L-1}(... block_0(x)),
  * all blocks with the same rows, positions, sigmas and packed-sample table

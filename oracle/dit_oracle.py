@@ -458,6 +458,92 @@ def stack(spec, x, rows, pos, sigmas, ws: Sequence[Dict[str, np.ndarray]], qrows
 
 
 # ---------------------------------------------------------------------------
+# Latent streams and one denoise evaluation ([MMH3] ``patchify_video``,
+# ``unpatchify_video``, ``pack_audio``, ``unpack_audio``, ``MiniMaxH3::forward``)
+# ---------------------------------------------------------------------------
+
+
+def patchify_video(x: np.ndarray) -> np.ndarray:
+    """[C, T, H, W] -> [T*(H/2)*(W/2), 4C]: row (t, h2, w2), column c*4 + p*2 + q
+    = x[c, t, 2*h2 + p, 2*w2 + q]."""
+    C, T, H, W = x.shape
+    out = np.empty((T * (H // 2) * (W // 2), 4 * C), dtype=x.dtype)
+    r = 0
+    for t in range(T):
+        for h2 in range(H // 2):
+            for w2 in range(W // 2):
+                out[r] = x[:, t, 2 * h2:2 * h2 + 2, 2 * w2:2 * w2 + 2].reshape(-1)
+                r += 1
+    return out
+
+
+def unpatchify_video(rows: np.ndarray, C: int, T: int, H: int, W: int) -> np.ndarray:
+    """Inverse of ``patchify_video``."""
+    x = np.empty((C, T, H, W), dtype=rows.dtype)
+    r = 0
+    for t in range(T):
+        for h2 in range(H // 2):
+            for w2 in range(W // 2):
+                x[:, t, 2 * h2:2 * h2 + 2, 2 * w2:2 * w2 + 2] = rows[r].reshape(C, 2, 2)
+                r += 1
+    return x
+
+
+def pack_audio(x: np.ndarray) -> np.ndarray:
+    """[C, 2, T] -> [2T, C]: row ch*T + t, column c = x[c, ch, t]."""
+    return np.ascontiguousarray(np.concatenate([x[:, 0, :].T, x[:, 1, :].T], axis=0))
+
+
+def unpack_audio(rows: np.ndarray, C: int, T: int) -> np.ndarray:
+    """Inverse of ``pack_audio``."""
+    x = np.empty((C, 2, T), dtype=rows.dtype)
+    x[:, 0, :] = rows[:T].T
+    x[:, 1, :] = rows[T:].T
+    return x
+
+
+def mmh3_forward(block_spec, head_v_spec, head_a_spec, segments, pos, text, video, audio, conds,
+                 sigma_v: float, w_blocks, w_head_v, w_head_a, w_vpatch, b_vpatch, w_apatch,
+                 b_apatch, shift_video=12.0, shift_audio=3.0, cond_aug=0.999,
+                 cond_aug_audio=1.0):
+    """One denoise evaluation: embed (video and condition frames through the
+    video patch projection, audio through the audio one, refined text as
+    given), the blocks with the evaluation's slots and token rows, the two
+    heads (negated) and the unpacking.  ``segments``: (kind, start, stop) with
+    kinds "text", "video", "audio", "cond".  Returns (video velocity [C, T, H,
+    W], audio velocity [Ca, 2, Ta] or None)."""
+    ts, slot = mmh3_slots(sigma_v, shift_video, shift_audio, cond_aug, cond_aug_audio,
+                          any(k == "cond" for k, _, _ in segments), False)
+    sig = [1.0 - t for t in ts] + [1.0 - ts[-1]] * (block_spec.slots - len(ts))
+    rows = mmh3_token_rows(segments, slot)
+    n, D = rows.shape[0], block_spec.D
+    C, T, H, W = video.shape
+    h = np.zeros((n, D))
+    ci = 0
+    for kind, a, b in segments:
+        if kind == "text":
+            h[a:b] = np.asarray(text, F64)
+        elif kind == "video":
+            h[a:b] = linear(patchify_video(np.asarray(video, F64)), w_vpatch, b_vpatch)
+        elif kind == "cond":
+            h[a:b] = linear(patchify_video(np.asarray(conds[ci], F64)), w_vpatch, b_vpatch)
+            ci += 1
+        elif kind == "audio":
+            h[a:b] = linear(pack_audio(np.asarray(audio, F64)), w_apatch, b_apatch)
+    for w in w_blocks:
+        h = mmh3_block(block_spec, h, rows, pos, sig, w)["out"]
+    out_v = out_a = None
+    for kind, a, b in segments:
+        if kind == "video":
+            r = final_layer(head_v_spec, h[a:b], np.full(b - a, slot["video"]), sig, w_head_v)["out"]
+            out_v = unpatchify_video(r, C, T, H, W)
+        elif kind == "audio":
+            r = final_layer(head_a_spec, h[a:b], np.full(b - a, slot["audio"]), sig, w_head_a)["out"]
+            out_a = unpack_audio(r, audio.shape[0], audio.shape[2])
+    return out_v, out_a
+
+
+# ---------------------------------------------------------------------------
 # SigLIP encoder layer ([SIGLIP] ``Layer::forward``, ``finish_attention``)
 # ---------------------------------------------------------------------------
 
@@ -576,6 +662,7 @@ __all__ = [
     "adaln_coords", "adaln_mods", "rms_norm", "layer_norm", "modulate", "silu",
     "gelu_tanh", "rope_angles", "rope_rotate", "attention", "sample_ranges",
     "attention_packed", "mmh3_block", "refiner_block", "linear", "final_layer", "stack",
+    "patchify_video", "unpatchify_video", "pack_audio", "unpack_audio", "mmh3_forward",
     "siglip_layer", "timestep_embedding", "zimage_mods", "zimage_block", "block",
     "rel_rms",
 ]

@@ -855,6 +855,45 @@ dit_status dit_linear(int32_t dtype, const void* a, int32_t lda, int32_t m, int3
   return DIT_OK;
 }
 
+dit_status dit_patchify_video(int32_t dtype, const float* x, int32_t C, int32_t T, int32_t H,
+                              int32_t W, void* rows, void* stream) {
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return fail(DIT_EDTYPE, "unknown dtype %d", dtype);
+  if (C < 0 || T < 0 || H < 0 || W < 0 || H % 2 || W % 2)
+    return fail(DIT_ESHAPE, "video [%d, %d, %d, %d]: sizes >= 0, H and W even", C, T, H, W);
+  if ((size_t)C * T * H * W == 0) return DIT_OK;
+  if (!x || !rows) return fail(DIT_EINVAL, "x/rows is NULL");
+  HIP_TRY(dit::patchify_video(dtype, x, C, T, H, W, rows, (hipStream_t)stream), "patchify");
+  return DIT_OK;
+}
+
+dit_status dit_unpatchify_video(const float* rows, int32_t C, int32_t T, int32_t H, int32_t W,
+                                float* x, void* stream) {
+  if (C < 0 || T < 0 || H < 0 || W < 0 || H % 2 || W % 2)
+    return fail(DIT_ESHAPE, "video [%d, %d, %d, %d]: sizes >= 0, H and W even", C, T, H, W);
+  if ((size_t)C * T * H * W == 0) return DIT_OK;
+  if (!x || !rows) return fail(DIT_EINVAL, "x/rows is NULL");
+  HIP_TRY(dit::unpatchify_video(rows, C, T, H, W, x, (hipStream_t)stream), "unpatchify");
+  return DIT_OK;
+}
+
+dit_status dit_pack_audio(int32_t dtype, const float* x, int32_t C, int32_t T, void* rows,
+                          void* stream) {
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return fail(DIT_EDTYPE, "unknown dtype %d", dtype);
+  if (C < 0 || T < 0) return fail(DIT_ESHAPE, "audio [%d, 2, %d]", C, T);
+  if ((size_t)C * T == 0) return DIT_OK;
+  if (!x || !rows) return fail(DIT_EINVAL, "x/rows is NULL");
+  HIP_TRY(dit::pack_audio(dtype, x, C, T, rows, (hipStream_t)stream), "pack_audio");
+  return DIT_OK;
+}
+
+dit_status dit_unpack_audio(const float* rows, int32_t C, int32_t T, float* x, void* stream) {
+  if (C < 0 || T < 0) return fail(DIT_ESHAPE, "audio [%d, 2, %d]", C, T);
+  if ((size_t)C * T == 0) return DIT_OK;
+  if (!x || !rows) return fail(DIT_EINVAL, "x/rows is NULL");
+  HIP_TRY(dit::unpack_audio(rows, C, T, x, (hipStream_t)stream), "unpack_audio");
+  return DIT_OK;
+}
+
 dit_status dit_stack_forward(const dit_config* c, const void* const* prepared, int32_t n_blocks,
                              const float* x, int32_t n, const int32_t* rows, const float* pos,
                              const double* sigmas, int32_t n_sigmas, const int32_t* seq_starts,
@@ -877,6 +916,185 @@ dit_status dit_block_forward_mods(const dit_config* c, const void* prepared, con
   if (!mods) return fail(DIT_EINVAL, "mods is NULL");
   return block_forward_impl(c, prepared, x, n, rows, pos, nullptr, 0, mods, seq_starts, nseq, out,
                             workspace, ws_bytes, stream);
+}
+
+dit_status dit_rms_norm(const float* x, int32_t n, int32_t D, const float* g, float eps, float* out,
+                        void* stream) {
+  if (n < 0 || D <= 0 || D % 4 || D > 4096) return fail(DIT_ESHAPE, "n=%d D=%d (D %% 4 == 0, <= 4096)", n, D);
+  if (!(eps >= 0.0f)) return fail(DIT_EINVAL, "eps must be >= 0");
+  if (n == 0) return DIT_OK;
+  if (!x || !g || !out) return fail(DIT_EINVAL, "x/g/out is NULL");
+  if (!aligned16(x) || !aligned16(g) || !aligned16(out)) return fail(DIT_EALIGN, "x/g/out not 16-byte aligned");
+  HIP_TRY(dit::norm_mod(dit::NORM_RMS, dit::MOD_NONE, false, x, n, D, g, nullptr, eps, nullptr, 0,
+                        nullptr, 0, 0, out, (hipStream_t)stream),
+          "rms_norm");
+  return DIT_OK;
+}
+
+// ------------------------------------------------------------ MMH3 model ----
+namespace {
+struct ModelPlan {
+  int n = 0, nv = 0, na = 0, text = -1, video = -1, audio = -1, ncond = 0;
+  // workspace offsets
+  size_t h = 0, rows = 0, hrows = 0, prow = 0, hout = 0, bws = 0, hws = 0, total = 0;
+};
+
+dit_status plan_model(const dit_mmh3_model* m, const dit_segment* segs, int32_t nseg, ModelPlan* P) {
+  if (!m || !segs || nseg < 1) return fail(DIT_EINVAL, "model/segments missing");
+  if (!m->block || !m->head_video || !m->blocks || m->n_blocks < 1)
+    return fail(DIT_EINVAL, "model needs a block config, blocks and a video head");
+  DIT_TRY(check_config(m->block));
+  if (m->block->variant != DIT_MMH3) return fail(DIT_EINVAL, "model blocks must be DIT_MMH3");
+  DIT_TRY(check_config(m->head_video));
+  if (m->head_video->variant != DIT_FINAL || m->head_video->F != 4 * m->latent_c ||
+      m->head_video->D != m->block->D || m->head_video->slots != m->block->slots)
+    return fail(DIT_EINVAL, "video head: DIT_FINAL, F = 4 * latent_c, the blocks' D and slots");
+  const bool bf = m->block->dtype == DIT_BF16;
+  if (m->latent_c <= 0 || (4 * m->latent_c) % (bf ? 64 : 16))
+    return fail(DIT_EUNSUPPORTED, "latent_c=%d: 4 * latent_c must be a multiple of %d", m->latent_c, bf ? 64 : 16);
+  int pos = 0;
+  for (int i = 0; i < nseg; ++i) {
+    const dit_segment& g = segs[i];
+    if (g.start != pos || g.stop < g.start) return fail(DIT_ESHAPE, "segment %d [%d, %d) must start at %d", i, g.start, g.stop, pos);
+    pos = g.stop;
+    switch (g.kind) {
+      case DIT_SEG_TEXT: if (P->text >= 0) return fail(DIT_EINVAL, "two TEXT segments"); P->text = i; break;
+      case DIT_SEG_VIDEO: if (P->video >= 0) return fail(DIT_EINVAL, "two VIDEO segments"); P->video = i; break;
+      case DIT_SEG_AUDIO: if (P->audio >= 0) return fail(DIT_EINVAL, "two AUDIO segments"); P->audio = i; break;
+      case DIT_SEG_COND: P->ncond++; break;
+      default: return fail(DIT_EINVAL, "segment %d: unknown kind %d", i, g.kind);
+    }
+  }
+  if (P->video < 0) return fail(DIT_EINVAL, "no VIDEO segment");
+  P->n = pos;
+  P->nv = segs[P->video].stop - segs[P->video].start;
+  P->na = P->audio >= 0 ? segs[P->audio].stop - segs[P->audio].start : 0;
+  if (P->audio >= 0) {
+    if (!m->head_audio || !m->audio_patch_w) return fail(DIT_EINVAL, "an AUDIO segment needs the audio head and patch");
+    DIT_TRY(check_config(m->head_audio));
+    if (m->head_audio->variant != DIT_FINAL || m->head_audio->F != m->audio_c ||
+        m->head_audio->D != m->block->D || m->head_audio->slots != m->block->slots)
+      return fail(DIT_EINVAL, "audio head: DIT_FINAL, F = audio_c, the blocks' D and slots");
+    if (m->audio_c <= 0 || m->audio_c % (bf ? 64 : 16))
+      return fail(DIT_EUNSUPPORTED, "audio_c=%d must be a multiple of %d", m->audio_c, bf ? 64 : 16);
+  }
+  const size_t D = m->block->D, es = bf ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  int max_cond_rows = 0;
+  for (int i = 0; i < nseg; ++i)
+    if (segs[i].kind == DIT_SEG_COND) max_cond_rows = std::max(max_cond_rows, segs[i].stop - segs[i].start);
+  const size_t prow_elems = std::max({(size_t)P->nv * 4 * m->latent_c, (size_t)max_cond_rows * 4 * m->latent_c,
+                                      (size_t)P->na * std::max(m->audio_c, 1)});
+  const size_t hout_elems = std::max((size_t)P->nv * 4 * m->latent_c, (size_t)P->na * std::max(m->audio_c, 1));
+  P->h = take((size_t)P->n * D * 4);
+  P->rows = take((size_t)P->n * 4);
+  P->hrows = take((size_t)std::max(P->nv, P->na) * 4);
+  P->prow = take(prow_elems * es);
+  P->hout = take(hout_elems * 4);
+  P->bws = take(ws_layout(m->block, P->n).total);
+  size_t hws = ws_layout(m->head_video, P->nv).total;
+  if (P->audio >= 0) hws = std::max(hws, ws_layout(m->head_audio, P->na).total);
+  P->hws = take(hws);
+  P->total = off;
+  return DIT_OK;
+}
+}  // namespace
+
+size_t dit_mmh3_workspace_size(const dit_mmh3_model* m, const dit_segment* segs, int32_t nseg) {
+  ModelPlan P;
+  return plan_model(m, segs, nseg, &P) == DIT_OK ? P.total : 0;
+}
+
+dit_status dit_mmh3_forward(const dit_mmh3_model* m, const dit_segment* segs, int32_t nseg,
+                            const float* pos, const float* text, const float* video, int32_t T,
+                            int32_t H, int32_t W, const float* audio, int32_t Ta,
+                            const float* const* cond, double sigma_v, float* video_out,
+                            float* audio_out, void* workspace, size_t ws_bytes, void* stream) {
+  ModelPlan P;
+  DIT_TRY(plan_model(m, segs, nseg, &P));
+  const dit_config* bc = m->block;
+  const int D = bc->D, C = m->latent_c;
+  if (T <= 0 || H <= 0 || W <= 0 || H % 2 || W % 2 || P.nv != T * (H / 2) * (W / 2))
+    return fail(DIT_ESHAPE, "video [%d, %d, %d, %d] does not give the VIDEO segment's %d rows", C, T, H, W, P.nv);
+  if (P.audio >= 0 && P.na != 2 * Ta) return fail(DIT_ESHAPE, "audio length %d does not give %d rows", Ta, P.na);
+  for (int i = 0; i < nseg; ++i)
+    if (segs[i].kind == DIT_SEG_COND && segs[i].stop - segs[i].start != (H / 2) * (W / 2))
+      return fail(DIT_ESHAPE, "COND segment %d must hold one frame of %d rows", i, (H / 2) * (W / 2));
+  if (!pos || !video || !video_out || (P.audio >= 0 && (!audio || !audio_out)) ||
+      (P.text >= 0 && segs[P.text].stop > segs[P.text].start && !text) || (P.ncond && !cond))
+    return fail(DIT_EINVAL, "an input or output pointer is NULL");
+  if (!isfinite(sigma_v)) return fail(DIT_EINVAL, "sigma_v not finite");
+  for (int k = 0; k < P.ncond; ++k)
+    if (!cond[k]) return fail(DIT_EINVAL, "condition frame %d is NULL", k);
+  if (!workspace || (uintptr_t)workspace % kAlign) return fail(DIT_EALIGN, "workspace NULL or not 256-byte aligned");
+  if (ws_bytes < P.total) return fail(DIT_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, P.total);
+  hipStream_t s = (hipStream_t)stream;
+
+  // timestep slots and per-token rows ([MMH3] MiniMaxH3::forward)
+  double ssig[4];
+  int32_t slot[4];
+  const int nt = dit_mmh3_slots(sigma_v, m->shift_video, m->shift_audio, m->cond_aug, m->cond_aug_audio,
+                                P.ncond > 0, 0, ssig, slot);
+  if (nt < 0) return (dit_status)nt;
+  if (nt > bc->slots) return fail(DIT_EUNSUPPORTED, "the evaluation needs %d slots, the blocks have %d", nt, bc->slots);
+  std::vector<double> sig(bc->slots, ssig[nt - 1]);  // slots beyond the plan: unused rows
+  for (int i = 0; i < nt; ++i) sig[i] = ssig[i];
+  float* h = at<float>(workspace, P.h);
+  int* rows = at<int>(workspace, P.rows);
+  int* hrows = at<int>(workspace, P.hrows);
+  void* prow = at<char>(workspace, P.prow);
+  float* hout = at<float>(workspace, P.hout);
+  const int dt = bc->dtype;
+  int ci = 0;
+  for (int i = 0; i < nseg; ++i) {
+    const dit_segment& g = segs[i];
+    const int len = g.stop - g.start;
+    if (len == 0) continue;
+    int row = 0;
+    switch (g.kind) {  // slot * 3 + tag (video 0, text 1, audio 2)
+      case DIT_SEG_TEXT: row = slot[0] * 3 + 1; break;
+      case DIT_SEG_VIDEO: row = slot[0] * 3 + 0; break;
+      case DIT_SEG_AUDIO: row = slot[1] * 3 + 2; break;
+      default: row = slot[2] * 3 + 0; break;
+    }
+    HIP_TRY(dit::fill_i32(rows + g.start, len, row, s), "token rows");
+    float* hs = h + (size_t)g.start * D;
+    if (g.kind == DIT_SEG_TEXT) {
+      HIP_TRY(hipMemcpyAsync(hs, text, (size_t)len * D * 4, hipMemcpyDeviceToDevice, s), "text rows");
+    } else if (g.kind == DIT_SEG_VIDEO || g.kind == DIT_SEG_COND) {
+      const float* src = g.kind == DIT_SEG_VIDEO ? video : cond[ci++];
+      HIP_TRY(dit::patchify_video(dt, src, C, g.kind == DIT_SEG_VIDEO ? T : 1, H, W, prow, s), "patchify");
+      DIT_TRY(dit_linear(dt, prow, 4 * C, len, 4 * C, m->video_patch_w, D, m->video_patch_b, 1.0f, hs, s));
+    } else {
+      HIP_TRY(dit::pack_audio(dt, audio, m->audio_c, Ta, prow, s), "pack_audio");
+      DIT_TRY(dit_linear(dt, prow, m->audio_c, len, m->audio_c, m->audio_patch_w, D, m->audio_patch_b, 1.0f, hs, s));
+    }
+  }
+  // blocks, in place on h
+  DIT_TRY(dit_stack_forward(bc, m->blocks, m->n_blocks, h, P.n, rows, pos, sig.data(), bc->slots, nullptr, 0, h,
+                            at<char>(workspace, P.bws), ws_layout(bc, P.n).total, s));
+  // heads: the row of a head is the stream's timestep slot
+  const size_t hws = P.total - P.hws;
+  {
+    const dit_segment& g = segs[P.video];
+    HIP_TRY(dit::fill_i32(hrows, P.nv, slot[0], s), "head rows");
+    DIT_TRY(dit_final_forward(m->head_video, m->head_video_w, h + (size_t)g.start * D, P.nv, hrows, sig.data(),
+                              bc->slots, hout, at<char>(workspace, P.hws), hws, s));
+    HIP_TRY(dit::unpatchify_video(hout, C, T, H, W, video_out, s), "unpatchify");
+  }
+  if (P.audio >= 0 && P.na > 0) {
+    const dit_segment& g = segs[P.audio];
+    HIP_TRY(dit::fill_i32(hrows, P.na, slot[1], s), "head rows");
+    DIT_TRY(dit_final_forward(m->head_audio, m->head_audio_w, h + (size_t)g.start * D, P.na, hrows, sig.data(),
+                              bc->slots, hout, at<char>(workspace, P.hws), hws, s));
+    HIP_TRY(dit::unpack_audio(hout, m->audio_c, Ta, audio_out, s), "unpack_audio");
+  }
+  return DIT_OK;
 }
 
 }  // extern "C"

@@ -103,6 +103,15 @@ hipError_t attention(int dtype, int hd, const void* q, const void* k, const void
                      int ldn, int H, float scale_log2, void* o, float* part, const SeqTable& seqs,
                      hipStream_t s);
 
+// ---- latent streams <-> token rows (k_streams.hip) --------------------------------------
+hipError_t patchify_video(int dtype, const float* x, int C, int T, int H, int W, void* rows,
+                          hipStream_t s);
+hipError_t unpatchify_video(const float* rows, int C, int T, int H, int W, float* x, hipStream_t s);
+hipError_t pack_audio(int dtype, const float* x, int C, int T, void* rows, hipStream_t s);
+hipError_t unpack_audio(const float* rows, int C, int T, float* x, hipStream_t s);
+// p[0, n) = v (a kernel rather than a memset: safe inside captured graphs)
+hipError_t fill_i32(int* p, int n, int v, hipStream_t s);
+
 // ---- weight preparation ---------------------------------------------------------------
 // dst[r, :] = src[perm(r), :] * (r < scale_rows ? scale : 1); perm = SwiGLU group interleave
 // when swiglu_F > 0.

@@ -55,6 +55,23 @@ class DitWsLayout(ctypes.Structure):
 
 NONE_OFFSET = (1 << (8 * ctypes.sizeof(c_size_t))) - 1
 
+SEG_KINDS = {"text": 0, "video": 1, "audio": 2, "cond": 3}
+
+
+class DitSegment(ctypes.Structure):
+    _fields_ = [("kind", c_int32), ("start", c_int32), ("stop", c_int32)]
+
+
+class DitMmh3Model(ctypes.Structure):
+    _fields_ = [("block", POINTER(DitConfig)), ("blocks", POINTER(c_void_p)), ("n_blocks", c_int32),
+                ("head_video", POINTER(DitConfig)), ("head_video_w", c_void_p),
+                ("head_audio", POINTER(DitConfig)), ("head_audio_w", c_void_p),
+                ("latent_c", c_int32), ("audio_c", c_int32),
+                ("video_patch_w", c_void_p), ("video_patch_b", c_void_p),
+                ("audio_patch_w", c_void_p), ("audio_patch_b", c_void_p),
+                ("shift_video", c_double), ("shift_audio", c_double),
+                ("cond_aug", c_double), ("cond_aug_audio", c_double)]
+
 
 class DitError(RuntimeError):
     def __init__(self, status: int, msg: str):
@@ -103,6 +120,19 @@ def _load() -> ctypes.CDLL:
         "dit_stack_forward": (c_int32, [P(DitConfig), P(c_void_p), c_int32, c_void_p, c_int32,
                                         c_void_p, c_void_p, P(c_double), c_int32, P(c_int32),
                                         c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "dit_patchify_video": (c_int32, [c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                         c_void_p, c_void_p]),
+        "dit_unpatchify_video": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                           c_void_p]),
+        "dit_pack_audio": (c_int32, [c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+        "dit_unpack_audio": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+        "dit_rms_norm": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_float, c_void_p,
+                                   c_void_p]),
+        "dit_mmh3_workspace_size": (c_size_t, [P(DitMmh3Model), P(DitSegment), c_int32]),
+        "dit_mmh3_forward": (c_int32, [P(DitMmh3Model), P(DitSegment), c_int32, c_void_p,
+                                       c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                       c_int32, P(c_void_p), c_double, c_void_p, c_void_p,
+                                       c_void_p, c_size_t, c_void_p]),
         "dit_attention": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                     c_float, c_void_p, c_void_p]),
         "dit_attention_packed": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_void_p, c_int32,
@@ -184,8 +214,15 @@ def make_config(spec) -> DitConfig:
     return c
 
 
-def _ptr(t) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+def _ptr(t, strided: bool = False) -> Optional[int]:
+    """Device address of a tensor the library reads as dense row-major memory
+    (a row-strided matrix with ``strided``: unit stride inside rows)."""
+    if t is None:
+        return None
+    if not (t.is_contiguous() or (strided and t.dim() == 2 and t.stride(1) == 1)):
+        raise ValueError(f"tensor of shape {tuple(t.shape)} and strides {t.stride()} is not "
+                         "row-major contiguous")
+    return t.data_ptr()
 
 
 def _stream(stream=None) -> int:
@@ -351,7 +388,7 @@ def linear(a, w, bias=None, alpha: float = 1.0, out=None, stream=None):
     dtype = BF16 if a.dtype == torch.bfloat16 else F32
     if out is None:
         out = torch.empty((m, nout), dtype=torch.float32, device=a.device)
-    _check(lib.dit_linear(dtype, _ptr(a), int(a.stride(0)), m, k, _ptr(w), nout, _ptr(bias),
+    _check(lib.dit_linear(dtype, _ptr(a, strided=True), int(a.stride(0)), m, k, _ptr(w), nout, _ptr(bias),
                           alpha, _ptr(out), _stream(stream)))
     return out
 
@@ -371,3 +408,100 @@ def stack_forward(blocks: Sequence["Block"], x, rows, pos, sigmas: Sequence[floa
                                  _ptr(rows), _ptr(pos), sg, ns, st, nseq, _ptr(out),
                                  ws.data_ptr(), ws.numel(), _stream(stream)))
     return out
+
+
+def patchify_video(x, dtype_out=None, stream=None):
+    """[C, T, H, W] fp32 -> rows [T*(H/2)*(W/2), 4C] (bfloat16 or float32)."""
+    import torch
+    C, T, H, W = (int(v) for v in x.shape)
+    td = torch.bfloat16 if dtype_out == "bf16" else torch.float32
+    rows = torch.empty((T * (H // 2) * (W // 2), 4 * C), dtype=td, device=x.device)
+    _check(lib.dit_patchify_video(BF16 if td == torch.bfloat16 else F32, _ptr(x), C, T, H, W,
+                                  _ptr(rows), _stream(stream)))
+    return rows
+
+
+def unpatchify_video(rows, C: int, T: int, H: int, W: int, stream=None):
+    import torch
+    x = torch.empty((C, T, H, W), dtype=torch.float32, device=rows.device)
+    _check(lib.dit_unpatchify_video(_ptr(rows), C, T, H, W, _ptr(x), _stream(stream)))
+    return x
+
+
+def pack_audio(x, dtype_out=None, stream=None):
+    """[C, 2, T] fp32 -> rows [2T, C]."""
+    import torch
+    C, _, T = (int(v) for v in x.shape)
+    td = torch.bfloat16 if dtype_out == "bf16" else torch.float32
+    rows = torch.empty((2 * T, C), dtype=td, device=x.device)
+    _check(lib.dit_pack_audio(BF16 if td == torch.bfloat16 else F32, _ptr(x), C, T, _ptr(rows),
+                              _stream(stream)))
+    return rows
+
+
+def unpack_audio(rows, C: int, T: int, stream=None):
+    import torch
+    x = torch.empty((C, 2, T), dtype=torch.float32, device=rows.device)
+    _check(lib.dit_unpack_audio(_ptr(rows), C, T, _ptr(x), _stream(stream)))
+    return x
+
+
+def rms_norm(x, g, eps: float, out=None, stream=None):
+    import torch
+    n, D = (int(v) for v in x.shape)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib.dit_rms_norm(_ptr(x), n, D, _ptr(g), eps, _ptr(out), _stream(stream)))
+    return out
+
+
+class Mmh3Model:
+    """The MMH3 denoise evaluation over prepared pieces: blocks (Block with a
+    DIT_MMH3 config), video/audio heads (Block with DIT_FINAL configs) and the
+    patch projections (device tensors [D, 4C] / [D, Ca] in the blocks' dtype)."""
+
+    def __init__(self, blocks: Sequence["Block"], head_video: "Block", head_audio: Optional["Block"],
+                 latent_c: int, audio_c: int, video_patch_w, video_patch_b=None,
+                 audio_patch_w=None, audio_patch_b=None, shift_video: float = 12.0,
+                 shift_audio: float = 3.0, cond_aug: float = 0.999, cond_aug_audio: float = 1.0):
+        self.blocks, self.head_video, self.head_audio = list(blocks), head_video, head_audio
+        self._preps = (c_void_p * len(self.blocks))(*[b.prepared.data_ptr() for b in self.blocks])
+        self._keep = (video_patch_w, video_patch_b, audio_patch_w, audio_patch_b)
+        m = DitMmh3Model()
+        m.block = ctypes.pointer(self.blocks[0].cfg)
+        m.blocks = self._preps
+        m.n_blocks = len(self.blocks)
+        m.head_video = ctypes.pointer(head_video.cfg)
+        m.head_video_w = head_video.prepared.data_ptr()
+        if head_audio is not None:
+            m.head_audio = ctypes.pointer(head_audio.cfg)
+            m.head_audio_w = head_audio.prepared.data_ptr()
+        m.latent_c, m.audio_c = latent_c, audio_c
+        m.video_patch_w, m.video_patch_b = _ptr(video_patch_w), _ptr(video_patch_b)
+        m.audio_patch_w, m.audio_patch_b = _ptr(audio_patch_w), _ptr(audio_patch_b)
+        m.shift_video, m.shift_audio = shift_video, shift_audio
+        m.cond_aug, m.cond_aug_audio = cond_aug, cond_aug_audio
+        self._m = m
+        self._ws = None
+
+    def forward(self, segments, pos, text, video, audio=None, conds=(), sigma_v: float = 0.5,
+                stream=None):
+        """segments: [(kind, start, stop)] with kinds text / video / audio / cond.
+        Returns (video velocity [C, T, H, W], audio velocity [Ca, 2, Ta] or None)."""
+        import torch
+        segs = (DitSegment * len(segments))(*[DitSegment(SEG_KINDS[k], a, b) for k, a, b in segments])
+        need = lib.dit_mmh3_workspace_size(ctypes.byref(self._m), segs, len(segments))
+        if need == 0:
+            raise DitError(-1, lib.dit_last_error().decode())
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        C, T, H, W = (int(v) for v in video.shape)
+        vout = torch.empty_like(video)
+        aout = None if audio is None else torch.empty_like(audio)
+        Ta = 0 if audio is None else int(audio.shape[2])
+        cp = (c_void_p * max(len(conds), 1))(*[c.data_ptr() for c in conds])
+        _check(lib.dit_mmh3_forward(ctypes.byref(self._m), segs, len(segments), _ptr(pos), _ptr(text),
+                                    _ptr(video), T, H, W, _ptr(audio), Ta, cp, sigma_v,
+                                    _ptr(vout), _ptr(aout), self._ws.data_ptr(), self._ws.numel(),
+                                    _stream(stream)))
+        return vout, aout

@@ -97,3 +97,89 @@ def test_stack_of_blocks(dit, dtype, starts):
     rms = lambda a: float(np.sqrt(np.mean(a * a)))  # noqa: E731
     floor = 2 * 2.0 ** -24 * (rms(ref) + rms(x64)) / rms(ref - x64)
     assert e_out <= tol and e_delta <= tol + floor
+
+
+def test_stream_packing_kernels(dit):
+    """patchify / unpatchify / pack / unpack against the oracle's layouts,
+    bit for bit (bf16 rows are the RNE rounding of the same values)."""
+    import torch
+    rng = np.random.default_rng(71)
+    v = rng.standard_normal((16, 3, 8, 12)).astype(np.float32)
+    a = rng.standard_normal((64, 2, 10)).astype(np.float32)
+    vd, ad = torch.from_numpy(v).cuda(), torch.from_numpy(a).cuda()
+    rv, ra = O.patchify_video(v), O.pack_audio(a)
+    for dt in ("f32", "bf16"):
+        want_v = rv if dt == "f32" else W.bf16_round(rv)
+        want_a = ra if dt == "f32" else W.bf16_round(ra)
+        got_v = dit.patchify_video(vd, dt).float().cpu().numpy()
+        got_a = dit.pack_audio(ad, dt).float().cpu().numpy()
+        assert np.array_equal(got_v, want_v) and np.array_equal(got_a, want_a)
+    back_v = dit.unpatchify_video(torch.from_numpy(rv).cuda(), 16, 3, 8, 12).cpu().numpy()
+    back_a = dit.unpack_audio(torch.from_numpy(ra).cuda(), 64, 10).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.array_equal(back_v, v) and np.array_equal(back_a, a)
+
+
+def test_rms_norm(dit):
+    import torch
+    rng = np.random.default_rng(72)
+    x = rng.standard_normal((77, 384)).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(384)).astype(np.float32)
+    got = dit.rms_norm(torch.from_numpy(x).cuda(), torch.from_numpy(g).cuda(), 1e-5).cpu().numpy()
+    ref = O.rms_norm(x.astype(np.float64), g.astype(np.float64), 1e-5)
+    assert O.rel_rms(got, ref) <= 1e-6
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mmh3_denoise_evaluation(dit, dtype):
+    """One whole evaluation at a small size: text, a first-frame keyframe,
+    stereo audio and two video frames; two blocks with their own weights;
+    video and audio heads.  Against the oracle's evaluation from the same
+    seeded pieces."""
+    import torch
+    from synth.device import to_device
+    hd = 128 if dtype == "bf16" else 64
+    lay = W.build_layout(16, 2, 8, 8, 12, keyframes=[(0, 2)])
+    n = lay.seq_len
+    C, Ca, D = 16, 64, 256
+    bspec = W.BlockSpec(f"model-{dtype}", "mmh3", dtype, n=n, D=D, H=D // hd, hd=hd,
+                        F=384 if dtype == "bf16" else 256, slots=3, rope="split_half",
+                        rope_axes=(hd // 4, hd // 8 * 3, hd // 8 * 3))
+    hv = W.BlockSpec("head-v", "final", dtype, n=n, D=D, H=D // hd, hd=hd, F=4 * C, slots=3, tags=1)
+    ha = W.BlockSpec("head-a", "final", dtype, n=n, D=D, H=D // hd, hd=hd, F=Ca, slots=3, tags=1)
+    wblocks = [W.make_custom_workload(bspec, 8000 + i).weights for i in range(2)]
+    whv = W.make_custom_workload(hv, 8100).weights
+    wha = W.make_custom_workload(ha, 8101).weights
+    rng = np.random.default_rng(81)
+
+    def lin(shape):
+        w = (0.02 * rng.standard_normal(shape)).astype(np.float32)
+        return W.bf16_round(w) if dtype == "bf16" else w
+    wv, bv = lin((D, 4 * C)), (0.02 * rng.standard_normal(D)).astype(np.float32)
+    wa, ba = lin((D, Ca)), (0.02 * rng.standard_normal(D)).astype(np.float32)
+    text = rng.standard_normal((16, D)).astype(np.float32)
+    video = rng.standard_normal((C, 2, 8, 8)).astype(np.float32)
+    audio = rng.standard_normal((Ca, 2, 12)).astype(np.float32)
+    cond = rng.standard_normal((C, 1, 8, 8)).astype(np.float32)
+    pos = lay.pos.astype(np.float32)
+    sigma_v = 0.42
+
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def dev_weights(spec, w):
+        wl = W.Workload(spec, np.zeros((1, D), np.float32), None, None, [], w, 0)
+        return to_device(wl).weights
+    blocks = [dit.Block(dit.make_config(bspec), dev_weights(bspec, w)) for w in wblocks]
+    head_v = dit.Block(dit.make_config(hv), dev_weights(hv, whv))
+    head_a = dit.Block(dit.make_config(ha), dev_weights(ha, wha))
+    cu = lambda a, t=torch.float32: torch.from_numpy(a).to(t).cuda()  # noqa: E731
+    model = dit.Mmh3Model(blocks, head_v, head_a, C, Ca, cu(wv, td), cu(bv), cu(wa, td), cu(ba))
+    vout, aout = model.forward(lay.segments, cu(pos), cu(text), cu(video), cu(audio), [cu(cond)],
+                               sigma_v)
+    torch.cuda.synchronize()
+    rv, ra = O.mmh3_forward(bspec, hv, ha, lay.segments, pos.astype(np.float64), text, video,
+                            audio, [cond], sigma_v, wblocks, whv, wha, wv, bv, wa, ba)
+    ev = O.rel_rms(vout.cpu().numpy(), rv)
+    ea = O.rel_rms(aout.cpu().numpy(), ra)
+    log(f"[case] mmh3 evaluation {dtype} n={n}: video={ev:.2e} audio={ea:.2e}")
+    assert ev <= TOL[dtype] and ea <= TOL[dtype]

@@ -438,6 +438,29 @@ def test_stack_is_sequential_blocks():
     np.testing.assert_array_equal(O.stack(spec, x, rows, pos, sig, [w, w2]), a)
 
 
+def test_patchify_is_the_einsum_layout_and_inverts():
+    """The page's patch layout is einsum("nctrhpwq->nthwcrpq") of [C, T, H/2,
+    2, W/2, 2]: rows (t, h, w), columns (c, r, p, q) -> (c, p, q)."""
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((3, 2, 6, 4))
+    C, T, H, W = x.shape
+    want = np.einsum("ctrhpw->trpchw", x.reshape(C, T, H // 2, 2, W // 2, 2)).reshape(-1, 4 * C)
+    rows = O.patchify_video(x)
+    np.testing.assert_array_equal(rows, want)
+    np.testing.assert_array_equal(O.unpatchify_video(rows, C, T, H, W), x)
+
+
+def test_pack_audio_layout_and_inverse():
+    rng = np.random.default_rng(62)
+    x = rng.standard_normal((5, 2, 7))
+    rows = O.pack_audio(x)
+    assert rows.shape == (14, 5)
+    for ch in range(2):
+        for t in range(7):
+            np.testing.assert_array_equal(rows[ch * 7 + t], x[:, ch, t])
+    np.testing.assert_array_equal(O.unpack_audio(rows, 5, 7), x)
+
+
 def test_packed_block_equals_samples_run_alone():
     """[ENC]: a ragged batch behaves exactly like its sequences run solo."""
     spec, x, rows, pos, sig, w = _tiny_mmh3_inputs(16, n=12)

@@ -75,7 +75,13 @@ enum { DIT_F32 = 0, DIT_BF16 = 1 };
 enum {
   DIT_ROPE_NONE = 0,
   DIT_ROPE_SPLIT_HALF = 1,  /* pair (j, j + hd/2) ([MMH3] norm_rope_w)  */
-  DIT_ROPE_INTERLEAVED = 2  /* pair (2j, 2j + 1) ([ZIMG] applyRoPE3D)  */
+  DIT_ROPE_INTERLEAVED = 2, /* pair (2j, 2j + 1) ([ZIMG] applyRoPE3D)  */
+  DIT_ROPE_PARTIAL = 3      /* the checkpoint form of [MMH3] rope_angles / norm_rope_w: k =
+                               rope_axes[0]/2 frequencies (weights.rope_freq) shared by the
+                               three axes (rope_axes all equal, 3 * rope_axes[0] <= hd), P = 3k
+                               angles per token, angle j = pos[j / k] * rope_freq[j % k], pair
+                               (j, j + P) for j < P, head dims [2P, hd) not rotated; rope_theta
+                               unused.  DIT_MMH3 and DIT_REFINER only. */
 };
 
 typedef struct dit_config {
@@ -95,6 +101,10 @@ typedef struct dit_config {
   int32_t temb_freq;     /* ZIMAGE: sinusoid width (256)                                */
   int32_t temb_hidden;   /* ZIMAGE: timestep MLP hidden width (1024)                    */
   float t_scale;         /* ZIMAGE: timestep multiplier before the sinusoid (1000)      */
+  int32_t adaln_shared;  /* MMH3 / FINAL: 0 = slot-major basis (one block of rows per slot);
+                            1 = one slot's rows [T*E*D, r] (and bias [T*E*D]) evaluated at
+                            every slot's timestep, as [MMH3] Adaln::eval applies one W at
+                            each distinct timestep                                      */
 } dit_config;
 
 /* Raw weights, device pointers.  GEMM weights (w_*) are [out, in] row-major in
@@ -114,6 +124,9 @@ typedef struct dit_config {
  *           temb_w2 [Tf, Th] + temb_b2; ada_w [4D, Tf] + ada_b [4D]
  *           (chunks scale_msa, gate_msa, scale_mlp, gate_mlp).
  *   REFINER: as MMH3 without the adaLN tensors.
+ *   rope_freq [rope_axes[0] / 2]: the shared frequency vector of DIT_ROPE_PARTIAL
+ *           (MMH3, REFINER), NULL otherwise.
+ *   adaln_shared = 1: adaln_basis [T*E*D, r] and adaln_bias [T*E*D] (one slot).
  *   FINAL:  norm1 [D] final RMSNorm gain; w_fc1 [F, D] head weight + b_fc1 [F]
  *           (NULL = 0); adaln_basis [S*2*D, r] (chunk 0 shift, 1 scale per
  *           slot), adaln_bias [S*2*D] (NULL = 0), adaln_table [G, r]. */
@@ -124,24 +137,31 @@ typedef struct dit_weights {
   const float *q_norm, *k_norm;
   const float *adaln_basis, *adaln_bias, *adaln_table;
   const float *temb_w1, *temb_b1, *temb_w2, *temb_b2, *ada_w, *ada_b;
+  const float *rope_freq;
 } dit_weights;
 
 /* Byte offsets of the intermediates inside the workspace of dit_block_forward
  * (for inspection after the call; `none` = SIZE_MAX when a variant has no such
  * buffer).  ldn = n rounded up to 128.  act = the config's dtype.
  *   mods  fp32 [R, E*D]   R = S*T (MMH3) or 1 (ZIMAGE), E = 6 or 4 (none: SIGLIP, REFINER)
- *   rope  fp32 [n, hd/2, 2] (cos, sin) per token and pair
+ *   rope  fp32 [n, hd/2, 2] (cos, sin) per token and pair (DIT_ROPE_PARTIAL: pairs
+ *                         [3k, hd/2) hold the identity (1, 0))
  *   xn    act  [n, D]     pre-norm + modulate of the FFN half after the call
  *                         (the attention half's is overwritten)
  *   qkv   act  [n, 3D]    QKV projection (+ bias); fp32 configurations only (the bf16
  *                         QKV GEMM writes q, k and vt directly from its epilogue)
- *   q, k  act  [H, ldn, hd]  after qk-norm and RoPE; q carries log2(e) * hd^-1/2
+ *   q, k  act  [H, ldn, hd]  after qk-norm and RoPE; q carries log2(e) * hd^-1/2.
+ *                         DIT_ROPE_PARTIAL runs as a split-half rotation over all of
+ *                         hd with the head dims of q and k permuted (scores are
+ *                         unchanged): with P = 3k, h = hd/2, stored dim d holds the
+ *                         page's dim d (d < P), d + P (P <= d < h), d - (h - P)
+ *                         (h <= d < h + P) or d (d >= h + P)
  *   vt    act  [H, hd, ldn]  V transposed per head
  *   o     act  [n, D]     attention output, head h at columns h*hd
  *   x1    fp32 [n, D]     residual stream after the attention half
  *   a     act  [n, F]     FFN activation (SwiGLU or GELU-tanh)
  *   y     fp32 [n, D]     ZIMAGE: last projection before its sandwich norm (fc2's after the call)
- *   part  fp32            bf16 only: key-range partials of the attention's split last round
+ *   part  fp32            bf16 only: key-range partials of the attention's split tail
  *                         (256 slots x 256 queries x (hd + 2) floats) */
 typedef struct dit_ws_layout {
   size_t mods, rope, xn, qkv, q, k, vt, o, x1, a, y, temb, part, total;
@@ -304,6 +324,11 @@ typedef struct dit_mmh3_model {
   const float* audio_patch_b;       /* [D] or NULL                                          */
   double shift_video, shift_audio;  /* flow shifts (12, 3)                                  */
   double cond_aug, cond_aug_audio;  /* condition timesteps (0.999, 1)                       */
+  int32_t audio_slope_rescale;      /* 0: both velocities unscaled, each on its own schedule;
+                                       1: the audio velocity times d(sigma_a)/d(sigma_v) =
+                                       dit_sigma_remap_slope(sigma_v, shift_video, shift_audio),
+                                       the single-schedule form [MMH3] ascribes to the
+                                       reference model                                     */
 } dit_mmh3_model;
 
 /* Workspace bytes of dit_mmh3_forward for these segments (0 if invalid). */

@@ -145,25 +145,34 @@ def adaln_coords(table: np.ndarray, t: float) -> np.ndarray:
 
 
 def adaln_mods(basis: np.ndarray, bias: Optional[np.ndarray], table: np.ndarray,
-               ts: Sequence[float], tags: int, chunks: int, D: int) -> np.ndarray:
+               ts: Sequence[float], tags: int, chunks: int, D: int,
+               shared: bool = False) -> np.ndarray:
     """Modulation rows [S*tags, chunks*D].
 
     Element (r, e, d) of row r = s*tags + tag is flat index (r*chunks + e)*D + d
     of the modulation buffer ([MMH3] ``Adaln::eval`` layout).  Flat element j
     is bias[j] + sum_k basis[j, k] * c_s[k], evaluated at its own slot's
     coordinates c_s = adaln_coords(table, ts[s]) (slot-major basis: rows
-    [s*tags*chunks*D, (s+1)*tags*chunks*D) belong to slot s)."""
+    [s*tags*chunks*D, (s+1)*tags*chunks*D) belong to slot s).  ``shared``:
+    the basis and bias hold one slot's tags*chunks*D rows and the same map is
+    applied at every slot's timestep (``Adaln::eval`` evaluating one W at
+    each distinct timestep)."""
     B = np.asarray(basis, dtype=F64)
+    bvec = None if bias is None else np.asarray(bias, dtype=F64)
     per_slot = tags * chunks * D
     S = len(ts)
-    assert B.shape[0] == S * per_slot, "basis rows must cover every slot"
+    if shared:
+        assert B.shape[0] == per_slot, "a shared basis holds one slot's rows"
+    else:
+        assert B.shape[0] == S * per_slot, "basis rows must cover every slot"
     out = np.empty(S * per_slot, dtype=F64)
     for s, t in enumerate(ts):
         c = adaln_coords(table, t)
         blk = slice(s * per_slot, (s + 1) * per_slot)
-        out[blk] = B[blk] @ c
-        if bias is not None:
-            out[blk] += np.asarray(bias, dtype=F64)[blk]
+        src = slice(0, per_slot) if shared else blk
+        out[blk] = B[src] @ c
+        if bvec is not None:
+            out[blk] += bvec[src]
     return out.reshape(S * tags, chunks * D)
 
 
@@ -228,6 +237,24 @@ def rope_angles(pos: np.ndarray, axes: Sequence[int], theta: float) -> np.ndarra
         omega = float(theta) ** (-2.0 * m / d)
         parts.append(pos[:, a:a + 1] * omega[None, :])
     return np.concatenate(parts, axis=1)
+
+
+def rope_angles_shared(pos: np.ndarray, freq: np.ndarray) -> np.ndarray:
+    """Rotation angles [n, 3k] of the checkpoint form: the k frequencies of
+    ``freq`` serve all three axes, angle a*k + j = pos[a] * freq[j], axes in
+    order t, h, w ([MMH3] ``rope_angles`` over ``inv_freq``).  With
+    split-half pairs (j, j + 3k), head dims from 6k on stay unrotated
+    ([MMH3] ``norm_rope_w``)."""
+    pos = np.asarray(pos, dtype=F64)
+    f = np.asarray(freq, dtype=F64)
+    return np.concatenate([pos[:, a:a + 1] * f[None, :] for a in range(3)], axis=1)
+
+
+def rope_for(spec, pos: np.ndarray, w: Dict[str, np.ndarray]):
+    """(angles [n, P], pair layout) of a block's RoPE."""
+    if spec.rope == "partial":
+        return rope_angles_shared(pos, w["rope_freq"]), "split_half"
+    return rope_angles(pos, spec.rope_axes, spec.rope_theta), spec.rope
 
 
 def rope_rotate(x: np.ndarray, ang: np.ndarray, mode: str) -> np.ndarray:
@@ -353,7 +380,7 @@ def mmh3_block(spec, x: np.ndarray, rows: np.ndarray, pos: Optional[np.ndarray],
     if mods is None:
         ts = [mmh3_timestep(s) for s in sigmas]
         mods = adaln_mods(w["adaln_basis"], w.get("adaln_bias"), w["adaln_table"], ts,
-                          spec.tags, 6, D)
+                          spec.tags, 6, D, bool(getattr(spec, "adaln_shared", 0)))
     mods = np.asarray(mods, F64)
     chunk = lambda r, e: mods[r, e * D:(e + 1) * D]  # noqa: E731
 
@@ -367,9 +394,9 @@ def mmh3_block(spec, x: np.ndarray, rows: np.ndarray, pos: Optional[np.ndarray],
     v = _heads(_lin(xn, wv), H, hd)
     q = rms_norm(_heads(_lin(xn[sel], wq), H, hd), w["q_norm"], spec.qk_eps)
     if spec.rope != "none":
-        ang = rope_angles(pos, spec.rope_axes, spec.rope_theta)
-        k = rope_rotate(k, ang[None], spec.rope)
-        q = rope_rotate(q, ang[sel][None], spec.rope)
+        ang, mode = rope_for(spec, pos, w)
+        k = rope_rotate(k, ang[None], mode)
+        q = rope_rotate(q, ang[sel][None], mode)
 
     o = _merge(_attend(q, k, v, 1.0 / math.sqrt(hd), sel, seq_starts))
     rs = rows[sel]
@@ -406,9 +433,9 @@ def refiner_block(spec, x: np.ndarray, pos: Optional[np.ndarray], w: Dict[str, n
     v = _heads(_lin(xn, wv), H, hd)
     q = rms_norm(_heads(_lin(xn[sel], wq), H, hd), w["q_norm"], spec.qk_eps)
     if spec.rope != "none":
-        ang = rope_angles(pos, spec.rope_axes, spec.rope_theta)
-        k = rope_rotate(k, ang[None], spec.rope)
-        q = rope_rotate(q, ang[sel][None], spec.rope)
+        ang, mode = rope_for(spec, pos, w)
+        k = rope_rotate(k, ang[None], mode)
+        q = rope_rotate(q, ang[sel][None], mode)
     o = _merge(_attend(q, k, v, 1.0 / math.sqrt(hd), sel, seq_starts))
     x1 = x[sel] + _lin(o, w["w_out"])
     xn2 = rms_norm(x1, w["norm2"], spec.eps)
@@ -441,7 +468,8 @@ def final_layer(spec, h: np.ndarray, rows: Optional[np.ndarray], sigmas: Sequenc
     h = np.asarray(h, F64)
     rows = np.zeros(h.shape[0], np.int64) if rows is None else np.asarray(rows, np.int64)
     ts = [mmh3_timestep(s) for s in sigmas]
-    mods = adaln_mods(w["adaln_basis"], w.get("adaln_bias"), w["adaln_table"], ts, spec.tags, 2, D)
+    mods = adaln_mods(w["adaln_basis"], w.get("adaln_bias"), w["adaln_table"], ts, spec.tags, 2, D,
+                      bool(getattr(spec, "adaln_shared", 0)))
     hn = modulate(rms_norm(h, w["norm1"], spec.eps), mods[rows, 0:D], mods[rows, D:2 * D])
     out = -_lin(hn, w["w_fc1"], w.get("b_fc1"))
     return dict(mods=mods, xn=hn, out=out)
@@ -505,13 +533,16 @@ def unpack_audio(rows: np.ndarray, C: int, T: int) -> np.ndarray:
 def mmh3_forward(block_spec, head_v_spec, head_a_spec, segments, pos, text, video, audio, conds,
                  sigma_v: float, w_blocks, w_head_v, w_head_a, w_vpatch, b_vpatch, w_apatch,
                  b_apatch, shift_video=12.0, shift_audio=3.0, cond_aug=0.999,
-                 cond_aug_audio=1.0):
+                 cond_aug_audio=1.0, audio_slope_rescale=False):
     """One denoise evaluation: embed (video and condition frames through the
     video patch projection, audio through the audio one, refined text as
     given), the blocks with the evaluation's slots and token rows, the two
     heads (negated) and the unpacking.  ``segments``: (kind, start, stop) with
     kinds "text", "video", "audio", "cond".  Returns (video velocity [C, T, H,
-    W], audio velocity [Ca, 2, Ta] or None)."""
+    W], audio velocity [Ca, 2, Ta] or None).  ``audio_slope_rescale``
+    multiplies the audio velocity by d(sigma_a)/d(sigma_v) (the pre-multiplied
+    single-schedule form the [MMH3] module docs describe of the reference
+    model; unscaled otherwise)."""
     ts, slot = mmh3_slots(sigma_v, shift_video, shift_audio, cond_aug, cond_aug_audio,
                           any(k == "cond" for k, _, _ in segments), False)
     sig = [1.0 - t for t in ts] + [1.0 - ts[-1]] * (block_spec.slots - len(ts))
@@ -540,6 +571,8 @@ def mmh3_forward(block_spec, head_v_spec, head_a_spec, segments, pos, text, vide
         elif kind == "audio":
             r = final_layer(head_a_spec, h[a:b], np.full(b - a, slot["audio"]), sig, w_head_a)["out"]
             out_a = unpack_audio(r, audio.shape[0], audio.shape[2])
+            if audio_slope_rescale:
+                out_a = out_a * sigma_remap_slope(sigma_v, shift_video, shift_audio)
     return out_v, out_a
 
 
@@ -660,7 +693,8 @@ __all__ = [
     "sigma_remap", "sigma_remap_slope", "resolve_sigmas", "mmh3_timestep", "mmh3_slots",
     "mmh3_token_rows",
     "adaln_coords", "adaln_mods", "rms_norm", "layer_norm", "modulate", "silu",
-    "gelu_tanh", "rope_angles", "rope_rotate", "attention", "sample_ranges",
+    "gelu_tanh", "rope_angles", "rope_angles_shared", "rope_for", "rope_rotate", "attention",
+    "sample_ranges",
     "attention_packed", "mmh3_block", "refiner_block", "linear", "final_layer", "stack",
     "patchify_video", "unpatchify_video", "pack_audio", "unpack_audio", "mmh3_forward",
     "siglip_layer", "timestep_embedding", "zimage_mods", "zimage_block", "block",

@@ -49,6 +49,9 @@ bool swiglu(const dit_config* c) { return c->variant != DIT_SIGLIP; }
 // modulated variants (adaLN rows, sigmas)
 bool has_mods(const dit_config* c) { return basis_mods(c) || c->variant == DIT_ZIMAGE; }
 int fc1_rows(const dit_config* c) { return swiglu(c) ? 2 * c->F : c->F; }
+// pair layout the kernels apply: the partial rotation runs as split-half over
+// head dims permuted at weight preparation
+int rope_pairs(const dit_config* c) { return c->rope == DIT_ROPE_PARTIAL ? DIT_ROPE_SPLIT_HALF : c->rope; }
 
 dit_status check_config(const dit_config* c) {
   if (!c) return fail(DIT_EINVAL, "config is NULL");
@@ -66,8 +69,15 @@ dit_status check_config(const dit_config* c) {
     return fail(DIT_EUNSUPPORTED, "F=%d must be a positive multiple of 128", c->F);
   }
   if (!(c->eps >= 0.0f) || !(c->qk_eps >= 0.0f)) return fail(DIT_EINVAL, "eps must be >= 0");
-  if (c->rope < DIT_ROPE_NONE || c->rope > DIT_ROPE_INTERLEAVED) return fail(DIT_EINVAL, "unknown rope %d", c->rope);
-  if (c->rope != DIT_ROPE_NONE && c->variant != DIT_FINAL) {
+  if (c->rope < DIT_ROPE_NONE || c->rope > DIT_ROPE_PARTIAL) return fail(DIT_EINVAL, "unknown rope %d", c->rope);
+  if (c->rope == DIT_ROPE_PARTIAL) {
+    if (c->variant != DIT_MMH3 && c->variant != DIT_REFINER)
+      return fail(DIT_EUNSUPPORTED, "DIT_ROPE_PARTIAL is an MMH3 / refiner layout");
+    const int d = c->rope_axes[0];
+    if (d <= 0 || d % 2 || c->rope_axes[1] != d || c->rope_axes[2] != d)
+      return fail(DIT_EINVAL, "DIT_ROPE_PARTIAL needs three equal, even, positive axis dims");
+    if (3 * d > c->hd) return fail(DIT_ESHAPE, "DIT_ROPE_PARTIAL rotates 3 * %d dims, head dim is %d", d, c->hd);
+  } else if (c->rope != DIT_ROPE_NONE && c->variant != DIT_FINAL) {
     int sum = 0;
     for (int a = 0; a < 3; ++a) {
       if (c->rope_axes[a] < 0 || c->rope_axes[a] % 2) return fail(DIT_EINVAL, "rope axis dims must be even and >= 0");
@@ -76,6 +86,8 @@ dit_status check_config(const dit_config* c) {
     if (sum != c->hd) return fail(DIT_ESHAPE, "rope axis dims sum to %d, head dim is %d", sum, c->hd);
     if (!(c->rope_theta > 0.0) || !isfinite(c->rope_theta)) return fail(DIT_EINVAL, "rope_theta must be > 0");
   }
+  if (c->adaln_shared != 0 && (c->adaln_shared != 1 || !basis_mods(c)))
+    return fail(DIT_EINVAL, "adaln_shared=%d (0, or 1 for MMH3 / FINAL)", c->adaln_shared);
   if (basis_mods(c)) {
     if (c->slots < 1 || c->slots > 8) return fail(DIT_EUNSUPPORTED, "slots=%d not in [1, 8]", c->slots);
     if (c->tags < 1 || c->tags > 16) return fail(DIT_EINVAL, "tags=%d not in [1, 16]", c->tags);
@@ -98,7 +110,7 @@ struct PrepLayout {
          post_ffn = kNone, w_qkv = kNone, w_out = kNone, w_fc1 = kNone, w_fc2 = kNone,
          b_qkv = kNone, b_out = kNone, b_fc1 = kNone, b_fc2 = kNone, q_norm = kNone,
          k_norm = kNone, basis = kNone, abias = kNone, table = kNone, tw1 = kNone, tb1 = kNone,
-         tw2 = kNone, tb2 = kNone, aw = kNone, ab = kNone, total = 0;
+         tw2 = kNone, tb2 = kNone, aw = kNone, ab = kNone, rope_freq = kNone, total = 0;
 };
 
 PrepLayout prep_layout(const dit_config* c) {
@@ -131,6 +143,7 @@ PrepLayout prep_layout(const dit_config* c) {
     L.q_norm = take(c->hd * 4);
     L.k_norm = take(c->hd * 4);
   }
+  if (c->rope == DIT_ROPE_PARTIAL) L.rope_freq = take(c->rope_axes[0] / 2 * 4);
   if (c->variant == DIT_SIGLIP) {
     L.ln1_b = take(D * 4);
     L.ln2_b = take(D * 4);
@@ -373,7 +386,7 @@ dit_status dit_profile_end(double* phase_ms, int32_t* calls) {
 }
 
 
-int32_t dit_abi_version(void) { return 2; }
+int32_t dit_abi_version(void) { return 3; }
 
 const char* dit_last_error(void) { return g_err; }
 
@@ -460,9 +473,11 @@ dit_status dit_prepare_weights(const dit_config* c, const dit_weights* w, void* 
     HIP_TRY(dit::prep_matrix(c->dtype, w->w_fc1, at<char>(prepared, P.w_fc1), F, D, 0, 0, 1.0f, s), "prep head");
     HIP_TRY(dit::prep_vector(w->norm1, at<float>(prepared, P.norm1), D, 0, 1.0f, s), "prep norm1");
     HIP_TRY(dit::prep_vector(w->b_fc1, at<float>(prepared, P.b_fc1), F, 0, 1.0f, s), "prep head bias");
-    HIP_TRY(dit::prep_matrix(dit::F32, w->adaln_basis, at<char>(prepared, P.basis), rows, c->rank, 0, 0, 1.0f, s),
+    dit::RowMap am;
+    am.src_mod = c->adaln_shared ? c->tags * 2 * D : 0;
+    HIP_TRY(dit::prep_matrix(dit::F32, w->adaln_basis, at<char>(prepared, P.basis), rows, c->rank, am, 0, 1.0f, s),
             "prep adaln_basis");
-    HIP_TRY(dit::prep_vector(w->adaln_bias, at<float>(prepared, P.abias), rows, 0, 1.0f, s), "prep adaln_bias");
+    HIP_TRY(dit::prep_vector(w->adaln_bias, at<float>(prepared, P.abias), rows, am, 0, 1.0f, s), "prep adaln_bias");
     HIP_TRY(dit::prep_matrix(dit::F32, w->adaln_table, at<char>(prepared, P.table), c->grid, c->rank, 0, 0, 1.0f, s),
             "prep adaln_table");
     return DIT_OK;
@@ -474,6 +489,7 @@ dit_status dit_prepare_weights(const dit_config* c, const dit_weights* w, void* 
     if (!aligned16(q.p)) return fail(DIT_EALIGN, "weight %s is not 16-byte aligned", q.name);
   }
   if (c->variant != DIT_SIGLIP && (!w->q_norm || !w->k_norm)) return fail(DIT_EINVAL, "q_norm/k_norm are NULL");
+  if (c->rope == DIT_ROPE_PARTIAL && !w->rope_freq) return fail(DIT_EINVAL, "rope_freq is NULL (DIT_ROPE_PARTIAL)");
   if (c->variant == DIT_MMH3 && (!w->adaln_basis || !w->adaln_table))
     return fail(DIT_EINVAL, "adaln_basis/adaln_table are NULL");
   if (c->variant == DIT_SIGLIP && (!w->ln1_b || !w->ln2_b))
@@ -486,7 +502,14 @@ dit_status dit_prepare_weights(const dit_config* c, const dit_weights* w, void* 
   // [SIGLIP] Layer::load folds hd^-1/2 into W_q and b_q.
   const bool fold = c->variant == DIT_SIGLIP;
   const float qs = fold ? (float)(1.0 / sqrt((double)c->hd)) : 1.0f;
-  HIP_TRY(dit::prep_matrix(dt, w->w_qkv, at<char>(prepared, P.w_qkv), 3 * D, D, 0, fold ? D : 0, qs, s), "prep w_qkv");
+  dit::RowMap qkmap;  // partial RoPE: permute the head dims of the q and k rows
+  if (c->rope == DIT_ROPE_PARTIAL) {
+    qkmap.perm_rows = 2 * D;
+    qkmap.perm_hd = c->hd;
+    qkmap.perm_P = 3 * (c->rope_axes[0] / 2);
+  }
+  HIP_TRY(dit::prep_matrix(dt, w->w_qkv, at<char>(prepared, P.w_qkv), 3 * D, D, qkmap, fold ? D : 0, qs, s),
+          "prep w_qkv");
   HIP_TRY(dit::prep_matrix(dt, w->w_out, at<char>(prepared, P.w_out), D, D, 0, 0, 1.0f, s), "prep w_out");
   HIP_TRY(dit::prep_matrix(dt, w->w_fc1, at<char>(prepared, P.w_fc1), fc1_rows(c), D,
                            swiglu(c) ? F : 0, 0, 1.0f, s), "prep w_fc1");
@@ -497,9 +520,13 @@ dit_status dit_prepare_weights(const dit_config* c, const dit_weights* w, void* 
   HIP_TRY(vec(w->norm1, P.norm1, D), "prep norm1");
   HIP_TRY(vec(w->norm2, P.norm2, D), "prep norm2");
   if (c->variant != DIT_SIGLIP) {
-    HIP_TRY(vec(w->q_norm, P.q_norm, c->hd), "prep q_norm");
-    HIP_TRY(vec(w->k_norm, P.k_norm, c->hd), "prep k_norm");
+    dit::RowMap gmap = qkmap;
+    gmap.perm_rows = gmap.perm_rows ? c->hd : 0;
+    HIP_TRY(dit::prep_vector(w->q_norm, at<float>(prepared, P.q_norm), c->hd, gmap, 0, 1.0f, s), "prep q_norm");
+    HIP_TRY(dit::prep_vector(w->k_norm, at<float>(prepared, P.k_norm), c->hd, gmap, 0, 1.0f, s), "prep k_norm");
   }
+  if (c->rope == DIT_ROPE_PARTIAL)
+    HIP_TRY(vec(w->rope_freq, P.rope_freq, c->rope_axes[0] / 2), "prep rope_freq");
   if (c->variant == DIT_SIGLIP) {
     HIP_TRY(vec(w->ln1_b, P.ln1_b, D), "prep ln1_b");
     HIP_TRY(vec(w->ln2_b, P.ln2_b, D), "prep ln2_b");
@@ -510,9 +537,11 @@ dit_status dit_prepare_weights(const dit_config* c, const dit_weights* w, void* 
   }
   if (c->variant == DIT_MMH3) {
     int rows = c->slots * c->tags * 6 * D;
-    HIP_TRY(dit::prep_matrix(dit::F32, w->adaln_basis, at<char>(prepared, P.basis), rows, c->rank, 0, 0, 1.0f, s),
+    dit::RowMap am;  // a shared basis is one slot's rows, repeated for every slot
+    am.src_mod = c->adaln_shared ? c->tags * 6 * D : 0;
+    HIP_TRY(dit::prep_matrix(dit::F32, w->adaln_basis, at<char>(prepared, P.basis), rows, c->rank, am, 0, 1.0f, s),
             "prep adaln_basis");
-    HIP_TRY(vec(w->adaln_bias, P.abias, rows), "prep adaln_bias");
+    HIP_TRY(dit::prep_vector(w->adaln_bias, at<float>(prepared, P.abias), rows, am, 0, 1.0f, s), "prep adaln_bias");
     HIP_TRY(dit::prep_matrix(dit::F32, w->adaln_table, at<char>(prepared, P.table), c->grid, c->rank, 0, 0, 1.0f, s),
             "prep adaln_table");
   }
@@ -655,7 +684,10 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
   // a1: modulation rows; RoPE table
   if (has_mods(c) && !mods_in)
     DIT_TRY(launch_mods(c, prepared, sigmas, at<float>(workspace, L.mods), at<float>(workspace, L.temb), s));
-  if (c->rope != DIT_ROPE_NONE)
+  if (c->rope == DIT_ROPE_PARTIAL)
+    HIP_TRY(dit::rope_table_shared(pos, n, hd / 2, c->rope_axes[0] / 2, atc<float>(prepared, P.rope_freq), cs, s),
+            "rope_table");
+  else if (c->rope != DIT_ROPE_NONE)
     HIP_TRY(dit::rope_table(pos, n, hd / 2, c->rope_axes, c->rope_theta, cs, s), "rope_table");
   pm.mark(0);
   // a2: pre-norm + modulate
@@ -682,7 +714,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
       ep.kn = kn;
       ep.qk_eps = c->qk_eps;
       ep.cs = cs;
-      ep.rope = c->rope;
+      ep.rope = rope_pairs(c);
       ep.q_scale = q_scale;
       ep.q = q;
       ep.k = k;
@@ -696,7 +728,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
       HIP_TRY(dit::gemm(dt, dit::EPI_STORE, false, xn, D, atc<char>(prepared, P.w_qkv), D, n, 3 * D, D, ep, s),
               "qkv gemm");
       pm.mark(2);
-      HIP_TRY(dit::qk_split(dt, hd, qkv, n, ldn, H, qn, kn, c->qk_eps, cs, c->rope, q_scale, q, k, vt, s),
+      HIP_TRY(dit::qk_split(dt, hd, qkv, n, ldn, H, qn, kn, c->qk_eps, cs, rope_pairs(c), q_scale, q, k, vt, s),
               "qk_split");
     }
   }
@@ -800,9 +832,12 @@ dit_status dit_block_forward_packed(const dit_config* c, const void* prepared, c
                             nseq, out, workspace, ws_bytes, stream);
 }
 
-dit_status dit_final_forward(const dit_config* c, const void* prepared, const float* h, int32_t n,
-                             const int32_t* rows, const double* sigmas, int32_t n_sigmas, float* out,
-                             void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+// The output head with the velocity's sign flip folded into alpha (-1, or
+// -d(sigma_a)/d(sigma_v) for a pre-multiplied audio velocity).
+dit_status final_forward_impl(const dit_config* c, const void* prepared, const float* h, int32_t n,
+                              const int32_t* rows, const double* sigmas, int32_t n_sigmas, float alpha,
+                              float* out, void* workspace, size_t ws_bytes, void* stream) {
   DIT_TRY(check_config(c));
   if (c->variant != DIT_FINAL) return fail(DIT_EINVAL, "dit_final_forward needs a DIT_FINAL config");
   if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
@@ -825,11 +860,20 @@ dit_status dit_final_forward(const dit_config* c, const void* prepared, const fl
   ep.out = out;
   ep.ldc = c->F;
   ep.bias = atc<float>(prepared, P.b_fc1);
-  ep.alpha = -1.0f;  // the head predicts toward the data: the velocity is its negative
+  ep.alpha = alpha;
   HIP_TRY(dit::gemm(c->dtype, dit::EPI_STORE, false, xn, c->D, atc<char>(prepared, P.w_fc1), c->D, n,
                     c->F, c->D, ep, s),
           "head gemm");
   return DIT_OK;
+}
+}  // namespace
+
+dit_status dit_final_forward(const dit_config* c, const void* prepared, const float* h, int32_t n,
+                             const int32_t* rows, const double* sigmas, int32_t n_sigmas, float* out,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  // the head predicts toward the data: the velocity is its negative
+  return final_forward_impl(c, prepared, h, n, rows, sigmas, n_sigmas, -1.0f, out, workspace, ws_bytes,
+                            stream);
 }
 
 dit_status dit_linear(int32_t dtype, const void* a, int32_t lda, int32_t m, int32_t k, const void* w,
@@ -945,6 +989,8 @@ dit_status plan_model(const dit_mmh3_model* m, const dit_segment* segs, int32_t 
     return fail(DIT_EINVAL, "model needs a block config, blocks and a video head");
   DIT_TRY(check_config(m->block));
   if (m->block->variant != DIT_MMH3) return fail(DIT_EINVAL, "model blocks must be DIT_MMH3");
+  if (m->audio_slope_rescale != 0 && m->audio_slope_rescale != 1)
+    return fail(DIT_EINVAL, "audio_slope_rescale=%d (0 or 1)", m->audio_slope_rescale);
   DIT_TRY(check_config(m->head_video));
   if (m->head_video->variant != DIT_FINAL || m->head_video->F != 4 * m->latent_c ||
       m->head_video->D != m->block->D || m->head_video->slots != m->block->slots)
@@ -1090,8 +1136,10 @@ dit_status dit_mmh3_forward(const dit_mmh3_model* m, const dit_segment* segs, in
   if (P.audio >= 0 && P.na > 0) {
     const dit_segment& g = segs[P.audio];
     HIP_TRY(dit::fill_i32(hrows, P.na, slot[1], s), "head rows");
-    DIT_TRY(dit_final_forward(m->head_audio, m->head_audio_w, h + (size_t)g.start * D, P.na, hrows, sig.data(),
-                              bc->slots, hout, at<char>(workspace, P.hws), hws, s));
+    const double slope =
+        m->audio_slope_rescale ? dit_sigma_remap_slope(sigma_v, m->shift_video, m->shift_audio) : 1.0;
+    DIT_TRY(final_forward_impl(m->head_audio, m->head_audio_w, h + (size_t)g.start * D, P.na, hrows, sig.data(),
+                               bc->slots, (float)-slope, hout, at<char>(workspace, P.hws), hws, s));
     HIP_TRY(dit::unpack_audio(hout, m->audio_c, Ta, audio_out, s), "unpack_audio");
   }
   return DIT_OK;

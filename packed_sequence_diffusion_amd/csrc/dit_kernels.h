@@ -71,6 +71,8 @@ hipError_t sandwich(const float* x, const float* y, int n, int D, const float* g
                     const float* scale, bool xf_bf16, void* xf, hipStream_t s);
 
 // cos/sin per token and rotation pair, from fp64 angles.
+hipError_t rope_table_shared(const float* pos, int n, int P, int k, const float* freq, float* cs,
+                             hipStream_t s);
 hipError_t rope_table(const float* pos, int n, int P, const int axes[3], double theta, float* cs,
                       hipStream_t s);
 
@@ -113,10 +115,23 @@ hipError_t unpack_audio(const float* rows, int C, int T, float* x, hipStream_t s
 hipError_t fill_i32(int* p, int n, int v, hipStream_t s);
 
 // ---- weight preparation ---------------------------------------------------------------
-// dst[r, :] = src[perm(r), :] * (r < scale_rows ? scale : 1); perm = SwiGLU group interleave
-// when swiglu_F > 0.
+// Source row of prepared row r, in this order: the SwiGLU group interleave (swiglu_F > 0);
+// for r < perm_rows, the head-dim permutation that runs the partial split-half RoPE as a
+// full one (perm_hd, perm_P = 3k rotated pairs); the source row modulo src_mod (> 0: one
+// slot's adaLN rows repeated for every slot).
+struct RowMap {
+  int swiglu_F = 0;
+  int perm_rows = 0, perm_hd = 0, perm_P = 0;
+  int src_mod = 0;
+};
+// dst[r, :] = src[map(r), :] * (r < scale_rows ? scale : 1)
+hipError_t prep_matrix(int dtype, const void* src, void* dst, int rows, int cols, const RowMap& m,
+                       int scale_rows, float scale, hipStream_t s);
 hipError_t prep_matrix(int dtype, const void* src, void* dst, int rows, int cols, int swiglu_F,
                        int scale_rows, float scale, hipStream_t s);
+// dst[i] = src[map(i)] * (i < scale_n ? scale : 1) (src NULL: zeros)
+hipError_t prep_vector(const float* src, float* dst, int n, const RowMap& m, int scale_n,
+                       float scale, hipStream_t s);
 hipError_t prep_vector(const float* src, float* dst, int n, int scale_n, float scale,
                        hipStream_t s);
 

@@ -351,6 +351,33 @@ hipError_t rope_table(const float* pos, int n, int P, const int axes[3], double 
   return hipGetLastError();
 }
 
+// Partial RoPE table ([MMH3] rope_angles with the checkpoint's frequency
+// vector): pair j < 3k turns by pos[i, j / k] * freq[j % k]; pairs [3k, P) by
+// zero (cos 1, sin 0), the head dims that stay unrotated.  fp64 angles.
+__global__ void k_rope_table_shared(const float* __restrict__ pos, int n, int P, int k,
+                                    const float* __restrict__ freq, float2* __restrict__ cs) {
+  int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n * P) return;
+  int i = idx / P, j = idx - i * P;
+  if (j >= 3 * k) {
+    cs[idx] = make_float2(1.0f, 0.0f);
+    return;
+  }
+  const int a = j / k;
+  double ang = (double)pos[(size_t)i * 3 + a] * (double)freq[j - a * k];
+  double sn, cn;
+  sincos(ang, &sn, &cn);
+  cs[idx] = make_float2((float)cn, (float)sn);
+}
+
+hipError_t rope_table_shared(const float* pos, int n, int P, int k, const float* freq, float* cs,
+                             hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int total = n * P;
+  k_rope_table_shared<<<(total + 255) / 256, 256, 0, s>>>(pos, n, P, k, freq, (float2*)cs);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------------------
 // Head split of the fused qkv panel with qk-RMSNorm and RoPE on q and k
 // ([MMH3] norm_rope_w; qk-norm before rotary as [ENC] rms_norm_heads).
@@ -467,53 +494,81 @@ hipError_t qk_split(int dtype, int hd, const void* qkv, int n, int ldn, int H, c
 }
 
 // ------------------------------------------------------------------------------
-// Weight preparation: row permutation (SwiGLU group interleave) and scaling.
-// Prepared row r of fc1 (N = 2F rows): group g = r / 64, j = r % 64;
+// Weight preparation: row maps (RowMap) and scaling.
+// SwiGLU group interleave of fc1 (N = 2F rows): group g = r / 64, j = r % 64;
 // j < 32 -> gate row 32 g + j, else up row F + 32 g + (j - 32).
+// Partial RoPE ([MMH3] norm_rope_w: pairs (j, j + P) for j < P = 3k, dims
+// [2P, hd) unrotated): stored head dim d takes the page's dim d (d < P),
+// d + P (P <= d < hd/2), d - (hd/2 - P) (hd/2 <= d < hd/2 + P) or d, so that
+// the rotated pairs land on (j, j + hd/2) and the unrotated dims on pairs that
+// the table turns by zero.
 // ------------------------------------------------------------------------------
+DIT_DEV int map_row(const RowMap& m, int r) {
+  if (m.swiglu_F > 0) {
+    int g = r >> 6, j = r & 63;
+    r = (j < 32) ? (32 * g + j) : (m.swiglu_F + 32 * g + (j - 32));
+  }
+  if (r < m.perm_rows) {
+    const int h = m.perm_hd / 2, P = m.perm_P;
+    const int d = r % m.perm_hd;
+    const int sd = d < P ? d : (d < h ? d + P : (d < h + P ? d - (h - P) : d));
+    r += sd - d;
+  }
+  if (m.src_mod > 0) r %= m.src_mod;
+  return r;
+}
+
 template <typename T>
 __global__ void k_prep_matrix(const T* __restrict__ src, T* __restrict__ dst, int rows, int cols,
-                              int swiglu_F, int scale_rows, float scale) {
+                              RowMap m, int scale_rows, float scale) {
   size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   size_t total = (size_t)rows * cols;
   if (idx >= total) return;
   int r = (int)(idx / cols), c = (int)(idx - (size_t)r * cols);
-  int sr = r;
-  if (swiglu_F > 0) {
-    int g = r >> 6, j = r & 63;
-    sr = (j < 32) ? (32 * g + j) : (swiglu_F + 32 * g + (j - 32));
-  }
-  float v = Elt<T>::ld(src + (size_t)sr * cols + c);
+  float v = Elt<T>::ld(src + (size_t)map_row(m, r) * cols + c);
   if (r < scale_rows) v *= scale;
   Elt<T>::st(dst + idx, v);
 }
 
-hipError_t prep_matrix(int dtype, const void* src, void* dst, int rows, int cols, int swiglu_F,
+hipError_t prep_matrix(int dtype, const void* src, void* dst, int rows, int cols, const RowMap& m,
                        int scale_rows, float scale, hipStream_t s) {
   size_t total = (size_t)rows * cols;
+  if (total == 0) return hipSuccess;
   dim3 grid((unsigned)((total + 255) / 256));
   if (dtype == BF16)
-    k_prep_matrix<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)src, (bf16_t*)dst, rows, cols,
-                                                swiglu_F, scale_rows, scale);
+    k_prep_matrix<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)src, (bf16_t*)dst, rows, cols, m,
+                                                scale_rows, scale);
   else
-    k_prep_matrix<float><<<grid, 256, 0, s>>>((const float*)src, (float*)dst, rows, cols,
-                                               swiglu_F, scale_rows, scale);
+    k_prep_matrix<float><<<grid, 256, 0, s>>>((const float*)src, (float*)dst, rows, cols, m,
+                                               scale_rows, scale);
   return hipGetLastError();
 }
 
+hipError_t prep_matrix(int dtype, const void* src, void* dst, int rows, int cols, int swiglu_F,
+                       int scale_rows, float scale, hipStream_t s) {
+  RowMap m;
+  m.swiglu_F = swiglu_F;
+  return prep_matrix(dtype, src, dst, rows, cols, m, scale_rows, scale, s);
+}
+
 __global__ void k_prep_vector(const float* __restrict__ src, float* __restrict__ dst, int n,
-                              int scale_n, float scale) {
+                              RowMap m, int scale_n, float scale) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  float v = src ? src[i] : 0.0f;
+  float v = src ? src[map_row(m, i)] : 0.0f;
   dst[i] = (i < scale_n) ? v * scale : v;
+}
+
+hipError_t prep_vector(const float* src, float* dst, int n, const RowMap& m, int scale_n,
+                       float scale, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_prep_vector<<<(n + 255) / 256, 256, 0, s>>>(src, dst, n, m, scale_n, scale);
+  return hipGetLastError();
 }
 
 hipError_t prep_vector(const float* src, float* dst, int n, int scale_n, float scale,
                        hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  k_prep_vector<<<(n + 255) / 256, 256, 0, s>>>(src, dst, n, scale_n, scale);
-  return hipGetLastError();
+  return prep_vector(src, dst, n, RowMap(), scale_n, scale, s);
 }
 
 }  // namespace dit

@@ -18,12 +18,13 @@ LIB_PATH = os.path.join(_HERE, "libdit.so")
 
 MMH3, SIGLIP, ZIMAGE, REFINER, FINAL = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
-ROPE_NONE, ROPE_SPLIT_HALF, ROPE_INTERLEAVED = 0, 1, 2
+ROPE_NONE, ROPE_SPLIT_HALF, ROPE_INTERLEAVED, ROPE_PARTIAL = 0, 1, 2, 3
 NPHASES = 9
 
 _VARIANTS = {"mmh3": MMH3, "siglip": SIGLIP, "zimage": ZIMAGE, "refiner": REFINER, "final": FINAL}
 _DTYPES = {"f32": F32, "bf16": BF16}
-_ROPES = {"none": ROPE_NONE, "split_half": ROPE_SPLIT_HALF, "interleaved": ROPE_INTERLEAVED}
+_ROPES = {"none": ROPE_NONE, "split_half": ROPE_SPLIT_HALF, "interleaved": ROPE_INTERLEAVED,
+          "partial": ROPE_PARTIAL}
 
 STATUS = {0: "DIT_OK", -1: "DIT_EINVAL", -2: "DIT_ESHAPE", -3: "DIT_EDTYPE", -4: "DIT_EALIGN",
           -5: "DIT_EWORKSPACE", -6: "DIT_EUNSUPPORTED", -7: "DIT_EHIP"}
@@ -35,13 +36,13 @@ class DitConfig(ctypes.Structure):
                 ("rank", c_int32), ("grid", c_int32), ("rope", c_int32),
                 ("rope_axes", c_int32 * 3), ("rope_theta", c_double), ("eps", c_float),
                 ("qk_eps", c_float), ("temb_freq", c_int32), ("temb_hidden", c_int32),
-                ("t_scale", c_float)]
+                ("t_scale", c_float), ("adaln_shared", c_int32)]
 
 
 WEIGHT_FIELDS = ["norm1", "norm2", "ln1_b", "ln2_b", "post_attn_norm", "post_ffn_norm",
                  "w_qkv", "w_out", "w_fc1", "w_fc2", "b_qkv", "b_out", "b_fc1", "b_fc2",
                  "q_norm", "k_norm", "adaln_basis", "adaln_bias", "adaln_table",
-                 "temb_w1", "temb_b1", "temb_w2", "temb_b2", "ada_w", "ada_b"]
+                 "temb_w1", "temb_b1", "temb_w2", "temb_b2", "ada_w", "ada_b", "rope_freq"]
 
 
 class DitWeights(ctypes.Structure):
@@ -70,7 +71,8 @@ class DitMmh3Model(ctypes.Structure):
                 ("video_patch_w", c_void_p), ("video_patch_b", c_void_p),
                 ("audio_patch_w", c_void_p), ("audio_patch_b", c_void_p),
                 ("shift_video", c_double), ("shift_audio", c_double),
-                ("cond_aug", c_double), ("cond_aug_audio", c_double)]
+                ("cond_aug", c_double), ("cond_aug_audio", c_double),
+                ("audio_slope_rescale", c_int32)]
 
 
 class DitError(RuntimeError):
@@ -199,7 +201,7 @@ def resolve_sigmas(plan: Sequence[tuple]) -> List[float]:
 def make_config(spec) -> DitConfig:
     """DitConfig from any object with the block-shape attributes (variant,
     dtype, D, H, hd, F, slots, tags, rank, grid, rope, rope_axes, rope_theta,
-    eps, qk_eps, temb_freq, temb_hidden, t_scale)."""
+    eps, qk_eps, temb_freq, temb_hidden, t_scale; optional adaln_shared)."""
     c = DitConfig()
     c.variant = _VARIANTS[spec.variant] if isinstance(spec.variant, str) else int(spec.variant)
     c.dtype = _DTYPES[spec.dtype] if isinstance(spec.dtype, str) else int(spec.dtype)
@@ -211,6 +213,7 @@ def make_config(spec) -> DitConfig:
     c.rope_theta = spec.rope_theta
     c.eps, c.qk_eps = spec.eps, spec.qk_eps
     c.temb_freq, c.temb_hidden, c.t_scale = spec.temb_freq, spec.temb_hidden, spec.t_scale
+    c.adaln_shared = int(getattr(spec, "adaln_shared", 0))
     return c
 
 
@@ -458,12 +461,15 @@ def rms_norm(x, g, eps: float, out=None, stream=None):
 class Mmh3Model:
     """The MMH3 denoise evaluation over prepared pieces: blocks (Block with a
     DIT_MMH3 config), video/audio heads (Block with DIT_FINAL configs) and the
-    patch projections (device tensors [D, 4C] / [D, Ca] in the blocks' dtype)."""
+    patch projections (device tensors [D, 4C] / [D, Ca] in the blocks' dtype).
+    ``audio_slope_rescale`` returns the audio velocity multiplied by
+    d(sigma_a)/d(sigma_v) instead of unscaled."""
 
     def __init__(self, blocks: Sequence["Block"], head_video: "Block", head_audio: Optional["Block"],
                  latent_c: int, audio_c: int, video_patch_w, video_patch_b=None,
                  audio_patch_w=None, audio_patch_b=None, shift_video: float = 12.0,
-                 shift_audio: float = 3.0, cond_aug: float = 0.999, cond_aug_audio: float = 1.0):
+                 shift_audio: float = 3.0, cond_aug: float = 0.999, cond_aug_audio: float = 1.0,
+                 audio_slope_rescale: bool = False):
         self.blocks, self.head_video, self.head_audio = list(blocks), head_video, head_audio
         self._preps = (c_void_p * len(self.blocks))(*[b.prepared.data_ptr() for b in self.blocks])
         self._keep = (video_patch_w, video_patch_b, audio_patch_w, audio_patch_b)
@@ -481,6 +487,7 @@ class Mmh3Model:
         m.audio_patch_w, m.audio_patch_b = _ptr(audio_patch_w), _ptr(audio_patch_b)
         m.shift_video, m.shift_audio = shift_video, shift_audio
         m.cond_aug, m.cond_aug_audio = cond_aug, cond_aug_audio
+        m.audio_slope_rescale = int(bool(audio_slope_rescale))
         self._m = m
         self._ws = None
 

@@ -49,7 +49,10 @@ class BlockSpec:
     tags: int = 3  # modality tags T (mmh3)
     rank: int = 24
     grid: int = 1025
-    rope: str = "none"  # "none" | "split_half" | "interleaved"
+    rope: str = "none"  # "none" | "split_half" | "interleaved" | "partial"
+    # partial: the checkpoint form, k = rope_axes[0] / 2 frequencies (weight
+    # "rope_freq") shared by the three axes, head dims from 3 * rope_axes[0] on
+    # unrotated
     rope_axes: Tuple[int, int, int] = (0, 0, 0)
     rope_theta: float = 10000.0
     eps: float = 1e-5
@@ -57,6 +60,7 @@ class BlockSpec:
     temb_freq: int = 256  # zimage sinusoid width
     temb_hidden: int = 1024  # zimage timestep MLP width
     t_scale: float = 1000.0
+    adaln_shared: int = 0  # mmh3 / final: one slot's basis rows used at every slot
 
     @property
     def chunks(self) -> int:
@@ -254,11 +258,16 @@ def weight_shapes(spec: BlockSpec) -> List[Tuple[str, Tuple[int, ...], str]]:
     """(name, shape, init) for every weight tensor, in a fixed order.
 
     init: "lin" = N(0, 0.02) GEMM weight (bf16-rounded in bf16 blocks),
-    "vec" = N(0, 0.02) fp32, "gain" = 1 + N(0, 0.02) fp32, "table" = N(0, 1).
+    "vec" = N(0, 0.02) fp32, "gain" = 1 + N(0, 0.02) fp32, "table" = N(0, 1),
+    "freq" = the k frequencies theta^(-m/k), m < k (fp32; a checkpoint's shared
+    RoPE frequency vector).
     """
     D, H, hd, F = spec.D, spec.H, spec.hd, spec.F
+    extra = []
+    if spec.rope == "partial":
+        extra = [("rope_freq", (spec.rope_axes[0] // 2,), "freq")]
     if spec.variant == "mmh3":
-        R = spec.slots * spec.tags * 6 * D
+        R = (1 if spec.adaln_shared else spec.slots) * spec.tags * 6 * D
         return [
             ("norm1", (D,), "gain"), ("norm2", (D,), "gain"),
             ("w_qkv", (3 * D, D), "lin"), ("w_out", (D, D), "lin"),
@@ -266,9 +275,9 @@ def weight_shapes(spec: BlockSpec) -> List[Tuple[str, Tuple[int, ...], str]]:
             ("w_fc1", (2 * F, D), "lin"), ("w_fc2", (D, F), "lin"),
             ("adaln_basis", (R, spec.rank), "vec"), ("adaln_bias", (R,), "vec"),
             ("adaln_table", (spec.grid, spec.rank), "table"),
-        ]
+        ] + extra
     if spec.variant == "final":  # output head: F = output width, tags = 1
-        R = spec.slots * spec.tags * 2 * D
+        R = (1 if spec.adaln_shared else spec.slots) * spec.tags * 2 * D
         return [
             ("norm1", (D,), "gain"), ("w_fc1", (F, D), "lin"), ("b_fc1", (F,), "vec"),
             ("adaln_basis", (R, spec.rank), "vec"), ("adaln_bias", (R,), "vec"),
@@ -280,7 +289,7 @@ def weight_shapes(spec: BlockSpec) -> List[Tuple[str, Tuple[int, ...], str]]:
             ("w_qkv", (3 * D, D), "lin"), ("w_out", (D, D), "lin"),
             ("q_norm", (hd,), "gain"), ("k_norm", (hd,), "gain"),
             ("w_fc1", (2 * F, D), "lin"), ("w_fc2", (D, F), "lin"),
-        ]
+        ] + extra
     if spec.variant == "siglip":
         return [
             ("ln1_w", (D,), "gain"), ("ln1_b", (D,), "vec"),
@@ -339,6 +348,9 @@ def make_weights(spec: BlockSpec, seed: int) -> Dict[str, np.ndarray]:
             a = np.float32(1.0) + z * np.float32(0.02)
         elif init == "table":
             a = z
+        elif init == "freq":
+            k = shape[0]
+            a = np.float64(spec.rope_theta) ** (-np.arange(k, dtype=np.float64) / k)
         else:  # pragma: no cover
             raise ValueError(init)
         out[name] = np.ascontiguousarray(a, dtype=np.float32)

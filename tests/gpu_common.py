@@ -26,6 +26,16 @@ def ws_view(ws, off: int, dtype, shape):
     return ws[off:off + nbytes].view(dtype).reshape(shape)
 
 
+def partial_rope_dims(hd: int, k: int) -> np.ndarray:
+    """The library's documented head-dim order of q and k under the partial
+    RoPE: stored dim d holds the page's dim pi[d] (P = 3k rotated pairs, the
+    rotated halves moved to (j, j + hd/2), the unrotated dims to the pairs
+    between)."""
+    P, h = 3 * k, hd // 2
+    d = np.arange(hd)
+    return np.where(d < P, d, np.where(d < h, d + P, np.where(d < h + P, d - (h - P), d)))
+
+
 def act_dtype(spec):
     import torch
     return torch.bfloat16 if spec.dtype == "bf16" else torch.float32
@@ -75,6 +85,12 @@ def run_gpu(spec, wl, dit, out_alias=False, seq_starts=None, mods_in=None):
     # q carries log2(e) * hd^-1/2 (the attention kernel works in base 2)
     st["q"] = f64(ws_view(ws, L.q, ad, (H, ldn, hd))[:, :n]) * (math.sqrt(hd) / math.log2(math.e))
     st["k"] = f64(ws_view(ws, L.k, ad, (H, ldn, hd))[:, :n])
+    if spec.rope == "partial":  # back to the page's head-dim order
+        pi = partial_rope_dims(hd, spec.rope_axes[0] // 2)
+        for name in ("q", "k"):
+            page = np.empty_like(st[name])
+            page[..., pi] = st[name]
+            st[name] = page
     st["v"] = f64(ws_view(ws, L.vt, ad, (H, hd, ldn))[:, :, :n].transpose(1, 2))
     st["o"] = f64(ws_view(ws, L.o, ad, (n, D)))
     st["x1"] = f64(ws_view(ws, L.x1, torch.float32, (n, D)))

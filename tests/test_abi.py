@@ -43,7 +43,7 @@ def test_header_functions_exported(dit):
 
 
 def test_abi_version(dit):
-    assert dit.lib.dit_abi_version() == 2
+    assert dit.lib.dit_abi_version() == 3
 
 
 def test_sigma_remap_printed_points(dit):
@@ -76,6 +76,7 @@ def _cfg(dit, **kw):
 @pytest.mark.parametrize("field,value,status", [
     ("hd", 96, -6), ("D", 2560, -2), ("dtype", 7, -3), ("variant", 9, -1), ("slots", 0, -6),
     ("slots", 9, -6), ("F", 100, -6), ("rank", 0, -6), ("grid", 1, -1), ("rope", 5, -1),
+    ("adaln_shared", -1, -1),
 ])
 def test_config_refusals(dit, field, value, status):
     c = _cfg(dit, **{field: value})
@@ -88,6 +89,41 @@ def test_rope_axes_must_sum_to_head_dim(dit):
     c = _cfg(dit)
     c.rope_axes[0] = 30
     assert dit.lib.dit_validate_config(ctypes.byref(c)) == -2
+
+
+def test_partial_rope_and_shared_adaln_configs(dit):
+    ok = _cfg(dit, rope=dit.ROPE_PARTIAL)
+    for a in range(3):
+        ok.rope_axes[a] = 32  # k = 16 shared frequencies, 96 of 128 dims rotated
+    assert dit.lib.dit_validate_config(ctypes.byref(ok)) == 0
+    # the shared frequency vector is part of the prepared weights
+    assert dit.lib.dit_prepared_size(ctypes.byref(ok)) > dit.lib.dit_prepared_size(ctypes.byref(_cfg(dit)))
+    bad = _cfg(dit, rope=dit.ROPE_PARTIAL)  # (32, 48, 48): axes differ
+    assert dit.lib.dit_validate_config(ctypes.byref(bad)) == -1
+    big = _cfg(dit, rope=dit.ROPE_PARTIAL)
+    for a in range(3):
+        big.rope_axes[a] = 44  # 3 * 44 > 128
+    assert dit.lib.dit_validate_config(ctypes.byref(big)) == -2
+    z = dit.make_config(W.spec_by_name("zimage"))
+    z.rope = dit.ROPE_PARTIAL
+    for a in range(3):
+        z.rope_axes[a] = 32
+    assert dit.lib.dit_validate_config(ctypes.byref(z)) == -6
+    sh = _cfg(dit, adaln_shared=1)
+    assert dit.lib.dit_validate_config(ctypes.byref(sh)) == 0
+    assert dit.lib.dit_prepared_size(ctypes.byref(sh)) == dit.lib.dit_prepared_size(ctypes.byref(_cfg(dit)))
+    assert dit.lib.dit_validate_config(ctypes.byref(_cfg(dit, adaln_shared=2))) == -1
+    sg = dit.make_config(W.spec_by_name("siglip"))
+    sg.adaln_shared = 1
+    assert dit.lib.dit_validate_config(ctypes.byref(sg)) == -1
+    # a partial-RoPE block needs its frequency vector
+    w = dit.DitWeights()
+    for f in ("w_qkv", "w_out", "w_fc1", "w_fc2", "norm1", "norm2", "q_norm", "k_norm",
+              "adaln_basis", "adaln_table"):
+        setattr(w, f, 256)
+    need = dit.lib.dit_prepared_size(ctypes.byref(ok))
+    assert dit.lib.dit_prepare_weights(ctypes.byref(ok), ctypes.byref(w), 256, need, None) == -1
+    assert "rope_freq" in dit.last_error()
 
 
 def test_workspace_layout_monotone(dit):

@@ -130,23 +130,30 @@ def test_rms_norm(dit):
     assert O.rel_rms(got, ref) <= 1e-6
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_mmh3_denoise_evaluation(dit, dtype):
+@pytest.mark.parametrize("dtype,compat", [("bf16", False), ("f32", False), ("bf16", True),
+                                          ("f32", True)])
+def test_mmh3_denoise_evaluation(dit, dtype, compat):
     """One whole evaluation at a small size: text, a first-frame keyframe,
     stereo audio and two video frames; two blocks with their own weights;
     video and audio heads.  Against the oracle's evaluation from the same
-    seeded pieces."""
+    seeded pieces.  ``compat``: the checkpoint forms (shared RoPE frequencies
+    over 3k pairs, one adaLN basis for every slot in blocks and heads) and the
+    audio velocity pre-multiplied by d(sigma_a)/d(sigma_v)."""
     import torch
     from synth.device import to_device
     hd = 128 if dtype == "bf16" else 64
     lay = W.build_layout(16, 2, 8, 8, 12, keyframes=[(0, 2)])
     n = lay.seq_len
     C, Ca, D = 16, 64, 256
+    rope = dict(rope="partial", rope_axes=(hd // 4,) * 3) if compat else dict(
+        rope="split_half", rope_axes=(hd // 4, hd // 8 * 3, hd // 8 * 3))
+    sh = int(compat)
     bspec = W.BlockSpec(f"model-{dtype}", "mmh3", dtype, n=n, D=D, H=D // hd, hd=hd,
-                        F=384 if dtype == "bf16" else 256, slots=3, rope="split_half",
-                        rope_axes=(hd // 4, hd // 8 * 3, hd // 8 * 3))
-    hv = W.BlockSpec("head-v", "final", dtype, n=n, D=D, H=D // hd, hd=hd, F=4 * C, slots=3, tags=1)
-    ha = W.BlockSpec("head-a", "final", dtype, n=n, D=D, H=D // hd, hd=hd, F=Ca, slots=3, tags=1)
+                        F=384 if dtype == "bf16" else 256, slots=3, adaln_shared=sh, **rope)
+    hv = W.BlockSpec("head-v", "final", dtype, n=n, D=D, H=D // hd, hd=hd, F=4 * C, slots=3, tags=1,
+                     adaln_shared=sh)
+    ha = W.BlockSpec("head-a", "final", dtype, n=n, D=D, H=D // hd, hd=hd, F=Ca, slots=3, tags=1,
+                     adaln_shared=sh)
     wblocks = [W.make_custom_workload(bspec, 8000 + i).weights for i in range(2)]
     whv = W.make_custom_workload(hv, 8100).weights
     wha = W.make_custom_workload(ha, 8101).weights
@@ -173,13 +180,15 @@ def test_mmh3_denoise_evaluation(dit, dtype):
     head_v = dit.Block(dit.make_config(hv), dev_weights(hv, whv))
     head_a = dit.Block(dit.make_config(ha), dev_weights(ha, wha))
     cu = lambda a, t=torch.float32: torch.from_numpy(a).to(t).cuda()  # noqa: E731
-    model = dit.Mmh3Model(blocks, head_v, head_a, C, Ca, cu(wv, td), cu(bv), cu(wa, td), cu(ba))
+    model = dit.Mmh3Model(blocks, head_v, head_a, C, Ca, cu(wv, td), cu(bv), cu(wa, td), cu(ba),
+                          audio_slope_rescale=compat)
     vout, aout = model.forward(lay.segments, cu(pos), cu(text), cu(video), cu(audio), [cu(cond)],
                                sigma_v)
     torch.cuda.synchronize()
     rv, ra = O.mmh3_forward(bspec, hv, ha, lay.segments, pos.astype(np.float64), text, video,
-                            audio, [cond], sigma_v, wblocks, whv, wha, wv, bv, wa, ba)
+                            audio, [cond], sigma_v, wblocks, whv, wha, wv, bv, wa, ba,
+                            audio_slope_rescale=compat)
     ev = O.rel_rms(vout.cpu().numpy(), rv)
     ea = O.rel_rms(aout.cpu().numpy(), ra)
-    log(f"[case] mmh3 evaluation {dtype} n={n}: video={ev:.2e} audio={ea:.2e}")
+    log(f"[case] mmh3 evaluation {dtype} compat={compat} n={n}: video={ev:.2e} audio={ea:.2e}")
     assert ev <= TOL[dtype] and ea <= TOL[dtype]

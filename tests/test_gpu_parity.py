@@ -118,6 +118,18 @@ def test_small_ragged(dit, variant, dtype, n, D, hd, F):
     _check(spec.name, spec, wl, dit)
 
 
+@pytest.mark.parametrize("dtype,n,hd,F", [("bf16", 333, 128, 384), ("f32", 77, 64, 384)])
+def test_small_checkpoint_rope_and_shared_adaln(dit, dtype, n, hd, F):
+    """The checkpoint forms: shared RoPE frequencies over 3k of hd/2 pairs
+    (k = hd/8: 96 of 128 dims rotated, as the page's model) and one adaLN
+    basis evaluated at both slots.  q and k are compared in the page's
+    head-dim order."""
+    d = hd // 4
+    spec = _small("mmh3", dtype, n, 256, hd, F, rope="partial", axes=(d, d, d), adaln_shared=1)
+    wl = W.make_custom_workload(spec, 1100 + n)
+    _check(spec.name, spec, wl, dit)
+
+
 def test_peakier_block_attention(dit):
     """qk-norm gains x2: logits with std ~4 instead of ~1 through the whole
     block.  (Much larger gains make the logits' own bf16 input rounding -- the

@@ -263,6 +263,43 @@ def test_rope_interleaved_is_permuted_split_half():
     np.testing.assert_allclose(got[..., 0::2], z.real, atol=1e-12)
 
 
+def test_rope_partial_angles_structure_and_full_special_case():
+    # [MMH3] rope_angles: k shared frequencies, axis-major, angle = pos[axis] * freq
+    rng = np.random.default_rng(9)
+    pos = rng.uniform(0, 600, (4, 3))
+    freq = np.exp(-rng.uniform(0, 9, 16))
+    ang = O.rope_angles_shared(pos, freq)
+    assert ang.shape == (4, 48)
+    unit = O.rope_angles_shared(np.array([[1.0, 2.0, 3.0]]), np.ones(16))
+    np.testing.assert_array_equal(unit[0], np.repeat([1.0, 2.0, 3.0], 16))
+    # frequencies theta^(-m/k) and 6k = hd: the per-axis table with three equal axes
+    k, theta = 16, 1e4
+    f = theta ** (-np.arange(k) / k)
+    np.testing.assert_allclose(O.rope_angles_shared(pos, f), O.rope_angles(pos, (32, 32, 32), theta),
+                               rtol=1e-14)
+
+
+def test_rope_partial_rotates_3k_pairs_and_keeps_the_tail():
+    # pairs (j, j + 48) turn as complex numbers; head dims 96..127 are untouched
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((2, 5, 128))
+    ang = O.rope_angles_shared(rng.uniform(0, 600, (5, 3)), np.exp(-rng.uniform(0, 9, 16)))
+    y = O.rope_rotate(x, ang[None], "split_half")
+    z = (x[..., :48] + 1j * x[..., 48:96]) * np.exp(1j * ang)[None]
+    np.testing.assert_allclose(y[..., :48], z.real, atol=1e-12)
+    np.testing.assert_allclose(y[..., 48:96], z.imag, atol=1e-12)
+    np.testing.assert_array_equal(y[..., 96:], x[..., 96:])
+
+
+def test_rope_for_selects_the_layout():
+    spec = W.small_spec(W.spec_by_name("t2va"), rope="partial", rope_axes=(32, 32, 32))
+    pos = np.array([[1.0, 2.0, 3.0]])
+    ang, mode = O.rope_for(spec, pos, {"rope_freq": np.ones(16)})
+    assert mode == "split_half" and ang.shape == (1, 48)
+    ang, mode = O.rope_for(W.spec_by_name("t2va"), pos, {})
+    assert mode == "split_half" and ang.shape == (1, 64)
+
+
 # ------------------------------------------------------------- attention ----
 
 def _brute_attention(q, k, v, scale):
@@ -531,7 +568,10 @@ def _tiny_mmh3_spec(n=7):
 
 
 def _brute_mmh3(spec, x, rows, pos, sigmas, w):
-    """Scalar loops, written independently of the oracle's array code."""
+    """Scalar loops, written independently of the oracle's array code.
+    ``spec.rope == "partial"``: the k frequencies of w["rope_freq"] serve every
+    axis, pair (j, j + 3k), dims from 6k on unrotated.  ``spec.adaln_shared``:
+    one slot's basis rows at every slot."""
     D, H, hd, F = spec.D, spec.H, spec.hd, spec.F
     n = len(x)
     T, E = spec.tags, 6
@@ -548,6 +588,8 @@ def _brute_mmh3(spec, x, rows, pos, sigmas, w):
             for e in range(E):
                 for d in range(D):
                     j = ((s * T + tag) * E + e) * D + d
+                    if spec.adaln_shared:
+                        j = (tag * E + e) * D + d
                     mods[(s * T + tag, e, d)] = w["adaln_bias"][j] + sum(
                         w["adaln_basis"][j][k] * c[k] for k in range(spec.rank))
 
@@ -560,9 +602,14 @@ def _brute_mmh3(spec, x, rows, pos, sigmas, w):
         return [sum(W_[r][c] * vec[c] for c in range(len(vec))) for r in range(r0, r1)]
 
     freqs = []
-    for a, d in enumerate(spec.rope_axes):
-        for m in range(d // 2):
-            freqs.append((a, spec.rope_theta ** (-2.0 * m / d)))
+    if spec.rope == "partial":
+        for a in range(3):
+            for f in w["rope_freq"]:
+                freqs.append((a, float(f)))
+    else:
+        for a, d in enumerate(spec.rope_axes):
+            for m in range(d // 2):
+                freqs.append((a, spec.rope_theta ** (-2.0 * m / d)))
     P = len(freqs)
 
     def rope(vec, i):
@@ -626,6 +673,68 @@ def test_mmh3_block_brute_force_tiny():
     sel = np.array([5, 0, 3])
     np.testing.assert_allclose(O.mmh3_block(spec, x, rows, pos, sig, w, qrows=sel)["out"],
                                got[sel], rtol=1e-12, atol=1e-12)
+
+
+def test_mmh3_block_brute_force_tiny_compat_modes():
+    # partial RoPE (k = 1: 3 of 4 pairs turn, dims 6, 7 stay) and a shared adaLN basis
+    spec = W.small_spec(_tiny_mmh3_spec(7), rope="partial", rope_axes=(2, 2, 2), adaln_shared=1)
+    wl = W.make_custom_workload(spec, 21, sigmas=[0.37, 0.81])
+    w = {k: v.astype(np.float64) for k, v in wl.weights.items()}
+    assert w["adaln_basis"].shape[0] == spec.tags * 6 * spec.D and w["rope_freq"].shape == (1,)
+    w["adaln_basis"] = w["adaln_basis"] * 10.0
+    w["rope_freq"] = np.array([0.37])
+    for k in ("w_qkv", "w_out", "w_fc1", "w_fc2"):
+        w[k] = w[k] * 10.0
+    x, pos = wl.x.astype(np.float64), wl.pos.astype(np.float64)
+    got = O.mmh3_block(spec, x, wl.rows, pos, [0.37, 0.81], w)
+    want = _brute_mmh3(spec, x, wl.rows, pos, [0.37, 0.81], w)
+    np.testing.assert_allclose(got["out"], want, rtol=1e-11, atol=1e-11)
+    # unrotated dims: q's last two dims are the qk-normed projection as is
+    proj = (got["xn"] @ w["w_qkv"][:spec.D].T).reshape(-1, spec.H, spec.hd).transpose(1, 0, 2)
+    q_plain = O.rms_norm(proj, w["q_norm"], spec.qk_eps)
+    np.testing.assert_array_equal(got["q"][..., 6:], q_plain[..., 6:])
+    # relative positions only
+    b = O.mmh3_block(spec, x, wl.rows, pos + np.array([5.0, -2.5, 9.0]), [0.37, 0.81], w)
+    np.testing.assert_allclose(b["out"], got["out"], rtol=1e-11, atol=1e-12)
+
+
+def test_shared_adaln_is_the_slot_major_basis_repeated():
+    rng = np.random.default_rng(11)
+    T, E, D, r = 3, 6, 8, 5
+    B = rng.standard_normal((T * E * D, r))
+    b = rng.standard_normal(T * E * D)
+    tab = rng.standard_normal((9, r))
+    ts = [0.3, 0.999]
+    shared = O.adaln_mods(B, b, tab, ts, T, E, D, shared=True)
+    tiled = O.adaln_mods(np.tile(B, (2, 1)), np.tile(b, 2), tab, ts, T, E, D)
+    np.testing.assert_array_equal(shared, tiled)
+    # equal timesteps give equal slot blocks
+    same = O.adaln_mods(B, b, tab, [0.6, 0.6], T, E, D, shared=True)
+    np.testing.assert_array_equal(same[:T], same[T:])
+
+
+def test_mmh3_forward_audio_slope_rescale_closed_form():
+    # the pre-multiplied audio velocity is the unscaled one times d(sigma_a)/d(sigma_v),
+    # which for the 12 -> 3 remap sigma / (4 - 3 sigma) is 4 / (4 - 3 sigma)^2
+    lay = W.build_layout(3, 1, 4, 4, 2)
+    n, D, C, Ca = lay.seq_len, 16, 4, 4
+    bs = W.BlockSpec("fwd-tiny", "mmh3", "f32", n=n, D=D, H=2, hd=8, F=12, slots=2, rank=3,
+                     grid=9, rope="split_half", rope_axes=(2, 2, 4), rope_theta=100.0)
+    hv = W.BlockSpec("hv", "final", "f32", n=n, D=D, H=2, hd=8, F=4 * C, slots=2, tags=1, rank=3, grid=9)
+    ha = W.BlockSpec("ha", "final", "f32", n=n, D=D, H=2, hd=8, F=Ca, slots=2, tags=1, rank=3, grid=9)
+    rng = np.random.default_rng(12)
+    wb = [W.make_custom_workload(bs, 40).weights]
+    whv, wha = W.make_custom_workload(hv, 41).weights, W.make_custom_workload(ha, 42).weights
+    wv, wa = 0.1 * rng.standard_normal((D, 4 * C)), 0.1 * rng.standard_normal((D, Ca))
+    text = rng.standard_normal((3, D))
+    video, audio = rng.standard_normal((C, 1, 4, 4)), rng.standard_normal((Ca, 2, 2))
+    sv = 0.63
+    args = (bs, hv, ha, lay.segments, lay.pos, text, video, audio, [], sv, wb, whv, wha, wv, None,
+            wa, None)
+    v0, a0 = O.mmh3_forward(*args)
+    v1, a1 = O.mmh3_forward(*args, audio_slope_rescale=True)
+    np.testing.assert_array_equal(v1, v0)
+    np.testing.assert_allclose(a1, a0 * 4.0 / (4.0 - 3.0 * sv) ** 2, rtol=1e-14)
 
 
 def test_mmh3_block_permutation_equivariant():

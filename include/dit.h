@@ -61,10 +61,18 @@ enum {
                      ([MMH3] refine_text: block_forward with no mods): RMSNorm pre-norms,
                      qk-RMSNorm, plain residuals, SwiGLU; RoPE as configured (the
                      refiner itself is unrotated: rope = NONE); no sigmas          */
-  DIT_FINAL = 4    /* the MMH3 output head, not a block: RMSNorm, a single-modality
+  DIT_FINAL = 4,   /* the MMH3 output head, not a block: RMSNorm, a single-modality
                      adaLN of two chunks (shift, scale) per timestep slot, a linear
                      head and the sign flip (tags = 1, F = output width; run by
                      dit_final_forward) ([MMH3] MiniMaxH3::forward, heads)        */
+  DIT_ZCONTEXT = 5, /* the Z-Image block without modulation, as its context (caption)
+                     refiner runs it ([ZIMG] TransformerBlock.Forward with no adaLN):
+                     x1 = x + RMSNorm(Attn(RMSNorm(x)); post_attn_norm), out = x1 +
+                     RMSNorm(FFN(RMSNorm(x1)); post_ffn_norm); no sigmas          */
+  DIT_ZFINAL = 6   /* the Z-Image final layer, not a block ([ZIMG] FinalLayer.Forward):
+                     temb from the timestep MLP, scale = ada_w silu(temb) + ada_b,
+                     out = W (LayerNorm_noaffine(h; eps) * (1 + scale)) + b (F = output
+                     width; run by dit_final_forward; no sign flip)               */
 };
 
 /* Arithmetic type of GEMM operands, attention inputs and the intermediates
@@ -124,6 +132,9 @@ typedef struct dit_config {
  *           temb_w2 [Tf, Th] + temb_b2; ada_w [4D, Tf] + ada_b [4D]
  *           (chunks scale_msa, gate_msa, scale_mlp, gate_mlp).
  *   REFINER: as MMH3 without the adaLN tensors.
+ *   ZCONTEXT: as ZIMAGE without the timestep and adaLN tensors.
+ *   ZFINAL: w_fc1 [F, D] output projection + b_fc1 [F] (NULL = 0); temb_w1,
+ *           temb_b1, temb_w2, temb_b2 as ZIMAGE; ada_w [D, Tf] + ada_b [D].
  *   rope_freq [rope_axes[0] / 2]: the shared frequency vector of DIT_ROPE_PARTIAL
  *           (MMH3, REFINER), NULL otherwise.
  *   adaln_shared = 1: adaln_basis [T*E*D, r] and adaln_bias [T*E*D] (one slot).
@@ -261,7 +272,10 @@ dit_status dit_block_forward_mods(const dit_config* cfg, const void* prepared, c
  * [S, 2D] of the head's own rank-r basis,
  *   out_i = -(W (RMSNorm(h_i; g, eps) * (1 + m[r, D:2D]) + m[r, 0:D]) + b)
  * for r = rows[i] (the token's timestep slot; NULL = 0).  h: device fp32
- * [n, D]; out: device fp32 [n, F]; workspace: dit_workspace_size(cfg, n). */
+ * [n, D]; out: device fp32 [n, F]; workspace: dit_workspace_size(cfg, n).
+ * With a DIT_ZFINAL config (the Z-Image final layer, one sigma = its t):
+ *   out_i = W (LayerNorm_noaffine(h_i; eps) * (1 + scale)) + b,
+ *   scale = ada_w silu(temb(t * t_scale)) + ada_b  (rows unused). */
 dit_status dit_final_forward(const dit_config* cfg, const void* prepared, const float* h,
                              int32_t n, const int32_t* rows, const double* sigmas,
                              int32_t n_sigmas, float* out, void* workspace, size_t ws_bytes,
@@ -289,6 +303,13 @@ dit_status dit_unpatchify_video(const float* rows, int32_t C, int32_t T, int32_t
                                 float* x, void* stream);
 dit_status dit_pack_audio(int32_t dtype, const float* x, int32_t C, int32_t T, void* rows,
                           void* stream);
+/* The Z-Image patch layout ([ZIMG] PatchifyLatents / UnpatchifyLatents):
+ * image device fp32 [C, H, W] (H, W even) <-> rows [(H/2)*(W/2), 4C], row
+ * (h2, w2), column (p*2 + q)*C + c = x[c, 2*h2 + p, 2*w2 + q] (channel fastest). */
+dit_status dit_patchify_image(int32_t dtype, const float* x, int32_t C, int32_t H, int32_t W,
+                              void* rows, void* stream);
+dit_status dit_unpatchify_image(const float* rows, int32_t C, int32_t H, int32_t W, float* x,
+                                void* stream);
 dit_status dit_unpack_audio(const float* rows, int32_t C, int32_t T, float* x, void* stream);
 
 /* One denoise evaluation of the MMH3 model ([MMH3] MiniMaxH3::forward):
@@ -348,6 +369,60 @@ dit_status dit_mmh3_forward(const dit_mmh3_model* m, const dit_segment* segs, in
                             int32_t H, int32_t W, const float* audio, int32_t Ta,
                             const float* const* cond, double sigma_v, float* video_out,
                             float* audio_out, void* workspace, size_t ws_bytes, void* stream);
+
+/* The Z-Image transformer ([ZIMG] Transformer.Forward / ForwardWithCache). */
+typedef struct dit_zimage_model {
+  const dit_config* block;            /* DIT_ZIMAGE: main layers and noise refiners      */
+  const void* const* layers;          /* n_layers prepared main layers (host array)      */
+  int32_t n_layers;
+  const void* const* noise_refiners;  /* image tokens only, modulated                    */
+  int32_t n_noise_refiners;
+  const dit_config* context;          /* DIT_ZCONTEXT, same D/H/hd/F as block            */
+  const void* const* context_refiners;/* caption tokens only, unmodulated                */
+  int32_t n_context_refiners;
+  const dit_config* final_layer;      /* DIT_ZFINAL, F = 4 * in_channels                 */
+  const void* final_w;
+  int32_t in_channels, cap_dim;
+  const void* x_embed_w;              /* [D, 4 * in_channels] in the block dtype         */
+  const float* x_embed_b;             /* [D] or NULL                                     */
+  const float* cap_norm;              /* [cap_dim] RMSNorm gain of the caption embedder  */
+  float cap_eps;                      /* its epsilon (1e-6)                              */
+  const void* cap_embed_w;            /* [D, cap_dim] in the block dtype                 */
+  const float* cap_embed_b;           /* [D] or NULL                                     */
+} dit_zimage_model;
+
+/* Step-level reuse state ([ZIMG] ForwardWithCache), caller-owned.  caption:
+ * device fp32 [cap_len, D], the embedded and refined caption, computed on the
+ * first call and reused while caption_valid (it depends on neither t nor the
+ * latents).  shallow: device fp32 [img_len + cap_len, D], the unified stream
+ * after the first `layers` main layers, stored on refresh steps (step %
+ * interval == 0) and reused on the others; a reused step skips the image
+ * embedding, the noise refiners and those layers, whose results the stored
+ * stream replaces.  The valid flags are set by dit_zimage_forward when it
+ * enqueues the stores; set both to 0 for a new generation.  Calls that share
+ * a cache must run in stream order. */
+typedef struct dit_zimage_cache {
+  float* caption;
+  float* shallow;
+  int32_t layers;    /* shallow layers, 0 <= layers <= n_layers (0: no layer reuse) */
+  int32_t interval;  /* >= 1 */
+  int32_t caption_valid, shallow_valid;
+} dit_zimage_cache;
+
+/* Workspace bytes of dit_zimage_forward (0 if invalid). */
+size_t dit_zimage_workspace_size(const dit_zimage_model* m, int32_t H, int32_t W, int32_t cap_len);
+
+/* latents: device fp32 [in_channels, H, W]; cap_feats: device fp32 [cap_len,
+ * cap_dim]; pos: device fp32 [img_len + cap_len, 3], image tokens first (the
+ * unified order; the refiners read their own parts); t: the timestep (the
+ * blocks embed t * t_scale); cache: NULL computes everything.  out: device
+ * fp32 [in_channels, H, W], the final layer's output unpatchified.  The
+ * embedding GEMMs need 4 * in_channels and cap_dim to be multiples of 64
+ * (bf16) or 16 (fp32); cap_dim <= 4096. */
+dit_status dit_zimage_forward(const dit_zimage_model* m, const float* latents, int32_t H, int32_t W,
+                              const float* cap_feats, int32_t cap_len, const float* pos, double t,
+                              int32_t step, dit_zimage_cache* cache, float* out, void* workspace,
+                              size_t ws_bytes, void* stream);
 
 /* RMSNorm of fp32 rows into fp32 rows: out_i = x_i / sqrt(mean(x_i^2) + eps) * g
  * (e.g. the token refiner's final norm, [MMH3] refine_text).  D % 4 == 0,

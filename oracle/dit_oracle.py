@@ -664,6 +664,117 @@ def zimage_block(spec, x: np.ndarray, pos: np.ndarray, t: float, w: Dict[str, np
                 out=out)
 
 
+def zimage_context_block(spec, x: np.ndarray, pos: np.ndarray, w: Dict[str, np.ndarray],
+                         qrows: Optional[np.ndarray] = None,
+                         seq_starts: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """The Z-Image block without modulation, as the context (caption) refiner
+    runs it ([ZIMG] ``TransformerBlock.Forward`` with no adaLN): x1 = x +
+    RMSNorm(Attn(RMSNorm(x; norm1)); post_attn_norm); out = x1 +
+    RMSNorm(FFN(RMSNorm(x1; norm2)); post_ffn_norm).  Stages as zimage_block
+    without mods."""
+    D, H, hd, F = spec.D, spec.H, spec.hd, spec.F
+    n = x.shape[0]
+    x = np.asarray(x, F64)
+    sel = _sel(qrows, n)
+    xn = rms_norm(x, w["norm1"], spec.eps)
+    wq, wk, wv = (w["w_qkv"][i * D:(i + 1) * D] for i in range(3))
+    ang = rope_angles(pos, spec.rope_axes, spec.rope_theta)
+    k = rope_rotate(rms_norm(_heads(_lin(xn, wk), H, hd), w["k_norm"], spec.qk_eps),
+                    ang[None], spec.rope)
+    v = _heads(_lin(xn, wv), H, hd)
+    q = rope_rotate(rms_norm(_heads(_lin(xn[sel], wq), H, hd), w["q_norm"], spec.qk_eps),
+                    ang[sel][None], spec.rope)
+    o = _merge(_attend(q, k, v, 1.0 / math.sqrt(hd), sel, seq_starts))
+    y = _lin(o, w["w_out"])
+    x1 = x[sel] + rms_norm(y, w["post_attn_norm"], spec.eps)
+    xn2 = rms_norm(x1, w["norm2"], spec.eps)
+    gu = _lin(xn2, w["w_fc1"])
+    a = silu(gu[:, :F]) * gu[:, F:]
+    y2 = _lin(a, w["w_fc2"])
+    out = x1 + rms_norm(y2, w["post_ffn_norm"], spec.eps)
+    return dict(xn=xn, q=q, k=k, v=v, o=o, y=y, x1=x1, xn2=xn2, a=a, y2=y2, out=out)
+
+
+def zimage_final_layer(spec, h: np.ndarray, t: float, w: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+    """[ZIMG] ``FinalLayer.Forward``: scale = W_a silu(temb) + b_a with temb
+    the timestep MLP's output at t * t_scale; out = W (LayerNorm without
+    affine(h; eps) * (1 + scale)) + b."""
+    D = spec.D
+    e = timestep_embedding(t * spec.t_scale, spec.temb_freq)
+    temb = _lin(silu(_lin(e[None], w["temb_w1"], w["temb_b1"])), w["temb_w2"], w["temb_b2"])
+    scale = _lin(silu(temb), w["ada_w"], w["ada_b"])
+    hn = layer_norm(np.asarray(h, F64), np.ones(D), np.zeros(D), spec.eps) * (1.0 + scale)
+    return dict(mods=scale, xn=hn, out=_lin(hn, w["w_fc1"], w.get("b_fc1")))
+
+
+def patchify_image(x: np.ndarray) -> np.ndarray:
+    """[C, H, W] -> [(H/2)*(W/2), 4C]: row (h2, w2), column (p*2 + q)*C + c =
+    x[c, 2*h2 + p, 2*w2 + q] ([ZIMG] ``PatchifyLatents``, channel fastest)."""
+    C, H, W = x.shape
+    out = np.empty(((H // 2) * (W // 2), 4 * C), dtype=x.dtype)
+    for h2 in range(H // 2):
+        for w2 in range(W // 2):
+            r = h2 * (W // 2) + w2
+            for p in range(2):
+                for q in range(2):
+                    out[r, (p * 2 + q) * C:(p * 2 + q + 1) * C] = x[:, 2 * h2 + p, 2 * w2 + q]
+    return out
+
+
+def unpatchify_image(rows: np.ndarray, C: int, H: int, W: int) -> np.ndarray:
+    """The inverse of patchify_image ([ZIMG] ``UnpatchifyLatents``)."""
+    x = np.empty((C, H, W), dtype=rows.dtype)
+    for h2 in range(H // 2):
+        for w2 in range(W // 2):
+            r = h2 * (W // 2) + w2
+            for p in range(2):
+                for q in range(2):
+                    x[:, 2 * h2 + p, 2 * w2 + q] = rows[r, (p * 2 + q) * C:(p * 2 + q + 1) * C]
+    return x
+
+
+def zimage_forward(bspec, cspec, fspec, latents, cap_feats, pos, t: float, w_layers, w_noise,
+                   w_context, w_final, x_embed_w, x_embed_b, cap_norm, cap_eps, cap_embed_w,
+                   cap_embed_b, step: int = 0, cache: Optional[dict] = None) -> np.ndarray:
+    """The Z-Image transformer ([ZIMG] ``Transformer.Forward``, and with
+    ``cache`` ``ForwardWithCache``): image patches through the x embedder and
+    the noise refiners (image positions), the caption through RMSNorm, the cap
+    embedder and the context refiners (caption positions), the main layers over
+    [image | caption], the final layer on the image tokens, unpatchified.
+
+    ``cache``: {"layers": k, "interval": m} plus the state this function keeps
+    in it across steps: the refined caption (computed once) and the output of
+    each of the first k main layers, stored on refresh steps (step % m == 0)
+    and read in place of computing the layer on the other steps."""
+    C, H, W = latents.shape
+    ni = (H // 2) * (W // 2)
+    pos = np.asarray(pos, F64)
+    x = linear(patchify_image(np.asarray(latents, F64)), x_embed_w, x_embed_b)
+    if cache is not None and cache.get("caption") is not None:
+        cap = cache["caption"]
+    else:
+        cap = linear(rms_norm(np.asarray(cap_feats, F64), cap_norm, cap_eps), cap_embed_w, cap_embed_b)
+        for w in w_context:
+            cap = zimage_context_block(cspec, cap, pos[ni:], w)["out"]
+        if cache is not None:
+            cache["caption"] = cap
+    for w in w_noise:
+        x = zimage_block(bspec, x, pos[:ni], t, w)["out"]
+    u = np.concatenate([x, cap], axis=0)
+    refresh = cache is None or step % cache["interval"] == 0
+    stored = cache.setdefault("outs", {}) if cache is not None else {}
+    k = cache["layers"] if cache is not None else 0
+    for i, w in enumerate(w_layers):
+        if i < k and not refresh and i in stored:
+            u = stored[i]
+        else:
+            u = zimage_block(bspec, u, pos, t, w)["out"]
+            if i < k and refresh:
+                stored[i] = u
+    out = zimage_final_layer(fspec, u[:ni], t, w_final)["out"]
+    return unpatchify_image(out, C, H, W)
+
+
 def block(spec, x, rows, pos, sigmas, w, qrows=None, seq_starts=None,
           mods=None) -> Dict[str, np.ndarray]:
     """Dispatch on the block variant.  ``sigmas``: slot sigmas (mmh3) or
@@ -677,6 +788,8 @@ def block(spec, x, rows, pos, sigmas, w, qrows=None, seq_starts=None,
         return zimage_block(spec, x, pos, sigmas[0] if sigmas else None, w, qrows, seq_starts, mods)
     if spec.variant == "refiner":
         return refiner_block(spec, x, pos, w, qrows, seq_starts)
+    if spec.variant == "zcontext":
+        return zimage_context_block(spec, x, pos, w, qrows, seq_starts)
     raise ValueError(spec.variant)
 
 
@@ -697,6 +810,7 @@ __all__ = [
     "sample_ranges",
     "attention_packed", "mmh3_block", "refiner_block", "linear", "final_layer", "stack",
     "patchify_video", "unpatchify_video", "pack_audio", "unpack_audio", "mmh3_forward",
-    "siglip_layer", "timestep_embedding", "zimage_mods", "zimage_block", "block",
+    "siglip_layer", "timestep_embedding", "zimage_mods", "zimage_block", "zimage_context_block",
+    "zimage_final_layer", "patchify_image", "unpatchify_image", "zimage_forward", "block",
     "rel_rms",
 ]

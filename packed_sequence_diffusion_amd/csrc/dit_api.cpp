@@ -37,17 +37,24 @@ int chunks(const dit_config* c) {
     case DIT_MMH3: return 6;
     case DIT_ZIMAGE: return 4;
     case DIT_FINAL: return 2;
+    case DIT_ZFINAL: return 1;
     default: return 0;
   }
 }
 // rank-r basis variants: modulation rows from the interpolated timestep table
 bool basis_mods(const dit_config* c) { return c->variant == DIT_MMH3 || c->variant == DIT_FINAL; }
+// modulation rows from the sinusoidal timestep MLP (one row)
+bool temb_variant(const dit_config* c) { return c->variant == DIT_ZIMAGE || c->variant == DIT_ZFINAL; }
+// output heads, run by dit_final_forward
+bool head(const dit_config* c) { return c->variant == DIT_FINAL || c->variant == DIT_ZFINAL; }
+// Z-Image sandwich-norm blocks (modulated or not)
+bool zsandwich(const dit_config* c) { return c->variant == DIT_ZIMAGE || c->variant == DIT_ZCONTEXT; }
 int mod_rows(const dit_config* c) {
-  return basis_mods(c) ? c->slots * c->tags : (c->variant == DIT_ZIMAGE ? 1 : 0);
+  return basis_mods(c) ? c->slots * c->tags : (temb_variant(c) ? 1 : 0);
 }
 bool swiglu(const dit_config* c) { return c->variant != DIT_SIGLIP; }
 // modulated variants (adaLN rows, sigmas)
-bool has_mods(const dit_config* c) { return basis_mods(c) || c->variant == DIT_ZIMAGE; }
+bool has_mods(const dit_config* c) { return basis_mods(c) || temb_variant(c); }
 int fc1_rows(const dit_config* c) { return swiglu(c) ? 2 * c->F : c->F; }
 // pair layout the kernels apply: the partial rotation runs as split-half over
 // head dims permuted at weight preparation
@@ -55,16 +62,16 @@ int rope_pairs(const dit_config* c) { return c->rope == DIT_ROPE_PARTIAL ? DIT_R
 
 dit_status check_config(const dit_config* c) {
   if (!c) return fail(DIT_EINVAL, "config is NULL");
-  if (c->variant < DIT_MMH3 || c->variant > DIT_FINAL)
+  if (c->variant < DIT_MMH3 || c->variant > DIT_ZFINAL)
     return fail(DIT_EINVAL, "unknown variant %d", c->variant);
   if (c->dtype != DIT_F32 && c->dtype != DIT_BF16) return fail(DIT_EDTYPE, "unknown dtype %d", c->dtype);
   if (c->hd != 64 && c->hd != 128) return fail(DIT_EUNSUPPORTED, "head dim %d not in {64, 128}", c->hd);
   if (c->H <= 0 || c->D != c->H * c->hd) return fail(DIT_ESHAPE, "D=%d != H*hd=%d*%d", c->D, c->H, c->hd);
   if (c->D % 128 || c->D > 4096) return fail(DIT_EUNSUPPORTED, "D=%d must be a multiple of 128 and <= 4096", c->D);
-  if (c->variant == DIT_FINAL) {
+  if (head(c)) {
     const int fm = c->dtype == DIT_BF16 ? 32 : 64;
     if (c->F <= 0 || c->F % fm) return fail(DIT_EUNSUPPORTED, "output width F=%d must be a positive multiple of %d", c->F, fm);
-    if (c->tags != 1) return fail(DIT_EINVAL, "the final layer has one modality (tags=%d)", c->tags);
+    if (c->variant == DIT_FINAL && c->tags != 1) return fail(DIT_EINVAL, "the final layer has one modality (tags=%d)", c->tags);
   } else if (c->F <= 0 || c->F % 128) {
     return fail(DIT_EUNSUPPORTED, "F=%d must be a positive multiple of 128", c->F);
   }
@@ -77,7 +84,7 @@ dit_status check_config(const dit_config* c) {
     if (d <= 0 || d % 2 || c->rope_axes[1] != d || c->rope_axes[2] != d)
       return fail(DIT_EINVAL, "DIT_ROPE_PARTIAL needs three equal, even, positive axis dims");
     if (3 * d > c->hd) return fail(DIT_ESHAPE, "DIT_ROPE_PARTIAL rotates 3 * %d dims, head dim is %d", d, c->hd);
-  } else if (c->rope != DIT_ROPE_NONE && c->variant != DIT_FINAL) {
+  } else if (c->rope != DIT_ROPE_NONE && !head(c)) {
     int sum = 0;
     for (int a = 0; a < 3; ++a) {
       if (c->rope_axes[a] < 0 || c->rope_axes[a] % 2) return fail(DIT_EINVAL, "rope axis dims must be even and >= 0");
@@ -96,7 +103,7 @@ dit_status check_config(const dit_config* c) {
   }
   if (c->variant == DIT_SIGLIP && c->rope != DIT_ROPE_NONE)
     return fail(DIT_EUNSUPPORTED, "the SigLIP layer takes no RoPE");
-  if (c->variant == DIT_ZIMAGE) {
+  if (temb_variant(c)) {
     if (c->temb_freq < 2 || c->temb_freq % 2 || c->temb_hidden < 1)
       return fail(DIT_EINVAL, "temb sizes freq=%d hidden=%d invalid", c->temb_freq, c->temb_hidden);
   }
@@ -133,6 +140,21 @@ PrepLayout prep_layout(const dit_config* c) {
     L.total = off;
     return L;
   }
+  if (c->variant == DIT_ZFINAL) {
+    L.w_fc1 = take(F * D * es);
+    L.b_fc1 = take(F * 4);
+    L.norm1 = take(D * 4);  // LayerNorm without affine: gain 1, bias 0
+    L.ln1_b = take(D * 4);
+    size_t tf = c->temb_freq, th = c->temb_hidden;
+    L.tw1 = take(th * tf * 4);
+    L.tb1 = take(th * 4);
+    L.tw2 = take(tf * th * 4);
+    L.tb2 = take(tf * 4);
+    L.aw = take(D * tf * 4);
+    L.ab = take(D * 4);
+    L.total = off;
+    return L;
+  }
   L.w_qkv = take(3 * D * D * es);
   L.w_out = take(D * D * es);
   L.w_fc1 = take((size_t)fc1_rows(c) * D * es);
@@ -158,9 +180,11 @@ PrepLayout prep_layout(const dit_config* c) {
     L.abias = take(rows * 4);
     L.table = take((size_t)c->grid * c->rank * 4);
   }
-  if (c->variant == DIT_ZIMAGE) {
+  if (zsandwich(c)) {
     L.post_attn = take(D * 4);
     L.post_ffn = take(D * 4);
+  }
+  if (c->variant == DIT_ZIMAGE) {
     size_t tf = c->temb_freq, th = c->temb_hidden;
     L.tw1 = take(th * tf * 4);
     L.tb1 = take(th * 4);
@@ -187,13 +211,14 @@ dit_ws_layout ws_layout(const dit_config* c, int n) {
   const int ldn = ldn_of(n);
   L.ldn = ldn;
   L.mods = mod_rows(c) ? take((size_t)mod_rows(c) * chunks(c) * D * 4) : kNone;
-  if (c->variant == DIT_FINAL) {  // the head: modulation rows and the normalized rows only
+  if (head(c)) {  // a head: modulation rows (+ timestep MLP scratch) and the normalized rows only
     L.rope = L.qkv = L.q = L.k = L.vt = L.o = L.x1 = L.a = L.y = L.temb = L.part = kNone;
+    if (c->variant == DIT_ZFINAL) L.temb = take((size_t)(c->temb_hidden + c->temb_freq) * 4);
     L.xn = take((size_t)n * D * es);
     L.total = off;
     return L;
   }
-  L.temb = c->variant == DIT_ZIMAGE ? take((size_t)(c->temb_hidden + c->temb_freq) * 4) : kNone;
+  L.temb = temb_variant(c) ? take((size_t)(c->temb_hidden + c->temb_freq) * 4) : kNone;
   L.rope = c->rope != DIT_ROPE_NONE ? take((size_t)n * (c->hd / 2) * 8) : kNone;
   L.xn = take((size_t)n * D * es);
   // the bf16 QKV GEMM writes q, k and v^T directly; only the fp32 path stages qkv
@@ -204,7 +229,7 @@ dit_ws_layout ws_layout(const dit_config* c, int n) {
   L.o = take((size_t)n * D * es);
   L.x1 = take((size_t)n * D * 4);
   L.a = take((size_t)n * F * es);
-  L.y = c->variant == DIT_ZIMAGE ? take((size_t)n * D * 4) : kNone;
+  L.y = zsandwich(c) ? take((size_t)n * D * 4) : kNone;
   L.part = c->dtype == DIT_BF16 ? take(dit::attention_part_bytes(c->hd)) : kNone;
   L.total = off;
   return L;
@@ -262,11 +287,13 @@ dit_status launch_mods(const dit_config* c, const void* prep, const double* sigm
     HIP_TRY(dit::adaln_interp(atc<float>(prep, P.basis), atc<float>(prep, P.abias),
                               atc<float>(prep, P.table), c->rank, per_slot, c->slots, sc, mods, s),
             "adaln_interp");
-  } else if (c->variant == DIT_ZIMAGE) {
-    HIP_TRY(dit::temb_mods(sigmas[0] * (double)c->t_scale, c->temb_freq, c->temb_hidden, 4 * c->D,
+  } else if (temb_variant(c)) {
+    // the final layer's adaLN reads silu(temb), the blocks' temb itself
+    const bool fin = c->variant == DIT_ZFINAL;
+    HIP_TRY(dit::temb_mods(sigmas[0] * (double)c->t_scale, c->temb_freq, c->temb_hidden, chunks(c) * c->D,
                            atc<float>(prep, P.tw1), atc<float>(prep, P.tb1), atc<float>(prep, P.tw2),
                            atc<float>(prep, P.tb2), atc<float>(prep, P.aw), atc<float>(prep, P.ab),
-                           temb, mods, s),
+                           temb, mods, s, fin),
             "temb_mods");
   }
   return DIT_OK;
@@ -291,7 +318,11 @@ dit_status launch_prenorm(const dit_config* c, const void* prep, const float* x,
     HIP_TRY(dit::norm_mod(dit::NORM_RMS, dit::MOD_SHIFT_SCALE, bf, x, n, D, g, nullptr, c->eps, mods,
                           2 * D, rows, 0, D, xn, s),
             "norm_mod");
-  } else if (c->variant == DIT_REFINER) {
+  } else if (c->variant == DIT_ZFINAL) {  // LayerNorm without affine (gain 1, bias 0), * (1 + scale)
+    HIP_TRY(dit::norm_mod(dit::NORM_LAYER, dit::MOD_SCALE, bf, x, n, D, g, atc<float>(prep, P.ln1_b), c->eps,
+                          mods, D, nullptr, 0, 0, xn, s),
+            "norm_mod");
+  } else if (c->variant == DIT_REFINER || c->variant == DIT_ZCONTEXT) {
     HIP_TRY(dit::norm_mod(dit::NORM_RMS, dit::MOD_NONE, bf, x, n, D, g, nullptr, c->eps, nullptr, 0,
                           nullptr, 0, 0, xn, s),
             "norm_mod");
@@ -482,6 +513,26 @@ dit_status dit_prepare_weights(const dit_config* c, const dit_weights* w, void* 
             "prep adaln_table");
     return DIT_OK;
   }
+  if (c->variant == DIT_ZFINAL) {
+    Need need[] = {{w->w_fc1, "w_fc1 (output)"}, {w->temb_w1, "temb_w1"}, {w->temb_w2, "temb_w2"},
+                   {w->ada_w, "ada_w"}};
+    for (auto& q : need) {
+      if (!q.p) return fail(DIT_EINVAL, "weight %s is NULL", q.name);
+      if (!aligned16(q.p)) return fail(DIT_EALIGN, "weight %s is not 16-byte aligned", q.name);
+    }
+    const int D = c->D, F = c->F, tf = c->temb_freq, th = c->temb_hidden;
+    HIP_TRY(dit::prep_matrix(c->dtype, w->w_fc1, at<char>(prepared, P.w_fc1), F, D, 0, 0, 1.0f, s), "prep output");
+    HIP_TRY(dit::prep_vector(w->b_fc1, at<float>(prepared, P.b_fc1), F, 0, 1.0f, s), "prep output bias");
+    HIP_TRY(dit::fill_f32(at<float>(prepared, P.norm1), D, 1.0f, s), "norm gain");
+    HIP_TRY(dit::prep_vector(nullptr, at<float>(prepared, P.ln1_b), D, 0, 1.0f, s), "norm bias");
+    HIP_TRY(dit::prep_matrix(dit::F32, w->temb_w1, at<char>(prepared, P.tw1), th, tf, 0, 0, 1.0f, s), "prep temb_w1");
+    HIP_TRY(dit::prep_vector(w->temb_b1, at<float>(prepared, P.tb1), th, 0, 1.0f, s), "prep temb_b1");
+    HIP_TRY(dit::prep_matrix(dit::F32, w->temb_w2, at<char>(prepared, P.tw2), tf, th, 0, 0, 1.0f, s), "prep temb_w2");
+    HIP_TRY(dit::prep_vector(w->temb_b2, at<float>(prepared, P.tb2), tf, 0, 1.0f, s), "prep temb_b2");
+    HIP_TRY(dit::prep_matrix(dit::F32, w->ada_w, at<char>(prepared, P.aw), D, tf, 0, 0, 1.0f, s), "prep ada_w");
+    HIP_TRY(dit::prep_vector(w->ada_b, at<float>(prepared, P.ab), D, 0, 1.0f, s), "prep ada_b");
+    return DIT_OK;
+  }
   Need common[] = {{w->w_qkv, "w_qkv"}, {w->w_out, "w_out"}, {w->w_fc1, "w_fc1"},
                    {w->w_fc2, "w_fc2"}, {w->norm1, "norm1"}, {w->norm2, "norm2"}};
   for (auto& q : common) {
@@ -497,6 +548,8 @@ dit_status dit_prepare_weights(const dit_config* c, const dit_weights* w, void* 
   if (c->variant == DIT_ZIMAGE &&
       (!w->post_attn_norm || !w->post_ffn_norm || !w->temb_w1 || !w->temb_w2 || !w->ada_w))
     return fail(DIT_EINVAL, "Z-Image norms or timestep weights are NULL");
+  if (c->variant == DIT_ZCONTEXT && (!w->post_attn_norm || !w->post_ffn_norm))
+    return fail(DIT_EINVAL, "Z-Image sandwich norms are NULL");
 
   const int D = c->D, F = c->F, dt = c->dtype;
   // [SIGLIP] Layer::load folds hd^-1/2 into W_q and b_q.
@@ -545,10 +598,12 @@ dit_status dit_prepare_weights(const dit_config* c, const dit_weights* w, void* 
     HIP_TRY(dit::prep_matrix(dit::F32, w->adaln_table, at<char>(prepared, P.table), c->grid, c->rank, 0, 0, 1.0f, s),
             "prep adaln_table");
   }
-  if (c->variant == DIT_ZIMAGE) {
-    const int tf = c->temb_freq, th = c->temb_hidden;
+  if (zsandwich(c)) {
     HIP_TRY(vec(w->post_attn_norm, P.post_attn, D), "prep post_attn_norm");
     HIP_TRY(vec(w->post_ffn_norm, P.post_ffn, D), "prep post_ffn_norm");
+  }
+  if (c->variant == DIT_ZIMAGE) {
+    const int tf = c->temb_freq, th = c->temb_hidden;
     HIP_TRY(dit::prep_matrix(dit::F32, w->temb_w1, at<char>(prepared, P.tw1), th, tf, 0, 0, 1.0f, s), "prep temb_w1");
     HIP_TRY(vec(w->temb_b1, P.tb1, th), "prep temb_b1");
     HIP_TRY(dit::prep_matrix(dit::F32, w->temb_w2, at<char>(prepared, P.tw2), tf, th, 0, 0, 1.0f, s), "prep temb_w2");
@@ -564,7 +619,7 @@ dit_status dit_adaln_eval(const dit_config* c, const void* prepared, const doubl
   DIT_TRY(check_config(c));
   if (!has_mods(c)) return fail(DIT_EUNSUPPORTED, "variant %d has no modulation", c->variant);
   if (!prepared || !mods_out) return fail(DIT_EINVAL, "prepared/mods_out is NULL");
-  if (c->variant == DIT_ZIMAGE && !temb_scratch) return fail(DIT_EINVAL, "temb_scratch is NULL");
+  if (temb_variant(c) && !temb_scratch) return fail(DIT_EINVAL, "temb_scratch is NULL");
   DIT_TRY(check_sigmas(c, sigmas, n_sigmas));
   return launch_mods(c, prepared, sigmas, mods_out, temb_scratch, (hipStream_t)stream);
 }
@@ -579,7 +634,7 @@ dit_status dit_adaln_modulate(const dit_config* c, const void* prepared, const f
   if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
   if (has_mods(c)) {
     if (!mods_out) return fail(DIT_EINVAL, "mods_out is NULL");
-    if (c->variant == DIT_ZIMAGE && !temb_scratch) return fail(DIT_EINVAL, "temb_scratch is NULL");
+    if (temb_variant(c) && !temb_scratch) return fail(DIT_EINVAL, "temb_scratch is NULL");
     DIT_TRY(check_sigmas(c, sigmas, n_sigmas));
   }
   if (n == 0) return DIT_OK;
@@ -644,7 +699,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
                               int32_t nseq, float* out, void* workspace, size_t ws_bytes,
                               void* stream) {
   DIT_TRY(check_config(c));
-  if (c->variant == DIT_FINAL) return fail(DIT_EUNSUPPORTED, "DIT_FINAL is run by dit_final_forward");
+  if (head(c)) return fail(DIT_EUNSUPPORTED, "output heads are run by dit_final_forward");
   if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
   if (seq_starts) DIT_TRY(check_seqs(seq_starts, nseq, n));
   if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
@@ -743,14 +798,16 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
   }
   pm.mark(4);
   // a6: out projection + residual
-  if (c->variant == DIT_ZIMAGE) {
+  // Z-Image chunks (scale_msa, gate_msa, scale_mlp, gate_mlp); none for the context refiner
+  auto zmod = [&](int e) -> const float* { return c->variant == DIT_ZIMAGE ? mods + e * D : nullptr; };
+  if (zsandwich(c)) {
     dit::Epi ep;
     ep.out = y;
     ep.ldc = D;
     HIP_TRY(dit::gemm(dt, dit::EPI_STORE, false, o, D, atc<char>(prepared, P.w_out), D, n, D, D, ep, s), "out gemm");
     // x1 = x + tanh(gate_msa) RMSNorm(y); xn = RMSNorm(x1) (1 + scale_mlp)
-    HIP_TRY(dit::sandwich(x, y, n, D, atc<float>(prepared, P.post_attn), mods + 1 * D, c->eps, x1,
-                          atc<float>(prepared, P.norm2), mods + 2 * D, bf, xn, s),
+    HIP_TRY(dit::sandwich(x, y, n, D, atc<float>(prepared, P.post_attn), zmod(1), c->eps, x1,
+                          atc<float>(prepared, P.norm2), zmod(2), bf, xn, s),
             "sandwich attn");
     pm.mark(5);
     pm.mark(6);
@@ -786,12 +843,12 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
   }
   pm.mark(7);
   // a9: fc2 + residual
-  if (c->variant == DIT_ZIMAGE) {
+  if (zsandwich(c)) {
     dit::Epi ep;
     ep.out = y;
     ep.ldc = D;
     HIP_TRY(dit::gemm(dt, dit::EPI_STORE, false, a, F, atc<char>(prepared, P.w_fc2), F, n, D, F, ep, s), "fc2 gemm");
-    HIP_TRY(dit::sandwich(x1, y, n, D, atc<float>(prepared, P.post_ffn), mods + 3 * D, c->eps, out, nullptr,
+    HIP_TRY(dit::sandwich(x1, y, n, D, atc<float>(prepared, P.post_ffn), zmod(3), c->eps, out, nullptr,
                           nullptr, bf, nullptr, s),
             "sandwich ffn");
   } else {
@@ -839,7 +896,7 @@ dit_status final_forward_impl(const dit_config* c, const void* prepared, const f
                               const int32_t* rows, const double* sigmas, int32_t n_sigmas, float alpha,
                               float* out, void* workspace, size_t ws_bytes, void* stream) {
   DIT_TRY(check_config(c));
-  if (c->variant != DIT_FINAL) return fail(DIT_EINVAL, "dit_final_forward needs a DIT_FINAL config");
+  if (!head(c)) return fail(DIT_EINVAL, "dit_final_forward needs a DIT_FINAL or DIT_ZFINAL config");
   if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
   if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
   DIT_TRY(check_sigmas(c, sigmas, n_sigmas));
@@ -854,7 +911,7 @@ dit_status final_forward_impl(const dit_config* c, const void* prepared, const f
   PrepLayout P = prep_layout(c);
   float* mods = at<float>(workspace, L.mods);
   void* xn = at<char>(workspace, L.xn);
-  DIT_TRY(launch_mods(c, prepared, sigmas, mods, nullptr, s));
+  DIT_TRY(launch_mods(c, prepared, sigmas, mods, at<float>(workspace, L.temb), s));
   DIT_TRY(launch_prenorm(c, prepared, h, n, rows, mods, 0, xn, s));
   dit::Epi ep;
   ep.out = out;
@@ -871,8 +928,9 @@ dit_status final_forward_impl(const dit_config* c, const void* prepared, const f
 dit_status dit_final_forward(const dit_config* c, const void* prepared, const float* h, int32_t n,
                              const int32_t* rows, const double* sigmas, int32_t n_sigmas, float* out,
                              void* workspace, size_t ws_bytes, void* stream) {
-  // the head predicts toward the data: the velocity is its negative
-  return final_forward_impl(c, prepared, h, n, rows, sigmas, n_sigmas, -1.0f, out, workspace, ws_bytes,
+  // the MMH3 head predicts toward the data: the velocity is its negative
+  const float alpha = c && c->variant == DIT_ZFINAL ? 1.0f : -1.0f;
+  return final_forward_impl(c, prepared, h, n, rows, sigmas, n_sigmas, alpha, out, workspace, ws_bytes,
                             stream);
 }
 
@@ -917,6 +975,27 @@ dit_status dit_unpatchify_video(const float* rows, int32_t C, int32_t T, int32_t
   if ((size_t)C * T * H * W == 0) return DIT_OK;
   if (!x || !rows) return fail(DIT_EINVAL, "x/rows is NULL");
   HIP_TRY(dit::unpatchify_video(rows, C, T, H, W, x, (hipStream_t)stream), "unpatchify");
+  return DIT_OK;
+}
+
+dit_status dit_patchify_image(int32_t dtype, const float* x, int32_t C, int32_t H, int32_t W,
+                              void* rows, void* stream) {
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return fail(DIT_EDTYPE, "unknown dtype %d", dtype);
+  if (C < 0 || H < 0 || W < 0 || H % 2 || W % 2)
+    return fail(DIT_ESHAPE, "image [%d, %d, %d]: sizes >= 0, H and W even", C, H, W);
+  if ((size_t)C * H * W == 0) return DIT_OK;
+  if (!x || !rows) return fail(DIT_EINVAL, "x/rows is NULL");
+  HIP_TRY(dit::patchify_image(dtype, x, C, H, W, rows, (hipStream_t)stream), "patchify_image");
+  return DIT_OK;
+}
+
+dit_status dit_unpatchify_image(const float* rows, int32_t C, int32_t H, int32_t W, float* x,
+                                void* stream) {
+  if (C < 0 || H < 0 || W < 0 || H % 2 || W % 2)
+    return fail(DIT_ESHAPE, "image [%d, %d, %d]: sizes >= 0, H and W even", C, H, W);
+  if ((size_t)C * H * W == 0) return DIT_OK;
+  if (!x || !rows) return fail(DIT_EINVAL, "x/rows is NULL");
+  HIP_TRY(dit::unpatchify_image(rows, C, H, W, x, (hipStream_t)stream), "unpatchify_image");
   return DIT_OK;
 }
 
@@ -1142,6 +1221,153 @@ dit_status dit_mmh3_forward(const dit_mmh3_model* m, const dit_segment* segs, in
                                bc->slots, (float)-slope, hout, at<char>(workspace, P.hws), hws, s));
     HIP_TRY(dit::unpack_audio(hout, m->audio_c, Ta, audio_out, s), "unpack_audio");
   }
+  return DIT_OK;
+}
+
+// ------------------------------------------------------------ Z-Image model ----
+namespace {
+struct ZPlan {
+  int ni = 0, nc = 0, n = 0;
+  size_t h = 0, prow = 0, crow = 0, hout = 0, bws = 0, bws_bytes = 0, total = 0;
+};
+
+// Runs blocks [b0, b1) of a stack in place on h (nothing when the range is empty).
+dit_status run_blocks(const dit_config* c, const void* const* prep, int b0, int b1, float* h, int n,
+                      const float* pos, const double* sig, int nsig, void* ws, size_t wsb, hipStream_t s) {
+  if (b1 <= b0 || n == 0) return DIT_OK;
+  return dit_stack_forward(c, prep + b0, b1 - b0, h, n, nullptr, pos, sig, nsig, nullptr, 0, h, ws, wsb, s);
+}
+
+dit_status plan_zimage(const dit_zimage_model* m, int H, int W, int cap_len, ZPlan* P) {
+  if (!m) return fail(DIT_EINVAL, "model is NULL");
+  if (!m->block || !m->context || !m->final_layer || !m->final_w)
+    return fail(DIT_EINVAL, "model needs block, context and final-layer configs and final weights");
+  DIT_TRY(check_config(m->block));
+  DIT_TRY(check_config(m->context));
+  DIT_TRY(check_config(m->final_layer));
+  const dit_config *b = m->block, *c = m->context, *f = m->final_layer;
+  if (b->variant != DIT_ZIMAGE || c->variant != DIT_ZCONTEXT || f->variant != DIT_ZFINAL)
+    return fail(DIT_EINVAL, "configs must be DIT_ZIMAGE, DIT_ZCONTEXT and DIT_ZFINAL");
+  if (c->D != b->D || c->H != b->H || c->hd != b->hd || c->dtype != b->dtype || f->D != b->D || f->dtype != b->dtype)
+    return fail(DIT_EINVAL, "block, context refiner and final layer must share D, heads and dtype");
+  if (f->F != 4 * m->in_channels) return fail(DIT_EINVAL, "final layer F=%d != 4 * in_channels", f->F);
+  if (m->n_layers < 0 || m->n_noise_refiners < 0 || m->n_context_refiners < 0)
+    return fail(DIT_EINVAL, "negative block counts");
+  if ((m->n_layers && !m->layers) || (m->n_noise_refiners && !m->noise_refiners) ||
+      (m->n_context_refiners && !m->context_refiners))
+    return fail(DIT_EINVAL, "block arrays are NULL");
+  if (!m->x_embed_w || !m->cap_embed_w || !m->cap_norm) return fail(DIT_EINVAL, "embedder weights are NULL");
+  const bool bf = b->dtype == DIT_BF16;
+  const int km = bf ? 64 : 16;
+  if (m->in_channels <= 0 || (4 * m->in_channels) % km)
+    return fail(DIT_EUNSUPPORTED, "4 * in_channels=%d must be a multiple of %d", 4 * m->in_channels, km);
+  if (m->cap_dim <= 0 || m->cap_dim % km || m->cap_dim > 4096)
+    return fail(DIT_EUNSUPPORTED, "cap_dim=%d must be a multiple of %d and <= 4096", m->cap_dim, km);
+  if (!(m->cap_eps >= 0.0f)) return fail(DIT_EINVAL, "cap_eps must be >= 0");
+  if (H <= 0 || W <= 0 || H % 2 || W % 2 || cap_len < 0)
+    return fail(DIT_ESHAPE, "image %d x %d (even, > 0), caption %d", H, W, cap_len);
+  P->ni = (H / 2) * (W / 2);
+  P->nc = cap_len;
+  P->n = P->ni + P->nc;
+  const size_t D = b->D, es = bf ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  P->h = take((size_t)P->n * D * 4);
+  P->prow = take((size_t)P->ni * 4 * m->in_channels * es);
+  P->crow = take((size_t)std::max(P->nc, 1) * m->cap_dim * es);
+  P->hout = take((size_t)P->ni * 4 * m->in_channels * 4);
+  P->bws_bytes = std::max({ws_layout(b, P->n).total, ws_layout(c, std::max(P->nc, 1)).total,
+                           ws_layout(f, P->ni).total});
+  P->bws = take(P->bws_bytes);
+  P->total = off;
+  return DIT_OK;
+}
+}  // namespace
+
+size_t dit_zimage_workspace_size(const dit_zimage_model* m, int32_t H, int32_t W, int32_t cap_len) {
+  ZPlan P;
+  return plan_zimage(m, H, W, cap_len, &P) == DIT_OK ? P.total : 0;
+}
+
+dit_status dit_zimage_forward(const dit_zimage_model* m, const float* latents, int32_t H, int32_t W,
+                              const float* cap_feats, int32_t cap_len, const float* pos, double t,
+                              int32_t step, dit_zimage_cache* cache, float* out, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  ZPlan P;
+  DIT_TRY(plan_zimage(m, H, W, cap_len, &P));
+  if (!latents || !pos || !out || (cap_len > 0 && !cap_feats)) return fail(DIT_EINVAL, "input/output is NULL");
+  if (!aligned16(latents) || !aligned16(pos) || !aligned16(out) || (cap_feats && !aligned16(cap_feats)))
+    return fail(DIT_EALIGN, "inputs/outputs not 16-byte aligned");
+  if (!isfinite(t)) return fail(DIT_EINVAL, "t is not finite");
+  if (!workspace) return fail(DIT_EINVAL, "workspace is NULL");
+  if ((uintptr_t)workspace % kAlign) return fail(DIT_EALIGN, "workspace must be 256-byte aligned");
+  if (ws_bytes < P.total) return fail(DIT_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, P.total);
+  if (cache) {
+    if (cache->interval < 1) return fail(DIT_EINVAL, "cache interval=%d < 1", cache->interval);
+    if (cache->layers < 0 || cache->layers > m->n_layers)
+      return fail(DIT_EINVAL, "cache layers=%d outside [0, %d]", cache->layers, m->n_layers);
+    if (cache->layers > 0 && !cache->shallow) return fail(DIT_EINVAL, "cache->shallow is NULL");
+    if (cap_len > 0 && !cache->caption) return fail(DIT_EINVAL, "cache->caption is NULL");
+    if (step < 0) return fail(DIT_EINVAL, "step=%d < 0", step);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const dit_config* b = m->block;
+  const int D = b->D, C = m->in_channels, dt = b->dtype;
+  const size_t rowb = (size_t)D * 4;
+  float* h = at<float>(workspace, P.h);
+  float* hc = h + (size_t)P.ni * D;  // caption rows of the unified stream
+  const float* pos_c = pos + (size_t)P.ni * 3;
+  void* bws = at<char>(workspace, P.bws);
+  const double sig[1] = {t};
+  // [ZIMG] ForwardWithCache: on a step that is not a refresh, every shallow layer reads its
+  // stored output, so the stream after them is the stored one and the image embedding and
+  // noise refiners before them have no effect on the result.
+  const int nshallow = cache ? cache->layers : 0;
+  const bool refresh = cache ? step % cache->interval == 0 : true;
+  const bool reuse = cache && nshallow > 0 && !refresh && cache->shallow_valid;
+  if (reuse) {
+    HIP_TRY(hipMemcpyAsync(h, cache->shallow, (size_t)P.n * rowb, hipMemcpyDeviceToDevice, s), "reuse layers");
+  } else {
+    // image: patchify + x embedder, then the noise refiners (modulated, image tokens only)
+    HIP_TRY(dit::patchify_image(dt, latents, C, H, W, at<char>(workspace, P.prow), s), "patchify_image");
+    DIT_TRY(dit_linear(dt, at<char>(workspace, P.prow), 4 * C, P.ni, 4 * C, m->x_embed_w, D, m->x_embed_b, 1.0f,
+                       h, s));
+    DIT_TRY(run_blocks(b, m->noise_refiners, 0, m->n_noise_refiners, h, P.ni, pos, sig, 1, bws, P.bws_bytes, s));
+    // caption: RMSNorm + cap embedder, then the context refiners; once per generation with a cache
+    if (P.nc > 0) {
+      if (cache && cache->caption_valid) {
+        HIP_TRY(hipMemcpyAsync(hc, cache->caption, (size_t)P.nc * rowb, hipMemcpyDeviceToDevice, s), "caption");
+      } else {
+        HIP_TRY(dit::norm_mod(dit::NORM_RMS, dit::MOD_NONE, dt == DIT_BF16, cap_feats, P.nc, m->cap_dim, m->cap_norm,
+                              nullptr, m->cap_eps, nullptr, 0, nullptr, 0, 0, at<char>(workspace, P.crow), s),
+                "caption norm");
+        DIT_TRY(dit_linear(dt, at<char>(workspace, P.crow), m->cap_dim, P.nc, m->cap_dim, m->cap_embed_w, D,
+                           m->cap_embed_b, 1.0f, hc, s));
+        DIT_TRY(run_blocks(m->context, m->context_refiners, 0, m->n_context_refiners, hc, P.nc, pos_c, nullptr, 0,
+                           bws, P.bws_bytes, s));
+        if (cache) {
+          HIP_TRY(hipMemcpyAsync(cache->caption, hc, (size_t)P.nc * rowb, hipMemcpyDeviceToDevice, s), "store caption");
+          cache->caption_valid = 1;
+        }
+      }
+    }
+    // the shallow main layers, stored on refresh steps
+    DIT_TRY(run_blocks(b, m->layers, 0, nshallow, h, P.n, pos, sig, 1, bws, P.bws_bytes, s));
+    if (cache && nshallow > 0 && refresh) {
+      HIP_TRY(hipMemcpyAsync(cache->shallow, h, (size_t)P.n * rowb, hipMemcpyDeviceToDevice, s), "store layers");
+      cache->shallow_valid = 1;
+    }
+  }
+  DIT_TRY(run_blocks(b, m->layers, nshallow, m->n_layers, h, P.n, pos, sig, 1, bws, P.bws_bytes, s));
+  // final layer on the image tokens, then back to [C, H, W]
+  float* hout = at<float>(workspace, P.hout);
+  DIT_TRY(final_forward_impl(m->final_layer, m->final_w, h, P.ni, nullptr, sig, 1, 1.0f, hout, bws,
+                             P.bws_bytes, s));
+  HIP_TRY(dit::unpatchify_image(hout, C, H, W, out, s), "unpatchify_image");
   return DIT_OK;
 }
 

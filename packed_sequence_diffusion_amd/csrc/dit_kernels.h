@@ -56,7 +56,8 @@ hipError_t adaln_interp(const float* basis, const float* bias, const float* tabl
 // Z-Image: sinusoid(t) -> L1 + SiLU -> L2 -> adaLN linear; scratch [hidden + freq].
 hipError_t temb_mods(double t_scaled, int freq, int hidden, int out_dim, const float* w1,
                      const float* b1, const float* w2, const float* b2, const float* wa,
-                     const float* ba, float* scratch, float* mods, hipStream_t s);
+                     const float* ba, float* scratch, float* mods, hipStream_t s,
+                     bool silu_temb = false);
 
 // ---- row kernels --------------------------------------------------------------------
 enum NormKind { NORM_RMS = 0, NORM_LAYER = 1 };
@@ -111,8 +112,12 @@ hipError_t patchify_video(int dtype, const float* x, int C, int T, int H, int W,
 hipError_t unpatchify_video(const float* rows, int C, int T, int H, int W, float* x, hipStream_t s);
 hipError_t pack_audio(int dtype, const float* x, int C, int T, void* rows, hipStream_t s);
 hipError_t unpack_audio(const float* rows, int C, int T, float* x, hipStream_t s);
+// channel-last patch columns ([ZIMG] PatchifyLatents), image [C, H, W]
+hipError_t patchify_image(int dtype, const float* x, int C, int H, int W, void* rows, hipStream_t s);
+hipError_t unpatchify_image(const float* rows, int C, int H, int W, float* x, hipStream_t s);
 // p[0, n) = v (a kernel rather than a memset: safe inside captured graphs)
 hipError_t fill_i32(int* p, int n, int v, hipStream_t s);
+hipError_t fill_f32(float* p, int n, float v, hipStream_t s);
 
 // ---- weight preparation ---------------------------------------------------------------
 // Source row of prepared row r, in this order: the SwiGLU group interleave (swiglu_F > 0);

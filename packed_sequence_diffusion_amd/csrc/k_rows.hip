@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void k_dense(const float* __restrict__ x, int 
 
 hipError_t temb_mods(double t_scaled, int freq, int hidden, int out_dim, const float* w1,
                      const float* b1, const float* w2, const float* b2, const float* wa,
-                     const float* ba, float* scratch, float* mods, hipStream_t s) {
+                     const float* ba, float* scratch, float* mods, hipStream_t s, bool silu_temb) {
   // scratch: h [hidden] then one [freq] slot that holds the sinusoid e until
   // the first layer has read it, then temb.
   float* h = scratch;
@@ -99,7 +99,11 @@ hipError_t temb_mods(double t_scaled, int freq, int hidden, int out_dim, const f
   const int half = freq / 2;
   k_temb_sin<<<(half + 127) / 128, 128, 0, s>>>(t_scaled, half, et);
   k_dense<true><<<(hidden + 3) / 4, 256, 0, s>>>(et, freq, hidden, w1, b1, h);
-  k_dense<false><<<(freq + 3) / 4, 256, 0, s>>>(h, hidden, freq, w2, b2, et);
+  // the final layer's adaLN reads silu(temb) ([ZIMG] FinalLayer.Forward)
+  if (silu_temb)
+    k_dense<true><<<(freq + 3) / 4, 256, 0, s>>>(h, hidden, freq, w2, b2, et);
+  else
+    k_dense<false><<<(freq + 3) / 4, 256, 0, s>>>(h, hidden, freq, w2, b2, et);
   k_dense<false><<<(out_dim + 3) / 4, 256, 0, s>>>(et, freq, out_dim, wa, ba, mods);
   return hipGetLastError();
 }
@@ -241,6 +245,8 @@ hipError_t norm_mod(int norm, int mod, bool out_bf16, const float* x, int n, int
 // Sandwich residual ([ZIMG] TransformerBlock.Forward):
 //   x1 = x + tanh(gate) * RMSNorm(y; g_post), and when g_next is given
 //   xf = RMSNorm(x1; g_next) * (1 + scale) for the next half.
+// Without modulation (the context refiner) gate and scale are NULL: a plain
+// residual and an unscaled pre-norm.
 // ------------------------------------------------------------------------------
 template <typename OutT>
 __global__ __launch_bounds__(256) void k_sandwich(const float* __restrict__ x,
@@ -273,12 +279,17 @@ __global__ __launch_bounds__(256) void k_sandwich(const float* __restrict__ x,
   for (int c = 0; c < kMaxChunks; ++c) {
     int i = lane + 64 * c;
     if (i < nc) {
-      float4 xx = xr[i], gp = ((const float4*)g_post)[i], gt = ((const float4*)gate)[i];
+      float4 xx = xr[i], gp = ((const float4*)g_post)[i];
+      float4 tg = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+      if (gate) {
+        const float4 gt = ((const float4*)gate)[i];
+        tg = make_float4(tanh_f(gt.x), tanh_f(gt.y), tanh_f(gt.z), tanh_f(gt.w));
+      }
       float4 o;
-      o.x = xx.x + tanh_f(gt.x) * (v[c].x * inv * gp.x);
-      o.y = xx.y + tanh_f(gt.y) * (v[c].y * inv * gp.y);
-      o.z = xx.z + tanh_f(gt.z) * (v[c].z * inv * gp.z);
-      o.w = xx.w + tanh_f(gt.w) * (v[c].w * inv * gp.w);
+      o.x = xx.x + tg.x * (v[c].x * inv * gp.x);
+      o.y = xx.y + tg.y * (v[c].y * inv * gp.y);
+      o.z = xx.z + tg.z * (v[c].z * inv * gp.z);
+      o.w = xx.w + tg.w * (v[c].w * inv * gp.w);
       ((float4*)(x1 + (size_t)row * D))[i] = o;
       v[c] = o;
       s2 += o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
@@ -291,7 +302,8 @@ __global__ __launch_bounds__(256) void k_sandwich(const float* __restrict__ x,
   for (int c = 0; c < kMaxChunks; ++c) {
     int i = lane + 64 * c;
     if (i < nc) {
-      float4 gn = ((const float4*)g_next)[i], sc = ((const float4*)scale)[i];
+      float4 gn = ((const float4*)g_next)[i];
+      const float4 sc = scale ? ((const float4*)scale)[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       float4 o;
       o.x = v[c].x * inv2 * gn.x * (1.0f + sc.x);
       o.y = v[c].y * inv2 * gn.y * (1.0f + sc.y);

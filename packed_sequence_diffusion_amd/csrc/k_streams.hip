@@ -4,7 +4,9 @@
 //     c*4 + p*2 + q holds x[c, t, 2*h2 + p, 2*w2 + q] (the 2 x 2 spatial patch,
 //     channel-major outer);
 //   audio [C, 2, T] -> rows [2T, C]: row ch*T + t, column c holds x[c, ch, t]
-//     (channel 0's frames, then channel 1's).
+//     (channel 0's frames, then channel 1's);
+//   with CL (channel-last columns, [ZIMG] PatchifyLatents, T = 1): column
+//     (p*2 + q)*C + c holds x[c, 2*h2 + p, 2*w2 + q].
 // One thread per row element on the row side, so that the rows (the GEMM
 // operand, written in the GEMM dtype) are written contiguously.
 #include "dev_common.h"
@@ -12,7 +14,7 @@
 
 namespace dit {
 
-template <typename OutT>
+template <typename OutT, bool CL>
 __global__ void k_patchify(const float* __restrict__ x, int C, int T, int H, int W,
                            OutT* __restrict__ rows) {
   const size_t total = (size_t)T * (H / 2) * (W / 2) * C * 4;
@@ -21,10 +23,13 @@ __global__ void k_patchify(const float* __restrict__ x, int C, int T, int H, int
   const int col = (int)(i % (4 * C));
   const size_t r = i / (4 * C);
   const int w2 = (int)(r % (W / 2)), h2 = (int)((r / (W / 2)) % (H / 2)), t = (int)(r / ((size_t)(W / 2) * (H / 2)));
-  const int c = col >> 2, p = (col >> 1) & 1, q = col & 1;
+  const int c = CL ? col % C : col >> 2;
+  const int pq = CL ? col / C : col & 3;
+  const int p = pq >> 1, q = pq & 1;
   Elt<OutT>::st(rows + i, x[(((size_t)c * T + t) * H + 2 * h2 + p) * W + 2 * w2 + q]);
 }
 
+template <bool CL>
 __global__ void k_unpatchify(const float* __restrict__ rows, int C, int T, int H, int W,
                              float* __restrict__ x) {
   const size_t total = (size_t)T * (H / 2) * (W / 2) * C * 4;
@@ -33,7 +38,9 @@ __global__ void k_unpatchify(const float* __restrict__ rows, int C, int T, int H
   const int col = (int)(i % (4 * C));
   const size_t r = i / (4 * C);
   const int w2 = (int)(r % (W / 2)), h2 = (int)((r / (W / 2)) % (H / 2)), t = (int)(r / ((size_t)(W / 2) * (H / 2)));
-  const int c = col >> 2, p = (col >> 1) & 1, q = col & 1;
+  const int c = CL ? col % C : col >> 2;
+  const int pq = CL ? col / C : col & 3;
+  const int p = pq >> 1, q = pq & 1;
   x[(((size_t)c * T + t) * H + 2 * h2 + p) * W + 2 * w2 + q] = rows[i];
 }
 
@@ -58,7 +65,8 @@ __global__ void k_unpack_audio(const float* __restrict__ rows, int C, int T, flo
   x[((size_t)c * 2 + ch) * T + t] = rows[i];
 }
 
-__global__ void k_fill_i32(int* __restrict__ p, int n, int v) {
+template <typename T>
+__global__ void k_fill(T* __restrict__ p, int n, T v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
 }
@@ -67,26 +75,52 @@ static unsigned blocks_for(size_t total) { return (unsigned)((total + 255) / 256
 
 hipError_t fill_i32(int* p, int n, int v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  k_fill_i32<<<blocks_for((size_t)n), 256, 0, s>>>(p, n, v);
+  k_fill<int><<<blocks_for((size_t)n), 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t fill_f32(float* p, int n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_fill<float><<<blocks_for((size_t)n), 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+template <bool CL>
+static hipError_t patchify_impl(int dtype, const float* x, int C, int T, int H, int W, void* rows,
+                                hipStream_t s) {
+  const size_t total = (size_t)T * (H / 2) * (W / 2) * C * 4;
+  if (total == 0) return hipSuccess;
+  if (dtype == BF16)
+    k_patchify<bf16_t, CL><<<blocks_for(total), 256, 0, s>>>(x, C, T, H, W, (bf16_t*)rows);
+  else
+    k_patchify<float, CL><<<blocks_for(total), 256, 0, s>>>(x, C, T, H, W, (float*)rows);
+  return hipGetLastError();
+}
+
+template <bool CL>
+static hipError_t unpatchify_impl(const float* rows, int C, int T, int H, int W, float* x,
+                                  hipStream_t s) {
+  const size_t total = (size_t)T * (H / 2) * (W / 2) * C * 4;
+  if (total == 0) return hipSuccess;
+  k_unpatchify<CL><<<blocks_for(total), 256, 0, s>>>(rows, C, T, H, W, x);
   return hipGetLastError();
 }
 
 hipError_t patchify_video(int dtype, const float* x, int C, int T, int H, int W, void* rows,
                           hipStream_t s) {
-  const size_t total = (size_t)T * (H / 2) * (W / 2) * C * 4;
-  if (total == 0) return hipSuccess;
-  if (dtype == BF16)
-    k_patchify<bf16_t><<<blocks_for(total), 256, 0, s>>>(x, C, T, H, W, (bf16_t*)rows);
-  else
-    k_patchify<float><<<blocks_for(total), 256, 0, s>>>(x, C, T, H, W, (float*)rows);
-  return hipGetLastError();
+  return patchify_impl<false>(dtype, x, C, T, H, W, rows, s);
 }
 
 hipError_t unpatchify_video(const float* rows, int C, int T, int H, int W, float* x, hipStream_t s) {
-  const size_t total = (size_t)T * (H / 2) * (W / 2) * C * 4;
-  if (total == 0) return hipSuccess;
-  k_unpatchify<<<blocks_for(total), 256, 0, s>>>(rows, C, T, H, W, x);
-  return hipGetLastError();
+  return unpatchify_impl<false>(rows, C, T, H, W, x, s);
+}
+
+hipError_t patchify_image(int dtype, const float* x, int C, int H, int W, void* rows, hipStream_t s) {
+  return patchify_impl<true>(dtype, x, C, 1, H, W, rows, s);
+}
+
+hipError_t unpatchify_image(const float* rows, int C, int H, int W, float* x, hipStream_t s) {
+  return unpatchify_impl<true>(rows, C, 1, H, W, x, s);
 }
 
 hipError_t pack_audio(int dtype, const float* x, int C, int T, void* rows, hipStream_t s) {

@@ -16,12 +16,13 @@ from typing import Dict, List, Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdit.so")
 
-MMH3, SIGLIP, ZIMAGE, REFINER, FINAL = 0, 1, 2, 3, 4
+MMH3, SIGLIP, ZIMAGE, REFINER, FINAL, ZCONTEXT, ZFINAL = 0, 1, 2, 3, 4, 5, 6
 F32, BF16 = 0, 1
 ROPE_NONE, ROPE_SPLIT_HALF, ROPE_INTERLEAVED, ROPE_PARTIAL = 0, 1, 2, 3
 NPHASES = 9
 
-_VARIANTS = {"mmh3": MMH3, "siglip": SIGLIP, "zimage": ZIMAGE, "refiner": REFINER, "final": FINAL}
+_VARIANTS = {"mmh3": MMH3, "siglip": SIGLIP, "zimage": ZIMAGE, "refiner": REFINER, "final": FINAL,
+             "zcontext": ZCONTEXT, "zfinal": ZFINAL}
 _DTYPES = {"f32": F32, "bf16": BF16}
 _ROPES = {"none": ROPE_NONE, "split_half": ROPE_SPLIT_HALF, "interleaved": ROPE_INTERLEAVED,
           "partial": ROPE_PARTIAL}
@@ -73,6 +74,21 @@ class DitMmh3Model(ctypes.Structure):
                 ("shift_video", c_double), ("shift_audio", c_double),
                 ("cond_aug", c_double), ("cond_aug_audio", c_double),
                 ("audio_slope_rescale", c_int32)]
+
+
+class DitZimageModel(ctypes.Structure):
+    _fields_ = [("block", POINTER(DitConfig)), ("layers", POINTER(c_void_p)), ("n_layers", c_int32),
+                ("noise_refiners", POINTER(c_void_p)), ("n_noise_refiners", c_int32),
+                ("context", POINTER(DitConfig)), ("context_refiners", POINTER(c_void_p)),
+                ("n_context_refiners", c_int32), ("final_layer", POINTER(DitConfig)),
+                ("final_w", c_void_p), ("in_channels", c_int32), ("cap_dim", c_int32),
+                ("x_embed_w", c_void_p), ("x_embed_b", c_void_p), ("cap_norm", c_void_p),
+                ("cap_eps", c_float), ("cap_embed_w", c_void_p), ("cap_embed_b", c_void_p)]
+
+
+class DitZimageCache(ctypes.Structure):
+    _fields_ = [("caption", c_void_p), ("shallow", c_void_p), ("layers", c_int32),
+                ("interval", c_int32), ("caption_valid", c_int32), ("shallow_valid", c_int32)]
 
 
 class DitError(RuntimeError):
@@ -127,6 +143,14 @@ def _load() -> ctypes.CDLL:
         "dit_unpatchify_video": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                            c_void_p]),
         "dit_pack_audio": (c_int32, [c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+        "dit_patchify_image": (c_int32, [c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                         c_void_p]),
+        "dit_unpatchify_image": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                           c_void_p]),
+        "dit_zimage_workspace_size": (c_size_t, [P(DitZimageModel), c_int32, c_int32, c_int32]),
+        "dit_zimage_forward": (c_int32, [P(DitZimageModel), c_void_p, c_int32, c_int32, c_void_p,
+                                         c_int32, c_void_p, c_double, c_int32, P(DitZimageCache),
+                                         c_void_p, c_void_p, c_size_t, c_void_p]),
         "dit_unpack_audio": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
         "dit_rms_norm": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_float, c_void_p,
                                    c_void_p]),
@@ -369,7 +393,8 @@ def profile_end() -> Dict[str, float]:
 def final_forward(blk: "Block", h, rows, sigmas: Sequence[float], out=None, workspace=None,
                   stream=None):
     """Output head (a Block prepared with a DIT_FINAL config): out = -(W
-    modulate(RMSNorm(h)) + b), fp32 [n, F]."""
+    modulate(RMSNorm(h)) + b), fp32 [n, F]; with a DIT_ZFINAL config the
+    Z-Image final layer (sigmas = [t])."""
     import torch
     n = int(h.shape[0])
     if out is None:
@@ -442,6 +467,24 @@ def pack_audio(x, dtype_out=None, stream=None):
     return rows
 
 
+def patchify_image(x, dtype_out=None, stream=None):
+    """[C, H, W] fp32 -> rows [(H/2)*(W/2), 4C], channel-fastest columns."""
+    import torch
+    C, H, W = (int(v) for v in x.shape)
+    td = torch.bfloat16 if dtype_out == "bf16" else torch.float32
+    rows = torch.empty(((H // 2) * (W // 2), 4 * C), dtype=td, device=x.device)
+    _check(lib.dit_patchify_image(BF16 if td == torch.bfloat16 else F32, _ptr(x), C, H, W,
+                                  _ptr(rows), _stream(stream)))
+    return rows
+
+
+def unpatchify_image(rows, C: int, H: int, W: int, stream=None):
+    import torch
+    x = torch.empty((C, H, W), dtype=torch.float32, device=rows.device)
+    _check(lib.dit_unpatchify_image(_ptr(rows), C, H, W, _ptr(x), _stream(stream)))
+    return x
+
+
 def unpack_audio(rows, C: int, T: int, stream=None):
     import torch
     x = torch.empty((C, 2, T), dtype=torch.float32, device=rows.device)
@@ -512,3 +555,80 @@ class Mmh3Model:
                                     _ptr(vout), _ptr(aout), self._ws.data_ptr(), self._ws.numel(),
                                     _stream(stream)))
         return vout, aout
+
+
+class ZimageCache:
+    """Step-level reuse state of ZimageModel.forward: device buffers for the
+    refined caption and the stream after the first ``layers`` main layers,
+    refreshed when step % interval == 0.  ``reset()`` starts a new generation."""
+
+    def __init__(self, model: "ZimageModel", H: int, W: int, cap_len: int, layers: int,
+                 interval: int):
+        import torch
+        D = model.D
+        n = (H // 2) * (W // 2) + cap_len
+        self.caption = torch.empty((max(cap_len, 1), D), dtype=torch.float32, device="cuda")
+        self.shallow = torch.empty((n, D), dtype=torch.float32, device="cuda")
+        c = DitZimageCache()
+        c.caption, c.shallow = self.caption.data_ptr(), self.shallow.data_ptr()
+        c.layers, c.interval = layers, interval
+        self.c = c
+
+    def reset(self) -> None:
+        self.c.caption_valid = 0
+        self.c.shallow_valid = 0
+
+
+class ZimageModel:
+    """The Z-Image transformer over prepared pieces: main layers and noise
+    refiners (Blocks with a DIT_ZIMAGE config), context refiners (DIT_ZCONTEXT),
+    the final layer (DIT_ZFINAL) and the embedders (device tensors: x_embed_w
+    [D, 4C] and cap_embed_w [D, cap_dim] in the blocks' dtype, fp32 biases and
+    the caption RMSNorm gain)."""
+
+    def __init__(self, layers: Sequence["Block"], noise_refiners: Sequence["Block"],
+                 context_refiners: Sequence["Block"], final: "Block", in_channels: int,
+                 x_embed_w, x_embed_b, cap_norm, cap_embed_w, cap_embed_b, cap_eps: float = 1e-6,
+                 block_cfg: Optional[DitConfig] = None, context_cfg: Optional[DitConfig] = None):
+        self.layers, self.noise, self.context = list(layers), list(noise_refiners), list(context_refiners)
+        self.final = final
+        arr = lambda bl: (c_void_p * max(len(bl), 1))(*[b.prepared.data_ptr() for b in bl])  # noqa: E731
+        self._arrs = (arr(self.layers), arr(self.noise), arr(self.context))
+        self._keep = (x_embed_w, x_embed_b, cap_norm, cap_embed_w, cap_embed_b)
+        bcfg = block_cfg or (self.layers or self.noise)[0].cfg
+        ccfg = context_cfg or self.context[0].cfg
+        self._cfgs = (bcfg, ccfg)
+        m = DitZimageModel()
+        m.block = ctypes.pointer(bcfg)
+        m.layers, m.n_layers = self._arrs[0], len(self.layers)
+        m.noise_refiners, m.n_noise_refiners = self._arrs[1], len(self.noise)
+        m.context = ctypes.pointer(ccfg)
+        m.context_refiners, m.n_context_refiners = self._arrs[2], len(self.context)
+        m.final_layer = ctypes.pointer(final.cfg)
+        m.final_w = final.prepared.data_ptr()
+        m.in_channels, m.cap_dim = in_channels, int(cap_embed_w.shape[1])
+        m.x_embed_w, m.x_embed_b = _ptr(x_embed_w), _ptr(x_embed_b)
+        m.cap_norm, m.cap_eps = _ptr(cap_norm), cap_eps
+        m.cap_embed_w, m.cap_embed_b = _ptr(cap_embed_w), _ptr(cap_embed_b)
+        self._m = m
+        self.D = bcfg.D
+        self._ws = None
+
+    def forward(self, latents, cap_feats, pos, t: float, step: int = 0,
+                cache: Optional[ZimageCache] = None, stream=None):
+        """latents [C, H, W] fp32, cap_feats [L, cap_dim] fp32, pos [(H/2)(W/2) + L, 3]
+        (image first).  Returns the final layer's output as [C, H, W]."""
+        import torch
+        C, H, W = (int(v) for v in latents.shape)
+        L = int(cap_feats.shape[0])
+        need = lib.dit_zimage_workspace_size(ctypes.byref(self._m), H, W, L)
+        if need == 0:
+            raise DitError(-1, lib.dit_last_error().decode())
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(latents)
+        cp = ctypes.byref(cache.c) if cache is not None else None
+        _check(lib.dit_zimage_forward(ctypes.byref(self._m), _ptr(latents), H, W, _ptr(cap_feats), L,
+                                      _ptr(pos), t, step, cp, _ptr(out), self._ws.data_ptr(),
+                                      self._ws.numel(), _stream(stream)))
+        return out

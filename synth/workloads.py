@@ -33,8 +33,10 @@ class BlockSpec:
     variant: "mmh3" (six-chunk adaLN from a rank-r timestep-curve basis,
     [MMH3] ``block_forward``), "siglip" (pre-LayerNorm encoder layer,
     [SIGLIP] ``Layer::forward``), "zimage" (four-chunk tanh-gated
-    sandwich-norm block, [ZIMG] ``TransformerBlock.Forward``) or "refiner"
-    (the mmh3 block without modulation, [MMH3] ``refine_text``).
+    sandwich-norm block, [ZIMG] ``TransformerBlock.Forward``), "refiner"
+    (the mmh3 block without modulation, [MMH3] ``refine_text``), "zcontext"
+    (the zimage block without modulation, its context refiner), and the output
+    heads "final" ([MMH3] heads) and "zfinal" ([ZIMG] ``FinalLayer``).
     """
 
     name: str
@@ -64,13 +66,14 @@ class BlockSpec:
 
     @property
     def chunks(self) -> int:
-        return {"mmh3": 6, "zimage": 4, "siglip": 0, "refiner": 0, "final": 2}[self.variant]
+        return {"mmh3": 6, "zimage": 4, "siglip": 0, "refiner": 0, "final": 2, "zcontext": 0,
+                "zfinal": 1}[self.variant]
 
     @property
     def mod_rows(self) -> int:
         if self.variant in ("mmh3", "final"):
             return self.slots * self.tags
-        if self.variant == "zimage":
+        if self.variant in ("zimage", "zfinal"):
             return 1
         return 0
 
@@ -299,6 +302,23 @@ def weight_shapes(spec: BlockSpec) -> List[Tuple[str, Tuple[int, ...], str]]:
             ("w_fc1", (F, D), "lin"), ("b_fc1", (F,), "vec"),
             ("w_fc2", (D, F), "lin"), ("b_fc2", (D,), "vec"),
         ]
+    if spec.variant == "zcontext":  # the Z-Image block without its timestep / adaLN tensors
+        return [
+            ("norm1", (D,), "gain"), ("post_attn_norm", (D,), "gain"),
+            ("norm2", (D,), "gain"), ("post_ffn_norm", (D,), "gain"),
+            ("w_qkv", (3 * D, D), "lin"), ("w_out", (D, D), "lin"),
+            ("q_norm", (hd,), "gain"), ("k_norm", (hd,), "gain"),
+            ("w_fc1", (2 * F, D), "lin"), ("w_fc2", (D, F), "lin"),
+        ]
+    if spec.variant == "zfinal":  # Z-Image final layer: F = output width
+        return [
+            ("w_fc1", (F, D), "lin"), ("b_fc1", (F,), "vec"),
+            ("temb_w1", (spec.temb_hidden, spec.temb_freq), "vec"),
+            ("temb_b1", (spec.temb_hidden,), "vec"),
+            ("temb_w2", (spec.temb_freq, spec.temb_hidden), "vec"),
+            ("temb_b2", (spec.temb_freq,), "vec"),
+            ("ada_w", (D, spec.temb_freq), "vec"), ("ada_b", (D,), "vec"),
+        ]
     if spec.variant == "zimage":
         return [
             ("norm1", (D,), "gain"), ("post_attn_norm", (D,), "gain"),
@@ -436,7 +456,7 @@ def make_custom_workload(spec: BlockSpec, seed: int, pos: Optional[np.ndarray] =
     if not sigmas:
         sigmas = [float(v) for v in rng.uniform(0.0, 1.0, size=max(spec.slots, 1))]
     plan = [("value", float(s)) for s in sigmas]
-    if spec.variant in ("siglip", "refiner"):
+    if spec.variant in ("siglip", "refiner", "zcontext"):
         plan = []
     return Workload(spec, x, rows, None if pos is None else np.asarray(pos, np.float32),
                     plan, make_weights(spec, seed + 1), seed)

@@ -96,7 +96,7 @@ def run_gpu(spec, wl, dit, out_alias=False, seq_starts=None, mods_in=None):
     st["x1"] = f64(ws_view(ws, L.x1, torch.float32, (n, D)))
     st["xn2"] = f64(ws_view(ws, L.xn, ad, (n, D)))
     st["a"] = f64(ws_view(ws, L.a, ad, (n, F)))
-    if spec.variant == "zimage":
+    if spec.variant in ("zimage", "zcontext"):
         st["y2"] = f64(ws_view(ws, L.y, torch.float32, (n, D)))
     st["out"] = f64(out)
     # padding of the head-major panels must be zero (finite keys/values)

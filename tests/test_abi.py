@@ -126,6 +126,39 @@ def test_partial_rope_and_shared_adaln_configs(dit):
     assert "rope_freq" in dit.last_error()
 
 
+def test_zimage_model_configs_and_workspace(dit):
+    z = W.spec_by_name("zimage")
+    cfgs = {v: dit.make_config(W.small_spec(z, variant=v, F=64 if v == "zfinal" else z.F))
+            for v in ("zimage", "zcontext", "zfinal")}
+    for c in cfgs.values():
+        assert dit.lib.dit_validate_config(ctypes.byref(c)) == 0
+    # the context refiner has no timestep tensors; the final layer no block weights
+    assert dit.lib.dit_prepared_size(ctypes.byref(cfgs["zcontext"])) < \
+        dit.lib.dit_prepared_size(ctypes.byref(cfgs["zimage"]))
+    Lc = dit.workspace_layout(cfgs["zcontext"], 512)
+    assert Lc.mods == dit.NONE_OFFSET and Lc.temb == dit.NONE_OFFSET and Lc.y != dit.NONE_OFFSET
+    Lf = dit.workspace_layout(cfgs["zfinal"], 4096)
+    assert Lf.q == dit.NONE_OFFSET and Lf.temb != dit.NONE_OFFSET and Lf.mods != dit.NONE_OFFSET
+    # a block entry point refuses the head, the head entry point refuses a block
+    assert _fwd(dit, cfgs["zfinal"]) == -6
+    m = dit.DitZimageModel()
+    m.block, m.context, m.final_layer = (ctypes.pointer(cfgs[v]) for v in ("zimage", "zcontext", "zfinal"))
+    arr = (ctypes.c_void_p * 2)(256, 512)
+    m.layers, m.n_layers = arr, 2
+    m.noise_refiners, m.n_noise_refiners = arr, 1
+    m.context_refiners, m.n_context_refiners = arr, 1
+    m.final_w, m.in_channels, m.cap_dim = 256, 16, 2560
+    m.x_embed_w, m.cap_norm, m.cap_embed_w, m.cap_eps = 256, 256, 256, 1e-6
+    size = dit.lib.dit_zimage_workspace_size(ctypes.byref(m), 128, 128, 512)
+    assert size > 4608 * 3072 * 4
+    assert dit.lib.dit_zimage_workspace_size(ctypes.byref(m), 127, 128, 512) == 0
+    m.in_channels = 15  # 4C = 60: not a multiple of the bf16 GEMM depth
+    assert dit.lib.dit_zimage_workspace_size(ctypes.byref(m), 128, 128, 512) == 0
+    m.in_channels = 16
+    m.context = ctypes.pointer(cfgs["zimage"])
+    assert dit.lib.dit_zimage_workspace_size(ctypes.byref(m), 128, 128, 512) == 0
+
+
 def test_workspace_layout_monotone(dit):
     c = _cfg(dit)
     L = dit.workspace_layout(c, 25600)

@@ -89,7 +89,7 @@ def _small(variant, dtype, n, D, hd, F, slots=2, rope=None, axes=None, theta=1e4
     H = D // hd
     if rope is None:
         rope = {"mmh3": "split_half", "zimage": "interleaved", "siglip": "none",
-                "refiner": "none"}[variant]
+                "refiner": "none", "zcontext": "interleaved"}[variant]
     if axes is None:
         axes = (0, 0, 0) if rope == "none" else ((hd // 4, hd // 8 * 3, hd // 8 * 3) if hd == 128 else (16, 24, 24))
     return W.BlockSpec(f"small-{variant}-{dtype}-{n}", variant, dtype, n=n, D=D, H=H, hd=hd, F=F,
@@ -108,6 +108,8 @@ SMALL = [
     ("zimage", "f32", 90, 256, 64, 256),
     ("refiner", "bf16", 333, 256, 128, 384),
     ("refiner", "f32", 77, 256, 64, 256),
+    ("zcontext", "bf16", 321, 256, 128, 384),
+    ("zcontext", "f32", 90, 256, 64, 256),
 ]
 
 

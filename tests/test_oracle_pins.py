@@ -902,6 +902,124 @@ def test_zimage_block_matches_torch_composition():
     np.testing.assert_allclose(got, want.numpy(), rtol=1e-11, atol=1e-12)
 
 
+def test_zimage_context_block_is_the_block_with_unit_gates():
+    # no modulation: scale 0 and tanh(gate) = 1 (tanh(+inf) is exactly 1)
+    spec, x, pos, w = _tiny_zimage()
+    cspec = W.small_spec(spec, variant="zcontext")
+    D = spec.D
+    mods = np.zeros((1, 4 * D))
+    mods[0, D:2 * D] = np.inf
+    mods[0, 3 * D:] = np.inf
+    got = O.zimage_context_block(cspec, x, pos, w)
+    want = O.zimage_block(spec, x, pos, None, w, mods=mods)
+    for k in ("xn", "q", "o", "x1", "a", "out"):
+        np.testing.assert_allclose(got[k], want[k], rtol=1e-13, atol=1e-14)
+    assert O.block(cspec, x, None, pos, [], w)["out"] is not None
+
+
+def test_zimage_final_layer_matches_torch_composition():
+    import torch
+    import torch.nn.functional as Fn
+    fspec = W.BlockSpec("tiny_zf", "zfinal", "f32", n=5, D=16, H=2, hd=8, F=32, eps=1e-6,
+                        temb_freq=16, temb_hidden=24)
+    w = {k: v.astype(np.float64) for k, v in W.make_custom_workload(fspec, 31).weights.items()}
+    h = np.random.default_rng(5).standard_normal((5, 16)) * 3.0 + 1.0
+    tw = {k: torch.from_numpy(v) for k, v in w.items()}
+    t = 0.7
+    half = 8
+    f = torch.exp(-math.log(10000.0) * torch.arange(half, dtype=torch.float64) / half)
+    arg = t * fspec.t_scale * f
+    emb = torch.cat([torch.cos(arg), torch.sin(arg)])
+    temb = Fn.linear(Fn.silu(Fn.linear(emb, tw["temb_w1"], tw["temb_b1"])), tw["temb_w2"], tw["temb_b2"])
+    scale = Fn.linear(Fn.silu(temb), tw["ada_w"], tw["ada_b"])
+    xn = Fn.layer_norm(torch.from_numpy(h), (16,), eps=1e-6) * (1 + scale)
+    want = Fn.linear(xn, tw["w_fc1"], tw["b_fc1"])
+    got = O.zimage_final_layer(fspec, h, t, w)["out"]
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_patchify_image_is_the_page_layout_and_inverts():
+    rng = np.random.default_rng(6)
+    C, H, W_ = 3, 6, 8
+    x = rng.standard_normal((C, H, W_))
+    # [C, H, W] -> [C, 1, 1, H/2, 2, W/2, 2] -> axes (1, 2, 3, 5, 4, 6, 0) -> [L, 4C]
+    via = x.reshape(C, 1, 1, H // 2, 2, W_ // 2, 2).transpose(1, 2, 3, 5, 4, 6, 0).reshape(-1, 4 * C)
+    rows = O.patchify_image(x)
+    np.testing.assert_array_equal(rows, via)
+    np.testing.assert_array_equal(O.unpatchify_image(rows, C, H, W_), x)
+
+
+def _tiny_zimage_model():
+    D, H_, hd, F, C, cap_dim = 16, 2, 8, 12, 4, 8
+    common = dict(D=D, H=H_, hd=hd, F=F, rope="interleaved", rope_axes=(2, 2, 4), rope_theta=256.0,
+                  temb_freq=16, temb_hidden=24, t_scale=1000.0)
+    bspec = W.BlockSpec("zm", "zimage", "f32", n=7, **common)
+    cspec = W.BlockSpec("zc", "zcontext", "f32", n=3, **common)
+    fspec = W.BlockSpec("zf", "zfinal", "f32", n=4, eps=1e-6, **dict(common, F=4 * C))
+    f64 = lambda d: {k: v.astype(np.float64) for k, v in d.items()}  # noqa: E731
+    wl = [f64(W.make_custom_workload(bspec, 50 + i).weights) for i in range(3)]
+    wn = [f64(W.make_custom_workload(bspec, 60).weights)]
+    wc = [f64(W.make_custom_workload(cspec, 70).weights)]
+    wf = f64(W.make_custom_workload(fspec, 80).weights)
+    rng = np.random.default_rng(81)
+    emb = dict(x_embed_w=0.3 * rng.standard_normal((D, 4 * C)), x_embed_b=0.1 * rng.standard_normal(D),
+               cap_norm=1 + 0.1 * rng.standard_normal(cap_dim), cap_eps=1e-6,
+               cap_embed_w=0.3 * rng.standard_normal((D, cap_dim)), cap_embed_b=0.1 * rng.standard_normal(D))
+    pos = W.zimage_positions(2, 2, 3)
+    return (bspec, cspec, fspec, wl, wn, wc, wf, emb, pos, C, cap_dim, rng)
+
+
+def _zf(m, lat, cap, t, step=0, cache=None):
+    bspec, cspec, fspec, wl, wn, wc, wf, emb, pos = m[:9]
+    return O.zimage_forward(bspec, cspec, fspec, lat, cap, pos, t, wl, wn, wc, wf, emb["x_embed_w"],
+                            emb["x_embed_b"], emb["cap_norm"], emb["cap_eps"], emb["cap_embed_w"],
+                            emb["cap_embed_b"], step=step, cache=cache)
+
+
+def test_zimage_forward_composes_the_pinned_pieces():
+    m = _tiny_zimage_model()
+    bspec, cspec, fspec, wl, wn, wc, wf, emb, pos, C, cap_dim, rng = m
+    lat = rng.standard_normal((C, 4, 4))
+    cap = rng.standard_normal((3, cap_dim))
+    t = 0.45
+    x = O.patchify_image(lat) @ emb["x_embed_w"].T + emb["x_embed_b"]
+    x = O.zimage_block(bspec, x, pos[:4], t, wn[0])["out"]
+    c = O.rms_norm(cap, emb["cap_norm"], 1e-6) @ emb["cap_embed_w"].T + emb["cap_embed_b"]
+    c = O.zimage_context_block(cspec, c, pos[4:], wc[0])["out"]
+    u = np.concatenate([x, c])
+    for w in wl:
+        u = O.zimage_block(bspec, u, pos, t, w)["out"]
+    want = O.unpatchify_image(O.zimage_final_layer(fspec, u[:4], t, wf)["out"], C, 4, 4)
+    np.testing.assert_allclose(_zf(m, lat, cap, t), want, rtol=1e-12, atol=1e-12)
+
+
+def test_zimage_forward_step_cache_semantics():
+    m = _tiny_zimage_model()
+    bspec, cspec, fspec, wl, wn, wc, wf, emb, pos, C, cap_dim, rng = m
+    lats = [rng.standard_normal((C, 4, 4)) for _ in range(4)]
+    cap = rng.standard_normal((3, cap_dim))
+    ts = [0.9, 0.7, 0.5, 0.3]
+    # interval 1: every step refreshes, so every step is the plain forward
+    c1 = {"layers": 2, "interval": 1}
+    for s in range(3):
+        np.testing.assert_allclose(_zf(m, lats[s], cap, ts[s], s, c1), _zf(m, lats[s], cap, ts[s]),
+                                   rtol=1e-12, atol=1e-12)
+    # interval 2, two shallow layers of three: step 0 stores, step 1 reads them
+    c2 = {"layers": 2, "interval": 2}
+    _zf(m, lats[0], cap, ts[0], 0, c2)
+    u_stored = c2["outs"][1]
+    got = _zf(m, lats[1], cap, ts[1], 1, c2)
+    u = O.zimage_block(bspec, u_stored, pos, ts[1], wl[2])["out"]
+    want = O.unpatchify_image(O.zimage_final_layer(fspec, u[:4], ts[1], wf)["out"], C, 4, 4)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    # a reused step does not see its latents or the caption features (computed once)
+    again = _zf(m, lats[3], rng.standard_normal((3, cap_dim)), ts[1], 1, c2)
+    np.testing.assert_array_equal(again, got)
+    # step 2 refreshes: the plain forward again (the caption is the stored one, equal)
+    np.testing.assert_allclose(_zf(m, lats[2], cap, ts[2], 2, c2), _zf(m, lats[2], cap, ts[2]),
+                               rtol=1e-12, atol=1e-12)
+
+
 def test_rel_rms():
     assert O.rel_rms(np.array([1.0, 2.0]), np.array([1.0, 2.0])) == 0.0
     assert O.rel_rms(np.array([2.0, 0.0]), np.array([1.0, 0.0])) == 1.0

@@ -48,10 +48,25 @@ template <> struct Elt<bf16_t> {
   }
 };
 
-DIT_DEV float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Sum over each 32-lane half of the wave, left in every lane of that half:
+// DPP exchanges inside rows of 16 lanes (quad_perm [1,0,3,2] and [2,3,0,1],
+// then row_ror by 4 and 8), then one ds_swizzle that swaps the two rows of
+// the half (bitmask mode, xor 16).
+#define DIT_DPP(v_, ctrl_) \
+  __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v_), (ctrl_), 0xF, 0xF, false))
+DIT_DEV float sum32(float v) {
+  v += DIT_DPP(v, 0xB1);   // quad_perm [1,0,3,2]
+  v += DIT_DPP(v, 0x4E);   // quad_perm [2,3,0,1]
+  v += DIT_DPP(v, 0x124);  // row_ror:4
+  v += DIT_DPP(v, 0x128);  // row_ror:8
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // lane ^ 16
   return v;
+}
+
+DIT_DEV float wave_sum(float v) {
+  v = sum32(v);
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 DIT_DEV float wave_max(float v) {

@@ -120,13 +120,11 @@ DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rb
         float s0 = (HD == 128) ? (x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3])
                                : x[0] * x[0] + x[1] * x[1];
         float s1 = (HD == 128) ? 0.0f : x[2] * x[2] + x[3] * x[3];
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) {
-          s0 += __shfl_xor(s0, o, 64);
-          if (HD != 128) s1 += __shfl_xor(s1, o, 64);
-        }
-        const float i0 = 1.0f / sqrtf(s0 * (1.0f / HD) + ep.qk_eps);
-        const float i1 = (HD == 128) ? i0 : 1.0f / sqrtf(s1 * (1.0f / HD) + ep.qk_eps);
+        s0 = sum32(s0);
+        if (HD != 128) s1 = sum32(s1);
+        // v_rsq_f32 (about one ulp): the result is rounded to bf16
+        const float i0 = __builtin_amdgcn_rsqf(s0 * (1.0f / HD) + ep.qk_eps);
+        const float i1 = (HD == 128) ? i0 : __builtin_amdgcn_rsqf(s1 * (1.0f / HD) + ep.qk_eps);
 #pragma unroll
         for (int ni = 0; ni < GNI; ++ni) x[ni] *= ((HD == 128 || ni < 2) ? i0 : i1) * gv[ni];
       }
@@ -153,7 +151,7 @@ DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rb
         } else {  // interleaved: pair (2i, 2i + 1) is in lanes cl and cl ^ 1
 #pragma unroll
           for (int ni = 0; ni < GNI; ++ni) {
-            const float oth = __shfl_xor(x[ni], 1, 64);
+            const float oth = DIT_DPP(x[ni], 0xB1);  // lane ^ 1
             const float2 c = csr[((32 * ni + cl) & (HD - 1)) >> 1];
             const float xe = even ? x[ni] : oth, xo = even ? oth : x[ni];
             x[ni] = even ? (xe * c.x - xo * c.y) : (xe * c.y + xo * c.x);

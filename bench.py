@@ -41,7 +41,7 @@ def cpu_baseline(spec, wl, seq_starts=None):
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
     sig = O.resolve_sigmas(wl.slot_plan)
-    m1, m2 = 64, 1088
+    m1, m2 = 64, 4096  # about 10-15 s of host work at the 25.6k-token block
     times = {}
     for m in (m1, m2):
         rows = np.linspace(0, spec.n - 1, m).astype(np.int64)

@@ -318,12 +318,15 @@ dit_status dit_unpack_audio(const float* rows, int32_t C, int32_t T, float* x, v
  * dit_mmh3_slots and the token rows, the blocks in order, then the video and
  * audio heads (dit_final_forward, negated) and the unpacking of their rows.
  * Condition latents are taken as given (any noise augmentation is the
- * caller's); the text span carries the text tag. */
+ * caller's); the text span carries the text tag unless per-token tags are
+ * given. */
 typedef enum {
   DIT_SEG_TEXT = 0,
-  DIT_SEG_VIDEO = 1,  /* the noisy target, T*(H/2)*(W/2) rows */
-  DIT_SEG_AUDIO = 2,  /* 2*Ta rows */
-  DIT_SEG_COND = 3    /* one condition frame, (H/2)*(W/2) rows */
+  DIT_SEG_VIDEO = 1,      /* the noisy target, T*(H/2)*(W/2) rows */
+  DIT_SEG_AUDIO = 2,      /* 2*Ta rows */
+  DIT_SEG_COND = 3,       /* one condition frame, (H/2)*(W/2) rows */
+  DIT_SEG_REF_IMAGE = 4,  /* layout only: a reference image, or a reference clip's frames */
+  DIT_SEG_REF_AUDIO = 5   /* layout only: reference audio, or a reference clip's soundtrack */
 } dit_segment_kind;
 
 typedef struct dit_segment {
@@ -352,12 +355,47 @@ typedef struct dit_mmh3_model {
                                        reference model                                     */
 } dit_mmh3_model;
 
+/* The packed layout of one evaluation ([MMH3] Layout::t2va / fl2va / ref2va):
+ * segments in order [text | references | keyframes | audio | video] and every
+ * row's (t, h, w) position, in fp64 as the page keeps them.
+ *   text token i at (i, 0, 0); the cursor starts at text_len;
+ *   the h and w axes of a lat_h x lat_w latent are the dim/2 points
+ *     32 * ((1 - r)/2 + i * r / (dim/2)), r = dim / sqrt(lat_h * lat_w);
+ *   references (refs, in order) advance the cursor: an image by 1 (its own
+ *     grid, one time step); an audio block by its frames (stereo at the
+ *     target's w extremes); a clip packs its soundtrack (its own grid's w
+ *     extremes) then its frames from the cursor and advances by the longer;
+ *   keyframes (pairs pixel_index, frame_count: the clip's first frame, at the
+ *     cursor, or its last, at cursor + all frame spans - 5/3) share the target
+ *     grid and do not advance the cursor;
+ *   audio: 2 * audio_t rows, channel-major, (cursor + i, 0, w_lo) then
+ *     (cursor + i, 0, w_hi); video: latent_t frames of the target grid from
+ *     the cursor, t advancing by 5/3 * (1, 4, 4, 4, 4)[k % 5].
+ * Host function.  lat_h, lat_w >= 2 (refs likewise).  Returns the row count
+ * and sets *n_segs; with pos == NULL only counts.  pos: [max_rows, 3];
+ * segs: [max_segs].  Errors (negative): DIT_EINVAL for a keyframe that is not
+ * a first or last frame or an unknown reference kind, DIT_ESHAPE for sizes or
+ * too-small outputs. */
+typedef struct dit_layout_ref {
+  int32_t kind;  /* DIT_SEG_REF_IMAGE (lat_h, lat_w), DIT_SEG_REF_AUDIO (audio_t) or
+                    DIT_SEG_VIDEO for a reference clip (latent_t, lat_h, lat_w, audio_t) */
+  int32_t latent_t, lat_h, lat_w, audio_t;
+} dit_layout_ref;
+
+int32_t dit_mmh3_layout(int32_t text_len, int32_t latent_t, int32_t lat_h, int32_t lat_w,
+                        int32_t audio_t, const int32_t* keyframes, int32_t n_keyframes,
+                        const dit_layout_ref* refs, int32_t n_refs, double* pos, int32_t max_rows,
+                        dit_segment* segs, int32_t max_segs, int32_t* n_segs);
+
 /* Workspace bytes of dit_mmh3_forward for these segments (0 if invalid). */
 size_t dit_mmh3_workspace_size(const dit_mmh3_model* m, const dit_segment* segs, int32_t nseg);
 
 /* segs: host, nseg entries covering [0, n) without gaps; one VIDEO, at most one
  * AUDIO, one TEXT, any number of COND.  pos: device fp32 [n, 3].  text:
  * device fp32 [text rows, D] (refined).  video: device fp32 [latent_c, T, H, W];
+ * text_tags: device int32 [text rows], each token's modality tag (0 video, 1
+ * text, 2 audio: a vision block inside the prompt carries the video tag,
+ * [MMH3] Layout text_tags), clamped to [0, 2]; NULL = every token text.
  * audio: device fp32 [audio_c, 2, Ta] (NULL without an AUDIO segment).  cond:
  * host array of device pointers, one fp32 [latent_c, 1, H, W] per COND segment
  * in order.  Outputs (device fp32, same shapes as the inputs): the video and
@@ -365,7 +403,8 @@ size_t dit_mmh3_workspace_size(const dit_mmh3_model* m, const dit_segment* segs,
  * 16 (fp32): latent_c % 16 == 0 and audio_c % 64 == 0 for bf16 blocks,
  * latent_c % 4 == 0 and audio_c % 16 == 0 for fp32 blocks. */
 dit_status dit_mmh3_forward(const dit_mmh3_model* m, const dit_segment* segs, int32_t nseg,
-                            const float* pos, const float* text, const float* video, int32_t T,
+                            const float* pos, const float* text, const int32_t* text_tags,
+                            const float* video, int32_t T,
                             int32_t H, int32_t W, const float* audio, int32_t Ta,
                             const float* const* cond, double sigma_v, float* video_out,
                             float* audio_out, void* workspace, size_t ws_bytes, void* stream);

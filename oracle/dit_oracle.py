@@ -103,12 +103,13 @@ def mmh3_slots(sigma_v: float, shift_video: float, shift_audio: float, cond_aug:
     return ts, slot
 
 
-def mmh3_token_rows(segments, slot, tags: int = 3) -> np.ndarray:
+def mmh3_token_rows(segments, slot, tags: int = 3, text_tags=None) -> np.ndarray:
     """Per-token modulation row slot * tags + tag from (kind, start, stop)
     segments ([MMH3] ``MiniMaxH3::forward``): text at the video slot with the
-    text tag; video, condition frames and reference images with the video tag
-    (the latter two at the condition slot); audio and reference audio with the
-    audio tag."""
+    text tag, or with its own entry of ``text_tags`` (the layout's per-token
+    modality of the prompt span); video, condition frames and reference images
+    with the video tag (the latter two at the condition slot); audio and
+    reference audio with the audio tag."""
     video, text, audio = 0, 1, 2
     of = {"text": (slot["video"], text), "video": (slot["video"], video),
           "audio": (slot["audio"], audio), "cond": (slot["cond"], video),
@@ -118,6 +119,8 @@ def mmh3_token_rows(segments, slot, tags: int = 3) -> np.ndarray:
     for kind, a, b in segments:
         s, t = of[kind]
         rows[a:b] = s * tags + t
+        if kind == "text" and text_tags is not None:
+            rows[a:b] = s * tags + np.asarray(text_tags, dtype=np.int64)
     return rows
 
 
@@ -533,7 +536,7 @@ def unpack_audio(rows: np.ndarray, C: int, T: int) -> np.ndarray:
 def mmh3_forward(block_spec, head_v_spec, head_a_spec, segments, pos, text, video, audio, conds,
                  sigma_v: float, w_blocks, w_head_v, w_head_a, w_vpatch, b_vpatch, w_apatch,
                  b_apatch, shift_video=12.0, shift_audio=3.0, cond_aug=0.999,
-                 cond_aug_audio=1.0, audio_slope_rescale=False):
+                 cond_aug_audio=1.0, audio_slope_rescale=False, text_tags=None):
     """One denoise evaluation: embed (video and condition frames through the
     video patch projection, audio through the audio one, refined text as
     given), the blocks with the evaluation's slots and token rows, the two
@@ -546,7 +549,7 @@ def mmh3_forward(block_spec, head_v_spec, head_a_spec, segments, pos, text, vide
     ts, slot = mmh3_slots(sigma_v, shift_video, shift_audio, cond_aug, cond_aug_audio,
                           any(k == "cond" for k, _, _ in segments), False)
     sig = [1.0 - t for t in ts] + [1.0 - ts[-1]] * (block_spec.slots - len(ts))
-    rows = mmh3_token_rows(segments, slot)
+    rows = mmh3_token_rows(segments, slot, text_tags=text_tags)
     n, D = rows.shape[0], block_spec.D
     C, T, H, W = video.shape
     h = np.zeros((n, D))

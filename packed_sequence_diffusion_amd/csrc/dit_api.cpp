@@ -417,7 +417,7 @@ dit_status dit_profile_end(double* phase_ms, int32_t* calls) {
 }
 
 
-int32_t dit_abi_version(void) { return 3; }
+int32_t dit_abi_version(void) { return 4; }
 
 const char* dit_last_error(void) { return g_err; }
 
@@ -426,6 +426,123 @@ double dit_sigma_remap(double sigma, double from_shift, double to_shift) {
   // ([MMH3] time_shift_sigma).
   double base = sigma / (from_shift + sigma * (1.0 - from_shift));
   return to_shift * base / (1.0 + (to_shift - 1.0) * base);
+}
+
+// ------------------------------------------------------------ MMH3 layout ----
+namespace {
+// Latent frames a video token spans, cycling with period 5, rescaled onto the
+// time axis ([MMH3] FRAME_PER_TOKEN, FRAME_RESCALE).
+constexpr double kFrameRescale = 5.0 / 3.0;
+double frame_t(int k) {
+  static const double span[5] = {1.0, 4.0, 4.0, 4.0, 4.0};
+  return kFrameRescale * span[k % 5];
+}
+// dim/2 grid points of one spatial axis spread over a window of width dim /
+// sqrt(area) centred on 1/2, times 32 ([MMH3] axis_from_sqrt_area).
+std::vector<double> frac_axis(int dim, double sqrt_area) {
+  const double r = dim / sqrt_area;
+  const int m = dim / 2;
+  std::vector<double> a(m);
+  for (int i = 0; i < m; ++i) a[i] = ((1.0 - r) / 2.0 + i * (r / m)) * 32.0;
+  return a;
+}
+}  // namespace
+
+int32_t dit_mmh3_layout(int32_t text_len, int32_t latent_t, int32_t lat_h, int32_t lat_w,
+                        int32_t audio_t, const int32_t* keyframes, int32_t n_keyframes,
+                        const dit_layout_ref* refs, int32_t n_refs, double* pos, int32_t max_rows,
+                        dit_segment* segs, int32_t max_segs, int32_t* n_segs) {
+  if (text_len < 0 || latent_t < 0 || audio_t < 0 || lat_h < 2 || lat_w < 2 || n_keyframes < 0 ||
+      n_refs < 0)
+    return fail(DIT_ESHAPE, "layout sizes: counts >= 0, lat_h and lat_w >= 2");
+  if ((n_keyframes && !keyframes) || (n_refs && !refs)) return fail(DIT_EINVAL, "keyframes/refs is NULL");
+  std::vector<double> P;  // (t, h, w) per row
+  std::vector<dit_segment> G;
+  auto row = [&](double t, double h, double w) { P.push_back(t); P.push_back(h); P.push_back(w); };
+  auto nrows = [&]() { return (int32_t)(P.size() / 3); };
+  auto seg = [&](int kind, int start) { G.push_back(dit_segment{kind, start, nrows()}); };
+  auto stereo = [&](double c0, int t, double w_lo, double w_hi) {
+    for (int ch = 0; ch < 2; ++ch)
+      for (int i = 0; i < t; ++i) row(c0 + i, 0.0, ch ? w_hi : w_lo);
+  };
+  const double sq = sqrt((double)lat_h * lat_w);
+  const std::vector<double> ha = frac_axis(lat_h, sq), wa = frac_axis(lat_w, sq);
+  for (int i = 0; i < text_len; ++i) row(i, 0.0, 0.0);
+  seg(DIT_SEG_TEXT, 0);
+  double cursor = text_len;
+  for (int r = 0; r < n_refs; ++r) {
+    const dit_layout_ref& f = refs[r];
+    const int start = nrows();
+    if (f.kind == DIT_SEG_REF_IMAGE || f.kind == DIT_SEG_VIDEO) {
+      if (f.lat_h < 2 || f.lat_w < 2 || f.latent_t < 0 || f.audio_t < 0)
+        return fail(DIT_ESHAPE, "reference %d: lat_h, lat_w >= 2", r);
+      const double rs = sqrt((double)f.lat_h * f.lat_w);
+      const std::vector<double> rh = frac_axis(f.lat_h, rs), rw = frac_axis(f.lat_w, rs);
+      if (f.kind == DIT_SEG_REF_IMAGE) {
+        for (double h : rh)
+          for (double w : rw) row(cursor, h, w);
+        seg(DIT_SEG_REF_IMAGE, start);
+        cursor += 1.0;
+      } else {  // a clip: its soundtrack first, then its frames, from the same origin
+        if (f.audio_t > 0) {
+          stereo(cursor, f.audio_t, rw.front(), rw.back());
+          seg(DIT_SEG_REF_AUDIO, start);
+        }
+        const int fs = nrows();
+        double t = cursor, spans = 0.0;
+        for (int k = 0; k < f.latent_t; ++k) {
+          for (double h : rh)
+            for (double w : rw) row(t, h, w);
+          t += frame_t(k);
+          spans += frame_t(k);
+        }
+        seg(DIT_SEG_REF_IMAGE, fs);
+        cursor += std::max((double)f.audio_t, spans);
+      }
+    } else if (f.kind == DIT_SEG_REF_AUDIO) {
+      if (f.audio_t < 0) return fail(DIT_ESHAPE, "reference %d: audio_t < 0", r);
+      if (f.audio_t > 0) {
+        stereo(cursor, f.audio_t, wa.front(), wa.back());
+        seg(DIT_SEG_REF_AUDIO, start);
+      }
+      cursor += f.audio_t;
+    } else {
+      return fail(DIT_EINVAL, "reference %d: unknown kind %d", r, f.kind);
+    }
+  }
+  double spans = 0.0;
+  for (int k = 0; k < latent_t; ++k) spans += frame_t(k);
+  for (int i = 0; i < n_keyframes; ++i) {
+    const int pix = keyframes[2 * i], count = keyframes[2 * i + 1];
+    double t;
+    if (pix == 0) t = cursor;
+    else if (count > 0 && pix == count - 1) t = cursor + spans - kFrameRescale;
+    else return fail(DIT_EINVAL, "keyframe %d: pixel index %d is neither the first nor the last of %d", i, pix, count);
+    const int start = nrows();
+    for (double h : ha)
+      for (double w : wa) row(t, h, w);
+    seg(DIT_SEG_COND, start);
+  }
+  int start = nrows();
+  stereo(cursor, audio_t, wa.front(), wa.back());
+  seg(DIT_SEG_AUDIO, start);
+  start = nrows();
+  double t = cursor;
+  for (int k = 0; k < latent_t; ++k) {
+    for (double h : ha)
+      for (double w : wa) row(t, h, w);
+    t += frame_t(k);
+  }
+  seg(DIT_SEG_VIDEO, start);
+  if (n_segs) *n_segs = (int32_t)G.size();
+  if (pos) {
+    if (max_rows < nrows() || max_segs < (int32_t)G.size() || !segs)
+      return fail(DIT_ESHAPE, "layout needs %d rows and %zu segments (have %d, %d)", nrows(), G.size(), max_rows, max_segs);
+    memcpy(pos, P.data(), P.size() * sizeof(double));
+    memcpy(segs, G.data(), G.size() * sizeof(dit_segment));
+  }
+  g_err[0] = 0;
+  return nrows();
 }
 
 int32_t dit_mmh3_slots(double sigma_v, double shift_video, double shift_audio, double cond_aug,
@@ -1136,7 +1253,8 @@ size_t dit_mmh3_workspace_size(const dit_mmh3_model* m, const dit_segment* segs,
 }
 
 dit_status dit_mmh3_forward(const dit_mmh3_model* m, const dit_segment* segs, int32_t nseg,
-                            const float* pos, const float* text, const float* video, int32_t T,
+                            const float* pos, const float* text, const int32_t* text_tags,
+                            const float* video, int32_t T,
                             int32_t H, int32_t W, const float* audio, int32_t Ta,
                             const float* const* cond, double sigma_v, float* video_out,
                             float* audio_out, void* workspace, size_t ws_bytes, void* stream) {
@@ -1187,7 +1305,10 @@ dit_status dit_mmh3_forward(const dit_mmh3_model* m, const dit_segment* segs, in
       case DIT_SEG_AUDIO: row = slot[1] * 3 + 2; break;
       default: row = slot[2] * 3 + 0; break;
     }
-    HIP_TRY(dit::fill_i32(rows + g.start, len, row, s), "token rows");
+    if (g.kind == DIT_SEG_TEXT && text_tags)  // per-token modality of the prompt span
+      HIP_TRY(dit::rows_from_tags(text_tags, len, slot[0] * 3, rows + g.start, s), "token rows");
+    else
+      HIP_TRY(dit::fill_i32(rows + g.start, len, row, s), "token rows");
     float* hs = h + (size_t)g.start * D;
     if (g.kind == DIT_SEG_TEXT) {
       HIP_TRY(hipMemcpyAsync(hs, text, (size_t)len * D * 4, hipMemcpyDeviceToDevice, s), "text rows");

@@ -118,6 +118,8 @@ hipError_t unpatchify_image(const float* rows, int C, int H, int W, float* x, hi
 // p[0, n) = v (a kernel rather than a memset: safe inside captured graphs)
 hipError_t fill_i32(int* p, int n, int v, hipStream_t s);
 hipError_t fill_f32(float* p, int n, float v, hipStream_t s);
+// rows[i] = base + clamp(tags[i], 0, 2) (per-token modality rows of the prompt span)
+hipError_t rows_from_tags(const int* tags, int n, int base, int* rows, hipStream_t s);
 
 // ---- weight preparation ---------------------------------------------------------------
 // Source row of prepared row r, in this order: the SwiGLU group interleave (swiglu_F > 0);

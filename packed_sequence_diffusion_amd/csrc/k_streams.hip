@@ -79,6 +79,18 @@ hipError_t fill_i32(int* p, int n, int v, hipStream_t s) {
   return hipGetLastError();
 }
 
+// rows[i] = base + tag[i], the tag clamped to the three modalities
+__global__ void k_rows_from_tags(const int* __restrict__ tags, int n, int base, int* __restrict__ rows) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) rows[i] = base + min(max(tags[i], 0), 2);
+}
+
+hipError_t rows_from_tags(const int* tags, int n, int base, int* rows, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_rows_from_tags<<<blocks_for((size_t)n), 256, 0, s>>>(tags, n, base, rows);
+  return hipGetLastError();
+}
+
 hipError_t fill_f32(float* p, int n, float v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   k_fill<float><<<blocks_for((size_t)n), 256, 0, s>>>(p, n, v);

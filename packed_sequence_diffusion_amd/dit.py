@@ -57,7 +57,8 @@ class DitWsLayout(ctypes.Structure):
 
 NONE_OFFSET = (1 << (8 * ctypes.sizeof(c_size_t))) - 1
 
-SEG_KINDS = {"text": 0, "video": 1, "audio": 2, "cond": 3}
+SEG_KINDS = {"text": 0, "video": 1, "audio": 2, "cond": 3, "ref_image": 4, "ref_audio": 5}
+SEG_NAMES = {v: k for k, v in SEG_KINDS.items()}
 
 
 class DitSegment(ctypes.Structure):
@@ -74,6 +75,11 @@ class DitMmh3Model(ctypes.Structure):
                 ("shift_video", c_double), ("shift_audio", c_double),
                 ("cond_aug", c_double), ("cond_aug_audio", c_double),
                 ("audio_slope_rescale", c_int32)]
+
+
+class DitLayoutRef(ctypes.Structure):
+    _fields_ = [("kind", c_int32), ("latent_t", c_int32), ("lat_h", c_int32), ("lat_w", c_int32),
+                ("audio_t", c_int32)]
 
 
 class DitZimageModel(ctypes.Structure):
@@ -154,9 +160,13 @@ def _load() -> ctypes.CDLL:
         "dit_unpack_audio": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
         "dit_rms_norm": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_float, c_void_p,
                                    c_void_p]),
+        "dit_mmh3_layout": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, P(c_int32),
+                                      c_int32, P(DitLayoutRef), c_int32, P(c_double), c_int32,
+                                      P(DitSegment), c_int32, P(c_int32)]),
         "dit_mmh3_workspace_size": (c_size_t, [P(DitMmh3Model), P(DitSegment), c_int32]),
         "dit_mmh3_forward": (c_int32, [P(DitMmh3Model), P(DitSegment), c_int32, c_void_p,
-                                       c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                       c_void_p,
                                        c_int32, P(c_void_p), c_double, c_void_p, c_void_p,
                                        c_void_p, c_size_t, c_void_p]),
         "dit_attention": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_void_p, c_int32, c_int32,
@@ -207,6 +217,42 @@ def mmh3_slots(sigma_v: float, shift_video: float = 12.0, shift_audio: float = 3
     if k < 0:
         raise DitError(k, lib.dit_last_error().decode())
     return [sg[i] for i in range(k)], dict(zip(("video", "audio", "cond", "ref_audio"), so))
+
+
+_REF_KINDS = {"image": SEG_KINDS["ref_image"], "audio": SEG_KINDS["ref_audio"], "video": SEG_KINDS["video"]}
+
+
+def mmh3_layout(text_len: int, latent_t: int, lat_h: int, lat_w: int, audio_t: int,
+                keyframes: Sequence[Sequence[int]] = (), refs: Sequence[tuple] = ()):
+    """(segments [(kind name, start, stop)], positions float64 [n, 3]) through
+    dit_mmh3_layout.  keyframes: (pixel_index, frame_count) pairs; refs:
+    ("image", lat_h, lat_w), ("audio", t) or ("video", latent_t, lat_h, lat_w,
+    audio_t)."""
+    import numpy as np
+    kf = (c_int32 * max(2 * len(keyframes), 1))(*[int(v) for k in keyframes for v in k])
+    rr = (DitLayoutRef * max(len(refs), 1))()
+    for i, r in enumerate(refs):
+        f = rr[i]
+        f.kind = _REF_KINDS[r[0]]
+        if r[0] == "image":
+            f.lat_h, f.lat_w = r[1], r[2]
+        elif r[0] == "audio":
+            f.audio_t = r[1]
+        else:
+            f.latent_t, f.lat_h, f.lat_w, f.audio_t = r[1:5]
+    ns = c_int32()
+    n = lib.dit_mmh3_layout(text_len, latent_t, lat_h, lat_w, audio_t, kf, len(keyframes), rr, len(refs),
+                            None, 0, None, 0, ctypes.byref(ns))
+    if n < 0:
+        raise DitError(n, lib.dit_last_error().decode())
+    pos = np.zeros((max(n, 1), 3), dtype=np.float64)
+    segs = (DitSegment * max(ns.value, 1))()
+    got = lib.dit_mmh3_layout(text_len, latent_t, lat_h, lat_w, audio_t, kf, len(keyframes), rr,
+                              len(refs), pos.ctypes.data_as(POINTER(c_double)), n, segs, ns.value,
+                              ctypes.byref(ns))
+    if got < 0:
+        raise DitError(got, lib.dit_last_error().decode())
+    return [(SEG_NAMES[segs[i].kind], segs[i].start, segs[i].stop) for i in range(ns.value)], pos[:n]
 
 
 def resolve_sigmas(plan: Sequence[tuple]) -> List[float]:
@@ -535,8 +581,9 @@ class Mmh3Model:
         self._ws = None
 
     def forward(self, segments, pos, text, video, audio=None, conds=(), sigma_v: float = 0.5,
-                stream=None):
-        """segments: [(kind, start, stop)] with kinds text / video / audio / cond.
+                stream=None, text_tags=None):
+        """segments: [(kind, start, stop)] with kinds text / video / audio / cond;
+        text_tags: device int32 [text rows] per-token modality (None = text).
         Returns (video velocity [C, T, H, W], audio velocity [Ca, 2, Ta] or None)."""
         import torch
         segs = (DitSegment * len(segments))(*[DitSegment(SEG_KINDS[k], a, b) for k, a, b in segments])
@@ -551,7 +598,7 @@ class Mmh3Model:
         Ta = 0 if audio is None else int(audio.shape[2])
         cp = (c_void_p * max(len(conds), 1))(*[c.data_ptr() for c in conds])
         _check(lib.dit_mmh3_forward(ctypes.byref(self._m), segs, len(segments), _ptr(pos), _ptr(text),
-                                    _ptr(video), T, H, W, _ptr(audio), Ta, cp, sigma_v,
+                                    _ptr(text_tags), _ptr(video), T, H, W, _ptr(audio), Ta, cp, sigma_v,
                                     _ptr(vout), _ptr(aout), self._ws.data_ptr(), self._ws.numel(),
                                     _stream(stream)))
         return vout, aout

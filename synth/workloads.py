@@ -162,12 +162,21 @@ class Layout:
 
 def build_layout(text_len: int, latent_t: int, lat_h: int, lat_w: int, audio_t: int,
                  keyframes: Sequence[Tuple[int, int]] = (),
-                 ref_images: Sequence[Tuple[int, int]] = ()) -> Layout:
-    """Place ``[text | reference images | keyframes | audio | video]`` on the
+                 ref_images: Sequence[Tuple[int, int]] = (),
+                 refs: Sequence[tuple] = ()) -> Layout:
+    """Place ``[text | references | keyframes | audio | video]`` on the
     3-D position grid ([MMH3] ``Layout::t2va``/``fl2va``/``ref2va``).
+
+    ``refs``: ("image", lat_h, lat_w), ("audio", t) or ("video", latent_t,
+    lat_h, lat_w, audio_t), in order; ``ref_images`` (lat_h, lat_w) pairs are
+    image references placed before them.
 
     * text token i sits at (i, 0, 0);
     * a reference image occupies one time step at the cursor and advances it;
+    * a reference audio is a stereo block at the cursor (the target grid's w
+      extremes) and advances it by its frames;
+    * a reference clip packs its soundtrack (its own grid's w extremes) and then
+      its frames from the cursor, and advances it by the longer of the two;
     * a keyframe shares the target grid, sits at the first frame's time (the
       cursor) or the last frame's (cursor + all spans - one rescale) and does
       not advance the cursor;
@@ -186,13 +195,43 @@ def build_layout(text_len: int, latent_t: int, lat_h: int, lat_w: int, audio_t: 
     pos.extend((float(i), 0.0, 0.0) for i in range(text_len))
     cursor = float(text_len)
 
-    for rh, rw in ref_images:
-        rsq = math.sqrt(rh * rw)
-        ha, wa = _frac_axis(rh, 2, rsq), _frac_axis(rw, 2, rsq)
-        start = len(pos)
-        pos.extend((cursor, h, w) for h in ha for w in wa)
-        segs.append(("ref_image", start, len(pos)))
-        cursor += 1.0
+    def stereo(c0, t, w_lo, w_hi):
+        for w in (w_lo, w_hi):
+            pos.extend((c0 + i, 0.0, w) for i in range(t))
+
+    for ref in [("image", rh, rw) for rh, rw in ref_images] + list(refs):
+        if ref[0] == "image":
+            rh, rw = ref[1], ref[2]
+            rsq = math.sqrt(rh * rw)
+            ha, wa = _frac_axis(rh, 2, rsq), _frac_axis(rw, 2, rsq)
+            start = len(pos)
+            pos.extend((cursor, h, w) for h in ha for w in wa)
+            segs.append(("ref_image", start, len(pos)))
+            cursor += 1.0
+        elif ref[0] == "audio":
+            t = ref[1]
+            if t > 0:
+                start = len(pos)
+                stereo(cursor, t, w_axis[0], w_axis[-1])
+                segs.append(("ref_audio", start, len(pos)))
+            cursor += float(t)
+        elif ref[0] == "video":
+            vt, rh, rw, rat = ref[1:5]
+            rsq = math.sqrt(rh * rw)
+            ha, wa = _frac_axis(rh, 2, rsq), _frac_axis(rw, 2, rsq)
+            if rat > 0:
+                start = len(pos)
+                stereo(cursor, rat, wa[0], wa[-1])
+                segs.append(("ref_audio", start, len(pos)))
+            start = len(pos)
+            tc = cursor
+            for k in range(vt):
+                pos.extend((tc, h, w) for h in ha for w in wa)
+                tc += _frame_t(k)
+            segs.append(("ref_image", start, len(pos)))
+            cursor += max(float(rat), sum(_frame_t(k) for k in range(vt)))
+        else:
+            raise ValueError(ref[0])
 
     spans = sum(_frame_t(k) for k in range(latent_t))
     for pix, count in keyframes:

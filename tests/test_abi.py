@@ -43,7 +43,7 @@ def test_header_functions_exported(dit):
 
 
 def test_abi_version(dit):
-    assert dit.lib.dit_abi_version() == 3
+    assert dit.lib.dit_abi_version() == 4
 
 
 def test_sigma_remap_printed_points(dit):
@@ -258,6 +258,63 @@ def test_given_mods_refusals(dit):
     assert F(ctypes.byref(sig), 256, 16, 10, 16, 16, 256, None, 0, 16, 256, 1 << 40, None) == -6
     st = (ctypes.c_int32 * 2)(0, 9)
     assert F(ctypes.byref(c), 256, 16, 10, 16, 16, 256, st, 1, 16, 256, 1 << 40, None) == -2
+
+
+def test_mmh3_layout_printed_facts(dit):
+    """The library's layout builder against the page's printed layout tests."""
+    import json
+    import numpy as np
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "layouts.json")))
+    tl, lt, lh, lw, at = g["t2va_args"]
+    segs, pos = dit.mmh3_layout(tl, lt, lh, lw, at)
+    frame_rows = (lh // 2) * (lw // 2)
+    assert frame_rows == g["t2va_frame_rows"] and len(pos) == g["t2va_seq_len"]
+    assert [s[0] for s in segs] == g["t2va_order"]
+    v = [s for s in segs if s[0] == "video"][0]
+    assert abs(pos[v[1] + frame_rows, 0] - pos[v[1], 0] - g["video_t_first_step"]) < 1e-12
+    ksegs, kpos = dit.mmh3_layout(tl, lt, lh, lw, at, keyframes=g["keyframes"])
+    assert [s[0] for s in ksegs] == g["keyframe_order"]
+    assert len(kpos) == len(pos) + 2 * frame_rows
+    conds = [s for s in ksegs if s[0] == "cond"]
+    spans = sum(5.0 / 3.0 * (1.0, 4.0, 4.0, 4.0, 4.0)[k % 5] for k in range(lt))
+    assert kpos[conds[0][1], 0] == tl
+    assert abs(kpos[conds[1][1], 0] - (tl + spans - 5.0 / 3.0)) < 1e-12
+    kv = [s for s in ksegs if s[0] == "video"][0]
+    # keyframes share the target grid and do not move the audio or video
+    np.testing.assert_array_equal(kpos[conds[0][1]:conds[0][2], 1:], kpos[kv[1]:kv[1] + frame_rows, 1:])
+    np.testing.assert_array_equal(kpos[kv[1]:kv[2]], pos[v[1]:v[2]])
+
+
+def test_mmh3_layout_matches_the_input_recipe(dit):
+    """dit_mmh3_layout equals the layouts the workloads are built from, bit for
+    bit, for t2va, keyframes and every kind of reference."""
+    import numpy as np
+    cases = [((512, 16, 64, 96, 256), {}), ((64, 3, 16, 16, 0), {}),
+             ((8, 3, 8, 12, 5), dict(keyframes=[(0, 39), (38, 39)])),
+             ((512, 1, 128, 128, 0), dict(ref_images=[(128, 128)])),
+             ((8, 3, 8, 12, 5), dict(refs=[("image", 8, 8), ("audio", 4), ("video", 2, 8, 8, 3),
+                                           ("audio", 0), ("video", 3, 6, 10, 0)]))]
+    for args, kw in cases:
+        lay = W.build_layout(*args, **kw)
+        refs = [("image", h, w) for h, w in kw.get("ref_images", [])] + list(kw.get("refs", []))
+        segs, pos = dit.mmh3_layout(*args, keyframes=kw.get("keyframes", ()), refs=refs)
+        assert segs == lay.segments
+        np.testing.assert_array_equal(pos, lay.pos)
+
+
+def test_mmh3_layout_refusals(dit):
+    import pytest as pt
+    with pt.raises(dit.DitError):
+        dit.mmh3_layout(8, 3, 8, 12, 5, keyframes=[(5, 39)])  # neither first nor last frame
+    with pt.raises(dit.DitError):
+        dit.mmh3_layout(8, 3, 1, 12, 5)
+    with pt.raises(dit.DitError):
+        dit.mmh3_layout(8, 3, 8, 12, 5, refs=[("image", 8, 1)])
+    n = ctypes.c_int32()
+    pos = (ctypes.c_double * 30)()
+    segs = (dit.DitSegment * 3)()
+    # outputs too small for the 90 rows
+    assert dit.lib.dit_mmh3_layout(8, 3, 8, 12, 5, None, 0, None, 0, pos, 10, segs, 3, ctypes.byref(n)) == -2
 
 
 def test_mmh3_slots_match_the_oracle(dit):

@@ -182,12 +182,15 @@ def test_mmh3_denoise_evaluation(dit, dtype, compat):
     cu = lambda a, t=torch.float32: torch.from_numpy(a).to(t).cuda()  # noqa: E731
     model = dit.Mmh3Model(blocks, head_v, head_a, C, Ca, cu(wv, td), cu(bv), cu(wa, td), cu(ba),
                           audio_slope_rescale=compat)
+    # compat also gives the prompt a vision block (tokens 4..9 carry the video tag)
+    tags = np.full(16, 1, np.int32)
+    tags[4:10] = 0
     vout, aout = model.forward(lay.segments, cu(pos), cu(text), cu(video), cu(audio), [cu(cond)],
-                               sigma_v)
+                               sigma_v, text_tags=cu(tags, torch.int32) if compat else None)
     torch.cuda.synchronize()
     rv, ra = O.mmh3_forward(bspec, hv, ha, lay.segments, pos.astype(np.float64), text, video,
                             audio, [cond], sigma_v, wblocks, whv, wha, wv, bv, wa, ba,
-                            audio_slope_rescale=compat)
+                            audio_slope_rescale=compat, text_tags=tags if compat else None)
     ev = O.rel_rms(vout.cpu().numpy(), rv)
     ea = O.rel_rms(aout.cpu().numpy(), ra)
     log(f"[case] mmh3 evaluation {dtype} compat={compat} n={n}: video={ev:.2e} audio={ea:.2e}")

@@ -76,6 +76,16 @@ def test_mmh3_slots_rules():
     assert rows.tolist() == [1, 1, 6, 5, 5, 0]
 
 
+def test_token_rows_with_text_tags():
+    # rows = slot * 3 + tag; a vision block in the prompt takes the video tag at the text's slot
+    segs = [("text", 0, 5), ("cond", 5, 9), ("audio", 9, 11), ("video", 11, 15)]
+    slot = {"video": 0, "audio": 1, "cond": 2, "ref_audio": -1}
+    plain = O.mmh3_token_rows(segs, slot)
+    assert plain.tolist() == [1] * 5 + [6] * 4 + [5] * 2 + [0] * 4
+    tagged = O.mmh3_token_rows(segs, slot, text_tags=[1, 0, 0, 1, 2])
+    assert tagged.tolist() == [1, 0, 0, 1, 2] + plain[5:].tolist()
+
+
 def test_timestep_of_sigma():
     assert O.mmh3_timestep(0.3) == pytest.approx(0.7, abs=1e-15)
     assert O.mmh3_timestep(0.0) == 1.0 - 1e-6

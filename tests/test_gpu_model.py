@@ -130,15 +130,13 @@ def test_rms_norm(dit):
     assert O.rel_rms(got, ref) <= 1e-6
 
 
-@pytest.mark.parametrize("dtype,compat", [("bf16", False), ("f32", False), ("bf16", True),
-                                          ("f32", True)])
-def test_mmh3_denoise_evaluation(dit, dtype, compat):
-    """One whole evaluation at a small size: text, a first-frame keyframe,
-    stereo audio and two video frames; two blocks with their own weights;
-    video and audio heads.  Against the oracle's evaluation from the same
-    seeded pieces.  ``compat``: the checkpoint forms (shared RoPE frequencies
-    over 3k pairs, one adaLN basis for every slot in blocks and heads) and the
-    audio velocity pre-multiplied by d(sigma_a)/d(sigma_v)."""
+def _mmh3_setup(dit, dtype, compat):
+    """A small MMH3 model and one evaluation's inputs: text, a first-frame
+    keyframe, stereo audio and two video frames; two blocks with their own
+    weights; video and audio heads.  ``compat``: the checkpoint forms (shared
+    RoPE frequencies over 3k pairs, one adaLN basis for every slot in blocks and
+    heads), the audio velocity pre-multiplied by d(sigma_a)/d(sigma_v) and a
+    vision block inside the prompt (per-token text tags)."""
     import torch
     from synth.device import to_device
     hd = 128 if dtype == "bf16" else 64
@@ -164,13 +162,14 @@ def test_mmh3_denoise_evaluation(dit, dtype, compat):
         return W.bf16_round(w) if dtype == "bf16" else w
     wv, bv = lin((D, 4 * C)), (0.02 * rng.standard_normal(D)).astype(np.float32)
     wa, ba = lin((D, Ca)), (0.02 * rng.standard_normal(D)).astype(np.float32)
-    text = rng.standard_normal((16, D)).astype(np.float32)
-    video = rng.standard_normal((C, 2, 8, 8)).astype(np.float32)
-    audio = rng.standard_normal((Ca, 2, 12)).astype(np.float32)
-    cond = rng.standard_normal((C, 1, 8, 8)).astype(np.float32)
-    pos = lay.pos.astype(np.float32)
-    sigma_v = 0.42
-
+    host = dict(text=rng.standard_normal((16, D)).astype(np.float32),
+                video=rng.standard_normal((C, 2, 8, 8)).astype(np.float32),
+                audio=rng.standard_normal((Ca, 2, 12)).astype(np.float32),
+                cond=rng.standard_normal((C, 1, 8, 8)).astype(np.float32),
+                pos=lay.pos.astype(np.float32), sigma_v=0.42, tags=None)
+    if compat:
+        host["tags"] = np.full(16, 1, np.int32)
+        host["tags"][4:10] = 0
     td = torch.bfloat16 if dtype == "bf16" else torch.float32
 
     def dev_weights(spec, w):
@@ -182,16 +181,64 @@ def test_mmh3_denoise_evaluation(dit, dtype, compat):
     cu = lambda a, t=torch.float32: torch.from_numpy(a).to(t).cuda()  # noqa: E731
     model = dit.Mmh3Model(blocks, head_v, head_a, C, Ca, cu(wv, td), cu(bv), cu(wa, td), cu(ba),
                           audio_slope_rescale=compat)
-    # compat also gives the prompt a vision block (tokens 4..9 carry the video tag)
-    tags = np.full(16, 1, np.int32)
-    tags[4:10] = 0
-    vout, aout = model.forward(lay.segments, cu(pos), cu(text), cu(video), cu(audio), [cu(cond)],
-                               sigma_v, text_tags=cu(tags, torch.int32) if compat else None)
+    dev = dict(pos=cu(host["pos"]), text=cu(host["text"]), video=cu(host["video"]),
+               audio=cu(host["audio"]), conds=[cu(host["cond"])],
+               tags=None if host["tags"] is None else cu(host["tags"], torch.int32))
+    oracle_args = (bspec, hv, ha, wblocks, whv, wha, wv, bv, wa, ba)
+    return lay, model, dev, host, oracle_args
+
+
+def _run(model, lay, dev, sigma_v):
+    return model.forward(lay.segments, dev["pos"], dev["text"], dev["video"], dev["audio"], dev["conds"],
+                         sigma_v, text_tags=dev["tags"])
+
+
+@pytest.mark.parametrize("dtype,compat", [("bf16", False), ("f32", False), ("bf16", True),
+                                          ("f32", True)])
+def test_mmh3_denoise_evaluation(dit, dtype, compat):
+    """One whole evaluation at a small size against the oracle's evaluation
+    from the same seeded pieces."""
+    import torch
+    lay, model, dev, host, oa = _mmh3_setup(dit, dtype, compat)
+    vout, aout = _run(model, lay, dev, host["sigma_v"])
     torch.cuda.synchronize()
-    rv, ra = O.mmh3_forward(bspec, hv, ha, lay.segments, pos.astype(np.float64), text, video,
-                            audio, [cond], sigma_v, wblocks, whv, wha, wv, bv, wa, ba,
-                            audio_slope_rescale=compat, text_tags=tags if compat else None)
+    bspec, hv, ha, wblocks, whv, wha, wv, bv, wa, ba = oa
+    rv, ra = O.mmh3_forward(bspec, hv, ha, lay.segments, host["pos"].astype(np.float64), host["text"],
+                            host["video"], host["audio"], [host["cond"]], host["sigma_v"], wblocks, whv,
+                            wha, wv, bv, wa, ba, audio_slope_rescale=compat, text_tags=host["tags"])
     ev = O.rel_rms(vout.cpu().numpy(), rv)
     ea = O.rel_rms(aout.cpu().numpy(), ra)
-    log(f"[case] mmh3 evaluation {dtype} compat={compat} n={n}: video={ev:.2e} audio={ea:.2e}")
+    log(f"[case] mmh3 evaluation {dtype} compat={compat} n={lay.seq_len}: video={ev:.2e} audio={ea:.2e}")
     assert ev <= TOL[dtype] and ea <= TOL[dtype]
+
+
+def test_mmh3_evaluation_graph_replay(dit):
+    """The whole evaluation (patch and audio embeddings, token rows, two blocks,
+    both heads, unpacking) captured in one HIP graph replays to the eager result
+    bit for bit, with eager evaluations at another sigma between the replays."""
+    import torch
+    lay, model, dev, host, _ = _mmh3_setup(dit, "bf16", True)
+    sv = host["sigma_v"]
+    v_ref, a_ref = _run(model, lay, dev, sv)  # also sizes the workspace before capture
+    torch.cuda.synchronize()
+    v_ref, a_ref = v_ref.clone(), a_ref.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            v_g, a_g = _run(model, lay, dev, sv)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        v_g.fill_(float("nan"))
+        a_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(v_g, v_ref) and torch.equal(a_g, a_ref)
+        log(f"[case] mmh3 evaluation graph replay {rep}: equal={same}")
+        assert same
+        _run(model, lay, dev, 0.9)  # eager work on the same workspace between replays
+        torch.cuda.synchronize()
+    assert torch.isfinite(v_ref).all() and torch.isfinite(a_ref).all()

@@ -393,3 +393,42 @@ def test_keyframe_conditioning_slots(dit):
     errs, bad, t = compare(spec, owl, st)
     log("[case] keyframe-3-slots: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert not bad, f"keyframe-3-slots: stages over {t}: {bad}"
+
+
+# ---- maximum sizes ----
+
+@pytest.mark.parametrize("variant,dtype,n", [("mmh3", "bf16", 200), ("zimage", "bf16", 150),
+                                             ("mmh3", "f32", 70)])
+def test_widest_hidden_size(dit, variant, dtype, n):
+    """D = 4096, the widest row the norm / modulate / sandwich kernels hold in
+    registers (16 float4 per lane), 32 heads of 128."""
+    spec = _small(variant, dtype, n, 4096, 128, 512, temb_hidden=64, temb_freq=32)
+    wl = W.make_custom_workload(spec, 3000 + n)
+    _check(spec.name + "-D4096", spec, wl, dit)
+
+
+def test_most_packed_samples(dit):
+    """64 samples (the table's maximum), with empty and one-token samples and
+    boundaries anywhere, in one sequence."""
+    rng = np.random.default_rng(64)
+    lens = rng.integers(0, 30, size=64)
+    lens[[3, 17, 40]] = 0
+    lens[[5, 6]] = 1
+    lens[10] = 130  # one sample that spans several key tiles and two query blocks
+    starts = [0] + np.cumsum(lens).tolist()
+    n = starts[-1]
+    spec = _small("mmh3", "bf16", n, 256, 128, 384)
+    wl = W.make_custom_workload(spec, 4000 + n)
+    _check(spec.name + "-64-samples", spec, wl, dit, seq_starts=starts)
+
+
+@pytest.mark.parametrize("rank", [7, 64])
+def test_most_slots_and_other_ranks(dit, rank):
+    """Eight timestep slots (24 modulation rows, rows drawn over all of them)
+    and adaLN ranks off the rank-24 fast path: 7 (not a multiple of 4) and the
+    largest, 64."""
+    spec = W.BlockSpec(f"slots8-r{rank}", "mmh3", "bf16", n=300, D=256, H=2, hd=128, F=384,
+                       slots=8, rank=rank, grid=33, rope="split_half", rope_axes=(32, 48, 48))
+    wl = W.make_custom_workload(spec, 5000 + rank,
+                                sigmas=[0.0, 1e-7, 0.1, 0.37, 0.5, 0.81, 0.999999, 1.0])
+    _check(spec.name, spec, wl, dit)

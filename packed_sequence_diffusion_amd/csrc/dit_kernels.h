@@ -117,6 +117,8 @@ hipError_t patchify_image(int dtype, const float* x, int C, int H, int W, void* 
 hipError_t unpatchify_image(const float* rows, int C, int H, int W, float* x, hipStream_t s);
 // p[0, n) = v (a kernel rather than a memset: safe inside captured graphs)
 hipError_t fill_i32(int* p, int n, int v, hipStream_t s);
+// compute units of the current device (cached per device; 256 if the query fails)
+int device_cus();
 hipError_t fill_f32(float* p, int n, float v, hipStream_t s);
 // rows[i] = base + clamp(tags[i], 0, 2) (per-token modality rows of the prompt span)
 hipError_t rows_from_tags(const int* tags, int n, int base, int* rows, hipStream_t s);

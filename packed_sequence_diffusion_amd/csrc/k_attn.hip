@@ -398,7 +398,6 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   for (int e = 0; e < PER; ++e) orow[e] = f2bf(acc[e] * inv);
 }
 
-namespace {
 int device_cus() {
   static int cus[64] = {};
   int dev = 0;
@@ -411,7 +410,6 @@ int device_cus() {
   }
   return cus[dev];
 }
-}  // namespace
 
 void make_seq_table(const int* seq_starts, int nseq, int n, SeqTable* t) {
   if (!seq_starts) {

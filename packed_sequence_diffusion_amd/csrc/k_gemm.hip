@@ -70,13 +70,14 @@ DIT_DEV void epi_gated_rows(const Epi& ep, const int (&row)[NR], int M, int cbas
 // so global latency hides behind a whole tile of MFMAs.  A partial last N tile
 // (N % 256 != 0, N % 32 == 0) clamps its B rows and masks its stores (per
 // 128-column wave strip, and per 32-column block in the plain-store epilogue).
-constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int GBM = 256, GBK = 64;
 constexpr int GWM = 4, GWN = 2;                 // wave grid
-constexpr int GTM = GBM / GWM, GTN = GBN / GWN;  // 64 x 128 per wave
-constexpr int GMI = GTM / 32, GNI = GTN / 32;
+constexpr int GTM = GBM / GWM;  // 64 rows per wave
+constexpr int GMI = GTM / 32;
+constexpr int kQkvNI = 4;  // the QKV epilogue's 128-column wave strips
 constexpr int GNT = 64 * GWM * GWN;             // 512 threads
 constexpr int GCPR = GBK / 8;                   // 16-byte chunks per tile row
-constexpr int GAL = GBM * GCPR / GNT, GBL = GBN * GCPR / GNT;
+constexpr int GAL = GBM * GCPR / GNT;
 constexpr int kGroupM = 4;  // tile rows per rasterization group
 
 // LDS element offset of 16-byte chunk `ch` of row `r` in a [rows][64] bf16
@@ -93,7 +94,7 @@ DIT_DEV int swz64(int r, int ch) { return r * GBK + ((ch ^ ((r >> 1) & 7)) << 3)
 // per head (keys contiguous) for the attention kernel's second product.
 // Rows are finished one at a time so that only the accumulators stay live.
 template <int HD, int ROPE>
-DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rbase, int c0,
+DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][kQkvNI], int M, int rbase, int c0,
                          int which, int lane) {
   constexpr int P = HD / 2;
   const int cl = lane & 31, rh = (lane >> 5) * 4;
@@ -102,18 +103,18 @@ DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rb
   const float qs = which == 0 ? ep.q_scale : 1.0f;
   bf16_t* dst = (bf16_t*)(which ? ep.k : ep.q);
   const float2* cs = (const float2*)ep.cs;
-  float gv[GNI];
+  float gv[kQkvNI];
 #pragma unroll
-  for (int ni = 0; ni < GNI; ++ni) gv[ni] = g ? g[(32 * ni + cl) & (HD - 1)] : 1.0f;
+  for (int ni = 0; ni < kQkvNI; ++ni) gv[ni] = g ? g[(32 * ni + cl) & (HD - 1)] : 1.0f;
   const bool even = (cl & 1) == 0;
 #pragma unroll
   for (int mi = 0; mi < GMI; ++mi)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int row = rbase + mi * 32 + (v >> 2) * 8 + rh + (v & 3);
-      float x[GNI];
+      float x[kQkvNI];
 #pragma unroll
-      for (int ni = 0; ni < GNI; ++ni) x[ni] = acc[mi][ni][v];
+      for (int ni = 0; ni < kQkvNI; ++ni) x[ni] = acc[mi][ni][v];
       if (g) {
         // blocks 0..3 are one head (HD = 128) or two (HD = 64: 0-1 and 2-3); the
         // other 31 lanes of this half-wave hold the rest of the row's columns
@@ -126,7 +127,7 @@ DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rb
         const float i0 = __builtin_amdgcn_rsqf(s0 * (1.0f / HD) + ep.qk_eps);
         const float i1 = (HD == 128) ? i0 : __builtin_amdgcn_rsqf(s1 * (1.0f / HD) + ep.qk_eps);
 #pragma unroll
-        for (int ni = 0; ni < GNI; ++ni) x[ni] *= ((HD == 128 || ni < 2) ? i0 : i1) * gv[ni];
+        for (int ni = 0; ni < kQkvNI; ++ni) x[ni] *= ((HD == 128 || ni < 2) ? i0 : i1) * gv[ni];
       }
       if (ROPE != 0) {
         const float2* csr = cs + (size_t)min(row, M - 1) * P;
@@ -142,7 +143,7 @@ DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rb
           } else {
             const float2 c = csr[cl];
 #pragma unroll
-            for (int ni = 0; ni < GNI; ni += 2) {
+            for (int ni = 0; ni < kQkvNI; ni += 2) {
               const float a = x[ni], b = x[ni + 1];
               x[ni] = a * c.x - b * c.y;
               x[ni + 1] = a * c.y + b * c.x;
@@ -150,7 +151,7 @@ DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rb
           }
         } else {  // interleaved: pair (2i, 2i + 1) is in lanes cl and cl ^ 1
 #pragma unroll
-          for (int ni = 0; ni < GNI; ++ni) {
+          for (int ni = 0; ni < kQkvNI; ++ni) {
             const float oth = DIT_DPP(x[ni], 0xB1);  // lane ^ 1
             const float2 c = csr[((32 * ni + cl) & (HD - 1)) >> 1];
             const float xe = even ? x[ni] : oth, xo = even ? oth : x[ni];
@@ -161,7 +162,7 @@ DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rb
       if (row < ldn) {
         const bool valid = row < M;
 #pragma unroll
-        for (int ni = 0; ni < GNI; ++ni) {
+        for (int ni = 0; ni < kQkvNI; ++ni) {
           const int col = c0 + 32 * ni + cl;
           const int h = col / HD, d = col - h * HD;
           dst[((size_t)h * ldn + row) * HD + d] = f2bf(valid ? x[ni] * qs : 0.0f);
@@ -170,7 +171,7 @@ DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rb
     }
 }
 
-DIT_DEV void epi_qkv(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rbase, int cbase,
+DIT_DEV void epi_qkv(const Epi& ep, f32x16_t (&acc)[GMI][kQkvNI], int M, int rbase, int cbase,
                      int lane) {
   const int cl = lane & 31, rh = (lane >> 5) * 4;
   const int D = ep.ldc, ldn = ep.ldn;
@@ -178,7 +179,7 @@ DIT_DEV void epi_qkv(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rbase,
   const int c0 = cbase - which * D;  // first column of the strip inside its q/k/v block
   if (ep.bias) {
 #pragma unroll
-    for (int ni = 0; ni < GNI; ++ni) {
+    for (int ni = 0; ni < kQkvNI; ++ni) {
       const float b = ep.bias[cbase + 32 * ni + cl];
 #pragma unroll
       for (int mi = 0; mi < GMI; ++mi)
@@ -196,7 +197,7 @@ DIT_DEV void epi_qkv(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rbase,
         const int row0 = rbase + mi * 32 + vq * 8 + rh;
         if (row0 >= ldn) continue;  // ldn is a multiple of 128: all four rows in or out
 #pragma unroll
-        for (int ni = 0; ni < GNI; ++ni) {
+        for (int ni = 0; ni < kQkvNI; ++ni) {
           const int col = c0 + 32 * ni + cl;  // h * hd + d
           float e[4];
 #pragma unroll
@@ -216,10 +217,16 @@ DIT_DEV void epi_qkv(const Epi& ep, f32x16_t (&acc)[GMI][GNI], int M, int rbase,
   }
 }
 
-template <int EPI, typename OutT>
+template <int EPI, typename OutT, int NI>
 __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A, int lda,
                                                    const bf16_t* __restrict__ B, int ldb, int M,
                                                    int N, int K, Epi ep) {
+  // NI 32-column blocks per wave: the tile is 256 x 64*NI (NI = 4, or 3 for widths that
+  // are a multiple of 192 but not of 256)
+  constexpr int GNI = NI, GTN = 32 * NI, GBN = GWN * GTN, GBL = GBN * GCPR / GNT;
+  static_assert(GBN * GCPR % GNT == 0, "whole 16-byte chunks per thread");
+  static_assert(EPI != EPI_QKV || NI == 4, "the QKV epilogue takes whole 128-column heads");
+  static_assert(EPI != EPI_SWIGLU || NI % 2 == 0, "SwiGLU pairs 32-column blocks");
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (GBM + GBN) * GBK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / GWN, wn = wave % GWN;
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A,
     // load of the staged tile, so neither burst leaves the matrix pipe idle.
     {
       constexpr int NR = GMI + GNI, NM = GMI * GNI, NS = GBK / 16, NL = GAL + GBL;
-      static_assert(NM >= NR && NM >= NL, "schedule pattern");
+      static_assert(NM >= NR, "schedule pattern");
       __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // ds_read
 #pragma unroll
       for (int st = 0; st < NS - 1; ++st) {
@@ -317,13 +324,18 @@ __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A,
         }
         __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
       }
+      constexpr int NP = NL < NM ? NL : NM;  // staged chunks paired with an MFMA
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
+      for (int i = 0; i < NP; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // ds_write
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, NM - NL, 0);
+      if (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
+      if (NL > NP) {
+        __builtin_amdgcn_sched_group_barrier(0x200, NL - NP, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, NL - NP, 0);
+      }
     }
     __syncthreads();
   }
@@ -335,11 +347,11 @@ __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A,
   const int cl = lane & 31, rh = (lane >> 5) * 4;
   const int cbase = n0 + wn * GTN;
   if (cbase >= N) return;  // the masked half of a partial last N tile
-  if (EPI == EPI_QKV) {
+  if constexpr (EPI == EPI_QKV) {
     epi_qkv(ep, acc, M, m0 + wm * GTM, cbase, lane);
     return;
   }
-  if (EPI == EPI_GATED_RES) {
+  if constexpr (EPI == EPI_GATED_RES) {
 #pragma unroll
     for (int mi = 0; mi < GMI; ++mi)
 #pragma unroll
@@ -433,22 +445,50 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
   }
 }
 
+// 192-wide tiles for N = 2688-like widths where they save rounds; DIT_GEMM_WIDE192=0
+// turns them off (A/B timing)
+static bool gemm_wide192() {
+  static const bool on = [] {
+    const char* e = getenv("DIT_GEMM_WIDE192");
+    return !(e && e[0] == '0');
+  }();
+  return on;
+}
+
 template <int EPI>
 static hipError_t launch_gemm(int dtype, bool out_bf16, const void* A, int lda, const void* B,
                               int ldb, int M, int N, int K, const Epi& ep, hipStream_t s) {
   if (dtype == BF16) {
-    const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+    // 192-wide tiles where they divide N and 256-wide ones do not (N = 2688: 14 full
+    // tiles per row instead of 10.5), if that saves whole rounds of the grid over the
+    // CUs: a 256 x 192 tile takes about 0.86 of a 256 x 256 one (measured at N = 2688).
+    bool w192 = false;
+    if ((EPI == EPI_GATED_RES || EPI == EPI_STORE) && N % 256 != 0 && N % 192 == 0 && gemm_wide192()) {
+      const int cus = device_cus(), tm = (M + GBM - 1) / GBM;
+      const int r4 = (tm * ((N + 255) / 256) + cus - 1) / cus, r3 = (tm * (N / 192) + cus - 1) / cus;
+      w192 = r3 * 0.86 < r4;
+    }
+    const int bn = w192 ? 192 : 256;
+    const int tiles = ((M + GBM - 1) / GBM) * ((N + bn - 1) / bn);
     dim3 grid((tiles + 7) / 8 * 8);  // a whole number of rounds over the 8 XCDs
-    if constexpr (EPI == EPI_QKV || EPI == EPI_GATED_RES) {
-      k_gemm_bf16<EPI, bf16_t><<<grid, GNT, 0, s>>>((const bf16_t*)A, lda, (const bf16_t*)B, ldb,
-                                                     M, N, K, ep);
+    const bf16_t *Ab = (const bf16_t*)A, *Bb = (const bf16_t*)B;
+    if constexpr (EPI == EPI_QKV) {
+      k_gemm_bf16<EPI, bf16_t, 4><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
+    } else if constexpr (EPI == EPI_GATED_RES) {
+      if (w192)
+        k_gemm_bf16<EPI, bf16_t, 3><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
+      else
+        k_gemm_bf16<EPI, bf16_t, 4><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
+    } else if constexpr (EPI == EPI_STORE) {
+      if (out_bf16 && w192) k_gemm_bf16<EPI, bf16_t, 3><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
+      else if (out_bf16) k_gemm_bf16<EPI, bf16_t, 4><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
+      else if (w192) k_gemm_bf16<EPI, float, 3><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
+      else k_gemm_bf16<EPI, float, 4><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
     } else {
       if (out_bf16)
-        k_gemm_bf16<EPI, bf16_t><<<grid, GNT, 0, s>>>((const bf16_t*)A, lda, (const bf16_t*)B,
-                                                       ldb, M, N, K, ep);
+        k_gemm_bf16<EPI, bf16_t, 4><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
       else
-        k_gemm_bf16<EPI, float><<<grid, GNT, 0, s>>>((const bf16_t*)A, lda, (const bf16_t*)B, ldb,
-                                                      M, N, K, ep);
+        k_gemm_bf16<EPI, float, 4><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
     }
   } else {
     if constexpr (EPI == EPI_QKV) {

@@ -42,6 +42,7 @@ def test_final_layer(dit, dtype, n, F):
 
 @pytest.mark.parametrize("dtype,m,k,nout,alpha", [("bf16", 300, 192, 96, -0.5),
                                                   ("bf16", 77, 64, 512, 1.0),
+                                                  ("bf16", 300, 128, 576, 1.0),  # 192-wide tiles
                                                   ("f32", 130, 48, 128, 2.0)])
 def test_linear(dit, dtype, m, k, nout, alpha):
     import torch

@@ -166,14 +166,20 @@ def main():
 
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    # one event after every step as well: per-step median and min
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     if not args.graph:
         dit.profile_begin(args.steps * len(blocks))
     torch.cuda.synchronize()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         run()
+        evs[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
+    step_ms = sorted([ev0.elapsed_time(evs[0])] +
+                     [evs[i - 1].elapsed_time(evs[i]) for i in range(1, args.steps)])
+    step_ms = [v / len(blocks) for v in step_ms]
     if args.graph:  # phase split from an eager pass of the same steps
         dit.profile_begin(args.steps * len(blocks))
         for _ in range(args.steps):
@@ -219,6 +225,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": step_ms[len(step_ms) // 2],
+        "ms_per_step_min": step_ms[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

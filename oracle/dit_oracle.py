@@ -18,11 +18,13 @@ Citation tags (web pages, cited by title and the item on the page):
 Pins (tests/test_oracle_pins.py) tie each function to something other than
 itself: printed test points, closed forms, library routines (numpy.interp,
 torch's scaled-dot-product attention, layer_norm and rms_norm in float64),
-invariants and pure-Python brute force on tiny inputs.  One result has no
-printed value to pin it: the whole block's output at the workloads' shapes
-(no golden forward is published on the pages).  It is pinned only through its
-pinned parts, brute force at tiny sizes and block-level invariants
-(permutation equivariance, zero-gate identity, RoPE translation invariance).
+invariants and pure-Python brute force on tiny inputs.  Parity unpinned: the
+whole block's output at the workloads' shapes, and the whole MMH3 / Z-Image
+evaluations built from it, have no printed value to pin them (no golden
+forward is published on the pages).  They are pinned only through their
+pinned parts, brute force at tiny sizes and invariants (permutation
+equivariance, zero-gate identity, RoPE translation invariance, the Z-Image
+cache identities, the audio slope's closed form).
 """
 
 from __future__ import annotations

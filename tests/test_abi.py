@@ -332,3 +332,103 @@ def test_mmh3_slots_match_the_oracle(dit):
                 np.testing.assert_allclose([1.0 - s for s in sig], ts, rtol=0, atol=1e-15)
     assert dit.lib.dit_mmh3_slots(float("nan"), 12.0, 3.0, 0.999, 1.0, 0, 0,
                                   (ctypes.c_double * 4)(), (ctypes.c_int32 * 4)()) == -1
+
+
+def _mmh3_model_struct(dit):
+    """A DitMmh3Model over valid configs and placeholder (aligned, never
+    dereferenced) pointers: the host-side checks run before any launch."""
+    spec = W.small_spec(W.spec_by_name("t2va"), D=256, H=2, F=384, slots=3)
+    blk = dit.make_config(spec)
+    hv = dit.make_config(W.BlockSpec("hv", "final", "bf16", n=1, D=256, H=2, hd=128, F=64, slots=3, tags=1))
+    ha = dit.make_config(W.BlockSpec("ha", "final", "bf16", n=1, D=256, H=2, hd=128, F=64, slots=3, tags=1))
+    keep = (blk, hv, ha, (ctypes.c_void_p * 2)(256, 512))
+    m = dit.DitMmh3Model()
+    m.block, m.blocks, m.n_blocks = ctypes.pointer(blk), keep[3], 2
+    m.head_video, m.head_video_w = ctypes.pointer(hv), 256
+    m.head_audio, m.head_audio_w = ctypes.pointer(ha), 256
+    m.latent_c, m.audio_c = 16, 64
+    m.video_patch_w, m.audio_patch_w = 256, 256
+    m.shift_video, m.shift_audio, m.cond_aug, m.cond_aug_audio = 12.0, 3.0, 0.999, 1.0
+    return m, keep
+
+
+def _segs(dit, spec):
+    return (dit.DitSegment * len(spec))(*[dit.DitSegment(dit.SEG_KINDS[k], a, b) for k, a, b in spec])
+
+
+def test_mmh3_evaluation_refusals(dit):
+    m, keep = _mmh3_model_struct(dit)
+    good = [("text", 0, 16), ("audio", 16, 40), ("video", 40, 72)]
+    assert dit.lib.dit_mmh3_workspace_size(ctypes.byref(m), _segs(dit, good), 3) > 0
+    bad = {
+        "gap": [("text", 0, 16), ("video", 20, 52)],
+        "two videos": [("video", 0, 32), ("video", 32, 64)],
+        "no video": [("text", 0, 16), ("audio", 16, 40)],
+        "reference in an evaluation": [("text", 0, 16), ("ref_image", 16, 32), ("video", 32, 64)],
+    }
+    for why, sg in bad.items():
+        assert dit.lib.dit_mmh3_workspace_size(ctypes.byref(m), _segs(dit, sg), len(sg)) == 0, why
+        assert dit.last_error(), why
+    m.audio_slope_rescale = 2
+    assert dit.lib.dit_mmh3_workspace_size(ctypes.byref(m), _segs(dit, good), 3) == 0
+    m.audio_slope_rescale = 0
+    m.latent_c = 15  # 4 * latent_c not a multiple of the bf16 GEMM depth
+    assert dit.lib.dit_mmh3_workspace_size(ctypes.byref(m), _segs(dit, good), 3) == 0
+    assert dit.lib.dit_mmh3_workspace_size(None, _segs(dit, good), 3) == 0
+
+
+def test_zimage_forward_cache_refusals(dit):
+    z = W.spec_by_name("zimage")
+    cfgs = [dit.make_config(W.small_spec(z, variant=v, D=256, H=2, F=384 if v != "zfinal" else 64))
+            for v in ("zimage", "zcontext", "zfinal")]
+    arr = (ctypes.c_void_p * 3)(256, 512, 768)
+    m = dit.DitZimageModel()
+    m.block, m.context, m.final_layer = (ctypes.pointer(c) for c in cfgs)
+    m.layers, m.n_layers, m.noise_refiners, m.n_noise_refiners = arr, 3, arr, 1
+    m.context_refiners, m.n_context_refiners = arr, 1
+    m.final_w, m.in_channels, m.cap_dim, m.cap_eps = 256, 16, 128, 1e-6
+    m.x_embed_w, m.cap_norm, m.cap_embed_w = 256, 256, 256
+    need = dit.lib.dit_zimage_workspace_size(ctypes.byref(m), 16, 16, 40)
+    assert need > 0
+
+    def fwd(cache, step=0):
+        return dit.lib.dit_zimage_forward(ctypes.byref(m), 256, 16, 16, 512, 40, 768, 0.5, step,
+                                          ctypes.byref(cache), 1024, 256, need, None)
+    c = dit.DitZimageCache()
+    c.caption, c.shallow, c.layers, c.interval = 256, 512, 2, 0
+    assert fwd(c) == -1 and "interval" in dit.last_error()
+    c.interval, c.layers = 2, 4  # more shallow layers than main layers
+    assert fwd(c) == -1
+    c.layers, c.shallow = 2, None
+    assert fwd(c) == -1
+    c.shallow = 512
+    assert fwd(c, step=-1) == -1
+    # workspace too small
+    c.layers = 1
+    assert dit.lib.dit_zimage_forward(ctypes.byref(m), 256, 16, 16, 512, 40, 768, 0.5, 0,
+                                      ctypes.byref(c), 1024, 256, need - 1, None) == -5
+
+
+def test_model_piece_refusals(dit):
+    L = dit.lib
+    # output head entry point takes head configs only; blocks refuse head configs
+    blk = _cfg(dit)
+    arr = (ctypes.c_double * 2)(0.5, 0.2)
+    assert L.dit_final_forward(ctypes.byref(blk), 256, 256, 10, None, arr, 2, 256, 256, 1 << 30, None) == -1
+    # linear: depth / width multiples, finite alpha
+    assert L.dit_linear(dit.BF16, 256, 100, 10, 100, 256, 64, None, 1.0, 256, None) == -6
+    assert L.dit_linear(dit.BF16, 256, 64, 10, 64, 256, 48, None, 1.0, 256, None) == -6
+    assert L.dit_linear(dit.BF16, 256, 64, 10, 64, 256, 64, None, float("nan"), 256, None) == -1
+    assert L.dit_linear(7, 256, 64, 10, 64, 256, 64, None, 1.0, 256, None) == -3
+    assert L.dit_linear(dit.BF16, 256, 64, 0, 64, 256, 64, None, 1.0, None, None) == 0  # m = 0: no-op
+    # stack: at least one block
+    assert L.dit_stack_forward(ctypes.byref(blk), (ctypes.c_void_p * 1)(256), 0, 256, 10, 256, 256,
+                               arr, 2, None, 0, 256, 256, 1 << 30, None) == -2
+    # rms_norm: row width
+    assert L.dit_rms_norm(256, 10, 6, 256, 1e-5, 256, None) == -2
+    assert L.dit_rms_norm(256, 10, 8192, 256, 1e-5, 256, None) == -2
+    # stream layouts: even spatial sizes, known dtype
+    assert L.dit_patchify_video(dit.BF16, 256, 4, 2, 7, 8, 256, None) == -2
+    assert L.dit_patchify_video(9, 256, 4, 2, 8, 8, 256, None) == -3
+    assert L.dit_patchify_image(dit.F32, 256, 4, 8, 5, 256, None) == -2
+    assert L.dit_pack_audio(dit.F32, 256, -1, 3, 256, None) == -2

@@ -93,8 +93,8 @@ DIT_DEV int swz64(int r, int ch) { return r * GBK + ((ch ^ ((r >> 1) & 7)) << 3)
 // softmax's base-2 score scale) and both are written head-major; v goes out transposed
 // per head (keys contiguous) for the attention kernel's second product.
 // Rows are finished one at a time so that only the accumulators stay live.
-template <int HD, int ROPE>
-DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][kQkvNI], int M, int rbase, int c0,
+template <int HD, int ROPE, int MI>
+DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[MI][kQkvNI], int M, int rbase, int c0,
                          int which, int lane) {
   constexpr int P = HD / 2;
   const int cl = lane & 31, rh = (lane >> 5) * 4;
@@ -108,7 +108,7 @@ DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][kQkvNI], int M, int
   for (int ni = 0; ni < kQkvNI; ++ni) gv[ni] = g ? g[(32 * ni + cl) & (HD - 1)] : 1.0f;
   const bool even = (cl & 1) == 0;
 #pragma unroll
-  for (int mi = 0; mi < GMI; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int row = rbase + mi * 32 + (v >> 2) * 8 + rh + (v & 3);
@@ -171,7 +171,8 @@ DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[GMI][kQkvNI], int M, int
     }
 }
 
-DIT_DEV void epi_qkv(const Epi& ep, f32x16_t (&acc)[GMI][kQkvNI], int M, int rbase, int cbase,
+template <int MI>
+DIT_DEV void epi_qkv(const Epi& ep, f32x16_t (&acc)[MI][kQkvNI], int M, int rbase, int cbase,
                      int lane) {
   const int cl = lane & 31, rh = (lane >> 5) * 4;
   const int D = ep.ldc, ldn = ep.ldn;
@@ -182,7 +183,7 @@ DIT_DEV void epi_qkv(const Epi& ep, f32x16_t (&acc)[GMI][kQkvNI], int M, int rba
     for (int ni = 0; ni < kQkvNI; ++ni) {
       const float b = ep.bias[cbase + 32 * ni + cl];
 #pragma unroll
-      for (int mi = 0; mi < GMI; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[mi][ni][v] += b;
     }
@@ -191,7 +192,7 @@ DIT_DEV void epi_qkv(const Epi& ep, f32x16_t (&acc)[GMI][kQkvNI], int M, int rba
     // v^T [H, hd, ldn]: a lane holds 4 consecutive rows of one column per (mi, ni, v/4)
     bf16_t* vt = (bf16_t*)ep.vt;
 #pragma unroll
-    for (int mi = 0; mi < GMI; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int vq = 0; vq < 4; ++vq) {
         const int row0 = rbase + mi * 32 + vq * 8 + rh;
@@ -208,12 +209,61 @@ DIT_DEV void epi_qkv(const Epi& ep, f32x16_t (&acc)[GMI][kQkvNI], int M, int rba
     return;
   }
   switch (ep.hd * 4 + ep.rope) {
-    case 128 * 4 + 0: epi_qk_rows<128, 0>(ep, acc, M, rbase, c0, which, lane); break;
-    case 128 * 4 + 1: epi_qk_rows<128, 1>(ep, acc, M, rbase, c0, which, lane); break;
-    case 128 * 4 + 2: epi_qk_rows<128, 2>(ep, acc, M, rbase, c0, which, lane); break;
-    case 64 * 4 + 0: epi_qk_rows<64, 0>(ep, acc, M, rbase, c0, which, lane); break;
-    case 64 * 4 + 1: epi_qk_rows<64, 1>(ep, acc, M, rbase, c0, which, lane); break;
-    default: epi_qk_rows<64, 2>(ep, acc, M, rbase, c0, which, lane); break;
+    case 128 * 4 + 0: epi_qk_rows<128, 0, MI>(ep, acc, M, rbase, c0, which, lane); break;
+    case 128 * 4 + 1: epi_qk_rows<128, 1, MI>(ep, acc, M, rbase, c0, which, lane); break;
+    case 128 * 4 + 2: epi_qk_rows<128, 2, MI>(ep, acc, M, rbase, c0, which, lane); break;
+    case 64 * 4 + 0: epi_qk_rows<64, 0, MI>(ep, acc, M, rbase, c0, which, lane); break;
+    case 64 * 4 + 1: epi_qk_rows<64, 1, MI>(ep, acc, M, rbase, c0, which, lane); break;
+    default: epi_qk_rows<64, 2, MI>(ep, acc, M, rbase, c0, which, lane); break;
+  }
+}
+
+// Epilogue of one wave's (32 MI) x (32 NI) accumulator strip whose first row is
+// rbase and first column cbase (< N).  C layout of a 32x32 block: lane holds column
+// (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4 for v = 0..15.
+template <int EPI, typename OutT, int MI, int NI>
+DIT_DEV void gemm_epilogue(const Epi& ep, f32x16_t (&acc)[MI][NI], int M, int N, int rbase,
+                           int cbase, int lane) {
+  const int cl = lane & 31, rh = (lane >> 5) * 4;
+  if constexpr (EPI == EPI_QKV) {
+    epi_qkv<MI>(ep, acc, M, rbase, cbase, lane);
+    return;
+  }
+  if constexpr (EPI == EPI_GATED_RES) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int vh = 0; vh < 2; ++vh) {
+        int rows8[8];
+        float a8[8][NI];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int v = vh * 8 + i;
+          rows8[i] = rbase + mi * 32 + (v >> 2) * 8 + rh + (v & 3);
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) a8[i][ni] = acc[mi][ni][v];
+        }
+        epi_gated_rows<8, NI>(ep, rows8, M, cbase, cl, a8);
+      }
+    return;
+  }
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = rbase + mi * 32 + (v >> 2) * 8 + rh + (v & 3);
+      if (row >= M) continue;
+      if (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ni += 2)
+          epi_swiglu<OutT>(ep, row, (cbase + ni * 32) / 2 + cl, acc[mi][ni][v], acc[mi][ni + 1][v]);
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          if (cbase + ni * 32 < N)  // N % 32 == 0: whole 32-column blocks in or out
+            epi_one<EPI, OutT>(ep, row, cbase + ni * 32 + cl, acc[mi][ni][v]);
+      }
+    }
   }
 }
 
@@ -342,51 +392,9 @@ __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A,
 #undef GEMM_GLOAD
 #undef GEMM_SSTORE
 
-  // C layout of a 32x32 block: lane holds column (lane & 31) and rows
-  // 8*(v/4) + 4*(lane/32) + v%4 for v = 0..15.
-  const int cl = lane & 31, rh = (lane >> 5) * 4;
   const int cbase = n0 + wn * GTN;
   if (cbase >= N) return;  // the masked half of a partial last N tile
-  if constexpr (EPI == EPI_QKV) {
-    epi_qkv(ep, acc, M, m0 + wm * GTM, cbase, lane);
-    return;
-  }
-  if constexpr (EPI == EPI_GATED_RES) {
-#pragma unroll
-    for (int mi = 0; mi < GMI; ++mi)
-#pragma unroll
-      for (int vh = 0; vh < 2; ++vh) {
-        int rows8[8];
-        float a8[8][GNI];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int v = vh * 8 + i;
-          rows8[i] = m0 + wm * GTM + mi * 32 + (v >> 2) * 8 + rh + (v & 3);
-#pragma unroll
-          for (int ni = 0; ni < GNI; ++ni) a8[i][ni] = acc[mi][ni][v];
-        }
-        epi_gated_rows<8, GNI>(ep, rows8, M, cbase, cl, a8);
-      }
-    return;
-  }
-#pragma unroll
-  for (int mi = 0; mi < GMI; ++mi) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = m0 + wm * GTM + mi * 32 + (v >> 2) * 8 + rh + (v & 3);
-      if (row >= M) continue;
-      if (EPI == EPI_SWIGLU) {
-#pragma unroll
-        for (int ni = 0; ni < GNI; ni += 2)
-          epi_swiglu<OutT>(ep, row, (cbase + ni * 32) / 2 + cl, acc[mi][ni][v], acc[mi][ni + 1][v]);
-      } else {
-#pragma unroll
-        for (int ni = 0; ni < GNI; ++ni)
-          if (cbase + ni * 32 < N)  // N % 32 == 0: whole 32-column blocks in or out
-            epi_one<EPI, OutT>(ep, row, cbase + ni * 32 + cl, acc[mi][ni][v]);
-      }
-    }
-  }
+  gemm_epilogue<EPI, OutT, GMI, GNI>(ep, acc, M, N, m0 + wm * GTM, cbase, lane);
 }
 
 // ---------------------------------------------------------------- fp32 FMA ----

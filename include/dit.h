@@ -172,8 +172,10 @@ typedef struct dit_weights {
  *   x1    fp32 [n, D]     residual stream after the attention half
  *   a     act  [n, F]     FFN activation (SwiGLU or GELU-tanh)
  *   y     fp32 [n, D]     ZIMAGE: last projection before its sandwich norm (fc2's after the call)
- *   part  fp32            bf16 only: key-range partials of the attention's split tail
- *                         (256 slots x 256 queries x (hd + 2) floats) */
+ *   part  fp32            bf16 only: scratch shared by the attention's split tail
+ *                         (key-range partials, 256 slots x 256 queries x (hd + 2)
+ *                         floats) and the GEMMs' split-K tails (up to 256 slots of
+ *                         256 x 256 accumulators); max of the two, contents undefined */
 typedef struct dit_ws_layout {
   size_t mods, rope, xn, qkv, q, k, vt, o, x1, a, y, temb, part, total;
   int32_t ldn;

@@ -219,7 +219,10 @@ dit_ws_layout ws_layout(const dit_config* c, int n) {
   L.x1 = take((size_t)n * D * 4);
   L.a = take((size_t)n * F * es);
   L.y = zsandwich(c) ? take((size_t)n * D * 4) : kNone;
-  L.part = c->dtype == DIT_BF16 ? take(dit::attention_part_bytes(c->hd)) : kNone;
+  // attention's split key ranges and the GEMMs' split-K tails (never live at once)
+  L.part = c->dtype == DIT_BF16
+               ? take(std::max(dit::attention_part_bytes(c->hd), dit::gemm_split_bytes()))
+               : kNone;
   L.total = off;
   return L;
 }
@@ -699,6 +702,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
   // a2: pre-norm + modulate
   DIT_TRY(launch_prenorm(c, prepared, x, n, rows, mods, 0, xn, s));
   pm.mark(1);
+  float* const gsplit = bf ? at<float>(workspace, L.part) : nullptr;  // split-K tails
   // a3 + a4: QKV projection (+ bias), qk-norm, RoPE and the score-scale fold into q,
   // head-major q and k and transposed v (fused into the GEMM epilogue for bf16)
   {
@@ -711,6 +715,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
     const float* qn = qkn ? atc<float>(prepared, P.q_norm) : nullptr;
     const float* kn = qkn ? atc<float>(prepared, P.k_norm) : nullptr;
     dit::Epi ep;
+    ep.split = gsplit;
     ep.bias = atc<float>(prepared, P.b_qkv);
     if (bf) {
       ep.ldc = D;
@@ -753,6 +758,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
   auto zmod = [&](int e) -> const float* { return c->variant == DIT_ZIMAGE ? mods + e * D : nullptr; };
   if (zsandwich(c)) {
     dit::Epi ep;
+    ep.split = gsplit;
     ep.out = y;
     ep.ldc = D;
     HIP_TRY(dit::gemm(dt, dit::EPI_STORE, false, o, D, atc<char>(prepared, P.w_out), D, n, D, D, ep, s), "out gemm");
@@ -764,6 +770,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
     pm.mark(6);
   } else {
     dit::Epi ep;
+    ep.split = gsplit;
     ep.out = x1;
     ep.ldc = D;
     ep.resid = x;
@@ -785,6 +792,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
   // a8: fc1 + activation
   {
     dit::Epi ep;
+    ep.split = gsplit;
     ep.out = a;
     ep.ldc = F;
     ep.bias = atc<float>(prepared, P.b_fc1);
@@ -796,6 +804,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
   // a9: fc2 + residual
   if (zsandwich(c)) {
     dit::Epi ep;
+    ep.split = gsplit;
     ep.out = y;
     ep.ldc = D;
     HIP_TRY(dit::gemm(dt, dit::EPI_STORE, false, a, F, atc<char>(prepared, P.w_fc2), F, n, D, F, ep, s), "fc2 gemm");
@@ -804,6 +813,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
             "sandwich ffn");
   } else {
     dit::Epi ep;
+    ep.split = gsplit;
     ep.out = out;
     ep.ldc = D;
     ep.resid = x1;

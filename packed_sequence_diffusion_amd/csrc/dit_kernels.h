@@ -41,7 +41,14 @@ struct Epi {
   void* q = nullptr;
   void* k = nullptr;
   void* vt = nullptr;
+  // bf16: scratch of gemm_split_bytes() for a split-K tail (null: no split)
+  float* split = nullptr;
 };
+
+// Scratch a bf16 GEMM may use for its split-K tail: at most kGemmSplitWgs
+// workgroups, each with one fp32 256 x 256 accumulator tile.
+constexpr int kGemmSplitWgs = 256;
+inline size_t gemm_split_bytes() { return (size_t)kGemmSplitWgs * 256 * 256 * sizeof(float); }
 
 hipError_t gemm(int dtype, int epi, bool out_bf16, const void* A, int lda, const void* B, int ldb,
                 int M, int N, int K, const Epi& ep, hipStream_t s);

@@ -267,10 +267,26 @@ DIT_DEV void gemm_epilogue(const Epi& ep, f32x16_t (&acc)[MI][NI], int M, int N,
   }
 }
 
+// Tile L of the raster: groups of kGroupM tile rows, row index fastest.
+DIT_DEV void tile_of(int L, int ntm, int ntn, int& tm, int& tn) {
+  const int gsz = kGroupM * ntn, g = L / gsz, gr = L - g * gsz;
+  const int gm = min(kGroupM, ntm - g * kGroupM);
+  tm = g * kGroupM + gr % gm;
+  tn = gr / gm;
+}
+
+// Split-K tail: tiles [F, total) of the raster, the ones a last partial round over
+// the CUs would leave alone on a mostly idle chip, are each computed as S
+// workgroups over consecutive K ranges; each writes its fp32 accumulators, in
+// register order, to its slot of ep.split and the fixup kernel sums the S slots in
+// order (deterministic) and applies the epilogue.
+template <int NI>
+constexpr int split_slot_floats() { return GMI * NI * 16 * 64 * (GNT / 64); }
+
 template <int EPI, typename OutT, int NI>
 __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A, int lda,
                                                    const bf16_t* __restrict__ B, int ldb, int M,
-                                                   int N, int K, Epi ep) {
+                                                   int N, int K, int F, int S, Epi ep) {
   // NI 32-column blocks per wave: the tile is 256 x 64*NI (NI = 4, or 3 for widths that
   // are a multiple of 192 but not of 256)
   constexpr int GNI = NI, GTN = 32 * NI, GBN = GWN * GTN, GBL = GBN * GCPR / GNT;
@@ -284,14 +300,25 @@ __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A,
   // own L2, so every XCD gets a contiguous chunk of the tile sequence, and the
   // sequence runs through groups of kGroupM tile rows with the row index
   // fastest: the workgroups resident on one XCD then share both A row panels
-  // and B column panels in its L2.
+  // and B column panels in its L2.  Workgroups from F on (F a multiple of 8)
+  // are the split tail, S per tile.
   const int ntn = (N + GBN - 1) / GBN, ntm = (M + GBM - 1) / GBM;
-  const int total = ntn * ntm, chunk = (total + 7) / 8;
-  const int L = (blockIdx.x % 8) * chunk + blockIdx.x / 8;
-  if (L >= total) return;
-  const int gsz = kGroupM * ntn, g = L / gsz, gr = L - g * gsz;
-  const int gm = min(kGroupM, ntm - g * kGroupM);
-  const int tm = g * kGroupM + gr % gm, tn = gr / gm;
+  const int total = ntn * ntm;
+  int L, part = -1;
+  if (EPI == EPI_QKV || (int)blockIdx.x < F) {  // QKV launches never split
+    L = (blockIdx.x % 8) * (F / 8) + blockIdx.x / 8;
+    if (L >= total) return;
+  } else {
+    const int j = blockIdx.x - F;
+    L = F + j / S;
+    part = j;
+    const int nkt = K / GBK, p = j % S, kb = nkt * p / S, ke = nkt * (p + 1) / S;
+    A += (size_t)kb * GBK;
+    B += (size_t)kb * GBK;
+    K = (ke - kb) * GBK;
+  }
+  int tm, tn;
+  tile_of(L, ntm, ntn, tm, tn);
   const int m0 = tm * GBM, n0 = tn * GBN;
 
   u32x4_t ra[GAL], rb[GBL];
@@ -392,8 +419,61 @@ __global__ __launch_bounds__(GNT) void k_gemm_bf16(const bf16_t* __restrict__ A,
 #undef GEMM_GLOAD
 #undef GEMM_SSTORE
 
+  // a split-tail workgroup: accumulators to its slot, in register order (not for
+  // QKV: a second reader of the accumulators beside its epilogue makes the
+  // register allocation spill; its launches never split)
+  if constexpr (EPI != EPI_QKV) {
+    if (part >= 0) {
+      f32x4_t* dst = (f32x4_t*)(ep.split + (size_t)part * split_slot_floats<NI>()) +
+                     (size_t)wave * GMI * GNI * 4 * 64 + lane;
+#pragma unroll
+      for (int mi = 0; mi < GMI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < GNI; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4_t v4 = {acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                          acc[mi][ni][4 * q + 3]};
+            dst[((mi * GNI + ni) * 4 + q) * 64] = v4;
+          }
+      return;
+    }
+  }
   const int cbase = n0 + wn * GTN;
   if (cbase >= N) return;  // the masked half of a partial last N tile
+  gemm_epilogue<EPI, OutT, GMI, GNI>(ep, acc, M, N, m0 + wm * GTM, cbase, lane);
+}
+
+// The split tail's second half: one wave per workgroup, workgroup 8 t + w sums wave
+// w's accumulators of tile F + t over the S slots in slot order and applies the
+// epilogue the unsplit kernel would have (one wave each: the reads and the epilogue
+// spread over eight times as many CUs as the tail has tiles).
+template <int EPI, typename OutT, int NI>
+__global__ __launch_bounds__(64) void k_gemm_fixup(int M, int N, int F, int S, Epi ep) {
+  constexpr int GNI = NI, GTN = 32 * NI, GBN = GWN * GTN;
+  const int lane = threadIdx.x, t = blockIdx.x >> 3, wave = blockIdx.x & 7;
+  const int wm = wave / GWN, wn = wave % GWN;
+  const int ntn = (N + GBN - 1) / GBN, ntm = (M + GBM - 1) / GBM;
+  int tm, tn;
+  tile_of(F + t, ntm, ntn, tm, tn);
+  const int m0 = tm * GBM, n0 = tn * GBN;
+  const int cbase = n0 + wn * GTN;
+  if (cbase >= N) return;
+  f32x16_t acc[GMI][GNI];
+  for (int p = 0; p < S; ++p) {
+    const f32x4_t* src = (const f32x4_t*)(ep.split + (size_t)(t * S + p) * split_slot_floats<NI>()) +
+                         (size_t)wave * GMI * GNI * 4 * 64 + lane;
+#pragma unroll
+    for (int mi = 0; mi < GMI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < GNI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t v4 = src[((mi * GNI + ni) * 4 + q) * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[mi][ni][4 * q + e] = p ? acc[mi][ni][4 * q + e] + v4[e] : v4[e];
+        }
+  }
   gemm_epilogue<EPI, OutT, GMI, GNI>(ep, acc, M, N, m0 + wm * GTM, cbase, lane);
 }
 
@@ -463,40 +543,85 @@ static bool gemm_wide192() {
   return on;
 }
 
+// Launch plan of a bf16 GEMM: tile width, and the split-K tail if it pays.
+struct GemmPlan {
+  bool w192 = false;
+  int F = 0, S = 1, tail = 0, grid = 0;
+};
+
+static GemmPlan plan_gemm(int epi, int M, int N, int K, bool can_split) {
+  GemmPlan P;
+  const int cus = device_cus(), tm = (M + GBM - 1) / GBM, nk = K / GBK;
+  const int tiles4 = tm * ((N + 255) / 256);
+  // Candidate costs in units of one 256 x 256 tile's time, per CU.  Plain 256-wide
+  // tiles: whole rounds over the CUs.
+  double best = (tiles4 + cus - 1) / cus;
+  // 192-wide tiles where they divide N and 256-wide ones do not (N = 2688: 14 full
+  // tiles per row instead of 10.5): a 256 x 192 tile takes about 0.86 of a 256 x 256
+  // one (measured at N = 2688).
+  if ((epi == EPI_GATED_RES || epi == EPI_STORE) && N % 256 != 0 && N % 192 == 0 && gemm_wide192()) {
+    const double c3 = 0.86 * ((tm * (N / 192) + cus - 1) / cus);
+    if (c3 < best) {
+      best = c3;
+      P.w192 = true;
+    }
+  }
+  // Split-K tail: the tiles beyond the last whole round over the CUs, when they fill
+  // at most half of them, each become S >= 2 workgroups over K ranges (at most
+  // kGemmSplitWgs in all, at least two K tiles each): full rounds + 1/S, plus the
+  // partial stores and the fixup pass (measured at N = 2688: about 0.2 of a tile
+  // plus the time of 17 K steps).
+  if (can_split && cus % 8 == 0) {
+    const int full = tiles4 / cus * cus, tail = tiles4 - full;
+    const int S = tail ? min(min(cus, kGemmSplitWgs) / tail, min(4, nk / 2)) : 1;
+    if (tail && S >= 2) {
+      const double cs = full / cus + 1.0 / S + 0.2 + 17.0 / nk;
+      if (cs < best) {
+        P.w192 = false;
+        P.F = full;
+        P.S = S;
+        P.tail = tail;
+        P.grid = full + tail * S;
+        return P;
+      }
+    }
+  }
+  const int tiles = P.w192 ? tm * (N / 192) : tiles4;
+  P.F = P.grid = (tiles + 7) / 8 * 8;  // a whole number of rounds over the 8 XCDs
+  return P;
+}
+
+template <int EPI, typename OutT, int NI>
+static void launch_bf16(const GemmPlan& P, const bf16_t* A, int lda, const bf16_t* B, int ldb,
+                        int M, int N, int K, const Epi& ep, hipStream_t s) {
+  k_gemm_bf16<EPI, OutT, NI><<<P.grid, GNT, 0, s>>>(A, lda, B, ldb, M, N, K, P.F, P.S, ep);
+  if constexpr (EPI != EPI_QKV)
+    if (P.tail) k_gemm_fixup<EPI, OutT, NI><<<P.tail * (GNT / 64), 64, 0, s>>>(M, N, P.F, P.S, ep);
+}
+
 template <int EPI>
 static hipError_t launch_gemm(int dtype, bool out_bf16, const void* A, int lda, const void* B,
                               int ldb, int M, int N, int K, const Epi& ep, hipStream_t s) {
   if (dtype == BF16) {
-    // 192-wide tiles where they divide N and 256-wide ones do not (N = 2688: 14 full
-    // tiles per row instead of 10.5), if that saves whole rounds of the grid over the
-    // CUs: a 256 x 192 tile takes about 0.86 of a 256 x 256 one (measured at N = 2688).
-    bool w192 = false;
-    if ((EPI == EPI_GATED_RES || EPI == EPI_STORE) && N % 256 != 0 && N % 192 == 0 && gemm_wide192()) {
-      const int cus = device_cus(), tm = (M + GBM - 1) / GBM;
-      const int r4 = (tm * ((N + 255) / 256) + cus - 1) / cus, r3 = (tm * (N / 192) + cus - 1) / cus;
-      w192 = r3 * 0.86 < r4;
-    }
-    const int bn = w192 ? 192 : 256;
-    const int tiles = ((M + GBM - 1) / GBM) * ((N + bn - 1) / bn);
-    dim3 grid((tiles + 7) / 8 * 8);  // a whole number of rounds over the 8 XCDs
+    const GemmPlan P = plan_gemm(EPI, M, N, K, EPI != EPI_QKV && ep.split != nullptr);
     const bf16_t *Ab = (const bf16_t*)A, *Bb = (const bf16_t*)B;
     if constexpr (EPI == EPI_QKV) {
-      k_gemm_bf16<EPI, bf16_t, 4><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
+      launch_bf16<EPI, bf16_t, 4>(P, Ab, lda, Bb, ldb, M, N, K, ep, s);
     } else if constexpr (EPI == EPI_GATED_RES) {
-      if (w192)
-        k_gemm_bf16<EPI, bf16_t, 3><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
+      if (P.w192)
+        launch_bf16<EPI, bf16_t, 3>(P, Ab, lda, Bb, ldb, M, N, K, ep, s);
       else
-        k_gemm_bf16<EPI, bf16_t, 4><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
+        launch_bf16<EPI, bf16_t, 4>(P, Ab, lda, Bb, ldb, M, N, K, ep, s);
     } else if constexpr (EPI == EPI_STORE) {
-      if (out_bf16 && w192) k_gemm_bf16<EPI, bf16_t, 3><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
-      else if (out_bf16) k_gemm_bf16<EPI, bf16_t, 4><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
-      else if (w192) k_gemm_bf16<EPI, float, 3><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
-      else k_gemm_bf16<EPI, float, 4><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
+      if (out_bf16 && P.w192) launch_bf16<EPI, bf16_t, 3>(P, Ab, lda, Bb, ldb, M, N, K, ep, s);
+      else if (out_bf16) launch_bf16<EPI, bf16_t, 4>(P, Ab, lda, Bb, ldb, M, N, K, ep, s);
+      else if (P.w192) launch_bf16<EPI, float, 3>(P, Ab, lda, Bb, ldb, M, N, K, ep, s);
+      else launch_bf16<EPI, float, 4>(P, Ab, lda, Bb, ldb, M, N, K, ep, s);
     } else {
       if (out_bf16)
-        k_gemm_bf16<EPI, bf16_t, 4><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
+        launch_bf16<EPI, bf16_t, 4>(P, Ab, lda, Bb, ldb, M, N, K, ep, s);
       else
-        k_gemm_bf16<EPI, float, 4><<<grid, GNT, 0, s>>>(Ab, lda, Bb, ldb, M, N, K, ep);
+        launch_bf16<EPI, float, 4>(P, Ab, lda, Bb, ldb, M, N, K, ep, s);
     }
   } else {
     if constexpr (EPI == EPI_QKV) {

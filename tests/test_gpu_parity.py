@@ -407,6 +407,18 @@ def test_widest_hidden_size(dit, variant, dtype, n):
     _check(spec.name + "-D4096", spec, wl, dit)
 
 
+@pytest.mark.parametrize("variant", ["mmh3", "zimage", "siglip"])
+def test_split_k_tail(dit, variant):
+    """A deep FFN (F = 4096) over two row tiles: on a 256-CU device the fc2 GEMM
+    (K = 4096, two 256 x 256 tiles) runs wholly as a split-K tail, each tile in 4
+    K parts whose fp32 accumulators the fixup pass sums before the epilogue: gated
+    residual (MMH3), plain fp32 store ahead of the sandwich norm (Z-Image), bias +
+    residual (SigLIP)."""
+    spec = _small(variant, "bf16", 300, 256, 64 if variant == "siglip" else 128, 4096)
+    wl = W.make_custom_workload(spec, 3200)
+    _check(spec.name + "-split-k", spec, wl, dit)
+
+
 def test_most_packed_samples(dit):
     """64 samples (the table's maximum), with empty and one-token samples and
     boundaries anywhere, in one sequence."""

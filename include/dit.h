@@ -376,7 +376,8 @@ typedef struct dit_mmh3_model {
  * Host function.  lat_h, lat_w >= 2 (refs likewise).  Returns the row count
  * and sets *n_segs; with pos == NULL only counts.  pos: [max_rows, 3];
  * segs: [max_segs].  Errors (negative): DIT_EINVAL for a keyframe that is not
- * a first or last frame or an unknown reference kind, DIT_ESHAPE for sizes or
+ * a first or last frame, an unknown reference kind or a failed host
+ * allocation, DIT_ESHAPE for sizes, a layout of more than 2^24 rows or
  * too-small outputs. */
 typedef struct dit_layout_ref {
   int32_t kind;  /* DIT_SEG_REF_IMAGE (lat_h, lat_w), DIT_SEG_REF_AUDIO (audio_t) or
@@ -535,7 +536,8 @@ double dit_sigma_remap(double sigma, double from_shift, double to_shift);
  * ref audio} slot indices (-1 when absent).  A token's modulation row is then
  * slot * 3 + tag (video 0, text 1, audio 2; condition frames and reference
  * images take the video tag, reference audio the audio tag).  Host function;
- * returns the slot count (1..4), or DIT_EINVAL for non-finite input. */
+ * returns the slot count (1..4), or DIT_EINVAL for non-finite input, a flow
+ * shift <= 0 or a remapped audio sigma that is not finite. */
 int32_t dit_mmh3_slots(double sigma_v, double shift_video, double shift_audio, double cond_aug,
                        double cond_aug_audio, int32_t has_cond, int32_t has_ref_audio,
                        double slot_sigmas[4], int32_t slot_of[4]);

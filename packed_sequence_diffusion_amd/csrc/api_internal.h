@@ -2,6 +2,7 @@
 // layouts, weight preparation and the block; dit_model.cpp: evaluation layouts,
 // slot plans and the whole-model forwards).  Not part of the public ABI.
 #pragma once
+#include <new>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -10,6 +11,8 @@
 #include "../../include/dit.h"
 
 namespace dit_host {
+
+constexpr int kMaxSlots = 8;  // timestep slots of one block, at most
 
 constexpr size_t kNone = SIZE_MAX;  // offset of a buffer a variant does not have
 constexpr size_t kAlign = 256;      // alignment of every workspace / prepared-weight region
@@ -58,3 +61,12 @@ dit_status final_forward_impl(const dit_config* c, const void* prepared, const f
     if (st_ != DIT_OK) return st_; \
   } while (0)
 #define HIP_TRY(expr, what) DIT_TRY(dit_host::hip_check((expr), what))
+// Host-side exceptions (a failed allocation) never cross the C ABI: the entry
+// points that allocate on the host end their body with this catch list.
+#define DIT_CATCH_ALL                                                                  \
+  catch (const std::bad_alloc&) {                                                      \
+    return dit_host::fail(DIT_EINVAL, "host memory allocation failed");                \
+  }                                                                                    \
+  catch (...) {                                                                        \
+    return dit_host::fail(DIT_EINVAL, "unexpected host exception");                    \
+  }

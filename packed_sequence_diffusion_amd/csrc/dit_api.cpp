@@ -92,7 +92,7 @@ dit_status check_config(const dit_config* c) {
   if (c->adaln_shared != 0 && (c->adaln_shared != 1 || !basis_mods(c)))
     return fail(DIT_EINVAL, "adaln_shared=%d (0, or 1 for MMH3 / FINAL)", c->adaln_shared);
   if (basis_mods(c)) {
-    if (c->slots < 1 || c->slots > 8) return fail(DIT_EUNSUPPORTED, "slots=%d not in [1, 8]", c->slots);
+    if (c->slots < 1 || c->slots > kMaxSlots) return fail(DIT_EUNSUPPORTED, "slots=%d not in [1, %d]", c->slots, kMaxSlots);
     if (c->tags < 1 || c->tags > 16) return fail(DIT_EINVAL, "tags=%d not in [1, 16]", c->tags);
     if (c->rank < 1 || c->rank > 64) return fail(DIT_EUNSUPPORTED, "rank=%d not in [1, 64]", c->rank);
     if (c->grid < 2) return fail(DIT_EINVAL, "grid=%d must be >= 2", c->grid);
@@ -352,7 +352,9 @@ const char* dit_phase_name(int32_t phase) {
 dit_status dit_profile_begin(int32_t max_calls) {
   if (max_calls < 1 || max_calls > 100000) return fail(DIT_EINVAL, "max_calls=%d not in [1, 100000]", max_calls);
   if (g_prof.on) return fail(DIT_EINVAL, "profiling already armed on this thread");
-  g_prof.ev.assign((size_t)max_calls * (DIT_NPHASES + 1), nullptr);
+  try {
+    g_prof.ev.assign((size_t)max_calls * (DIT_NPHASES + 1), nullptr);
+  } DIT_CATCH_ALL
   for (auto& e : g_prof.ev) {
     hipError_t err = hipEventCreate(&e);
     if (err != hipSuccess) {

@@ -22,6 +22,7 @@ namespace {
 // Latent frames a video token spans, cycling with period 5, rescaled onto the
 // time axis ([MMH3] FRAME_PER_TOKEN, FRAME_RESCALE).
 constexpr double kFrameRescale = 5.0 / 3.0;
+constexpr int kMaxLayoutRows = 1 << 24;  // rows of one layout, at most
 double frame_t(int k) {
   static const double span[5] = {1.0, 4.0, 4.0, 4.0, 4.0};
   return kFrameRescale * span[k % 5];
@@ -47,6 +48,20 @@ int32_t dit_mmh3_layout(int32_t text_len, int32_t latent_t, int32_t lat_h, int32
       n_refs < 0)
     return fail(DIT_ESHAPE, "layout sizes: counts >= 0, lat_h and lat_w >= 2");
   if ((n_keyframes && !keyframes) || (n_refs && !refs)) return fail(DIT_EINVAL, "keyframes/refs is NULL");
+  // the rows the layout will hold, counted before it is built (int32 row indices, and
+  // far below what the host buffers could take)
+  const double hw = (double)(lat_h / 2) * (lat_w / 2);
+  double est = text_len + 2.0 * audio_t + (double)latent_t * hw + (double)n_keyframes * hw;
+  for (int r = 0; r < n_refs; ++r) {
+    const dit_layout_ref& f = refs[r];
+    const double rhw = (double)std::max(f.lat_h / 2, 0) * std::max(f.lat_w / 2, 0);
+    if (f.kind == DIT_SEG_REF_IMAGE) est += rhw;
+    else if (f.kind == DIT_SEG_VIDEO) est += 2.0 * std::max(f.audio_t, 0) + std::max(f.latent_t, 0) * rhw;
+    else if (f.kind == DIT_SEG_REF_AUDIO) est += 2.0 * std::max(f.audio_t, 0);
+  }
+  if (est > (double)kMaxLayoutRows)
+    return fail(DIT_ESHAPE, "layout of %.0f rows exceeds %d", est, kMaxLayoutRows);
+  try {
   std::vector<double> P;  // (t, h, w) per row
   std::vector<dit_segment> G;
   auto row = [&](double t, double h, double w) { P.push_back(t); P.push_back(h); P.push_back(w); };
@@ -134,6 +149,7 @@ int32_t dit_mmh3_layout(int32_t text_len, int32_t latent_t, int32_t lat_h, int32
   }
   g_err[0] = 0;
   return nrows();
+  } DIT_CATCH_ALL
 }
 
 int32_t dit_mmh3_slots(double sigma_v, double shift_video, double shift_audio, double cond_aug,
@@ -143,9 +159,11 @@ int32_t dit_mmh3_slots(double sigma_v, double shift_video, double shift_audio, d
   if (!isfinite(sigma_v) || !isfinite(shift_video) || !isfinite(shift_audio) || !isfinite(cond_aug) ||
       !isfinite(cond_aug_audio))
     return fail(DIT_EINVAL, "non-finite slot input");
+  if (!(shift_video > 0.0) || !(shift_audio > 0.0)) return fail(DIT_EINVAL, "flow shifts must be > 0");
   const double sv = std::max(sigma_v, 1e-6);
   const double tv = 1.0 - sv;
   const double ta = 1.0 - dit_sigma_remap(sv, shift_video, shift_audio);
+  if (!isfinite(ta)) return fail(DIT_EINVAL, "audio sigma of sigma_v=%g is not finite", sigma_v);
   double t[4] = {tv, ta, 0.0, 0.0};
   int nt = 2;
   const double tc = std::max(tv, cond_aug), tca = std::max(ta, cond_aug_audio);
@@ -280,8 +298,8 @@ dit_status dit_mmh3_forward(const dit_mmh3_model* m, const dit_segment* segs, in
                                 P.ncond > 0, 0, ssig, slot);
   if (nt < 0) return (dit_status)nt;
   if (nt > bc->slots) return fail(DIT_EUNSUPPORTED, "the evaluation needs %d slots, the blocks have %d", nt, bc->slots);
-  std::vector<double> sig(bc->slots, ssig[nt - 1]);  // slots beyond the plan: unused rows
-  for (int i = 0; i < nt; ++i) sig[i] = ssig[i];
+  double sig[kMaxSlots];  // slots beyond the plan: unused rows
+  for (int i = 0; i < bc->slots; ++i) sig[i] = i < nt ? ssig[i] : ssig[nt - 1];
   float* h = at<float>(workspace, P.h);
   int* rows = at<int>(workspace, P.rows);
   int* hrows = at<int>(workspace, P.hrows);
@@ -317,14 +335,14 @@ dit_status dit_mmh3_forward(const dit_mmh3_model* m, const dit_segment* segs, in
     }
   }
   // blocks, in place on h
-  DIT_TRY(dit_stack_forward(bc, m->blocks, m->n_blocks, h, P.n, rows, pos, sig.data(), bc->slots, nullptr, 0, h,
+  DIT_TRY(dit_stack_forward(bc, m->blocks, m->n_blocks, h, P.n, rows, pos, sig, bc->slots, nullptr, 0, h,
                             at<char>(workspace, P.bws), ws_layout(bc, P.n).total, s));
   // heads: the row of a head is the stream's timestep slot
   const size_t hws = P.total - P.hws;
   {
     const dit_segment& g = segs[P.video];
     HIP_TRY(dit::fill_i32(hrows, P.nv, slot[0], s), "head rows");
-    DIT_TRY(dit_final_forward(m->head_video, m->head_video_w, h + (size_t)g.start * D, P.nv, hrows, sig.data(),
+    DIT_TRY(dit_final_forward(m->head_video, m->head_video_w, h + (size_t)g.start * D, P.nv, hrows, sig,
                               bc->slots, hout, at<char>(workspace, P.hws), hws, s));
     HIP_TRY(dit::unpatchify_video(hout, C, T, H, W, video_out, s), "unpatchify");
   }
@@ -333,7 +351,7 @@ dit_status dit_mmh3_forward(const dit_mmh3_model* m, const dit_segment* segs, in
     HIP_TRY(dit::fill_i32(hrows, P.na, slot[1], s), "head rows");
     const double slope =
         m->audio_slope_rescale ? dit_sigma_remap_slope(sigma_v, m->shift_video, m->shift_audio) : 1.0;
-    DIT_TRY(final_forward_impl(m->head_audio, m->head_audio_w, h + (size_t)g.start * D, P.na, hrows, sig.data(),
+    DIT_TRY(final_forward_impl(m->head_audio, m->head_audio_w, h + (size_t)g.start * D, P.na, hrows, sig,
                                bc->slots, (float)-slope, hout, at<char>(workspace, P.hws), hws, s));
     HIP_TRY(dit::unpack_audio(hout, m->audio_c, Ta, audio_out, s), "unpack_audio");
   }

@@ -22,7 +22,9 @@
  *     On failure nothing is written and a negative dit_status is returned; the
  *     message is in dit_last_error() (thread-local).  Launch failures return
  *     DIT_EHIP.  Device faults surface at the caller's next synchronization.
- *   - n == 0 is valid and does nothing.
+ *   - n == 0 is valid and does nothing.  Every token count (a block's n, an
+ *     evaluation's segments, a Z-Image image plus caption, a layout) is at
+ *     most 2^24; larger ones are refused with DIT_ESHAPE (size queries: 0).
  *   - There is no CPU fallback: every step runs in the library's HIP kernels.
  *   - Supported shapes: hd in {64, 128}, D = H*hd, D % 128 == 0,
  *     F % 128 == 0, D <= 4096, 1 <= slots <= 8, rank <= 64, grid >= 2;

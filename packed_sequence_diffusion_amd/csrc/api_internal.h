@@ -13,6 +13,10 @@
 namespace dit_host {
 
 constexpr int kMaxSlots = 8;  // timestep slots of one block, at most
+// Tokens of one call, at most: every int product the kernels form from a row
+// count (rows x head-dim pairs of the cos/sin table, grid sizes) stays below 2^31.
+constexpr int kMaxTokens = 1 << 24;
+inline bool bad_tokens(long long n) { return n < 0 || n > kMaxTokens; }
 
 constexpr size_t kNone = SIZE_MAX;  // offset of a buffer a variant does not have
 constexpr size_t kAlign = 256;      // alignment of every workspace / prepared-weight region

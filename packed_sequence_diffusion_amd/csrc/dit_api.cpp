@@ -424,13 +424,13 @@ size_t dit_prepared_size(const dit_config* cfg) {
 }
 
 size_t dit_workspace_size(const dit_config* cfg, int32_t n) {
-  if (check_config(cfg) != DIT_OK || n < 0) return 0;
+  if (check_config(cfg) != DIT_OK || bad_tokens(n)) return 0;
   return ws_layout(cfg, n).total;
 }
 
 dit_status dit_workspace_layout(const dit_config* cfg, int32_t n, dit_ws_layout* out) {
   DIT_TRY(check_config(cfg));
-  if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
+  if (bad_tokens(n)) return fail(DIT_ESHAPE, "n=%d not in [0, %d]", n, kMaxTokens);
   if (!out) return fail(DIT_EINVAL, "out is NULL");
   *out = ws_layout(cfg, n);
   return DIT_OK;
@@ -585,7 +585,7 @@ dit_status dit_adaln_modulate(const dit_config* c, const void* prepared, const f
                               int32_t half, void* xn_out, float* mods_out, float* temb_scratch,
                               void* stream) {
   DIT_TRY(check_config(c));
-  if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
+  if (bad_tokens(n)) return fail(DIT_ESHAPE, "n=%d not in [0, %d]", n, kMaxTokens);
   if (half != 0 && half != 1) return fail(DIT_EINVAL, "half=%d not in {0, 1}", half);
   if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
   if (has_mods(c)) {
@@ -620,7 +620,8 @@ static dit_status attention_impl(const dit_config* c, const void* q, const void*
                           int32_t n, int32_t ldn, const int32_t* seq_starts, int32_t nseq,
                           float score_scale, void* o, void* stream) {
   DIT_TRY(check_config(c));
-  if (n < 0 || ldn < n || ldn % 128) return fail(DIT_ESHAPE, "need 0 <= n <= ldn, ldn %% 128 == 0 (n=%d ldn=%d)", n, ldn);
+  if (bad_tokens(n) || ldn < n || ldn % 128 || bad_tokens(ldn))
+    return fail(DIT_ESHAPE, "need 0 <= n <= ldn <= %d, ldn %% 128 == 0 (n=%d ldn=%d)", kMaxTokens, n, ldn);
   if (seq_starts) DIT_TRY(check_seqs(seq_starts, nseq, n));
   if (n == 0) return DIT_OK;
   if (!q || !k || !vt || !o) return fail(DIT_EINVAL, "q/k/vt/o is NULL");
@@ -656,7 +657,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
                               void* stream) {
   DIT_TRY(check_config(c));
   if (head(c)) return fail(DIT_EUNSUPPORTED, "output heads are run by dit_final_forward");
-  if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
+  if (bad_tokens(n)) return fail(DIT_ESHAPE, "n=%d not in [0, %d]", n, kMaxTokens);
   if (seq_starts) DIT_TRY(check_seqs(seq_starts, nseq, n));
   if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
   if (mods_in) {
@@ -861,7 +862,7 @@ dit_status dit_host::final_forward_impl(const dit_config* c, const void* prepare
                               float* out, void* workspace, size_t ws_bytes, void* stream) {
   DIT_TRY(check_config(c));
   if (!head(c)) return fail(DIT_EINVAL, "dit_final_forward needs a DIT_FINAL or DIT_ZFINAL config");
-  if (n < 0) return fail(DIT_ESHAPE, "n=%d < 0", n);
+  if (bad_tokens(n)) return fail(DIT_ESHAPE, "n=%d not in [0, %d]", n, kMaxTokens);
   if (!prepared) return fail(DIT_EINVAL, "prepared is NULL");
   DIT_TRY(check_sigmas(c, sigmas, n_sigmas));
   if (n == 0) return DIT_OK;
@@ -1007,7 +1008,8 @@ dit_status dit_block_forward_mods(const dit_config* c, const void* prepared, con
 
 dit_status dit_rms_norm(const float* x, int32_t n, int32_t D, const float* g, float eps, float* out,
                         void* stream) {
-  if (n < 0 || D <= 0 || D % 4 || D > 4096) return fail(DIT_ESHAPE, "n=%d D=%d (D %% 4 == 0, <= 4096)", n, D);
+  if (bad_tokens(n) || D <= 0 || D % 4 || D > 4096)
+    return fail(DIT_ESHAPE, "n=%d D=%d (n <= %d, D %% 4 == 0, <= 4096)", n, D, kMaxTokens);
   if (!(eps >= 0.0f)) return fail(DIT_EINVAL, "eps must be >= 0");
   if (n == 0) return DIT_OK;
   if (!x || !g || !out) return fail(DIT_EINVAL, "x/g/out is NULL");

@@ -22,7 +22,6 @@ namespace {
 // Latent frames a video token spans, cycling with period 5, rescaled onto the
 // time axis ([MMH3] FRAME_PER_TOKEN, FRAME_RESCALE).
 constexpr double kFrameRescale = 5.0 / 3.0;
-constexpr int kMaxLayoutRows = 1 << 24;  // rows of one layout, at most
 double frame_t(int k) {
   static const double span[5] = {1.0, 4.0, 4.0, 4.0, 4.0};
   return kFrameRescale * span[k % 5];
@@ -59,8 +58,8 @@ int32_t dit_mmh3_layout(int32_t text_len, int32_t latent_t, int32_t lat_h, int32
     else if (f.kind == DIT_SEG_VIDEO) est += 2.0 * std::max(f.audio_t, 0) + std::max(f.latent_t, 0) * rhw;
     else if (f.kind == DIT_SEG_REF_AUDIO) est += 2.0 * std::max(f.audio_t, 0);
   }
-  if (est > (double)kMaxLayoutRows)
-    return fail(DIT_ESHAPE, "layout of %.0f rows exceeds %d", est, kMaxLayoutRows);
+  if (est > (double)kMaxTokens)
+    return fail(DIT_ESHAPE, "layout of %.0f rows exceeds %d", est, kMaxTokens);
   try {
   std::vector<double> P;  // (t, h, w) per row
   std::vector<dit_segment> G;
@@ -203,6 +202,7 @@ dit_status plan_model(const dit_mmh3_model* m, const dit_segment* segs, int32_t 
       m->head_video->D != m->block->D || m->head_video->slots != m->block->slots)
     return fail(DIT_EINVAL, "video head: DIT_FINAL, F = 4 * latent_c, the blocks' D and slots");
   const bool bf = m->block->dtype == DIT_BF16;
+  if (m->latent_c > 65536 || m->audio_c > 65536) return fail(DIT_EUNSUPPORTED, "latent_c/audio_c > 65536");
   if (m->latent_c <= 0 || (4 * m->latent_c) % (bf ? 64 : 16))
     return fail(DIT_EUNSUPPORTED, "latent_c=%d: 4 * latent_c must be a multiple of %d", m->latent_c, bf ? 64 : 16);
   int pos = 0;
@@ -219,6 +219,7 @@ dit_status plan_model(const dit_mmh3_model* m, const dit_segment* segs, int32_t 
     }
   }
   if (P->video < 0) return fail(DIT_EINVAL, "no VIDEO segment");
+  if (bad_tokens(pos)) return fail(DIT_ESHAPE, "%d tokens (at most %d)", pos, kMaxTokens);
   P->n = pos;
   P->nv = segs[P->video].stop - segs[P->video].start;
   P->na = P->audio >= 0 ? segs[P->audio].stop - segs[P->audio].start : 0;
@@ -275,12 +276,12 @@ dit_status dit_mmh3_forward(const dit_mmh3_model* m, const dit_segment* segs, in
   DIT_TRY(plan_model(m, segs, nseg, &P));
   const dit_config* bc = m->block;
   const int D = bc->D, C = m->latent_c;
-  if (T <= 0 || H <= 0 || W <= 0 || H % 2 || W % 2 || P.nv != T * (H / 2) * (W / 2))
+  if (T <= 0 || H <= 0 || W <= 0 || H % 2 || W % 2 || (long long)P.nv != (long long)T * (H / 2) * (W / 2))
     return fail(DIT_ESHAPE, "video [%d, %d, %d, %d] does not give the VIDEO segment's %d rows", C, T, H, W, P.nv);
   if (P.audio >= 0 && P.na != 2 * Ta) return fail(DIT_ESHAPE, "audio length %d does not give %d rows", Ta, P.na);
   for (int i = 0; i < nseg; ++i)
-    if (segs[i].kind == DIT_SEG_COND && segs[i].stop - segs[i].start != (H / 2) * (W / 2))
-      return fail(DIT_ESHAPE, "COND segment %d must hold one frame of %d rows", i, (H / 2) * (W / 2));
+    if (segs[i].kind == DIT_SEG_COND && (long long)segs[i].stop - segs[i].start != (long long)(H / 2) * (W / 2))
+      return fail(DIT_ESHAPE, "COND segment %d must hold one frame of (H/2)(W/2) rows", i);
   if (!pos || !video || !video_out || (P.audio >= 0 && (!audio || !audio_out)) ||
       (P.text >= 0 && segs[P.text].stop > segs[P.text].start && !text) || (P.ncond && !cond))
     return fail(DIT_EINVAL, "an input or output pointer is NULL");
@@ -386,6 +387,7 @@ dit_status plan_zimage(const dit_zimage_model* m, int H, int W, int cap_len, ZPl
     return fail(DIT_EINVAL, "configs must be DIT_ZIMAGE, DIT_ZCONTEXT and DIT_ZFINAL");
   if (c->D != b->D || c->H != b->H || c->hd != b->hd || c->dtype != b->dtype || f->D != b->D || f->dtype != b->dtype)
     return fail(DIT_EINVAL, "block, context refiner and final layer must share D, heads and dtype");
+  if (m->in_channels > 65536) return fail(DIT_EUNSUPPORTED, "in_channels=%d > 65536", m->in_channels);
   if (f->F != 4 * m->in_channels) return fail(DIT_EINVAL, "final layer F=%d != 4 * in_channels", f->F);
   if (m->n_layers < 0 || m->n_noise_refiners < 0 || m->n_context_refiners < 0)
     return fail(DIT_EINVAL, "negative block counts");
@@ -400,8 +402,10 @@ dit_status plan_zimage(const dit_zimage_model* m, int H, int W, int cap_len, ZPl
   if (m->cap_dim <= 0 || m->cap_dim % km || m->cap_dim > 4096)
     return fail(DIT_EUNSUPPORTED, "cap_dim=%d must be a multiple of %d and <= 4096", m->cap_dim, km);
   if (!(m->cap_eps >= 0.0f)) return fail(DIT_EINVAL, "cap_eps must be >= 0");
-  if (H <= 0 || W <= 0 || H % 2 || W % 2 || cap_len < 0)
-    return fail(DIT_ESHAPE, "image %d x %d (even, > 0), caption %d", H, W, cap_len);
+  if (H <= 0 || W <= 0 || H % 2 || W % 2 || cap_len < 0 ||
+      bad_tokens((long long)(H / 2) * (W / 2) + cap_len))
+    return fail(DIT_ESHAPE, "image %d x %d (even, > 0), caption %d: at most %d tokens", H, W, cap_len,
+                kMaxTokens);
   P->ni = (H / 2) * (W / 2);
   P->nc = cap_len;
   P->n = P->ni + P->nc;

@@ -107,6 +107,10 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run packed_sequence_diffusion_amd.build "
                           "(there is no CPU fallback)")
+    # torch first: its bundled HIP runtime (soname libamdhip64.so.7, the library's
+    # dependency) is then the one the library binds to.  Loaded the other way round,
+    # the process would hold two HIP runtimes and torch's would see no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P = POINTER
     sig = {

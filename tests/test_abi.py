@@ -377,7 +377,9 @@ def test_mmh3_evaluation_refusals(dit):
     assert dit.lib.dit_mmh3_workspace_size(None, _segs(dit, good), 3) == 0
 
 
-def test_zimage_forward_cache_refusals(dit):
+def _zimage_model_struct(dit):
+    """A DitZimageModel over valid configs and placeholder (aligned, never
+    dereferenced) pointers: 3 main layers, 1 noise and 1 context refiner."""
     z = W.spec_by_name("zimage")
     cfgs = [dit.make_config(W.small_spec(z, variant=v, D=256, H=2, F=384 if v != "zfinal" else 64))
             for v in ("zimage", "zcontext", "zfinal")]
@@ -388,6 +390,11 @@ def test_zimage_forward_cache_refusals(dit):
     m.context_refiners, m.n_context_refiners = arr, 1
     m.final_w, m.in_channels, m.cap_dim, m.cap_eps = 256, 16, 128, 1e-6
     m.x_embed_w, m.cap_norm, m.cap_embed_w = 256, 256, 256
+    return m, (cfgs, arr)
+
+
+def test_zimage_forward_cache_refusals(dit):
+    m, keep = _zimage_model_struct(dit)
     need = dit.lib.dit_zimage_workspace_size(ctypes.byref(m), 16, 16, 40)
     assert need > 0
 

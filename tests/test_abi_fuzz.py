@@ -153,3 +153,60 @@ def test_slot_planner_and_remap_never_crash():
         s = L.dit_sigma_remap(_pick(rng, vals), _pick(rng, [0.0, 3.0, 12.0, -1.0]),
                               _pick(rng, [0.0, 3.0, 12.0]))
         assert isinstance(s, float)
+
+
+def test_model_workspace_queries_never_crash():
+    """The MMH3 and Z-Image evaluation planners on random segment lists, image
+    sizes and model fields: a size or 0, never a crash."""
+    from tests.test_abi import _mmh3_model_struct, _zimage_model_struct
+    rng = np.random.default_rng(19)
+    m, keep = _mmh3_model_struct(dit)
+    kinds = [-1, 0, 1, 2, 3, 4, 5, 6]
+    for _ in range(1500):
+        nseg = int(rng.integers(0, 7))
+        segs = (dit.DitSegment * max(nseg, 1))()
+        pos = 0
+        for i in range(nseg):
+            ln = _pick(rng, [-4, 0, 1, 16, 32, 77, 1 << 20, (1 << 31) - 1])
+            start = pos if rng.random() < 0.8 else _pick(rng, [-1, 0, pos + 3])
+            segs[i] = dit.DitSegment(_pick(rng, kinds), start, max(-(1 << 31), min(start + ln, (1 << 31) - 1)))
+            pos = segs[i].stop
+        m.n_blocks = _pick(rng, [-1, 0, 1, 2])
+        m.latent_c = _pick(rng, [-16, 0, 15, 16, 1 << 20])
+        m.audio_c = _pick(rng, [0, 64, 100])
+        m.audio_slope_rescale = _pick(rng, [0, 1, 2])
+        got = L.dit_mmh3_workspace_size(ctypes.byref(m), segs, nseg)
+        assert got >= 0
+    z, zkeep = _zimage_model_struct(dit)
+    for _ in range(1500):
+        hw = [_pick(rng, [-2, 0, 1, 2, 15, 16, 128, 1 << 15, 1 << 20, (1 << 31) - 2]) for _ in range(2)]
+        cap = _pick(rng, [-1, 0, 1, 40, 512, 1 << 20, (1 << 31) - 1])
+        z.n_layers = _pick(rng, [-1, 0, 1, 2])
+        z.n_noise_refiners = _pick(rng, [-1, 0, 1])
+        z.n_context_refiners = _pick(rng, [-1, 0, 1])
+        z.in_channels = _pick(rng, [-16, 0, 15, 16, 1 << 20])
+        z.cap_dim = _pick(rng, [-1, 0, 64, 128, 100])
+        got = L.dit_zimage_workspace_size(ctypes.byref(z), hw[0], hw[1], cap)
+        assert got >= 0
+
+
+def test_token_counts_past_the_cap_are_refused():
+    """Token counts past 2^24 (where int row products in the planners used to
+    wrap) give no size rather than a wrong one."""
+    from tests.test_abi import _mmh3_model_struct, _zimage_model_struct
+    z, zkeep = _zimage_model_struct(dit)
+    assert L.dit_zimage_workspace_size(ctypes.byref(z), 16, 16, 40) > 0
+    for h, w, cap in [(1 << 20, 1 << 20, 40), ((1 << 31) - 2, (1 << 31) - 2, 40),
+                      (128, 128, (1 << 31) - 1), (8192, 8192, 1)]:
+        assert L.dit_zimage_workspace_size(ctypes.byref(z), h, w, cap) == 0
+    m, keep = _mmh3_model_struct(dit)
+    big = (1 << 24) + 64
+    segs = (dit.DitSegment * 3)(dit.DitSegment(0, 0, big - 56), dit.DitSegment(2, big - 56, big - 32),
+                                dit.DitSegment(1, big - 32, big))
+    assert L.dit_mmh3_workspace_size(ctypes.byref(m), segs, 3) == 0
+    assert "tokens" in dit.last_error()
+    cfg = dit.make_config(W.spec_by_name("t2va"))
+    assert L.dit_workspace_size(ctypes.byref(cfg), 1 << 24) > 0
+    assert L.dit_workspace_size(ctypes.byref(cfg), (1 << 24) + 1) == 0
+    assert L.dit_mmh3_layout(1 << 24, 1, 2, 2, 0, None, 0, None, 0, None, 0, None, 0,
+                             ctypes.byref(ctypes.c_int32())) < 0

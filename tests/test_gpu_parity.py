@@ -419,6 +419,15 @@ def test_split_k_tail(dit, variant):
     _check(spec.name + "-split-k", spec, wl, dit)
 
 
+def test_split_k_tail_wide_encoder(dit):
+    """A SigLIP-shaped layer at D = 4096 over two row tiles: the fc1 GEMM (K =
+    4096, bias + GELU-tanh epilogue) and the out projection (K = 4096, bias +
+    residual) run as split-K tails."""
+    spec = _small("siglip", "bf16", 300, 4096, 64, 256)
+    wl = W.make_custom_workload(spec, 3300)
+    _check(spec.name + "-D4096-split-k", spec, wl, dit)
+
+
 def test_most_packed_samples(dit):
     """64 samples (the table's maximum), with empty and one-token samples and
     boundaries anywhere, in one sequence."""

@@ -428,6 +428,15 @@ def test_split_k_tail_wide_encoder(dit):
     _check(spec.name + "-D4096-split-k", spec, wl, dit)
 
 
+def test_long_sequence_sampled(dit):
+    """65613 tokens (ragged against every tile size) at D = 512: GEMM grids of
+    257 row tiles, an attention grid of 4 x 257 units with a split last round,
+    ldn past 65536; sampled rows (with the last token) against the oracle."""
+    spec = _small("mmh3", "bf16", 65613, 512, 128, 1024)
+    wl = W.make_custom_workload(spec, 6561)
+    _check(spec.name + "-long", spec, wl, dit, qrows=_sample_rows(spec.n, SAMPLE, 8))
+
+
 def test_most_packed_samples(dit):
     """64 samples (the table's maximum), with empty and one-token samples and
     boundaries anywhere, in one sequence."""

@@ -332,6 +332,9 @@ typedef enum {
   DIT_SEG_REF_IMAGE = 4,  /* layout only: a reference image, or a reference clip's frames */
   DIT_SEG_REF_AUDIO = 5   /* layout only: reference audio, or a reference clip's soundtrack */
 } dit_segment_kind;
+/* dit_mmh3_forward refuses the two reference kinds: [MMH3] MiniMaxH3::forward
+ * plans their slots and rows (see dit_mmh3_slots) but embeds no hidden rows for
+ * them; a caller that embeds references runs the blocks with dit_stack_forward. */
 
 typedef struct dit_segment {
   int32_t kind, start, stop; /* rows [start, stop) of the packed sequence */

@@ -424,7 +424,8 @@ typedef struct dit_zimage_model {
   int32_t n_layers;
   const void* const* noise_refiners;  /* image tokens only, modulated                    */
   int32_t n_noise_refiners;
-  const dit_config* context;          /* DIT_ZCONTEXT, same D/H/hd/F as block            */
+  const dit_config* context;          /* DIT_ZCONTEXT, same D/H/hd as block (may be NULL
+                                         with no context refiners)                       */
   const void* const* context_refiners;/* caption tokens only, unmodulated                */
   int32_t n_context_refiners;
   const dit_config* final_layer;      /* DIT_ZFINAL, F = 4 * in_channels                 */

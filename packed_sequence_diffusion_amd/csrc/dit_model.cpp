@@ -377,15 +377,17 @@ dit_status run_blocks(const dit_config* c, const void* const* prep, int b0, int 
 
 dit_status plan_zimage(const dit_zimage_model* m, int H, int W, int cap_len, ZPlan* P) {
   if (!m) return fail(DIT_EINVAL, "model is NULL");
-  if (!m->block || !m->context || !m->final_layer || !m->final_w)
-    return fail(DIT_EINVAL, "model needs block, context and final-layer configs and final weights");
+  if (!m->block || !m->final_layer || !m->final_w || (m->n_context_refiners > 0 && !m->context))
+    return fail(DIT_EINVAL, "model needs block and final-layer configs, final weights and (with context "
+                            "refiners) their config");
   DIT_TRY(check_config(m->block));
-  DIT_TRY(check_config(m->context));
+  if (m->context) DIT_TRY(check_config(m->context));
   DIT_TRY(check_config(m->final_layer));
   const dit_config *b = m->block, *c = m->context, *f = m->final_layer;
-  if (b->variant != DIT_ZIMAGE || c->variant != DIT_ZCONTEXT || f->variant != DIT_ZFINAL)
+  if (b->variant != DIT_ZIMAGE || (c && c->variant != DIT_ZCONTEXT) || f->variant != DIT_ZFINAL)
     return fail(DIT_EINVAL, "configs must be DIT_ZIMAGE, DIT_ZCONTEXT and DIT_ZFINAL");
-  if (c->D != b->D || c->H != b->H || c->hd != b->hd || c->dtype != b->dtype || f->D != b->D || f->dtype != b->dtype)
+  if ((c && (c->D != b->D || c->H != b->H || c->hd != b->hd || c->dtype != b->dtype)) || f->D != b->D ||
+      f->dtype != b->dtype)
     return fail(DIT_EINVAL, "block, context refiner and final layer must share D, heads and dtype");
   if (m->in_channels > 65536) return fail(DIT_EUNSUPPORTED, "in_channels=%d > 65536", m->in_channels);
   if (f->F != 4 * m->in_channels) return fail(DIT_EINVAL, "final layer F=%d != 4 * in_channels", f->F);
@@ -420,7 +422,7 @@ dit_status plan_zimage(const dit_zimage_model* m, int H, int W, int cap_len, ZPl
   P->prow = take((size_t)P->ni * 4 * m->in_channels * es);
   P->crow = take((size_t)std::max(P->nc, 1) * m->cap_dim * es);
   P->hout = take((size_t)P->ni * 4 * m->in_channels * 4);
-  P->bws_bytes = std::max({ws_layout(b, P->n).total, ws_layout(c, std::max(P->nc, 1)).total,
+  P->bws_bytes = std::max({ws_layout(b, P->n).total, c ? ws_layout(c, std::max(P->nc, 1)).total : (size_t)0,
                            ws_layout(f, P->ni).total});
   P->bws = take(P->bws_bytes);
   P->total = off;

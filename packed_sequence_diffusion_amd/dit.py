@@ -646,14 +646,16 @@ class ZimageModel:
         arr = lambda bl: (c_void_p * max(len(bl), 1))(*[b.prepared.data_ptr() for b in bl])  # noqa: E731
         self._arrs = (arr(self.layers), arr(self.noise), arr(self.context))
         self._keep = (x_embed_w, x_embed_b, cap_norm, cap_embed_w, cap_embed_b)
+        if block_cfg is None and not (self.layers or self.noise):
+            raise ValueError("ZimageModel needs a block config (block_cfg) when it has no blocks")
         bcfg = block_cfg or (self.layers or self.noise)[0].cfg
-        ccfg = context_cfg or self.context[0].cfg
+        ccfg = context_cfg or (self.context[0].cfg if self.context else None)
         self._cfgs = (bcfg, ccfg)
         m = DitZimageModel()
         m.block = ctypes.pointer(bcfg)
         m.layers, m.n_layers = self._arrs[0], len(self.layers)
         m.noise_refiners, m.n_noise_refiners = self._arrs[1], len(self.noise)
-        m.context = ctypes.pointer(ccfg)
+        m.context = ctypes.pointer(ccfg) if ccfg is not None else None
         m.context_refiners, m.n_context_refiners = self._arrs[2], len(self.context)
         m.final_layer = ctypes.pointer(final.cfg)
         m.final_w = final.prepared.data_ptr()

@@ -685,6 +685,33 @@ def test_mmh3_block_brute_force_tiny():
                                got[sel], rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_mmh3_block_brute_force_random_tiny(seed):
+    """Seeded random tiny shapes (tokens, width, heads, FFN, slots, adaLN rank
+    and grid, RoPE axes and base, random segment rows) against the scalar
+    brute force."""
+    rng = np.random.default_rng(300 + seed)
+    hd = int(rng.choice([8, 12, 16]))
+    H = int(rng.choice([1, 2]))
+    axes = {8: (2, 2, 4), 12: (4, 4, 4), 16: (4, 6, 6)}[hd]
+    slots = int(rng.integers(1, 4))
+    spec = W.BlockSpec("rtiny", "mmh3", "f32", n=int(rng.integers(1, 10)), D=H * hd, H=H, hd=hd,
+                       F=int(rng.choice([4, 12])), slots=slots, rank=int(rng.integers(1, 5)),
+                       grid=int(rng.choice([3, 9])), rope="split_half", rope_axes=axes,
+                       rope_theta=float(rng.choice([10.0, 100.0, 1e4])))
+    sig = [float(v) for v in rng.uniform(0.0, 1.0, size=slots)]
+    wl = W.make_custom_workload(spec, 400 + seed, sigmas=sig)
+    w = {k: v.astype(np.float64) for k, v in wl.weights.items()}
+    w["adaln_basis"] = w["adaln_basis"] * 10.0
+    for k in ("w_qkv", "w_out", "w_fc1", "w_fc2"):
+        w[k] = w[k] * 10.0
+    x, pos = wl.x.astype(np.float64), wl.pos.astype(np.float64)
+    rows = rng.integers(0, slots * spec.tags, size=spec.n).astype(np.int32)
+    got = O.mmh3_block(spec, x, rows, pos, sig, w)["out"]
+    want = _brute_mmh3(spec, x, rows, pos, sig, w)
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-10)
+
+
 def test_mmh3_block_brute_force_tiny_compat_modes():
     # partial RoPE (k = 1: 3 of 4 pairs turn, dims 6, 7 stay) and a shared adaLN basis
     spec = W.small_spec(_tiny_mmh3_spec(7), rope="partial", rope_axes=(2, 2, 2), adaln_shared=1)

@@ -845,11 +845,14 @@ def test_qk_norm_unit_rms_in_block():
     assert np.all(np.abs(rq - 1.0) < 1e-3)
 
 
-def test_siglip_layer_matches_torch_composition():
+@pytest.mark.parametrize("shape", [(20, 32, 4, 8, 48, 21), (1, 16, 1, 16, 8, 22), (9, 48, 3, 16, 20, 23),
+                                   (33, 24, 2, 12, 64, 24)])
+def test_siglip_layer_matches_torch_composition(shape):
     import torch
     import torch.nn.functional as Fn
-    spec = W.BlockSpec("tiny_siglip", "siglip", "f32", n=20, D=32, H=4, hd=8, F=48, eps=1e-6)
-    wl = W.make_custom_workload(spec, 21)
+    n, D, H, hd, F, seed = shape
+    spec = W.BlockSpec("tiny_siglip", "siglip", "f32", n=n, D=D, H=H, hd=hd, F=F, eps=1e-6)
+    wl = W.make_custom_workload(spec, seed)
     w = {k: torch.from_numpy(v.astype(np.float64)) for k, v in wl.weights.items()}
     x = torch.from_numpy(wl.x.astype(np.float64))
     D, H, hd = spec.D, spec.H, spec.hd
@@ -875,11 +878,11 @@ def test_timestep_embedding_closed_forms():
     assert e[255] == pytest.approx(math.sin(0.7 * 10000.0 ** (-127.0 / 128.0)), rel=1e-13)
 
 
-def _tiny_zimage():
-    spec = W.BlockSpec("tiny_z", "zimage", "f32", n=10, D=16, H=2, hd=8, F=12,
-                       rope="interleaved", rope_axes=(2, 2, 4), rope_theta=256.0,
+def _tiny_zimage(n=10, H=2, hd=8, F=12, axes=(2, 2, 4), seed=22):
+    spec = W.BlockSpec("tiny_z", "zimage", "f32", n=n, D=H * hd, H=H, hd=hd, F=F,
+                       rope="interleaved", rope_axes=axes, rope_theta=256.0,
                        temb_freq=16, temb_hidden=24)
-    wl = W.make_custom_workload(spec, 22)
+    wl = W.make_custom_workload(spec, seed)
     w = {k: v.astype(np.float64) for k, v in wl.weights.items()}
     return spec, wl.x.astype(np.float64), wl.pos.astype(np.float64), w
 
@@ -895,13 +898,15 @@ def test_zimage_zero_gates_identity():
     np.testing.assert_array_equal(out, x)
 
 
-def test_zimage_block_matches_torch_composition():
+@pytest.mark.parametrize("shape", [(10, 2, 8, 12, (2, 2, 4), 22, 0.3), (1, 1, 16, 8, (4, 6, 6), 23, 0.9),
+                                   (17, 3, 8, 20, (2, 2, 4), 24, 0.05), (6, 2, 12, 16, (4, 4, 4), 25, 0.6)])
+def test_zimage_block_matches_torch_composition(shape):
     import torch
     import torch.nn.functional as Fn
-    spec, x, pos, w = _tiny_zimage()
+    spec, x, pos, w = _tiny_zimage(*shape[:6])
     D, H, hd, F = spec.D, spec.H, spec.hd, spec.F
     tw = {k: torch.from_numpy(v) for k, v in w.items()}
-    t = 0.3
+    t = shape[6]
     half = spec.temb_freq // 2
     f = torch.exp(-math.log(10000.0) * torch.arange(half, dtype=torch.float64) / half)
     arg = t * spec.t_scale * f

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -40,6 +41,26 @@ def test_header_functions_exported(dit):
     assert not missing, missing
     for n in names:
         assert hasattr(dit.lib, n)
+
+
+def test_binding_refuses_to_import_without_the_library(tmp_path):
+    """The binding has no CPU fallback: a copy of it next to no built library
+    raises ImportError on import instead of running anything."""
+    pkg = tmp_path / "pkg_without_lib"
+    pkg.mkdir()
+    (pkg / "__init__.py").write_text("")
+    src = os.path.join(ROOT, "packed_sequence_diffusion_amd", "dit.py")
+    (pkg / "dit.py").write_text(open(src).read())
+    code = ("import sys\n"
+            "try:\n"
+            "    import pkg_without_lib.dit\n"
+            "except ImportError as e:\n"
+            "    print('refused:', e); sys.exit(0)\n"
+            "sys.exit(3)\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=str(tmp_path), capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "not built" in r.stdout and "no CPU fallback" in r.stdout
 
 
 def test_abi_version(dit):

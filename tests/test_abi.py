@@ -460,3 +460,13 @@ def test_model_piece_refusals(dit):
     assert L.dit_patchify_video(9, 256, 4, 2, 8, 8, 256, None) == -3
     assert L.dit_patchify_image(dit.F32, 256, 4, 8, 5, 256, None) == -2
     assert L.dit_pack_audio(dit.F32, 256, -1, 3, 256, None) == -2
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_bench_refuses_more_than_one_gpu(n):
+    """bench.py measures one GPU: asked for several, it exits with status 2 and
+    says so before touching a device."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(n)],
+                       cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""

@@ -127,8 +127,12 @@ def mmh3_token_rows(segments, slot, tags: int = 3, text_tags=None) -> np.ndarray
 
 
 def mmh3_timestep(sigma: float) -> float:
-    """Slot timestep t = 1 - max(sigma, 1e-6) ([MMH3] ``MiniMaxH3::forward``)."""
-    return 1.0 - max(sigma, 1e-6)
+    """Slot timestep t = 1 - sigma of a block's slot sigma.  [MMH3]
+    ``MiniMaxH3::forward`` floors only the video sigma at 1e-6, before the
+    audio remap (``mmh3_slots`` does that); every slot timestep it hands to
+    ``Adaln::eval`` is used as it is, so a condition slot at t = 1 reads the
+    table's last row with weight 1."""
+    return 1.0 - sigma
 
 
 # ---------------------------------------------------------------------------

@@ -87,9 +87,37 @@ def test_token_rows_with_text_tags():
 
 
 def test_timestep_of_sigma():
+    # the page floors the video sigma inside its forward only; a slot sigma of
+    # 0 is the condition timestep t = 1 exactly
     assert O.mmh3_timestep(0.3) == pytest.approx(0.7, abs=1e-15)
-    assert O.mmh3_timestep(0.0) == 1.0 - 1e-6
-    assert O.mmh3_timestep(-5.0) == 1.0 - 1e-6
+    assert O.mmh3_timestep(0.0) == 1.0
+    # the evaluation's floor: sigma_v = 0 puts video at 1 - 1e-6 and audio at
+    # 1 - 1e-6 / (4 - 3e-6), later, so ascending order is [video, audio]
+    ts, _ = O.mmh3_slots(0.0, 12.0, 3.0, 0.999, 1.0, False, False)
+    assert ts == [1.0 - 1e-6, 1.0 - 1e-6 / (4.0 - 3e-6)]
+
+
+def test_slot_at_t_one_reads_the_last_table_row():
+    """A reference-audio slot (t = max(t_a, 1) = 1) evaluates the curve at the
+    table's last row with weight 1 ([MMH3] Adaln::eval keeps the last
+    interval whole): mods = basis @ table[G-1] + bias, exactly."""
+    rng = np.random.default_rng(7)
+    T, E, D, r, G = 3, 6, 4, 5, 9
+    basis = rng.normal(size=(2 * T * E * D, r))
+    bias = rng.normal(size=2 * T * E * D)
+    table = rng.normal(size=(G, r))
+    ts, slot = O.mmh3_slots(0.4, 12.0, 3.0, 0.999, 1.0, False, True)
+    assert ts[slot["ref_audio"]] == 1.0
+    sig = [0.4, 0.0]  # a video slot and a slot at t = 1 exactly
+    mods = O.adaln_mods(basis, bias, table, [O.mmh3_timestep(s) for s in sig], T, E, D)
+    half = T * E * D
+    want = basis[half:] @ table[G - 1] + bias[half:]
+    np.testing.assert_allclose(mods[T:].reshape(-1), want, rtol=1e-13, atol=1e-13)
+    # and not the coordinates one millionth of t earlier (the floor applied to
+    # every slot would move them by 1e-6 * (G - 1) of a table step)
+    p = (1.0 - 1e-6) * (G - 1)
+    c = table[G - 2] + (p - (G - 2)) * (table[G - 1] - table[G - 2])
+    assert np.max(np.abs(mods[T:].reshape(-1) - (basis[half:] @ c + bias[half:]))) > 1e-7
 
 
 def test_resolve_sigmas_plan():
@@ -464,7 +492,7 @@ def test_final_layer_matches_torch_composition():
     rows_per_slot = 2 * spec.D
     mods = []
     for s_, sig in enumerate([0.3, 0.85]):
-        t = 1.0 - max(sig, 1e-6)
+        t = 1.0 - sig
         p = min(max(t, 0.0), 1.0) * (spec.grid - 1)
         i0 = min(int(math.floor(p)), spec.grid - 2)
         c = tw["adaln_table"][i0] + (p - i0) * (tw["adaln_table"][i0 + 1] - tw["adaln_table"][i0])
@@ -588,7 +616,7 @@ def _brute_mmh3(spec, x, rows, pos, sigmas, w):
     G = spec.grid
     mods = {}
     for s, sg in enumerate(sigmas):
-        t = 1.0 - max(sg, 1e-6)
+        t = 1.0 - sg
         p = min(max(t, 0.0), 1.0) * (G - 1)
         i0 = min(int(math.floor(p)), G - 2)
         f = p - i0
@@ -1065,3 +1093,84 @@ def test_zimage_forward_step_cache_semantics():
 def test_rel_rms():
     assert O.rel_rms(np.array([1.0, 2.0]), np.array([1.0, 2.0])) == 0.0
     assert O.rel_rms(np.array([2.0, 0.0]), np.array([1.0, 0.0])) == 1.0
+
+
+def _tiny_mmh3_model(seed=60):
+    """A two-block, three-slot MMH3 model on a keyframe layout small enough
+    to compose by hand: text 3, one condition frame, audio 2 x 2, video 2
+    frames of a 4 x 4 latent (2 x 2 patch grid)."""
+    lay = W.build_layout(3, 2, 4, 4, 2, keyframes=[(0, 9)])
+    n, D, C, Ca = lay.seq_len, 16, 4, 8
+    bs = W.BlockSpec("fwd-tiny", "mmh3", "f32", n=n, D=D, H=2, hd=8, F=12, slots=3, rank=3,
+                     grid=9, rope="split_half", rope_axes=(2, 2, 4), rope_theta=100.0)
+    hv = W.BlockSpec("hv", "final", "f32", n=n, D=D, H=2, hd=8, F=4 * C, slots=3, tags=1, rank=3, grid=9)
+    ha = W.BlockSpec("ha", "final", "f32", n=n, D=D, H=2, hd=8, F=Ca, slots=3, tags=1, rank=3, grid=9)
+    rng = np.random.default_rng(seed)
+    wb = []
+    for i in range(2):
+        w = {k: v.astype(np.float64) for k, v in W.make_custom_workload(bs, seed + 10 + i).weights.items()}
+        for k in ("w_qkv", "w_out", "w_fc1", "w_fc2", "adaln_basis"):
+            w[k] = w[k] * 10.0  # strong branches, so every piece shows in the output
+        wb.append(w)
+    whv = {k: v.astype(np.float64) for k, v in W.make_custom_workload(hv, seed + 20).weights.items()}
+    wha = {k: v.astype(np.float64) for k, v in W.make_custom_workload(ha, seed + 21).weights.items()}
+    for w in (whv, wha):
+        w["adaln_basis"] = w["adaln_basis"] * 10.0
+    wv, bv = rng.standard_normal((D, 4 * C)), rng.standard_normal(D)
+    wa, ba = rng.standard_normal((D, Ca)), rng.standard_normal(D)
+    text = rng.standard_normal((3, D))
+    video = rng.standard_normal((C, 2, 4, 4))
+    audio = rng.standard_normal((Ca, 2, 2))
+    cond = [rng.standard_normal((C, 1, 4, 4))]
+    return lay, bs, hv, ha, wb, whv, wha, wv, bv, wa, ba, text, video, audio, cond
+
+
+def test_mmh3_forward_composes_the_pinned_pieces():
+    """[MMH3] MiniMaxH3::forward written out step by step from pinned pieces:
+    slot timesteps by hand (t_v = 1 - sigma_v, the 12 -> 3 audio remap
+    sigma / (4 - 3 sigma), condition frames at 0.999), token rows slot * 3 +
+    tag, video and condition frames through the video patch projection, audio
+    through the audio one, text as given, the blocks in order, each head at its
+    stream's slot, unpacked.  Wrong pairings (condition frames through the
+    audio projection, the two heads' slots exchanged, the condition frame at
+    the video slot) each change the result."""
+    (lay, bs, hv, ha, wb, whv, wha, wv, bv, wa, ba, text, video, audio, cond) = _tiny_mmh3_model()
+    sv = 0.63
+    got_v, got_a = O.mmh3_forward(bs, hv, ha, lay.segments, lay.pos, text, video, audio, cond, sv,
+                                  wb, whv, wha, wv, bv, wa, ba)
+    seg = {k: (a, b) for k, a, b in lay.segments}
+    assert set(seg) == {"text", "cond", "audio", "video"}
+
+    def compose(cond_proj=(wv, bv), head_slots=(0, 1), cond_slot=2):
+        ts = [1.0 - sv, 1.0 - sv / (4.0 - 3.0 * sv), 0.999]  # ascending: video, audio, cond
+        assert ts == sorted(ts)
+        sig = [1.0 - t for t in ts]
+        rows = np.empty(lay.seq_len, np.int64)
+        rows[slice(*seg["text"])] = 0 * 3 + 1
+        rows[slice(*seg["cond"])] = cond_slot * 3 + 0
+        rows[slice(*seg["audio"])] = 1 * 3 + 2
+        rows[slice(*seg["video"])] = 0 * 3 + 0
+        h = np.zeros((lay.seq_len, bs.D))
+        h[slice(*seg["text"])] = text
+        h[slice(*seg["video"])] = O.patchify_video(video) @ wv.T + bv
+        cw, cb = cond_proj  # the audio projection is narrower: its first columns only
+        h[slice(*seg["cond"])] = O.patchify_video(cond[0])[:, :cw.shape[1]] @ cw.T + cb
+        h[slice(*seg["audio"])] = O.pack_audio(audio) @ wa.T + ba
+        for w in wb:
+            h = O.mmh3_block(bs, h, rows, lay.pos, sig, w)["out"]
+        a, b = seg["video"]
+        rv = O.final_layer(hv, h[a:b], np.full(b - a, head_slots[0]), sig, whv)["out"]
+        a, b = seg["audio"]
+        ra = O.final_layer(ha, h[a:b], np.full(b - a, head_slots[1]), sig, wha)["out"]
+        return (O.unpatchify_video(rv, *video.shape), O.unpack_audio(ra, audio.shape[0], audio.shape[2]))
+
+    want_v, want_a = compose()
+    np.testing.assert_allclose(got_v, want_v, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(got_a, want_a, rtol=1e-11, atol=1e-11)
+    scale = float(np.sqrt(np.mean(want_v ** 2)))
+    for why, kw in {"condition frames through the audio projection": dict(cond_proj=(wa, ba)),
+                    "heads' slots exchanged": dict(head_slots=(1, 0)),
+                    "condition frame at the video slot": dict(cond_slot=0)}.items():
+        bad_v, bad_a = compose(**kw)
+        d = max(np.max(np.abs(bad_v - got_v)), np.max(np.abs(bad_a - got_a)))
+        assert d > 1e-3 * scale, why

@@ -26,6 +26,15 @@
  *     evaluation's segments, a Z-Image image plus caption, a layout) is at
  *     most 2^24; larger ones are refused with DIT_ESHAPE (size queries: 0).
  *   - There is no CPU fallback: every step runs in the library's HIP kernels.
+ *   - HIP graph capture: every launch goes to `stream`, nothing allocates and
+ *     padding is cleared by kernels (no memset nodes), so calls can be
+ *     captured.  Host arguments are frozen into the captured launches: the
+ *     sigmas (as slot coordinates), seq_starts, n and the launch plans.  A
+ *     replay of a captured dit_block_forward therefore uses the capture-time
+ *     timestep.  For a new timestep per replay, capture
+ *     dit_block_forward_mods (its modulation rows are read from device
+ *     memory) and refresh those rows with dit_adaln_eval, outside the graph,
+ *     before each replay.
  *   - Supported shapes: hd in {64, 128}, D = H*hd, D % 128 == 0,
  *     F % 128 == 0, D <= 4096, 1 <= slots <= 8, rank <= 64, grid >= 2;
  *     pointers 16-byte aligned; tensors contiguous row-major.
@@ -205,9 +214,12 @@ dit_status dit_workspace_layout(const dit_config* cfg, int32_t n, dit_ws_layout*
 
 /* Modulation rows ([MMH3] Adaln::eval; [ZIMG] TimestepEmbedder + adaLN).
  * sigmas (host, n_sigmas = S for MMH3, 1 for ZIMAGE):
- *   MMH3:   slot s's sigma; t_s = 1 - max(sigma_s, 1e-6), grid coordinate
- *           p = clamp(t_s, 0, 1)*(G-1) taken in fp64 on the host; row j of
- *           the basis is evaluated at its own slot's interpolated coordinates.
+ *   MMH3:   slot s's sigma; t_s = 1 - sigma_s as given (no floor: a slot
+ *           sigma of 0 is t = 1, which reads table row G-1 with weight 1),
+ *           grid coordinate p = clamp(t_s, 0, 1)*(G-1) taken in fp64 on the
+ *           host; row j of the basis is evaluated at its own slot's
+ *           interpolated coordinates.  The evaluation's 1e-6 floor of the
+ *           video sigma is dit_mmh3_slots'.
  *   ZIMAGE: sigmas[0] is the timestep t (multiplied by t_scale).
  * mods_out: device fp32 [R, E*D], element (r, e, d) at (r*E + e)*D + d.
  * temb_scratch: ZIMAGE only, device fp32 [temb_hidden + temb_freq] (else NULL). */
@@ -537,8 +549,8 @@ double dit_sigma_remap(double sigma, double from_shift, double to_shift);
  * reference audio (has_ref_audio) at t_ca = max(t_a, cond_aug_audio).  The
  * distinct values, sorted ascending, are the slots (so the order is part of
  * the contract).  Writes slot_sigmas[s] = 1 - t_s, the sigmas that the block
- * entry points take (they evaluate slot s at 1 - max(sigma, 1e-6): a slot at
- * t = 1 exactly is evaluated at 1 - 1e-6), and slot_of = {video, audio, cond,
+ * entry points take (they evaluate slot s at 1 - sigma: the reference-audio
+ * slot at t = 1 exactly reads the adaLN table's last row), and slot_of = {video, audio, cond,
  * ref audio} slot indices (-1 when absent).  A token's modulation row is then
  * slot * 3 + tag (video 0, text 1, audio 2; condition frames and reference
  * images take the video tag, reference audio the audio tag).  Host function;

@@ -244,10 +244,12 @@ dit_status check_sigmas(const dit_config* c, const double* sigmas, int n_sigmas)
   return DIT_OK;
 }
 
-// Modulation rows into `mods` (device).  MMH3: slot timestep t = 1 -
-// max(sigma, 1e-6) and grid coordinate p = clamp(t, 0, 1) * (G - 1), i0 =
-// min(floor(p), G - 2), f = p - i0, all in fp64 ([MMH3] MiniMaxH3::forward and
-// Adaln::eval).
+// Modulation rows into `mods` (device).  MMH3: slot timestep t = 1 - sigma
+// and grid coordinate p = clamp(t, 0, 1) * (G - 1), i0 = min(floor(p), G - 2),
+// f = p - i0, all in fp64 ([MMH3] Adaln::eval; a slot at t = 1 reads table row
+// G - 1 with weight 1).  The page floors only the video sigma, inside its
+// forward and before the audio remap; dit_mmh3_slots applies that floor, so
+// the slot sigmas are taken here as given.
 dit_status launch_mods(const dit_config* c, const void* prep, const double* sigmas, float* mods,
                        float* temb, hipStream_t s) {
   PrepLayout P = prep_layout(c);
@@ -255,7 +257,7 @@ dit_status launch_mods(const dit_config* c, const void* prep, const double* sigm
     dit::SlotCoords sc;
     memset(&sc, 0, sizeof(sc));
     for (int i = 0; i < c->slots; ++i) {
-      double t = 1.0 - std::max(sigmas[i], 1e-6);
+      double t = 1.0 - sigmas[i];
       double p = std::min(std::max(t, 0.0), 1.0) * (double)(c->grid - 1);
       int i0 = std::min((int)floor(p), c->grid - 2);
       sc.i0[i] = i0;
@@ -399,7 +401,7 @@ dit_status dit_profile_end(double* phase_ms, int32_t* calls) {
 }
 
 
-int32_t dit_abi_version(void) { return 4; }
+int32_t dit_abi_version(void) { return 5; }
 
 const char* dit_last_error(void) { return g_err; }
 

@@ -195,6 +195,11 @@ dit_status plan_model(const dit_mmh3_model* m, const dit_segment* segs, int32_t 
     return fail(DIT_EINVAL, "model needs a block config, blocks and a video head");
   DIT_TRY(check_config(m->block));
   if (m->block->variant != DIT_MMH3) return fail(DIT_EINVAL, "model blocks must be DIT_MMH3");
+  // token rows are slot * 3 + tag over the page's three modalities (video 0,
+  // text 1, audio 2); the modulation table's row stride is the block's tags
+  if (m->block->tags != 3)
+    return fail(DIT_EUNSUPPORTED, "the evaluation's blocks need tags = 3 (video, text, audio), got %d",
+                m->block->tags);
   if (m->audio_slope_rescale != 0 && m->audio_slope_rescale != 1)
     return fail(DIT_EINVAL, "audio_slope_rescale=%d (0 or 1)", m->audio_slope_rescale);
   DIT_TRY(check_config(m->head_video));

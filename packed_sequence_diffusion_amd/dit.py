@@ -302,6 +302,98 @@ def _ptr(t, strided: bool = False) -> Optional[int]:
     return t.data_ptr()
 
 
+_TORCH_DT = {}
+
+
+def _tdt(name: str):
+    """torch dtype by short name ("f32", "bf16", "i32", "u8")."""
+    import torch
+    if not _TORCH_DT:
+        _TORCH_DT.update(f32=torch.float32, bf16=torch.bfloat16, i32=torch.int32, u8=torch.uint8)
+    return _TORCH_DT[name]
+
+
+def _act(cfg: "DitConfig") -> str:
+    return "bf16" if cfg.dtype == BF16 else "f32"
+
+
+def _arg(t, name: str, dtype: str, shape: Optional[Sequence[int]] = None,
+         optional: bool = False, strided: bool = False, min_numel: int = 0) -> Optional[int]:
+    """Device address of ``t`` after checking what the C ABI cannot: a CUDA
+    tensor of the given dtype and shape (entries None are free), row-major
+    (``strided``: unit stride inside rows), at least ``min_numel`` elements.
+    Raises ValueError instead of handing the library a buffer it would read
+    or write out of bounds."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if t.dtype != _tdt(dtype):
+        raise ValueError(f"{name} must be {_tdt(dtype)}, got {t.dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(g) != int(w)
+                                        for g, w in zip(t.shape, shape)):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected "
+                             f"{tuple('*' if w is None else int(w) for w in shape)}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {min_numel}")
+    return _ptr(t, strided)
+
+
+def weight_shapes(cfg: "DitConfig") -> Dict[str, tuple]:
+    """{field: (dtype, shape)} of the raw weights a configuration reads
+    (include/dit.h, dit_weights); GEMM weights in the config's dtype, the rest
+    fp32."""
+    D, H, hd, F, S, T, r, G = cfg.D, cfg.H, cfg.hd, cfg.F, cfg.slots, cfg.tags, cfg.rank, cfg.grid
+    a, f = _act(cfg), "f32"
+    v = cfg.variant
+    out: Dict[str, tuple] = {}
+    if v == FINAL:
+        rows = (1 if cfg.adaln_shared else S) * T * 2 * D
+        out.update(norm1=(f, (D,)), w_fc1=(a, (F, D)), b_fc1=(f, (F,)),
+                   adaln_basis=(f, (rows, r)), adaln_bias=(f, (rows,)), adaln_table=(f, (G, r)))
+        return out
+    tf, th = cfg.temb_freq, cfg.temb_hidden
+    temb = dict(temb_w1=(f, (th, tf)), temb_b1=(f, (th,)), temb_w2=(f, (tf, th)), temb_b2=(f, (tf,)))
+    if v == ZFINAL:
+        out.update(w_fc1=(a, (F, D)), b_fc1=(f, (F,)), ada_w=(f, (D, tf)), ada_b=(f, (D,)), **temb)
+        return out
+    swiglu = v != SIGLIP
+    out.update(norm1=(f, (D,)), norm2=(f, (D,)), w_qkv=(a, (3 * D, D)), w_out=(a, (D, D)),
+               w_fc1=(a, (2 * F if swiglu else F, D)), w_fc2=(a, (D, F)))
+    if v != SIGLIP:
+        out.update(q_norm=(f, (hd,)), k_norm=(f, (hd,)))
+    if cfg.rope == ROPE_PARTIAL:
+        out["rope_freq"] = (f, (cfg.rope_axes[0] // 2,))
+    if v == SIGLIP:
+        out.update(ln1_b=(f, (D,)), ln2_b=(f, (D,)), b_qkv=(f, (3 * D,)), b_out=(f, (D,)),
+                   b_fc1=(f, (F,)), b_fc2=(f, (D,)))
+    if v == MMH3:
+        rows = (1 if cfg.adaln_shared else S) * T * 6 * D
+        out.update(adaln_basis=(f, (rows, r)), adaln_bias=(f, (rows,)), adaln_table=(f, (G, r)))
+    if v in (ZIMAGE, ZCONTEXT):
+        out.update(post_attn_norm=(f, (D,)), post_ffn_norm=(f, (D,)))
+    if v == ZIMAGE:
+        out.update(ada_w=(f, (4 * D, tf)), ada_b=(f, (4 * D,)), **temb)
+    return out
+
+
+def mod_shape(cfg: "DitConfig") -> tuple:
+    """Shape of the modulation rows [R, E*D] (dit_adaln_eval's output)."""
+    if cfg.variant == MMH3:
+        return (cfg.slots * cfg.tags, 6 * cfg.D)
+    if cfg.variant == FINAL:
+        return (cfg.slots * cfg.tags, 2 * cfg.D)
+    if cfg.variant == ZIMAGE:
+        return (1, 4 * cfg.D)
+    if cfg.variant == ZFINAL:
+        return (1, cfg.D)
+    raise ValueError("the configuration has no modulation rows")
+
+
 def _stream(stream=None) -> int:
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -339,16 +431,29 @@ class Block:
         import torch
         validate(cfg)
         self.cfg = cfg
+        shapes = weight_shapes(cfg)
         w = DitWeights()
         for f in WEIGHT_FIELDS:
             t = weights.get(f)
-            if t is not None and not t.is_contiguous():
-                raise ValueError(f"weight {f} must be contiguous")
-            setattr(w, f, _ptr(t))
+            if f in shapes:  # read by this variant: dtype and shape checked
+                dt, shp = shapes[f]
+                setattr(w, f, _arg(t, f"weight {f}", dt, shp, optional=True))
+            else:  # not read by this variant
+                setattr(w, f, None)
         nbytes = lib.dit_prepared_size(ctypes.byref(cfg))
         self.prepared = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         _check(lib.dit_prepare_weights(ctypes.byref(cfg), ctypes.byref(w), self.prepared.data_ptr(),
                                        nbytes, _stream(stream)))
+        cur = torch.cuda.current_stream()
+        if stream is not None and stream != cur:
+            # preparation ran on another stream: order later use on the current
+            # stream after it, and keep the raw weights alive until it has run
+            cur.wait_stream(stream)
+            self.prepared.record_stream(stream)
+            for f in shapes:
+                t = weights.get(f)
+                if t is not None:
+                    t.record_stream(stream)
         self._ws = None
 
     def workspace(self, n: int):
@@ -367,18 +472,31 @@ class Block:
         if out is None:
             out = torch.empty_like(x)
         ws = self.workspace(n) if workspace is None else workspace
+        px, prow, ppos, pout, pws = self._io(x, rows, pos, out, ws)
         sg, ns = _dbl(sigmas)
         if seq_starts is None:
-            _check(lib.dit_block_forward(ctypes.byref(self.cfg), self.prepared.data_ptr(), _ptr(x),
-                                         n, _ptr(rows), _ptr(pos), sg, ns, _ptr(out),
-                                         ws.data_ptr(), ws.numel(), _stream(stream)))
+            _check(lib.dit_block_forward(ctypes.byref(self.cfg), self.prepared.data_ptr(), px,
+                                         n, prow, ppos, sg, ns, pout,
+                                         pws, ws.numel(), _stream(stream)))
         else:
             st, nseq = _starts(seq_starts)
             _check(lib.dit_block_forward_packed(ctypes.byref(self.cfg), self.prepared.data_ptr(),
-                                                _ptr(x), n, _ptr(rows), _ptr(pos), sg, ns, st,
-                                                nseq, _ptr(out), ws.data_ptr(), ws.numel(),
+                                                px, n, prow, ppos, sg, ns, st,
+                                                nseq, pout, pws, ws.numel(),
                                                 _stream(stream)))
         return out
+
+    def _io(self, x, rows, pos, out, ws):
+        """Checked addresses of a block call's x [n, D], rows int32 [n], pos
+        fp32 [n, 3], out [n, D] (fp32) and workspace (uint8)."""
+        D = self.cfg.D
+        n = int(x.shape[0]) if hasattr(x, "shape") and len(x.shape) else -1
+        px = _arg(x, "x", "f32", (None, D))
+        prow = _arg(rows, "rows", "i32", (n,), optional=True)
+        ppos = _arg(pos, "pos", "f32", (n, 3), optional=True)
+        pout = _arg(out, "out", "f32", (n, D))
+        pws = _arg(ws, "workspace", "u8", (None,))
+        return px, prow, ppos, pout, pws
 
     def forward_mods(self, x, rows, pos, mods, out=None, workspace=None, stream=None,
                      seq_starts: Optional[Sequence[int]] = None):
@@ -389,40 +507,58 @@ class Block:
         if out is None:
             out = torch.empty_like(x)
         ws = self.workspace(n) if workspace is None else workspace
+        px, prow, ppos, pout, pws = self._io(x, rows, pos, out, ws)
+        pm = _arg(mods, "mods", "f32", mod_shape(self.cfg))
         if seq_starts is None:
             st, nseq = None, 0
         else:
             st, nseq = _starts(seq_starts)
-        _check(lib.dit_block_forward_mods(ctypes.byref(self.cfg), self.prepared.data_ptr(), _ptr(x),
-                                          n, _ptr(rows), _ptr(pos), _ptr(mods), st, nseq, _ptr(out),
-                                          ws.data_ptr(), ws.numel(), _stream(stream)))
+        _check(lib.dit_block_forward_mods(ctypes.byref(self.cfg), self.prepared.data_ptr(), px,
+                                          n, prow, ppos, pm, st, nseq, pout,
+                                          pws, ws.numel(), _stream(stream)))
         return out
 
     def adaln_modulate(self, x, rows, sigmas: Sequence[float], half: int, xn_out, mods_out=None,
                        temb_scratch=None, stream=None):
         n = int(x.shape[0])
+        c = self.cfg
+        px = _arg(x, "x", "f32", (n, c.D))
+        prow = _arg(rows, "rows", "i32", (n,), optional=True)
+        pxn = _arg(xn_out, "xn_out", _act(c), (n, c.D))
+        pm = _arg(mods_out, "mods_out", "f32", mod_shape(c), optional=True) \
+            if c.variant in (MMH3, ZIMAGE, FINAL, ZFINAL) else None
+        pt = _arg(temb_scratch, "temb_scratch", "f32", None, optional=True,
+                  min_numel=c.temb_hidden + c.temb_freq)
         sg, ns = _dbl(sigmas)
-        _check(lib.dit_adaln_modulate(ctypes.byref(self.cfg), self.prepared.data_ptr(), _ptr(x), n,
-                                      _ptr(rows), sg, ns, half, _ptr(xn_out), _ptr(mods_out),
-                                      _ptr(temb_scratch), _stream(stream)))
+        _check(lib.dit_adaln_modulate(ctypes.byref(c), self.prepared.data_ptr(), px, n,
+                                      prow, sg, ns, half, pxn, pm, pt, _stream(stream)))
         return xn_out
 
     def adaln_eval(self, sigmas: Sequence[float], mods_out, temb_scratch=None, stream=None):
+        c = self.cfg
+        pm = _arg(mods_out, "mods_out", "f32", mod_shape(c))
+        pt = _arg(temb_scratch, "temb_scratch", "f32", None, optional=True,
+                  min_numel=c.temb_hidden + c.temb_freq)
         sg, ns = _dbl(sigmas)
-        _check(lib.dit_adaln_eval(ctypes.byref(self.cfg), self.prepared.data_ptr(), sg, ns,
-                                  _ptr(mods_out), _ptr(temb_scratch), _stream(stream)))
+        _check(lib.dit_adaln_eval(ctypes.byref(c), self.prepared.data_ptr(), sg, ns,
+                                  pm, pt, _stream(stream)))
         return mods_out
 
 
 def attention(cfg: DitConfig, q, k, vt, n: int, ldn: int, score_scale: float, o, stream=None,
               seq_starts: Optional[Sequence[int]] = None):
+    a = _act(cfg)
+    pq = _arg(q, "q", a, (cfg.H, ldn, cfg.hd))
+    pk = _arg(k, "k", a, (cfg.H, ldn, cfg.hd))
+    pv = _arg(vt, "vt", a, (cfg.H, cfg.hd, ldn))
+    po = _arg(o, "o", a, (n, cfg.D))
     if seq_starts is None:
-        _check(lib.dit_attention(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(vt), n, ldn,
-                                 score_scale, _ptr(o), _stream(stream)))
+        _check(lib.dit_attention(ctypes.byref(cfg), pq, pk, pv, n, ldn,
+                                 score_scale, po, _stream(stream)))
     else:
         st, nseq = _starts(seq_starts)
-        _check(lib.dit_attention_packed(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(vt), n, ldn, st,
-                                        nseq, score_scale, _ptr(o), _stream(stream)))
+        _check(lib.dit_attention_packed(ctypes.byref(cfg), pq, pk, pv, n, ldn, st,
+                                        nseq, score_scale, po, _stream(stream)))
     return o
 
 
@@ -450,9 +586,13 @@ def final_forward(blk: "Block", h, rows, sigmas: Sequence[float], out=None, work
     if out is None:
         out = torch.empty((n, blk.cfg.F), dtype=torch.float32, device=h.device)
     ws = blk.workspace(n) if workspace is None else workspace
+    ph = _arg(h, "h", "f32", (n, blk.cfg.D))
+    prow = _arg(rows, "rows", "i32", (n,), optional=True)
+    pout = _arg(out, "out", "f32", (n, blk.cfg.F))
+    pws = _arg(ws, "workspace", "u8", (None,))
     sg, ns = _dbl(sigmas)
-    _check(lib.dit_final_forward(ctypes.byref(blk.cfg), blk.prepared.data_ptr(), _ptr(h), n,
-                                 _ptr(rows), sg, ns, _ptr(out), ws.data_ptr(), ws.numel(),
+    _check(lib.dit_final_forward(ctypes.byref(blk.cfg), blk.prepared.data_ptr(), ph, n,
+                                 prow, sg, ns, pout, pws, ws.numel(),
                                  _stream(stream)))
     return out
 
@@ -464,10 +604,15 @@ def linear(a, w, bias=None, alpha: float = 1.0, out=None, stream=None):
     m, k = int(a.shape[0]), int(a.shape[1])
     nout = int(w.shape[0])
     dtype = BF16 if a.dtype == torch.bfloat16 else F32
+    dn = "bf16" if dtype == BF16 else "f32"
     if out is None:
         out = torch.empty((m, nout), dtype=torch.float32, device=a.device)
-    _check(lib.dit_linear(dtype, _ptr(a, strided=True), int(a.stride(0)), m, k, _ptr(w), nout, _ptr(bias),
-                          alpha, _ptr(out), _stream(stream)))
+    pa = _arg(a, "a", dn, (m, k), strided=True)
+    pw = _arg(w, "w", dn, (nout, k))
+    pb = _arg(bias, "bias", "f32", (nout,), optional=True)
+    po = _arg(out, "out", "f32", (m, nout))
+    _check(lib.dit_linear(dtype, pa, int(a.stride(0)), m, k, pw, nout, pb,
+                          alpha, po, _stream(stream)))
     return out
 
 
@@ -479,12 +624,13 @@ def stack_forward(blocks: Sequence["Block"], x, rows, pos, sigmas: Sequence[floa
     if out is None:
         out = torch.empty_like(x)
     ws = blocks[0].workspace(n) if workspace is None else workspace
+    px, prow, ppos, pout, pws = blocks[0]._io(x, rows, pos, out, ws)
     preps = (c_void_p * len(blocks))(*[b.prepared.data_ptr() for b in blocks])
     sg, ns = _dbl(sigmas)
     st, nseq = (None, 0) if seq_starts is None else _starts(seq_starts)
-    _check(lib.dit_stack_forward(ctypes.byref(blocks[0].cfg), preps, len(blocks), _ptr(x), n,
-                                 _ptr(rows), _ptr(pos), sg, ns, st, nseq, _ptr(out),
-                                 ws.data_ptr(), ws.numel(), _stream(stream)))
+    _check(lib.dit_stack_forward(ctypes.byref(blocks[0].cfg), preps, len(blocks), px, n,
+                                 prow, ppos, sg, ns, st, nseq, pout,
+                                 pws, ws.numel(), _stream(stream)))
     return out
 
 

@@ -64,7 +64,7 @@ def test_binding_refuses_to_import_without_the_library(tmp_path):
 
 
 def test_abi_version(dit):
-    assert dit.lib.dit_abi_version() == 4
+    assert dit.lib.dit_abi_version() == 5
 
 
 def test_sigma_remap_printed_points(dit):
@@ -393,6 +393,15 @@ def test_mmh3_evaluation_refusals(dit):
     m.audio_slope_rescale = 2
     assert dit.lib.dit_mmh3_workspace_size(ctypes.byref(m), _segs(dit, good), 3) == 0
     m.audio_slope_rescale = 0
+    # token rows are slot * 3 + tag: a block with another tag count is refused
+    # (its modulation rows would be indexed with the wrong stride)
+    blk = keep[0]
+    for tags in (1, 2, 4):
+        blk.tags = tags
+        assert dit.lib.dit_mmh3_workspace_size(ctypes.byref(m), _segs(dit, good), 3) == 0, tags
+        assert "tags = 3" in dit.last_error()
+    blk.tags = 3
+    assert dit.lib.dit_mmh3_workspace_size(ctypes.byref(m), _segs(dit, good), 3) > 0
     m.latent_c = 15  # 4 * latent_c not a multiple of the bf16 GEMM depth
     assert dit.lib.dit_mmh3_workspace_size(ctypes.byref(m), _segs(dit, good), 3) == 0
     assert dit.lib.dit_mmh3_workspace_size(None, _segs(dit, good), 3) == 0

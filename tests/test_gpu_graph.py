@@ -63,3 +63,46 @@ def test_graph_replay_matches_eager(dit, name, seq_starts):
         blk.forward(dev.x, dev.rows, dev.pos, sig, out=x2, workspace=ws, seq_starts=seq_starts)
         torch.cuda.synchronize()
     assert np.isfinite(ref.cpu().numpy()).all()
+
+
+def test_graph_with_mods_refreshed_between_replays(dit):
+    """Slot sigmas are host values frozen into a captured dit_block_forward; the
+    graph path for a new timestep per replay is dit_block_forward_mods reading
+    modulation rows from device memory, refreshed by dit_adaln_eval before each
+    replay.  Every replay equals the eager block at that replay's sigmas, bit
+    for bit."""
+    import torch
+    from synth.device import to_device
+    spec = W.BlockSpec("graph-mods", "mmh3", "bf16", n=333, D=256, H=2, hd=128, F=384, slots=2,
+                       rope="split_half", rope_axes=(32, 48, 48))
+    wl = W.make_custom_workload(spec, 4343)
+    dev = to_device(wl)
+    blk = dit.Block(dit.make_config(spec), dev.weights)
+    n = spec.n
+    ws = blk.workspace(n)
+    mods = torch.empty(dit.mod_shape(blk.cfg), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(dev.x)
+    blk.adaln_eval([0.5, 0.2], mods)
+    blk.forward_mods(dev.x, dev.rows, dev.pos, mods, out=out, workspace=ws)  # warm-up
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            blk.forward_mods(dev.x, dev.rows, dev.pos, mods, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ws_eager = torch.empty_like(ws)
+    for rep, sig in enumerate([[0.9, 0.6923076923], [0.3, 0.0967741935], [0.05, 0.0131578947],
+                               [0.7, 0.3684210526]]):
+        blk.adaln_eval(sig, mods)  # eager, outside the graph
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = blk.forward(dev.x, dev.rows, dev.pos, sig, workspace=ws_eager)
+        torch.cuda.synchronize()
+        same = torch.equal(out, ref)
+        log(f"[case] graph mods replay {rep} sigmas={sig}: equal={same}")
+        assert same

@@ -243,3 +243,65 @@ def test_mmh3_evaluation_graph_replay(dit):
         _run(model, lay, dev, 0.9)  # eager work on the same workspace between replays
         torch.cuda.synchronize()
     assert torch.isfinite(v_ref).all() and torch.isfinite(a_ref).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_reference_layout_stack(dit, dtype):
+    """A reference layout ([MMH3] Layout::ref2va: a reference image, a
+    reference clip with its soundtrack and a reference audio block before the
+    target's audio and video) through two blocks: four timestep slots (video,
+    audio, the condition slot at max(t_v, 0.999) and the reference-audio slot
+    at t = 1 exactly), token rows slot * 3 + tag as [MMH3] MiniMaxH3::forward
+    assigns them.  The library's slot planner and the oracle's are run
+    independently and must agree; the stack's output is checked per token
+    row, and the modulation rows of the t = 1 slot are checked directly
+    (they read the adaLN table's last row with weight 1)."""
+    import torch
+    from synth.device import to_device
+    from tests.gpu_common import row_rel
+    lay = W.build_layout(16, 3, 8, 8, 4, refs=[("image", 8, 8), ("video", 2, 8, 8, 3), ("audio", 4)])
+    n = lay.seq_len
+    sv = 0.6
+    lib_sig, lib_slot = dit.mmh3_slots(sv, has_cond=True, has_ref_audio=True)
+    ts, o_slot = O.mmh3_slots(sv, 12.0, 3.0, 0.999, 1.0, True, True)
+    assert len(lib_sig) == 4 and lib_slot == o_slot
+    assert ts[o_slot["ref_audio"]] == 1.0 and lib_sig[lib_slot["ref_audio"]] == 0.0
+    np.testing.assert_allclose(lib_sig, [1.0 - t for t in ts], rtol=0, atol=1e-15)
+    kind_slot_tag = {"text": (lib_slot["video"], W.TAG_TEXT), "video": (lib_slot["video"], W.TAG_VIDEO),
+                     "audio": (lib_slot["audio"], W.TAG_AUDIO), "ref_image": (lib_slot["cond"], W.TAG_VIDEO),
+                     "ref_audio": (lib_slot["ref_audio"], W.TAG_AUDIO)}
+    rows = W._rows_for(lay, kind_slot_tag, 3)
+    np.testing.assert_array_equal(rows, O.mmh3_token_rows(lay.segments, o_slot))
+    hd = 128 if dtype == "bf16" else 64
+    spec = W.BlockSpec(f"ref-{dtype}", "mmh3", dtype, n=n, D=256, H=256 // hd, hd=hd,
+                       F=384 if dtype == "bf16" else 256, slots=4, rope="split_half",
+                       rope_axes=(hd // 4, hd // 8 * 3, hd // 8 * 3))
+    pos = lay.pos.astype(np.float32)
+    wls = [W.make_custom_workload(spec, 7100 + i, pos=pos, rows=rows, sigmas=lib_sig) for i in range(2)]
+    devs = [to_device(wl) for wl in wls]
+    cfg = dit.make_config(spec)
+    blocks = [dit.Block(cfg, d.weights) for d in devs]
+    x, drows, dpos = devs[0].x, devs[0].rows, devs[0].pos
+    out = dit.stack_forward(blocks, x, drows, dpos, lib_sig)
+    mods = torch.empty(dit.mod_shape(cfg), dtype=torch.float32, device="cuda")
+    blocks[0].adaln_eval(lib_sig, mods)
+    torch.cuda.synchronize()
+    o_sig = [1.0 - t for t in ts]
+    ref = O.stack(spec, wls[0].x, rows, pos, o_sig, [wl.weights for wl in wls])
+    got = out.cpu().numpy().astype(np.float64)
+    x64 = wls[0].x.astype(np.float64)
+    u = 2.0 ** -24
+    nrm = lambda a: np.sqrt(np.sum(a * a, axis=-1))  # noqa: E731
+    e_out = row_rel(got, ref)
+    e_delta = row_rel(got - x64, ref - x64) - 2 * u * (nrm(ref) + nrm(x64)) / nrm(ref - x64)
+    w0 = {k: v.astype(np.float64) for k, v in wls[0].weights.items()}
+    tsv = [O.mmh3_timestep(s) for s in o_sig]
+    ref_mods = O.adaln_mods(w0["adaln_basis"], w0["adaln_bias"], w0["adaln_table"], tsv, 3, 6, spec.D)
+    e_mods = row_rel(mods.cpu().numpy(), ref_mods)
+    ra = lib_slot["ref_audio"]
+    log(f"[case] reference layout {dtype} n={n} slots={len(lib_sig)}: out max={e_out.max():.2e} "
+        f"out-x max={e_delta.max():.2e} mods max={e_mods.max():.2e} "
+        f"(t=1 slot rows {e_mods[3 * ra:3 * ra + 3].max():.2e})")
+    tol = TOL[dtype]
+    assert e_out.max() <= tol and e_delta.max() <= tol
+    assert e_mods.max() <= 1e-5  # modulation rows are fp32 in both configurations

@@ -226,6 +226,21 @@ dit_status dit_workspace_layout(const dit_config* cfg, int32_t n, dit_ws_layout*
 dit_status dit_adaln_eval(const dit_config* cfg, const void* prepared, const double* sigmas,
                           int32_t n_sigmas, float* mods_out, float* temb_scratch, void* stream);
 
+/* dit_adaln_eval without the scratch argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments and result as
+ * dit_adaln_eval; the Z-Image timestep MLP's scratch (temb_hidden + temb_freq
+ * floats) is a library-owned device array of DIT_NOALLOC_TEMB_MAX floats per
+ * GPU, held until the process ends.  A configuration needing more is refused
+ * with DIT_EUNSUPPORTED before anything is launched.  The array is shared by
+ * every call on one GPU: calls that overlap on one GPU (other streams or
+ * threads) race on it and must be ordered by the caller.  MMH3 and FINAL
+ * configurations use no scratch.  Allocates nothing. */
+#define DIT_NOALLOC_TEMB_MAX 16384
+dit_status dit_adaln_eval_noalloc(const dit_config* cfg, const void* prepared,
+                                  const double* sigmas, int32_t n_sigmas, float* mods_out,
+                                  void* stream);
+
 /* Modulation + segment gather + pre-norm + modulate of one half of the block:
  * mods_out = dit_adaln_eval(...), then for every token i with r = rows[i]:
  *   MMH3:   xn_i = RMSNorm(x_i; g, eps) * (1 + mods[r, scale]) + mods[r, shift]

@@ -52,6 +52,14 @@ struct PrepLayout {
 PrepLayout prep_layout(const dit_config* c);
 dit_ws_layout ws_layout(const dit_config* c, int n);
 
+// Variant predicates and the modulation-row launch shared by the entry points.
+bool has_mods(const dit_config* c);
+bool temb_variant(const dit_config* c);
+// Modulation rows into `mods` on stream s; `temb` is the timestep MLP's
+// scratch ([temb_hidden + temb_freq] floats; Z-Image variants only).
+dit_status launch_mods(const dit_config* c, const void* prep, const double* sigmas, float* mods,
+                       float* temb, hipStream_t s);
+
 // An output head (DIT_FINAL / DIT_ZFINAL) with its scale factor alpha.
 dit_status final_forward_impl(const dit_config* c, const void* prepared, const float* h, int32_t n,
                               const int32_t* rows, const double* sigmas, int32_t n_sigmas, float alpha,

@@ -401,7 +401,7 @@ dit_status dit_profile_end(double* phase_ms, int32_t* calls) {
 }
 
 
-int32_t dit_abi_version(void) { return 5; }
+int32_t dit_abi_version(void) { return 6; }
 
 const char* dit_last_error(void) { return g_err; }
 

@@ -127,6 +127,8 @@ def _load() -> ctypes.CDLL:
         "dit_workspace_layout": (c_int32, [P(DitConfig), c_int32, P(DitWsLayout)]),
         "dit_adaln_eval": (c_int32, [P(DitConfig), c_void_p, P(c_double), c_int32, c_void_p,
                                      c_void_p, c_void_p]),
+        "dit_adaln_eval_noalloc": (c_int32, [P(DitConfig), c_void_p, P(c_double), c_int32,
+                                             c_void_p, c_void_p]),
         "dit_adaln_modulate": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_int32, c_void_p,
                                          P(c_double), c_int32, c_int32, c_void_p, c_void_p,
                                          c_void_p, c_void_p]),
@@ -533,6 +535,15 @@ class Block:
         _check(lib.dit_adaln_modulate(ctypes.byref(c), self.prepared.data_ptr(), px, n,
                                       prow, sg, ns, half, pxn, pm, pt, _stream(stream)))
         return xn_out
+
+    def adaln_eval_noalloc(self, sigmas: Sequence[float], mods_out, stream=None):
+        """dit_adaln_eval_noalloc: the modulation rows with the timestep MLP's
+        scratch in the library's own device array (no scratch argument)."""
+        pm = _arg(mods_out, "mods_out", "f32", mod_shape(self.cfg))
+        sg, ns = _dbl(sigmas)
+        _check(lib.dit_adaln_eval_noalloc(ctypes.byref(self.cfg), self.prepared.data_ptr(), sg, ns,
+                                          pm, _stream(stream)))
+        return mods_out
 
     def adaln_eval(self, sigmas: Sequence[float], mods_out, temb_scratch=None, stream=None):
         c = self.cfg

@@ -64,7 +64,7 @@ def test_binding_refuses_to_import_without_the_library(tmp_path):
 
 
 def test_abi_version(dit):
-    assert dit.lib.dit_abi_version() == 5
+    assert dit.lib.dit_abi_version() == 6
 
 
 def test_sigma_remap_printed_points(dit):
@@ -479,3 +479,19 @@ def test_bench_refuses_more_than_one_gpu(n):
                        cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr and r.stdout == ""
+
+
+def test_adaln_eval_noalloc_refusals(dit):
+    """The no-allocation adaLN entry point refuses a timestep MLP larger than
+    its scratch array, and the usual bad arguments, before any launch."""
+    z = W.spec_by_name("zimage")
+    ok = dit.make_config(W.small_spec(z, D=256, H=2, F=384, temb_hidden=64, temb_freq=32))
+    huge = dit.make_config(W.small_spec(z, D=256, H=2, F=384, temb_hidden=16384, temb_freq=32))
+    sig = (ctypes.c_double * 1)(0.5)
+    L = dit.lib
+    assert L.dit_adaln_eval_noalloc(ctypes.byref(huge), 256, sig, 1, 256, None) == -6
+    assert "scratch" in dit.last_error()
+    assert L.dit_adaln_eval_noalloc(ctypes.byref(ok), None, sig, 1, 256, None) == -1
+    assert L.dit_adaln_eval_noalloc(ctypes.byref(ok), 256, sig, 2, 256, None) == -2
+    sl = dit.make_config(W.spec_by_name("siglip"))
+    assert L.dit_adaln_eval_noalloc(ctypes.byref(sl), 256, sig, 1, 256, None) == -6

@@ -27,6 +27,15 @@ DIT_DEV uint32_t pack2bf(float a, float b) {
   return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
 }
 
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// Streaming accesses (non-temporal: no allocation in the caches) for data a
+// kernel touches once, such as the rows of a bandwidth-bound row kernel.
+DIT_DEV float4 ld4_stream(const float* p) {
+  const f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)p);
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 template <typename T> struct Elt;
 template <> struct Elt<float> {
   static DIT_DEV float ld(const float* p) { return *p; }
@@ -34,6 +43,10 @@ template <> struct Elt<float> {
   // four consecutive elements
   static DIT_DEV float4 ld4(const float* p) { return *(const float4*)p; }
   static DIT_DEV void st4(float* p, float4 v) { *(float4*)p = v; }
+  static DIT_DEV void st4_stream(float* p, float4 v) {
+    const f32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, (f32x4_t*)p);
+  }
 };
 template <> struct Elt<bf16_t> {
   static DIT_DEV float ld(const bf16_t* p) { return bf2f(*p); }
@@ -45,6 +58,10 @@ template <> struct Elt<bf16_t> {
   }
   static DIT_DEV void st4(bf16_t* p, float4 v) {
     *(uint2*)p = make_uint2(pack2bf(v.x, v.y), pack2bf(v.z, v.w));
+  }
+  static DIT_DEV void st4_stream(bf16_t* p, float4 v) {
+    const u32x2_t w = {pack2bf(v.x, v.y), pack2bf(v.z, v.w)};
+    __builtin_nontemporal_store(w, (u32x2_t*)p);
   }
 };
 
@@ -88,14 +105,20 @@ DIT_DEV float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-DIT_DEV float silu_f(float v) { return v / (1.0f + __expf(-v)); }
+// The reciprocals below are v_rcp_f32 (about one ulp) rather than an IEEE
+// division (a ten-instruction sequence): these feed GEMM epilogues whose
+// results are rounded to bf16, or checked at 1e-5 on the fp32 path.  At the
+// extremes exp overflows to +inf and rcp(inf) = 0, the limits of the functions.
+DIT_DEV float rcp_f(float v) { return __builtin_amdgcn_rcpf(v); }
+
+DIT_DEV float silu_f(float v) { return v * rcp_f(1.0f + __expf(-v)); }
 
 // Tanh-form GELU; tanh(u) = 1 - 2 / (exp(2u) + 1).
 DIT_DEV float gelu_tanh_f(float v) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
   float u = k0 * (v + 0.044715f * v * v * v);
-  float t = 1.0f - 2.0f / (__expf(2.0f * u) + 1.0f);
+  float t = 1.0f - 2.0f * rcp_f(__expf(2.0f * u) + 1.0f);
   return 0.5f * v * (1.0f + t);
 }
 
-DIT_DEV float tanh_f(float u) { return 1.0f - 2.0f / (__expf(2.0f * u) + 1.0f); }
+DIT_DEV float tanh_f(float u) { return 1.0f - 2.0f * rcp_f(__expf(2.0f * u) + 1.0f); }

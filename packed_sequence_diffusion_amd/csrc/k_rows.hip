@@ -113,53 +113,74 @@ hipError_t temb_mods(double t_scaled, int freq, int hidden, int out_dim, const f
 // ([MMH3] norm_rows + modulate; [SIGLIP] layer_norm; [ZIMG] RMSNorm * (1 + scale)).
 //   RMS:   y = x / sqrt(mean(x^2) + eps) * g
 //   LAYER: y = (x - mean) / sqrt(var + eps) * g + beta   (two passes in registers)
-//   then y * (1 + mods[r, scale]) (+ mods[r, shift]).
-// The multiplier G = g * (1 + scale) and the additive term B = beta + shift are
-// fetched (from L2: they are shared by every row with the same segment row)
-// right after the row's own loads, so their latency overlaps the HBM reads;
-// y = (x - mean) * inv * G + B.  NCH = float4 chunks per lane (D <= 256 * NCH).
+//   then y * (1 + mods[r, scale]) (+ mods[r, shift]);  y = (x - mean) * inv * G + B
+// with the multiplier G = g (1 + scale) and the additive term B = beta (1 + scale)
+// + shift.  A block is four consecutive rows.  When they share their segment row
+// (all but a few blocks of a packing), the block builds G and B once in LDS
+// (2 D floats) before its rows are read: fetching the three D-vectors from L2
+// for every row costs the kernel about a fifth of its time at D = 2688.  A block
+// whose rows differ reads them per chunk from L2.  Rows are read and outputs
+// written once, with non-temporal accesses.  NCH = float4 chunks per lane
+// (D <= 256 * NCH).
 // ------------------------------------------------------------------------------
 constexpr int kMaxChunks = 16;  // D <= 4096: 1024 float4 per row, 16 per lane
+constexpr int kNormRows = 4;    // rows (waves) per block
 
 template <int NORM, int MOD, int NCH, typename OutT>
-__global__ __launch_bounds__(256) void k_norm_mod(const float* __restrict__ x, int n, int D,
-                                                  const float* __restrict__ g,
-                                                  const float* __restrict__ beta, float eps,
-                                                  const float* __restrict__ mods, int mstride,
-                                                  const int* __restrict__ rows, int shift_off,
-                                                  int scale_off, OutT* __restrict__ y) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= n) return;
+__global__ __launch_bounds__(64 * kNormRows) void k_norm_mod(
+    const float* __restrict__ x, int n, int D, const float* __restrict__ g,
+    const float* __restrict__ beta, float eps, const float* __restrict__ mods, int mstride,
+    const int* __restrict__ rows, int shift_off, int scale_off, OutT* __restrict__ y) {
+  extern __shared__ float4 gb_lds[];  // [0, nc): G, [nc, 2 nc): B
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int row0 = blockIdx.x * kNormRows;
+  const int row = row0 + (t >> 6);
   const int nc = D >> 2;
-  const float4* xr = (const float4*)(x + (size_t)row * D);
-  float4 v[NCH], G[NCH], B[NCH];
+  const bool per_row = MOD != MOD_NONE && rows != nullptr;
+  // G and B of modulation row mr, chunk i (0 <= i < nc)
+  auto gb = [&](int mr, int i, float4& G, float4& B) {
+    G = ((const float4*)g)[i];
+    B = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (NORM == NORM_LAYER) B = ((const float4*)beta)[i];
+    if (MOD != MOD_NONE) {
+      const float* mrow = mods + (size_t)mr * mstride;
+      const float4 sc = ((const float4*)(mrow + scale_off))[i];
+      G = make_float4(G.x * (1.0f + sc.x), G.y * (1.0f + sc.y), G.z * (1.0f + sc.z),
+                      G.w * (1.0f + sc.w));
+      if (NORM == NORM_LAYER)
+        B = make_float4(B.x * (1.0f + sc.x), B.y * (1.0f + sc.y), B.z * (1.0f + sc.z),
+                        B.w * (1.0f + sc.w));
+      if (MOD == MOD_SHIFT_SCALE) {
+        const float4 sh = ((const float4*)(mrow + shift_off))[i];
+        B = make_float4(B.x + sh.x, B.y + sh.y, B.z + sh.z, B.w + sh.w);
+      }
+    }
+  };
+  bool shared = true;
+  int mr0 = 0;
+  if (per_row) {
+    mr0 = rows[row0];
+    bool same = true;
+    if (t < kNormRows && row0 + t < n) same = rows[row0 + t] == mr0;
+    shared = __syncthreads_and(same);
+  }
+  if (shared) {
+    for (int i = t; i < nc; i += 64 * kNormRows) {
+      float4 G, B;
+      gb(mr0, i, G, B);
+      gb_lds[i] = G;
+      gb_lds[nc + i] = B;
+    }
+    __syncthreads();
+  }
+  if (row >= n) return;
+  const float* xr = x + (size_t)row * D;
+  float4 v[NCH];
   // loads clamp their chunk index (always in bounds); sums and stores skip the
   // chunks beyond the row
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) v[c] = xr[min(lane + 64 * c, nc - 1)];
-  const float* mrow = nullptr;
-  if (MOD != MOD_NONE) mrow = mods + (size_t)(rows ? rows[row] : 0) * mstride;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int i = min(lane + 64 * c, nc - 1);
-    G[c] = ((const float4*)g)[i];
-    B[c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (NORM == NORM_LAYER) B[c] = ((const float4*)beta)[i];
-    if (MOD != MOD_NONE) {
-      const float4 sc = ((const float4*)(mrow + scale_off))[i];
-      // (g x + beta)(1 + sc) + sh: G = g (1 + sc), B = beta (1 + sc) + sh
-      G[c] = make_float4(G[c].x * (1.0f + sc.x), G[c].y * (1.0f + sc.y), G[c].z * (1.0f + sc.z),
-                         G[c].w * (1.0f + sc.w));
-      if (NORM == NORM_LAYER)
-        B[c] = make_float4(B[c].x * (1.0f + sc.x), B[c].y * (1.0f + sc.y), B[c].z * (1.0f + sc.z),
-                           B[c].w * (1.0f + sc.w));
-      if (MOD == MOD_SHIFT_SCALE) {
-        const float4 sh = ((const float4*)(mrow + shift_off))[i];
-        B[c] = make_float4(B[c].x + sh.x, B[c].y + sh.y, B[c].z + sh.z, B[c].w + sh.w);
-      }
-    }
-  }
+  for (int c = 0; c < NCH; ++c) v[c] = ld4_stream(xr + 4 * min(lane + 64 * c, nc - 1));
   float s = 0.0f;
 #pragma unroll
   for (int c = 0; c < NCH; ++c)
@@ -182,17 +203,25 @@ __global__ __launch_bounds__(256) void k_norm_mod(const float* __restrict__ x, i
     q = wave_sum(q);
     inv = 1.0f / sqrtf(q / (float)D + eps);
   }
+  const int mr = per_row ? rows[row] : 0;
   OutT* yr = y + (size_t)row * D;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int i = lane + 64 * c;
     if (i < nc) {
+      float4 G, B;
+      if (shared) {
+        G = gb_lds[i];
+        B = gb_lds[nc + i];
+      } else {
+        gb(mr, i, G, B);
+      }
       float4 o;
-      o.x = (v[c].x - mean) * inv * G[c].x + B[c].x;
-      o.y = (v[c].y - mean) * inv * G[c].y + B[c].y;
-      o.z = (v[c].z - mean) * inv * G[c].z + B[c].z;
-      o.w = (v[c].w - mean) * inv * G[c].w + B[c].w;
-      Elt<OutT>::st4(yr + 4 * i, o);
+      o.x = (v[c].x - mean) * inv * G.x + B.x;
+      o.y = (v[c].y - mean) * inv * G.y + B.y;
+      o.z = (v[c].z - mean) * inv * G.z + B.z;
+      o.w = (v[c].w - mean) * inv * G.w + B.w;
+      Elt<OutT>::st4_stream(yr + 4 * i, o);
     }
   }
 }
@@ -201,13 +230,14 @@ template <int NORM, int MOD, int NCH>
 static void launch_norm_mod(bool out_bf16, const float* x, int n, int D, const float* g,
                             const float* beta, float eps, const float* mods, int mstride,
                             const int* rows, int so, int sc, void* y, hipStream_t s) {
-  dim3 grid((n + 3) / 4);
+  const dim3 grid((n + kNormRows - 1) / kNormRows);
+  const size_t lds = (size_t)2 * (D / 4) * sizeof(float4);  // G and B: 8 D bytes
   if (out_bf16)
-    k_norm_mod<NORM, MOD, NCH, bf16_t><<<grid, 256, 0, s>>>(x, n, D, g, beta, eps, mods, mstride,
-                                                             rows, so, sc, (bf16_t*)y);
+    k_norm_mod<NORM, MOD, NCH, bf16_t><<<grid, 64 * kNormRows, lds, s>>>(
+        x, n, D, g, beta, eps, mods, mstride, rows, so, sc, (bf16_t*)y);
   else
-    k_norm_mod<NORM, MOD, NCH, float><<<grid, 256, 0, s>>>(x, n, D, g, beta, eps, mods, mstride,
-                                                            rows, so, sc, (float*)y);
+    k_norm_mod<NORM, MOD, NCH, float><<<grid, 64 * kNormRows, lds, s>>>(
+        x, n, D, g, beta, eps, mods, mstride, rows, so, sc, (float*)y);
 }
 
 template <int NORM, int MOD>

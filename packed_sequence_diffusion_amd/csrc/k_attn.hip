@@ -27,6 +27,12 @@
 
 namespace dit {
 
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+// Word 3 of a buffer resource for raw (unstrided, untyped) loads on gfx9-class
+// parts: a 32-bit data format, so that the loads are range-checked in bytes.
+constexpr int kBufferFlags = 0x00020000;
+
 // Row permutation of a 32-key block: swap bits 2 and 3.
 DIT_DEV int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
@@ -114,19 +120,33 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
   for (int c = 0; c < NC; ++c)
     qf[c] = *(const bf16x8_t*)(Qh + (size_t)min(q0 + l32, ldn - 1) * HD + 16 * c + 8 * half);
 
+  // K and V tiles arrive through buffer loads: a thread's byte offsets inside a
+  // tile are fixed and the tile's position is the scalar offset, so stepping
+  // to the next tile costs no vector address arithmetic.
+  const __amdgpu_buffer_rsrc_t rsK =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, ldn * HD * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsV =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, ldn * HD * 2, kBufferFlags);
+  int koff[KPT], voff[VPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int c_ = tid + kAttnThreads * i;
+    koff[i] = ((c_ / KCH) * HD + (c_ % KCH) * 8) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int c_ = tid + kAttnThreads * i;
+    voff[i] = ((c_ / (KT / 8)) * ldn + (c_ % (KT / 8)) * 8) * 2;
+  }
   u32x4_t rk[KPT], rv[VPT];
 #define KOFF(row, ch) ((row) * KLD + ((ch) << 3))
 #define VOFF(row, ch) ((row) * VLD + ((ch) << 3))
 #define ATT_GLOAD(k0)                                                              \
   do {                                                                             \
-    _Pragma("unroll") for (int i = 0; i < KPT; ++i) {                              \
-      int c_ = tid + kAttnThreads * i, row_ = c_ / KCH, ch_ = c_ % KCH;                     \
-      rk[i] = *(const u32x4_t*)(Kh + (size_t)((k0) + row_) * HD + ch_ * 8);        \
-    }                                                                              \
-    _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                              \
-      int c_ = tid + kAttnThreads * i, row_ = c_ / (KT / 8), ch_ = c_ % (KT / 8);           \
-      rv[i] = *(const u32x4_t*)(Vh + (size_t)row_ * ldn + (k0) + ch_ * 8);         \
-    }                                                                              \
+    _Pragma("unroll") for (int i = 0; i < KPT; ++i)                                \
+      rk[i] = __builtin_amdgcn_raw_buffer_load_b128(rsK, koff[i], (k0) * HD * 2, 0); \
+    _Pragma("unroll") for (int i = 0; i < VPT; ++i)                                \
+      rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsV, voff[i], (k0) * 2, 0);    \
   } while (0)
 #define ATT_SSTORE(b)                                                              \
   do {                                                                             \
@@ -210,13 +230,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
         _Pragma("unroll") for (int v = 0; v < 16; ++v) cneg[v] = -cm;                      \
       }                                                                                    \
     }                                                                                      \
+    /* the row sum adds the bf16 weights the second product uses, two per  */           \
+    /* v_dot2 against (1, 1); each pair is converted once, as one word      */           \
+    /* (taking the words back out of the bf16x8 operand instead gave every  */           \
+    /* v_dot2 of a group the same word with this compiler)                  */           \
     bf16x8_t p_[2][2];                                                                     \
     _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                       \
-    _Pragma("unroll") for (int cc = 0; cc < 2; ++cc)                                       \
-    _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                        \
-      const float pv_ = __builtin_amdgcn_exp2f(s_[kb][8 * cc + e]);                        \
-      l4[e & 3] += pv_;                                                                    \
-      p_[kb][cc][e] = (__bf16)pv_;                                                         \
+    _Pragma("unroll") for (int cc = 0; cc < 2; ++cc) {                                     \
+      u32x4_t w_;                                                                          \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                      \
+        const bf16x2_t pr_ = {(__bf16)__builtin_amdgcn_exp2f(s_[kb][8 * cc + 2 * q]),      \
+                              (__bf16)__builtin_amdgcn_exp2f(s_[kb][8 * cc + 2 * q + 1])}; \
+        l4[q] = __builtin_amdgcn_fdot2_f32_bf16(pr_, kOnes2, l4[q], false);                \
+        w_[q] = __builtin_bit_cast(unsigned, pr_);                                         \
+      }                                                                                    \
+      p_[kb][cc] = __builtin_bit_cast(bf16x8_t, w_);                                       \
     }                                                                                      \
     _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                       \
     _Pragma("unroll") for (int cc = 0; cc < 2; ++cc)                                       \

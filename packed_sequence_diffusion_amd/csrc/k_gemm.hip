@@ -62,6 +62,50 @@ DIT_DEV void epi_gated_rows(const Epi& ep, const int (&row)[NR], int M, int cbas
   }
 }
 
+// Gated residual of a wave's (32 MI) x (32 NI) strip whose rows all read one
+// modulation row (the wave's vote in gemm_epilogue): one gate per column and lane,
+// and the residual rows in batches of 8 whose loads are issued one batch ahead of
+// the stores, so the strip waits for memory about twice instead of 2 MI times.
+template <int MI, int NI>
+DIT_DEV void epi_gated_uniform(const Epi& ep, f32x16_t (&acc)[MI][NI], int M, int rbase, int cbase,
+                               int lane, int mrow) {
+  const int cl = lane & 31, rh = (lane >> 5) * 4;
+  const float* __restrict__ resid = ep.resid;
+  float* __restrict__ out = (float*)ep.out;
+  float gv[NI], bv[NI];
+  const float* gr = ep.mods ? ep.mods + (size_t)mrow * ep.mstride + ep.goff + cbase + cl : nullptr;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    gv[j] = gr ? gr[32 * j] : 1.0f;
+    bv[j] = ep.bias ? ep.bias[cbase + 32 * j + cl] : 0.0f;
+  }
+  constexpr int NB = 2 * MI;  // batches of 8 rows: (mi, half of the 16 values)
+  auto row_of = [&](int b, int i) { return rbase + (b >> 1) * 32 + ((8 * (b & 1) + i) >> 2) * 8 + rh + (i & 3); };
+  float rv[2][8][NI];
+  auto load = [&](int b, float (&dst)[8][NI]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float* rr = resid + (size_t)min(row_of(b, i), M - 1) * ep.ldr + cbase + cl;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) dst[i][j] = rr[32 * j];
+    }
+  };
+  load(0, rv[0]);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b + 1 < NB) load(b + 1, rv[(b + 1) & 1]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = row_of(b, i);
+      if (row >= M) continue;
+      float* orow = out + (size_t)row * ep.ldc + cbase + cl;
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        orow[32 * j] = rv[b & 1][i][j] + gv[j] * (acc[b >> 1][j][8 * (b & 1) + i] + bv[j]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- bf16 MFMA ----
 // 256x256x64 workgroup tile, 512 threads = 8 waves as 4 (M) x 2 (N); each wave
 // owns a 64x128 strip (2x4 blocks of 32x32, 128 fp32 accumulators per lane).
@@ -230,6 +274,18 @@ DIT_DEV void gemm_epilogue(const Epi& ep, f32x16_t (&acc)[MI][NI], int M, int N,
     return;
   }
   if constexpr (EPI == EPI_GATED_RES) {
+    // the strip's 32 MI rows, one per lane: do they share one modulation row?
+    int mrow = 0;
+    bool uniform = true;
+    if (ep.mods && ep.rows) {
+      mrow = ep.rows[min(rbase, M - 1)];
+      const int own = ep.rows[min(rbase + (lane & (32 * MI - 1)), M - 1)];
+      uniform = __all(own == mrow);
+    }
+    if (uniform) {
+      epi_gated_uniform<MI, NI>(ep, acc, M, rbase, cbase, lane, mrow);
+      return;
+    }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll

@@ -361,14 +361,28 @@ hipError_t sandwich(const float* x, const float* y, int n, int D, const float* g
 // ------------------------------------------------------------------------------
 // RoPE table: angle (i, j) = pos[i, a] * theta^(-2m/d_a) for pair j = (axis a,
 // frequency m), axes concatenated t, h, w ([MMH3] rope_angles; per-axis
-// frequencies as [ZIMG] prepareRoPE3D).  Angles and their cos/sin are taken in
-// fp64 and stored as fp32 (cos, sin).
+// frequencies as [ZIMG] prepareRoPE3D).  A thread owns one pair j (its
+// frequency is computed once, in fp64) and walks the tokens.  The angle is
+// formed and reduced to [-pi, pi] in fp64, and its cosine and sine are taken in
+// fp32 from there: the table is stored in fp32, and the reduced angle's fp32
+// rounding (at most 2^-24 pi) keeps them within two fp32 ulps of the fp64 values.
 // ------------------------------------------------------------------------------
-__global__ void k_rope_table(const float* __restrict__ pos, int n, int P, int d0, int d1, int d2,
-                             double theta, float2* __restrict__ cs) {
-  int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n * P) return;
-  int i = idx / P, j = idx - i * P;
+constexpr int kRopeTokRows = 4;     // token rows of a block (blockDim = 64 x 4)
+constexpr int kRopeMaxBlocks = 512;
+
+DIT_DEV float2 cos_sin_reduced(double ang) {
+  constexpr double kTwoPi = 6.283185307179586476925287;
+  const double r = ang - rint(ang * (1.0 / kTwoPi)) * kTwoPi;
+  float sn, cn;
+  sincosf((float)r, &sn, &cn);
+  return make_float2(cn, sn);
+}
+
+__global__ __launch_bounds__(64 * kRopeTokRows) void k_rope_table(
+    const float* __restrict__ pos, int n, int P, int d0, int d1, int d2, double theta,
+    float2* __restrict__ cs) {
+  const int j = threadIdx.x & 63;
+  if (j >= P) return;
   int a, m, d;
   if (j < d0 / 2) {
     a = 0; m = j; d = d0;
@@ -377,46 +391,46 @@ __global__ void k_rope_table(const float* __restrict__ pos, int n, int P, int d0
   } else {
     a = 2; m = j - d0 / 2 - d1 / 2; d = d2;
   }
-  double omega = pow(theta, -2.0 * (double)m / (double)d);
-  double ang = (double)pos[(size_t)i * 3 + a] * omega;
-  double sn, cn;
-  sincos(ang, &sn, &cn);
-  cs[idx] = make_float2((float)cn, (float)sn);
+  const double omega = pow(theta, -2.0 * (double)m / (double)d);
+  for (int i = blockIdx.x * kRopeTokRows + (threadIdx.x >> 6); i < n; i += gridDim.x * kRopeTokRows)
+    cs[(size_t)i * P + j] = cos_sin_reduced((double)pos[(size_t)i * 3 + a] * omega);
+}
+
+static int rope_grid(int n) {
+  return min((n + kRopeTokRows - 1) / kRopeTokRows, kRopeMaxBlocks);
 }
 
 hipError_t rope_table(const float* pos, int n, int P, const int axes[3], double theta, float* cs,
                       hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  int total = n * P;
-  k_rope_table<<<(total + 255) / 256, 256, 0, s>>>(pos, n, P, axes[0], axes[1], axes[2], theta,
-                                                    (float2*)cs);
+  if (P > 64) return hipErrorInvalidValue;  // one lane per rotation pair
+  k_rope_table<<<rope_grid(n), 64 * kRopeTokRows, 0, s>>>(pos, n, P, axes[0], axes[1], axes[2],
+                                                          theta, (float2*)cs);
   return hipGetLastError();
 }
 
 // Partial RoPE table ([MMH3] rope_angles with the checkpoint's frequency
 // vector): pair j < 3k turns by pos[i, j / k] * freq[j % k]; pairs [3k, P) by
-// zero (cos 1, sin 0), the head dims that stay unrotated.  fp64 angles.
-__global__ void k_rope_table_shared(const float* __restrict__ pos, int n, int P, int k,
-                                    const float* __restrict__ freq, float2* __restrict__ cs) {
-  int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n * P) return;
-  int i = idx / P, j = idx - i * P;
-  if (j >= 3 * k) {
-    cs[idx] = make_float2(1.0f, 0.0f);
-    return;
-  }
-  const int a = j / k;
-  double ang = (double)pos[(size_t)i * 3 + a] * (double)freq[j - a * k];
-  double sn, cn;
-  sincos(ang, &sn, &cn);
-  cs[idx] = make_float2((float)cn, (float)sn);
+// zero (cos 1, sin 0), the head dims that stay unrotated.  fp64 angles, reduced
+// as above.
+__global__ __launch_bounds__(64 * kRopeTokRows) void k_rope_table_shared(
+    const float* __restrict__ pos, int n, int P, int k, const float* __restrict__ freq,
+    float2* __restrict__ cs) {
+  const int j = threadIdx.x & 63;
+  if (j >= P) return;
+  const int a = j < 3 * k ? j / k : 0;
+  const double f = j < 3 * k ? (double)freq[j - a * k] : 0.0;
+  for (int i = blockIdx.x * kRopeTokRows + (threadIdx.x >> 6); i < n; i += gridDim.x * kRopeTokRows)
+    cs[(size_t)i * P + j] = j < 3 * k ? cos_sin_reduced((double)pos[(size_t)i * 3 + a] * f)
+                                      : make_float2(1.0f, 0.0f);
 }
 
 hipError_t rope_table_shared(const float* pos, int n, int P, int k, const float* freq, float* cs,
                              hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  int total = n * P;
-  k_rope_table_shared<<<(total + 255) / 256, 256, 0, s>>>(pos, n, P, k, freq, (float2*)cs);
+  if (P > 64) return hipErrorInvalidValue;
+  k_rope_table_shared<<<rope_grid(n), 64 * kRopeTokRows, 0, s>>>(pos, n, P, k, freq,
+                                                                 (float2*)cs);
   return hipGetLastError();
 }
 

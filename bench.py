@@ -61,11 +61,11 @@ def cpu_baseline(spec, wl, seq_starts=None):
             "cpu": cpu_model()}
 
 
-def measured_traffic(kernel_sources):
-    """HBM bytes per attention dispatch from the committed counter summary, if
-    it was taken on the current kernel sources (sha256 match), else None."""
+def profile_record(name, kernel_sources):
+    """The JSON record of a committed profile summary, if it was taken on the
+    current kernel sources (sha256 match), else None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "attention_t2va_hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", name)
     try:
         txt = open(path).read()
         block = txt.split("```json", 1)[1].split("```", 1)[0]
@@ -76,7 +76,20 @@ def measured_traffic(kernel_sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() != rec["sources_sha256"].get(rel):
                 return None
-    return rec["traffic_bytes"]
+    return rec
+
+
+def measured_traffic(kernel_sources):
+    """HBM bytes per attention dispatch from the committed counter summary."""
+    rec = profile_record("attention_t2va_hbm_traffic.md", kernel_sources)
+    return rec["traffic_bytes"] if rec else None
+
+
+def measured_mfma(kernel_sources):
+    """MFMA-busy fraction and sustained clock of the attention kernel from the
+    committed counter summary."""
+    rec = profile_record("t2va_block_mfma_counters.md", kernel_sources)
+    return (rec["mfma_busy"], rec["clock_ghz"]) if rec else (None, None)
 
 
 ATTN_SOURCES = ("packed_sequence_diffusion_amd/csrc/k_attn.hip",
@@ -218,6 +231,8 @@ def main():
     norm_bytes = spec.n * spec.D * (4 + 2)
     norm_gbs = norm_bytes / (ph["norm1"] * 1e-3) / 1e9
 
+    mfma_busy, clock_ghz = (measured_mfma(ATTN_SOURCES)
+                            if spec.name == "t2va" and seq_starts is None else (None, None))
     res = {
         "metric": METRIC if spec.name == "t2va" else METRIC.replace("25.6k tokens",
                                                                      f"{spec.n} tokens"),
@@ -263,6 +278,10 @@ def main():
             "frac": attn_tf / PEAK_BF16_TFLOPS,
             "traffic": (measured_traffic(ATTN_SOURCES)
                         if spec.name == "t2va" and seq_starts is None else None),
+            # rocprofv3 counters of the same kernel: the matrix pipe's busy fraction and
+            # the clock the chip sustained (the peak above assumes 2.4 GHz)
+            "mfma_busy": mfma_busy,
+            "clock_ghz": clock_ghz,
         },
     }
     if not args.no_cpu_baseline:

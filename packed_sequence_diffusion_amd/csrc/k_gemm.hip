@@ -151,11 +151,40 @@ DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[MI][kQkvNI], int M, int 
 #pragma unroll
   for (int ni = 0; ni < kQkvNI; ++ni) gv[ni] = g ? g[(32 * ni + cl) & (HD - 1)] : 1.0f;
   const bool even = (cl & 1) == 0;
+  // The rows' (cos, sin) pairs are fetched in batches of RB rows, one batch
+  // ahead of the rows that use them, so that the strip waits for them about once
+  // instead of once per row.  NCS pairs per row and lane: split-half 2 (hd 128:
+  // pairs cl and cl + 32) or 1 (hd 64), interleaved one per 32-column block.
+  constexpr int NCS = ROPE == 0 ? 0 : ROPE == 1 ? (HD == 128 ? 2 : 1) : kQkvNI;
+  constexpr int NCA = NCS > 0 ? NCS : 1;
+  constexpr int RB = NCS <= 2 ? 8 : 4;
+  constexpr int BPM = 16 / RB, NB = MI * BPM;
+  auto row_of = [&](int b, int i) {
+    const int v = (b % BPM) * RB + i;
+    return rbase + (b / BPM) * 32 + (v >> 2) * 8 + rh + (v & 3);
+  };
+  auto cs_index = [&](int c) {
+    return ROPE == 1 ? (HD == 128 ? 32 * c + cl : cl) : ((32 * c + cl) & (HD - 1)) >> 1;
+  };
+  float2 csb[2][RB][NCA];
+  auto load_cs = [&](int b, float2 (&d)[RB][NCA]) __attribute__((always_inline)) {
+    if (NCS == 0) return;
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+    for (int i = 0; i < RB; ++i) {
+      const float2* csr = cs + (size_t)min(row_of(b, i), M - 1) * P;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = rbase + mi * 32 + (v >> 2) * 8 + rh + (v & 3);
+      for (int c = 0; c < NCS; ++c) d[i][c] = csr[cs_index(c)];
+    }
+  };
+  load_cs(0, csb[0]);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b + 1 < NB) load_cs(b + 1, csb[(b + 1) & 1]);
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int mi = b / BPM, v = (b % BPM) * RB + i;
+      const int row = row_of(b, i);
+      const float2* cr = csb[b & 1][i];
       float x[kQkvNI];
 #pragma unroll
       for (int ni = 0; ni < kQkvNI; ++ni) x[ni] = acc[mi][ni][v];
@@ -173,34 +202,31 @@ DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[MI][kQkvNI], int M, int 
 #pragma unroll
         for (int ni = 0; ni < kQkvNI; ++ni) x[ni] *= ((HD == 128 || ni < 2) ? i0 : i1) * gv[ni];
       }
-      if (ROPE != 0) {
-        const float2* csr = cs + (size_t)min(row, M - 1) * P;
-        if (ROPE == 1) {  // split-half: pair (d, d + P) is in this lane, blocks ni, ni + P/32
-          if (HD == 128) {
+      if (ROPE == 1) {  // split-half: pair (d, d + P) is in this lane, blocks ni, ni + P/32
+        if (HD == 128) {
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-              const float2 c = csr[32 * ni + cl];
-              const float a = x[ni], b = x[ni + 2];
-              x[ni] = a * c.x - b * c.y;
-              x[ni + 2] = a * c.y + b * c.x;
-            }
-          } else {
-            const float2 c = csr[cl];
-#pragma unroll
-            for (int ni = 0; ni < kQkvNI; ni += 2) {
-              const float a = x[ni], b = x[ni + 1];
-              x[ni] = a * c.x - b * c.y;
-              x[ni + 1] = a * c.y + b * c.x;
-            }
+          for (int ni = 0; ni < 2; ++ni) {
+            const float2 c = cr[ni];
+            const float a = x[ni], bb = x[ni + 2];
+            x[ni] = a * c.x - bb * c.y;
+            x[ni + 2] = a * c.y + bb * c.x;
           }
-        } else {  // interleaved: pair (2i, 2i + 1) is in lanes cl and cl ^ 1
+        } else {
+          const float2 c = cr[0];
 #pragma unroll
-          for (int ni = 0; ni < kQkvNI; ++ni) {
-            const float oth = DIT_DPP(x[ni], 0xB1);  // lane ^ 1
-            const float2 c = csr[((32 * ni + cl) & (HD - 1)) >> 1];
-            const float xe = even ? x[ni] : oth, xo = even ? oth : x[ni];
-            x[ni] = even ? (xe * c.x - xo * c.y) : (xe * c.y + xo * c.x);
+          for (int ni = 0; ni < kQkvNI; ni += 2) {
+            const float a = x[ni], bb = x[ni + 1];
+            x[ni] = a * c.x - bb * c.y;
+            x[ni + 1] = a * c.y + bb * c.x;
           }
+        }
+      } else if (ROPE == 2) {  // interleaved: pair (2i, 2i + 1) is in lanes cl and cl ^ 1
+#pragma unroll
+        for (int ni = 0; ni < kQkvNI; ++ni) {
+          const float oth = DIT_DPP(x[ni], 0xB1);  // lane ^ 1
+          const float2 c = cr[ni];
+          const float xe = even ? x[ni] : oth, xo = even ? oth : x[ni];
+          x[ni] = even ? (xe * c.x - xo * c.y) : (xe * c.y + xo * c.x);
         }
       }
       if (row < ldn) {
@@ -213,6 +239,7 @@ DIT_DEV void epi_qk_rows(const Epi& ep, f32x16_t (&acc)[MI][kQkvNI], int M, int 
         }
       }
     }
+  }
 }
 
 template <int MI>

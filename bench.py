@@ -97,6 +97,96 @@ ATTN_SOURCES = ("packed_sequence_diffusion_amd/csrc/k_attn.hip",
                 "packed_sequence_diffusion_amd/csrc/dit_kernels.h")
 
 
+def shard_bench(args, spec):
+    """One GPU's share of a P-way token shard: the token-local steps of the block
+    (adaLN, pre-norms, GEMMs with their epilogues) at n/P tokens, timed as the
+    block at that size minus its attention phase, and the attention of the
+    shard's n/P queries against all n keys (dit_attention_shard), timed alone.
+    The all-gather of K and V that would precede it is not run (one GPU)."""
+    import torch
+    from packed_sequence_diffusion_amd import dit
+    from synth import workloads as W
+    from synth.device import to_device
+
+    P = args.shard
+    if spec.n % P or (spec.n // P) % 128:
+        print(f"--shard {P}: n = {spec.n} must split into shards of a multiple of 128 tokens",
+              file=sys.stderr)
+        sys.exit(2)
+    m = spec.n // P
+    wl = W.make_workload(spec, n=m)  # the packing's first n/P tokens
+    dev = to_device(wl)
+    cfg = dit.make_config(spec)
+    blk = dit.Block(cfg, dev.weights)
+    sig = dit.resolve_sigmas(wl.slot_plan)
+    out = torch.empty_like(dev.x)
+    ws = blk.workspace(m)
+    for _ in range(args.warmup):
+        blk.forward(dev.x, dev.rows, dev.pos, sig, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    dit.profile_begin(args.steps)
+    for _ in range(args.steps):
+        blk.forward(dev.x, dev.rows, dev.pos, sig, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ph = dit.profile_end()
+    calls = ph.pop("calls")
+    ph = {k: v / calls for k, v in ph.items()}
+    local_ms = sum(v for k, v in ph.items() if k != "attention")
+
+    # the shard's attention: synthetic q (its m rows), k and v^T of all n tokens
+    n, H, hd = spec.n, spec.H, spec.hd
+    gen = torch.Generator(device="cuda").manual_seed(0xD17500)
+    q = (torch.randn((H, m, hd), generator=gen, device="cuda") * 0.1).to(torch.bfloat16)
+    k = (torch.randn((H, n, hd), generator=gen, device="cuda") * 0.1).to(torch.bfloat16)
+    vt = torch.randn((H, hd, n), generator=gen, device="cuda").to(torch.bfloat16)
+    o = torch.empty((m, H * hd), dtype=torch.bfloat16, device="cuda")
+    acfg = dit.make_config(spec)
+    wsa = torch.empty(dit.lib.dit_attention_shard_workspace_size(acfg), dtype=torch.uint8,
+                      device="cuda")
+    qlo = (P // 2) * m  # a middle shard; every shard does the same work
+    stream = torch.cuda.current_stream()
+
+    def attn():
+        dit.attention_shard(acfg, q, m, qlo, qlo + m, k, vt, n, n, hd ** -0.5, o, workspace=wsa)
+
+    for _ in range(args.warmup):
+        attn()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        attn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = ev0.elapsed_time(ev1) / args.steps
+    attn_tf = 4.0 * m * n * spec.D / (attn_ms * 1e-3) / 1e12
+    gemm_ms = ph["qkv_gemm"] + ph["out_gemm"] + ph["fc1_gemm"] + ph["fc2_gemm"]
+    per_gpu_ms = local_ms + attn_ms
+    kv_bytes = 2 * n * spec.D * 2 * (P - 1) / P  # K and V of the other shards, bf16
+    res = {
+        "metric": f"one GPU's share of a {P}-way token shard of the {spec.name} block",
+        "value": m / (per_gpu_ms * 1e-3),
+        "unit": "tokens/s per GPU (the K/V all-gather not included)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "shard_tokens": m,
+        "keys": n,
+        "per_gpu_ms": per_gpu_ms,
+        "token_local_ms": local_ms,
+        "shard_attention_ms": attn_ms,
+        "shard_attention_tflops": attn_tf,
+        "shard_attention_frac_mfma_peak": attn_tf / PEAK_BF16_TFLOPS,
+        "shard_gemm_tflops": spec.gemm_flops() / P / (gemm_ms * 1e-3) / 1e12,
+        "kv_allgather_bytes_per_gpu": kv_bytes,
+        "phases_ms": ph,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +202,10 @@ def main():
                          "(dit_stack_forward); value stays tokens/s per block")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays")
+    ap.add_argument("--shard", type=int, default=1, metavar="P",
+                    help="time one GPU's share of a P-way token shard of the workload instead "
+                         "(the block's token-local phases at n/P tokens and the attention of "
+                         "n/P queries against all n keys) and print that line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times (the "
                          "calibration kernel for the HBM byte counters) and exit")
@@ -135,6 +229,9 @@ def main():
     from synth.device import to_device
 
     spec = W.spec_by_name(args.workload)
+    if args.shard > 1:
+        shard_bench(args, spec)
+        return
     seq_starts = None
     if args.seqs > 1:
         seq_starts = [spec.n * i // args.seqs for i in range(args.seqs + 1)]

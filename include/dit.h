@@ -535,6 +535,27 @@ dit_status dit_attention_packed(const dit_config* cfg, const void* q, const void
                                 const int32_t* seq_starts, int32_t nseq, float score_scale,
                                 void* o, void* stream);
 
+/* One GPU's share of the attention of a token-sharded sequence: the queries of
+ * tokens [qlo, qhi) against all n keys of one sequence (the state after the
+ * keys and values of every shard have been gathered; [MMH3] attention, every
+ * token attends to every token, run for a contiguous range of query tokens).
+ *   q: device [H, ldq, hd], row r = token qlo + r (rows >= qhi - qlo ignored);
+ *   k: device [H, ldn, hd]; vt: device [H, hd, ldn] (V transposed), as in
+ *   dit_attention;
+ *   o: device [qhi - qlo, H*hd], row r = token qlo + r; all in the config's dtype;
+ *   workspace: device, 256-byte aligned, at least
+ *   dit_attention_shard_workspace_size(cfg) bytes (key-range partials of the
+ *   grid's split last round; 0 bytes, and NULL allowed, for fp32).
+ * 0 <= qlo <= qhi <= n <= ldn, ldn % 128 == 0, qhi - qlo <= ldq, ldq % 128 == 0.
+ * Row r of o equals row qlo + r of dit_attention's o over the whole sequence up
+ * to rounding order.  Errors: DIT_ESHAPE for the ranges, DIT_EALIGN,
+ * DIT_EWORKSPACE, DIT_EINVAL (NULL pointers, a non-finite score_scale). */
+size_t dit_attention_shard_workspace_size(const dit_config* cfg);
+dit_status dit_attention_shard(const dit_config* cfg, const void* q, int32_t ldq, int32_t qlo,
+                               int32_t qhi, const void* k, const void* vt, int32_t n,
+                               int32_t ldn, float score_scale, void* o, void* workspace,
+                               size_t ws_bytes, void* stream);
+
 /* Per-phase timing of dit_block_forward ([MMH3] per-phase profiler: one
  * stopwatch per phase, none overlapping).  dit_profile_begin(max_calls) arms
  * hipEvents (created on the host; no device memory) for the next max_calls

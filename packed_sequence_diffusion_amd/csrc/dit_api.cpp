@@ -401,7 +401,7 @@ dit_status dit_profile_end(double* phase_ms, int32_t* calls) {
 }
 
 
-int32_t dit_abi_version(void) { return 6; }
+int32_t dit_abi_version(void) { return 7; }
 
 const char* dit_last_error(void) { return g_err; }
 
@@ -633,8 +633,8 @@ static dit_status attention_impl(const dit_config* c, const void* q, const void*
   const float log2e = 1.4426950408889634f;
   dit::SeqTable tab;
   dit::make_seq_table(seq_starts, nseq, n, &tab);
-  HIP_TRY(dit::attention(c->dtype, c->hd, q, k, vt, n, ldn, c->H, score_scale * log2e, o, nullptr,
-                         tab, (hipStream_t)stream),
+  HIP_TRY(dit::attention(c->dtype, c->hd, q, ldn, k, vt, n, ldn, c->H, score_scale * log2e, o,
+                         nullptr, tab, (hipStream_t)stream),
           "attention");
   return DIT_OK;
 }
@@ -649,6 +649,40 @@ dit_status dit_attention_packed(const dit_config* c, const void* q, const void* 
                                 float score_scale, void* o, void* stream) {
   if (!seq_starts) return fail(DIT_EINVAL, "seq_starts is NULL");
   return attention_impl(c, q, k, vt, n, ldn, seq_starts, nseq, score_scale, o, stream);
+}
+
+size_t dit_attention_shard_workspace_size(const dit_config* c) {
+  if (check_config(c) != DIT_OK) return 0;
+  return c->dtype == DIT_BF16 ? dit::attention_part_bytes(c->hd) : 0;
+}
+
+dit_status dit_attention_shard(const dit_config* c, const void* q, int32_t ldq, int32_t qlo,
+                               int32_t qhi, const void* k, const void* vt, int32_t n, int32_t ldn,
+                               float score_scale, void* o, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  DIT_TRY(check_config(c));
+  if (bad_tokens(n) || ldn < n || ldn % 128 || bad_tokens(ldn))
+    return fail(DIT_ESHAPE, "need 0 <= n <= ldn <= %d, ldn %% 128 == 0 (n=%d ldn=%d)", kMaxTokens, n, ldn);
+  if (qlo < 0 || qhi < qlo || qhi > n)
+    return fail(DIT_ESHAPE, "need 0 <= qlo <= qhi <= n (qlo=%d qhi=%d n=%d)", qlo, qhi, n);
+  if (ldq < qhi - qlo || ldq % 128 || bad_tokens(ldq))
+    return fail(DIT_ESHAPE, "need qhi - qlo <= ldq <= %d, ldq %% 128 == 0 (ldq=%d)", kMaxTokens, ldq);
+  if (qhi == qlo) return DIT_OK;
+  if (!q || !k || !vt || !o) return fail(DIT_EINVAL, "q/k/vt/o is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
+    return fail(DIT_EALIGN, "q/k/vt/o not 16-byte aligned");
+  if (!isfinite(score_scale)) return fail(DIT_EINVAL, "score_scale not finite");
+  const size_t need = dit_attention_shard_workspace_size(c);
+  if (need && (!workspace || ws_bytes < need))
+    return fail(DIT_EWORKSPACE, "workspace %zu < %zu bytes", workspace ? ws_bytes : (size_t)0, need);
+  if (need && (uintptr_t)workspace % kAlign) return fail(DIT_EALIGN, "workspace must be 256-byte aligned");
+  const float log2e = 1.4426950408889634f;
+  dit::SeqTable tab;
+  dit::make_shard_table(n, qlo, qhi, &tab);
+  HIP_TRY(dit::attention(c->dtype, c->hd, q, ldq, k, vt, n, ldn, c->H, score_scale * log2e, o,
+                         need ? (float*)workspace : nullptr, tab, (hipStream_t)stream),
+          "attention shard");
+  return DIT_OK;
 }
 
 // mods_in: modulation rows supplied by the caller (skips their evaluation).
@@ -753,7 +787,7 @@ static dit_status block_forward_impl(const dit_config* c, const void* prepared, 
   {
     dit::SeqTable tab;
     dit::make_seq_table(seq_starts, nseq, n, &tab);
-    HIP_TRY(dit::attention(dt, hd, q, k, vt, n, ldn, H, 1.0f, o,
+    HIP_TRY(dit::attention(dt, hd, q, ldn, k, vt, n, ldn, H, 1.0f, o,
                            bf ? at<float>(workspace, L.part) : nullptr, tab, s),
             "attention");
   }

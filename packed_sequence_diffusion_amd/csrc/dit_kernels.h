@@ -102,16 +102,24 @@ inline size_t attention_part_bytes(int hd) {
 // blk[s] = query blocks of kAttnQueryRows before sample s (blk[nseq] = total).
 // Passed by value to the kernels.
 constexpr int kMaxSeqs = 64;
+// With one sample, the queries may be a contiguous range [qlo, qhi) of its
+// tokens (one GPU's share of a token-sharded sequence: the queries of that
+// range against every key); q and o then hold those queries only, row r being
+// token qbase + r.  Otherwise qlo = 0, qhi = n, qbase = 0.
 struct SeqTable {
   int nseq;
   int start[kMaxSeqs + 1];
   int blk[kMaxSeqs + 1];
+  int qlo, qhi, qbase;
 };
 // Builds the table from host offsets (nullptr: one sequence of n tokens).
 void make_seq_table(const int* seq_starts, int nseq, int n, SeqTable* t);
-hipError_t attention(int dtype, int hd, const void* q, const void* k, const void* vt, int n,
-                     int ldn, int H, float scale_log2, void* o, float* part, const SeqTable& seqs,
-                     hipStream_t s);
+// One sequence of n tokens whose queries are the tokens [qlo, qhi).
+void make_shard_table(int n, int qlo, int qhi, SeqTable* t);
+// q: [H, ldq, hd] (ldq = ldn without a query range), k: [H, ldn, hd], vt: [H, hd, ldn].
+hipError_t attention(int dtype, int hd, const void* q, int ldq, const void* k, const void* vt,
+                     int n, int ldn, int H, float scale_log2, void* o, float* part,
+                     const SeqTable& seqs, hipStream_t s);
 
 // ---- latent streams <-> token rows (k_streams.hip) --------------------------------------
 hipError_t patchify_video(int dtype, const float* x, int C, int T, int H, int W, void* rows,

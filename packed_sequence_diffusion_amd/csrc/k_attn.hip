@@ -41,10 +41,11 @@ constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kAttnRows = 32 * kAttnWaves;
 static_assert(kAttnRows == kAttnQueryRows, "partial-buffer rows");
 
-// Unit u -> head h, its sample's token range [ks, ke) and first query q0.  The
-// scan over the table is unrolled (constant indices: scalar kernel-argument
-// loads) and keeps the last sample whose first block is <= the unit's block.
-DIT_DEV void unit_of(const SeqTable& t, int u, int& h, int& ks, int& ke, int& q0) {
+// Unit u -> head h, its sample's key range [ks, ke), first query q0 and query
+// end qe (the sample's end, or the query range's with one sample).  The scan
+// over the table is unrolled (constant indices: scalar kernel-argument loads)
+// and keeps the last sample whose first block is <= the unit's block.
+DIT_DEV void unit_of(const SeqTable& t, int u, int& h, int& ks, int& ke, int& q0, int& qe) {
   const int per_head = t.blk[t.nseq];
   h = u / per_head;
   const int b = u - h * per_head;
@@ -59,7 +60,9 @@ DIT_DEV void unit_of(const SeqTable& t, int u, int& h, int& ks, int& ke, int& q0
       ke = t.start[i + 1];
     }
   }
-  q0 = ks + (b - b0) * kAttnRows;
+  const int qs = t.nseq == 1 ? t.qlo : ks;
+  qe = t.nseq == 1 ? t.qhi : ke;
+  q0 = qs + (b - b0) * kAttnRows;
 }
 
 // Work units are (head, block of 256 queries of one sample), head-major, the
@@ -74,7 +77,7 @@ template <int HD, bool UNIT>
 __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __restrict__ Q,
                                                       const bf16_t* __restrict__ Kp,
                                                       const bf16_t* __restrict__ Vt, int n,
-                                                      int ldn, int H, float scale_log2,
+                                                      int ldn, int ldq, int H, float scale_log2,
                                                       bf16_t* __restrict__ O, int whole,
                                                       int nsplit, float* __restrict__ part,
                                                       SeqTable seqs) {
@@ -105,20 +108,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
   const int u = split ? whole + (w - whole) / nsplit : w;
   const int j = split ? (w - whole) % nsplit : 0;
   const int ns = split ? nsplit : 1;
-  int h, ks, ke, q0;
-  unit_of(seqs, u, h, ks, ke, q0);
+  int h, ks, ke, q0, qe;
+  unit_of(seqs, u, h, ks, ke, q0, qe);
   q0 += wave * 32;
   // key tiles [t_lo, t_hi) of this workgroup, out of the sample's [T0, T1)
   const int T0 = ks / KT, T1 = (ke + KT - 1) / KT;
   const int t_lo = T0 + j * (T1 - T0) / ns, t_hi = T0 + (j + 1) * (T1 - T0) / ns;
-  const bf16_t* Qh = Q + (size_t)h * ldn * HD;
+  const bf16_t* Qh = Q + (size_t)h * ldq * HD;
   const bf16_t* Kh = Kp + (size_t)h * ldn * HD;
   const bf16_t* Vh = Vt + (size_t)h * HD * ldn;
 
   bf16x8_t qf[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
-    qf[c] = *(const bf16x8_t*)(Qh + (size_t)min(q0 + l32, ldn - 1) * HD + 16 * c + 8 * half);
+    qf[c] = *(const bf16x8_t*)(Qh + (size_t)min(q0 - seqs.qbase + l32, ldq - 1) * HD + 16 * c + 8 * half);
 
   // K and V tiles arrive through buffer loads: a thread's byte offsets inside a
   // tile are fixed and the tile's position is the scalar offset, so stepping
@@ -303,8 +306,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(const bf16_t* __r
     return;
   }
   const float inv = 1.0f / lt;
-  if (qi < ke) {
-    bf16_t* orow = O + (size_t)qi * (H * HD) + h * HD;
+  if (qi < qe) {
+    bf16_t* orow = O + (size_t)(qi - seqs.qbase) * (H * HD) + h * HD;
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -336,17 +339,19 @@ template <int HD>
 __global__ __launch_bounds__(128) void k_attn_f32(const float* __restrict__ Q,
                                                   const float* __restrict__ Kp,
                                                   const float* __restrict__ Vt, int n, int ldn,
-                                                  float scale_log2, SeqTable seqs,
+                                                  int ldq, float scale_log2, SeqTable seqs,
                                                   float* __restrict__ O) {
   __shared__ float sk[32][HD + 1];
   __shared__ float sv[32][HD + 1];
   const int h = blockIdx.y, H = gridDim.y;
-  const int qi = blockIdx.x * 128 + threadIdx.x;
+  const int b0 = seqs.qlo + blockIdx.x * 128;  // first query token of the block
+  const int qi = b0 + threadIdx.x;
   int qs, qe, blo, bhi, t0, t1;
   sample_of(seqs, min(qi, n - 1), qs, qe);
-  sample_of(seqs, blockIdx.x * 128, blo, t0);
-  sample_of(seqs, min(blockIdx.x * 128 + 127, n - 1), t1, bhi);
-  const float* qr = Q + ((size_t)h * ldn + qi) * HD;
+  sample_of(seqs, b0, blo, t0);
+  sample_of(seqs, min(b0 + 127, n - 1), t1, bhi);
+  // rows past the query range read rows of q the caller padded (ldq % 128 == 0)
+  const float* qr = Q + ((size_t)h * ldq + (qi - seqs.qbase)) * HD;
   float q[HD], acc[HD];
 #pragma unroll
   for (int d = 0; d < HD; ++d) {
@@ -387,9 +392,9 @@ __global__ __launch_bounds__(128) void k_attn_f32(const float* __restrict__ Q,
     }
     __syncthreads();
   }
-  if (qi < n) {
+  if (qi < seqs.qhi) {
     float inv = 1.0f / l;
-    float* orow = O + (size_t)qi * (H * HD) + h * HD;
+    float* orow = O + (size_t)(qi - seqs.qbase) * (H * HD) + h * HD;
 #pragma unroll
     for (int d = 0; d < HD; ++d) orow[d] = acc[d] * inv;
   }
@@ -406,10 +411,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);  // (split unit, query) row
   if (r >= nunits * kAttnRows) return;
   const int us = r / kAttnRows, ql = r % kAttnRows;
-  int h, ks, ke, q0;
-  unit_of(seqs, whole + us, h, ks, ke, q0);
+  int h, ks, ke, q0, qe;
+  unit_of(seqs, whole + us, h, ks, ke, q0, qe);
   const int qi = q0 + ql;
-  if (qi >= ke) return;
+  if (qi >= qe) return;
   const float* pml = part + (size_t)kAttnMaxSlots * kAttnRows * HD;
   float M = -INFINITY;
   for (int j = 0; j < nsplit; ++j)
@@ -427,7 +432,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
     for (int e = 0; e < PER; ++e) acc[e] += wgt * po[lane * PER + e];
   }
   const float inv = 1.0f / L;
-  bf16_t* orow = O + (size_t)qi * (H * HD) + h * HD + lane * PER;
+  bf16_t* orow = O + (size_t)(qi - seqs.qbase) * (H * HD) + h * HD + lane * PER;
 #pragma unroll
   for (int e = 0; e < PER; ++e) orow[e] = f2bf(acc[e] * inv);
 }
@@ -446,12 +451,9 @@ int device_cus() {
 }
 
 void make_seq_table(const int* seq_starts, int nseq, int n, SeqTable* t) {
+  t->qbase = 0;
   if (!seq_starts) {
-    t->nseq = 1;
-    t->start[0] = 0;
-    t->start[1] = n;
-    t->blk[0] = 0;
-    t->blk[1] = (n + kAttnRows - 1) / kAttnRows;
+    make_shard_table(n, 0, n, t);
     return;
   }
   t->nseq = nseq;
@@ -459,12 +461,25 @@ void make_seq_table(const int* seq_starts, int nseq, int n, SeqTable* t) {
   for (int i = 0; i <= nseq; ++i) t->start[i] = seq_starts[i];
   for (int i = 0; i < nseq; ++i)
     t->blk[i + 1] = t->blk[i] + (seq_starts[i + 1] - seq_starts[i] + kAttnRows - 1) / kAttnRows;
+  t->qlo = seq_starts[0];
+  t->qhi = seq_starts[nseq];
 }
 
-hipError_t attention(int dtype, int hd, const void* q, const void* k, const void* vt, int n,
-                     int ldn, int H, float scale_log2, void* o, float* part, const SeqTable& seqs,
-                     hipStream_t s) {
-  if (n <= 0) return hipSuccess;
+void make_shard_table(int n, int qlo, int qhi, SeqTable* t) {
+  t->nseq = 1;
+  t->start[0] = 0;
+  t->start[1] = n;
+  t->blk[0] = 0;
+  t->blk[1] = (qhi - qlo + kAttnRows - 1) / kAttnRows;
+  t->qlo = qlo;
+  t->qhi = qhi;
+  t->qbase = qlo;
+}
+
+hipError_t attention(int dtype, int hd, const void* q, int ldq, const void* k, const void* vt,
+                     int n, int ldn, int H, float scale_log2, void* o, float* part,
+                     const SeqTable& seqs, hipStream_t s) {
+  if (n <= 0 || seqs.qhi <= seqs.qlo) return hipSuccess;
   if (dtype == BF16) {
     const bf16_t *Qb = (const bf16_t*)q, *Kb = (const bf16_t*)k, *Vb = (const bf16_t*)vt;
     bf16_t* Ob = (bf16_t*)o;
@@ -487,8 +502,8 @@ hipError_t attention(int dtype, int hd, const void* q, const void* k, const void
     const int grid = whole + (units - whole) * nsplit;
     const bool unit = scale_log2 == 1.0f;
 #define ATT_LAUNCH(HD_, U_)                                                                      \
-  k_attn_bf16<HD_, U_><<<grid, kAttnThreads, 0, s>>>(Qb, Kb, Vb, n, ldn, H, scale_log2, Ob, whole, \
-                                                     nsplit, part, seqs)
+  k_attn_bf16<HD_, U_><<<grid, kAttnThreads, 0, s>>>(Qb, Kb, Vb, n, ldn, ldq, H, scale_log2, Ob, \
+                                                     whole, nsplit, part, seqs)
     if (hd == 128 && unit) ATT_LAUNCH(128, true);
     else if (hd == 128) ATT_LAUNCH(128, false);
     else if (unit) ATT_LAUNCH(64, true);
@@ -502,13 +517,13 @@ hipError_t attention(int dtype, int hd, const void* q, const void* k, const void
         k_attn_merge<64><<<(rows + 3) / 4, 256, 0, s>>>(part, H, whole, nsplit, units - whole, seqs, Ob);
     }
   } else {
-    dim3 grid((n + 127) / 128, H);
+    dim3 grid((seqs.qhi - seqs.qlo + 127) / 128, H);
     if (hd == 128)
       k_attn_f32<128><<<grid, 128, 0, s>>>((const float*)q, (const float*)k, (const float*)vt, n,
-                                           ldn, scale_log2, seqs, (float*)o);
+                                           ldn, ldq, scale_log2, seqs, (float*)o);
     else
       k_attn_f32<64><<<grid, 128, 0, s>>>((const float*)q, (const float*)k, (const float*)vt, n,
-                                          ldn, scale_log2, seqs, (float*)o);
+                                          ldn, ldq, scale_log2, seqs, (float*)o);
   }
   return hipGetLastError();
 }

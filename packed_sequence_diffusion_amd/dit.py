@@ -180,6 +180,10 @@ def _load() -> ctypes.CDLL:
         "dit_attention_packed": (c_int32, [P(DitConfig), c_void_p, c_void_p, c_void_p, c_int32,
                                            c_int32, P(c_int32), c_int32, c_float, c_void_p,
                                            c_void_p]),
+        "dit_attention_shard_workspace_size": (c_size_t, [P(DitConfig)]),
+        "dit_attention_shard": (c_int32, [P(DitConfig), c_void_p, c_int32, c_int32, c_int32,
+                                          c_void_p, c_void_p, c_int32, c_int32, c_float, c_void_p,
+                                          c_void_p, c_size_t, c_void_p]),
         "dit_profile_begin": (c_int32, [c_int32]),
         "dit_profile_end": (c_int32, [P(c_double), P(c_int32)]),
         "dit_phase_name": (ctypes.c_char_p, [c_int32]),
@@ -570,6 +574,28 @@ def attention(cfg: DitConfig, q, k, vt, n: int, ldn: int, score_scale: float, o,
         st, nseq = _starts(seq_starts)
         _check(lib.dit_attention_packed(ctypes.byref(cfg), pq, pk, pv, n, ldn, st,
                                         nseq, score_scale, po, _stream(stream)))
+    return o
+
+
+def attention_shard(cfg: DitConfig, q, ldq: int, qlo: int, qhi: int, k, vt, n: int, ldn: int,
+                    score_scale: float, o, workspace=None, stream=None):
+    """dit_attention_shard: the queries of tokens [qlo, qhi) (q rows 0..qhi-qlo)
+    against all n keys; o [qhi - qlo, D].  The workspace (the split tail's
+    partials) is allocated here when not given."""
+    import torch
+    a = _act(cfg)
+    m = qhi - qlo
+    pq = _arg(q, "q", a, (cfg.H, ldq, cfg.hd))
+    pk = _arg(k, "k", a, (cfg.H, ldn, cfg.hd))
+    pv = _arg(vt, "vt", a, (cfg.H, cfg.hd, ldn))
+    po = _arg(o, "o", a, (m, cfg.D))
+    need = lib.dit_attention_shard_workspace_size(ctypes.byref(cfg))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    pw = _arg(workspace, "workspace", "u8", None, optional=True, min_numel=need)
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(lib.dit_attention_shard(ctypes.byref(cfg), pq, ldq, qlo, qhi, pk, pv, n, ldn,
+                                   score_scale, po, pw, nbytes, _stream(stream)))
     return o
 
 

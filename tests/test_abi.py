@@ -64,7 +64,7 @@ def test_binding_refuses_to_import_without_the_library(tmp_path):
 
 
 def test_abi_version(dit):
-    assert dit.lib.dit_abi_version() == 6
+    assert dit.lib.dit_abi_version() == 7
 
 
 def test_sigma_remap_printed_points(dit):
@@ -236,6 +236,33 @@ def test_attention_refusals(dit):
     assert L(ctypes.byref(c), 16, 16, 16, 300, 256, 1.0, 16, None) == -2  # ldn < n
     assert L(ctypes.byref(c), None, 16, 16, 10, 128, 1.0, 16, None) == -1
     assert L(ctypes.byref(c), 16, 16, 16, 0, 128, 1.0, 16, None) == 0
+
+
+def test_attention_shard_refusals(dit):
+    """dit_attention_shard checks its query range, q stride and workspace on the
+    host (n = 25600, ldn = 25600, an 8-way shard of 3200 queries)."""
+    c = _cfg(dit)
+    L = dit.lib.dit_attention_shard
+    need = dit.lib.dit_attention_shard_workspace_size(ctypes.byref(c))
+    assert need == 256 * 256 * (128 + 2) * 4  # 256 slots x 256 rows x (O row, max, sum)
+    f32 = dit.make_config(W.spec_by_name("toy"))
+    assert dit.lib.dit_attention_shard_workspace_size(ctypes.byref(f32)) == 0
+
+    def call(q=256, ldq=3200, qlo=3200, qhi=6400, n=25600, ldn=25600, ws=256, wsb=1 << 30, cfg=c):
+        return L(ctypes.byref(cfg), q, ldq, qlo, qhi, 256, 256, n, ldn, 1.0, 256, ws, wsb, None)
+
+    assert call(qlo=-1) == -2
+    assert call(qlo=6400, qhi=6399) == -2
+    assert call(qhi=25601) == -2
+    assert call(ldq=3199) == -2   # < qhi - qlo
+    assert call(ldq=3300) == -2   # % 128
+    assert call(ldn=25500) == -2  # ldn < n
+    assert call(ws=None) == -5
+    assert call(wsb=need - 1) == -5
+    assert call(ws=16) == -4      # workspace not 256-byte aligned
+    assert call(q=8) == -4        # q not 16-byte aligned
+    assert call(q=None) == -1
+    assert call(qlo=100, qhi=100) == 0  # empty range: nothing to do
 
 
 def test_profile_arming(dit):

@@ -10,7 +10,7 @@ import pytest
 
 import oracle as O
 from synth import workloads as W
-from tests.gpu_common import compare, log, run_gpu
+from tests.gpu_common import TOL, compare, log, row_rel, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -237,6 +237,87 @@ def test_standalone_attention(dit, hd, n, qnorm):
     err = O.rel_rms(o.float().cpu().numpy(), ref)
     log(f"[case] attention hd={hd} n={n} |q|={qnorm}: rel_rms={err:.2e}")
     assert err <= 1e-2
+
+
+# ---- one GPU's share of a token-sharded sequence (dit_attention_shard) ----
+
+def _shard_case(dit, dtype, H, hd, n, qlo, qhi, qnorm, seed):
+    """q (|q| = qnorm), unit-norm k and normal v on both sides (bf16-exact for
+    bf16); the shard's output, the same rows of dit_attention over the whole
+    sequence, and the oracle's rows for the shard's queries."""
+    import torch
+    from synth.workloads import bf16_round
+    ldn = (n + 127) // 128 * 128
+    m = qhi - qlo
+    ldq = max(128, (m + 127) // 128 * 128)
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((H, n, hd)).astype(np.float32) for _ in range(3))
+    q *= qnorm / np.sqrt(np.sum(q * q, axis=-1, keepdims=True))
+    k /= np.sqrt(np.sum(k * k, axis=-1, keepdims=True))
+    if dtype == "bf16":
+        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
+    spec = _small("mmh3", dtype, max(n, 1), H * hd, hd, 256)
+    cfg = dit.make_config(spec)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def pad(a, rows):
+        out = np.zeros((H, rows, hd), np.float32)
+        out[:, :a.shape[1]] = a
+        return torch.from_numpy(out).to(tdt).cuda()
+
+    qd, qfull, kd = pad(q[:, qlo:qhi], ldq), pad(q, ldn), pad(k, ldn)
+    vtd = pad(v, ldn).transpose(1, 2).contiguous()
+    o = torch.empty((m, H * hd), dtype=tdt, device="cuda")
+    dit.attention_shard(cfg, qd, ldq, qlo, qhi, kd, vtd, n, ldn, 1.0, o)
+    ofull = torch.empty((n, H * hd), dtype=tdt, device="cuda")
+    dit.attention(cfg, qfull, kd, vtd, n, ldn, 1.0, ofull)
+    torch.cuda.synchronize()
+    return q, k, v, o.float().cpu().numpy(), ofull.float().cpu().numpy()[qlo:qhi]
+
+
+@pytest.mark.parametrize("dtype,hd,n,qlo,qhi", [
+    ("bf16", 128, 1000, 0, 256), ("bf16", 128, 1000, 300, 777), ("bf16", 128, 777, 700, 777),
+    ("bf16", 64, 515, 129, 515), ("bf16", 128, 3000, 1000, 2000),
+    ("f32", 64, 300, 0, 300), ("f32", 128, 333, 100, 250)])
+def test_attention_shard(dit, dtype, hd, n, qlo, qhi):
+    """dit_attention_shard: the queries of tokens [qlo, qhi) against all n keys
+    (ragged ranges, a range that starts mid-block, the sequence's last rows),
+    per (token, head) against the oracle's rows for those queries, and against
+    the same rows of dit_attention over the whole sequence."""
+    H = 3 if hd == 128 else 4
+    q, k, v, got, same = _shard_case(dit, dtype, H, hd, n, qlo, qhi, 8.0, 51 + n + qlo)
+    m = qhi - qlo
+    ref = O.attention_packed(q[:, qlo:qhi].astype(np.float64), k.astype(np.float64),
+                             v.astype(np.float64), 1.0, np.arange(qlo, qhi), [0, n])
+    ref = ref.transpose(1, 0, 2).reshape(m, H * hd)
+    tol = TOL[dtype]
+    e = row_rel(got.reshape(m, H, hd), ref.reshape(m, H, hd))
+    e_same = O.rel_rms(got, same)
+    log(f"[case] attention shard {dtype} hd={hd} n={n} [{qlo},{qhi}): max per (token, head) "
+        f"{e.max():.2e}, against the whole-sequence rows {e_same:.2e}")
+    assert e.max() <= tol
+    # dit_attention runs without the key-range split of a small grid's last
+    # round (it takes no partial buffer), so the two differ in rounding order
+    assert e_same <= tol
+
+
+def test_attention_shard_t2va_sampled(dit):
+    """One GPU's share of an 8-way token shard at the t2va shape: 3200 queries
+    (tokens 9600..12799) against 25600 keys, 21 heads x 128 (the grid's last
+    round split along the keys); sampled rows against the oracle, all rows
+    against dit_attention over the whole sequence."""
+    H, hd, n, qlo, qhi = 21, 128, 25600, 9600, 12800
+    q, k, v, got, same = _shard_case(dit, "bf16", H, hd, n, qlo, qhi, 11.3, 8)
+    rows = np.unique(np.concatenate([_sample_rows(qhi - qlo, SAMPLE, 9), [0, 255, 256]]))
+    ref = O.attention_packed(q[:, qlo + rows].astype(np.float64), k.astype(np.float64),
+                             v.astype(np.float64), 1.0, qlo + rows, [0, n])
+    ref = ref.transpose(1, 0, 2).reshape(rows.size, H * hd)
+    e = row_rel(got[rows].reshape(rows.size, H, hd), ref.reshape(rows.size, H, hd))
+    e_same = O.rel_rms(got, same)
+    log(f"[case] attention shard t2va [{qlo},{qhi}) of {n}: max per (token, head) {e.max():.2e} "
+        f"over {rows.size} rows, against the whole-sequence rows {e_same:.2e}")
+    assert e.max() <= TOL["bf16"]
+    assert e_same <= TOL["bf16"]
 
 
 # ---- independent samples packed in one sequence (block-diagonal attention) ----

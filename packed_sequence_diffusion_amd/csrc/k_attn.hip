@@ -37,6 +37,9 @@ constexpr int kBufferFlags = 0x00020000;
 DIT_DEV int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 constexpr int kAttnWaves = 8;  // 8 waves x 32 queries per workgroup
+// key ranges a unit of the grid's last round splits into, at most (a shard of
+// 3200 queries leaves 17 units past one round: 15 ranges fill the CUs)
+constexpr int kAttnMaxSplit = 16;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kAttnRows = 32 * kAttnWaves;
 static_assert(kAttnRows == kAttnQueryRows, "partial-buffer rows");
@@ -496,7 +499,7 @@ hipError_t attention(int dtype, int hd, const void* q, int ldq, const void* k, c
     }
     const int cus = min(device_cus(), kAttnMaxSlots);
     const int tail = units % cus;
-    int nsplit = tail ? min(min(cus / tail, 8), min_tiles) : 1;
+    int nsplit = tail ? min(min(cus / tail, kAttnMaxSplit), min_tiles) : 1;
     if (!part || nsplit < 2) nsplit = 1;
     const int whole = nsplit > 1 ? units - tail : units;
     const int grid = whole + (units - whole) * nsplit;

@@ -508,6 +508,16 @@ def test_bench_refuses_more_than_one_gpu(n):
     assert "one GPU only" in r.stderr and r.stdout == ""
 
 
+@pytest.mark.parametrize("p", [3, 256])
+def test_bench_shard_refuses_uneven_shards(p):
+    """bench.py --shard P needs shards of a multiple of 128 tokens (25600 / 3 is
+    not whole, 25600 / 256 = 100): it exits with status 2 before any device work."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--shard", str(p)],
+                       cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "multiple of 128 tokens" in r.stderr and r.stdout == ""
+
+
 def test_adaln_eval_noalloc_refusals(dit):
     """The no-allocation adaLN entry point refuses a timestep MLP larger than
     its scratch array, and the usual bad arguments, before any launch."""

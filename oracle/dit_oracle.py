@@ -18,13 +18,15 @@ Citation tags (web pages, cited by title and the item on the page):
 Pins (tests/test_oracle_pins.py) tie each function to something other than
 itself: printed test points, closed forms, library routines (numpy.interp,
 torch's scaled-dot-product attention, layer_norm and rms_norm in float64),
-invariants and pure-Python brute force on tiny inputs.  Parity unpinned: the
-whole block's output at the workloads' shapes, and the whole MMH3 / Z-Image
-evaluations built from it, have no printed value to pin them (no golden
-forward is published on the pages).  They are pinned only through their
-pinned parts, brute force at tiny sizes and invariants (permutation
-equivariance, zero-gate identity, RoPE translation invariance, the Z-Image
-cache identities, the audio slope's closed form).
+invariants and pure-Python brute force on tiny inputs.  No function is left
+without a pin.  The pages print no golden forward of a whole block or
+evaluation at any size, so those are pinned through code that is the same at
+every size: the block by brute force at tiny sizes (random seeds, the
+checkpoint modes), by torch compositions (SigLIP layer, Z-Image block) and by
+invariants (permutation equivariance, zero-gate identity, RoPE translation
+invariance); the MMH3 and Z-Image evaluations as compositions of their pinned
+pieces and by their own identities (the Z-Image cache rules, the audio
+slope's closed form).
 """
 
 from __future__ import annotations

@@ -616,16 +616,6 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
   }
 }
 
-// 192-wide tiles for N = 2688-like widths where they save rounds; DIT_GEMM_WIDE192=0
-// turns them off (A/B timing)
-static bool gemm_wide192() {
-  static const bool on = [] {
-    const char* e = getenv("DIT_GEMM_WIDE192");
-    return !(e && e[0] == '0');
-  }();
-  return on;
-}
-
 // Launch plan of a bf16 GEMM: tile width, and the split-K tail if it pays.
 struct GemmPlan {
   bool w192 = false;
@@ -642,7 +632,7 @@ static GemmPlan plan_gemm(int epi, int M, int N, int K, bool can_split) {
   // 192-wide tiles where they divide N and 256-wide ones do not (N = 2688: 14 full
   // tiles per row instead of 10.5): a 256 x 192 tile takes about 0.86 of a 256 x 256
   // one (measured at N = 2688).
-  if ((epi == EPI_GATED_RES || epi == EPI_STORE) && N % 256 != 0 && N % 192 == 0 && gemm_wide192()) {
+  if ((epi == EPI_GATED_RES || epi == EPI_STORE) && N % 256 != 0 && N % 192 == 0) {
     const double c3 = 0.86 * ((tm * (N / 192) + cus - 1) / cus);
     if (c3 < best) {
       best = c3;

@@ -187,6 +187,106 @@ def shard_bench(args, spec):
     print(json.dumps(res), flush=True)
 
 
+def evaluation_bench(args, spec):
+    """One whole MMH3 denoise evaluation per step (dit_mmh3_forward): patch and
+    audio embeddings, the slot plan and token rows, a stack of B blocks of the
+    t2va shape with their own weights, the video and audio heads and the
+    unpacking of their rows, over the t2va layout (512 text + 512 audio +
+    24576 video tokens).  Weights and inputs are seeded synthetic tensors made
+    on the device (linear weights N(0, 0.02), gains 1 + N(0, 0.02), adaLN basis
+    and bias N(0, 0.02), its table N(0, 1); text, latents N(0, 1)); latent
+    channels 16 (video) and 64 (audio) are a synthetic choice."""
+    import statistics
+    import torch
+    from packed_sequence_diffusion_amd import dit
+    from synth import workloads as W
+
+    if spec.name != "t2va":
+        print("--evaluation runs the t2va layout only", file=sys.stderr)
+        sys.exit(2)
+    B, C, Ca = args.evaluation, 16, 64
+    lay = W.build_layout(512, 16, 64, 96, 256)
+    n = lay.seq_len
+    gen = torch.Generator(device="cuda")
+    gains = ("norm1", "norm2", "q_norm", "k_norm")
+
+    def weights(cfg, seed):
+        gen.manual_seed(seed)
+        out = {}
+        for f, (dt, shp) in dit.weight_shapes(cfg).items():
+            t = torch.randn(shp, generator=gen, device="cuda")
+            if f in gains:
+                t = 1.0 + 0.02 * t
+            elif f != "adaln_table":
+                t = 0.02 * t
+            out[f] = t.to(torch.bfloat16 if dt == "bf16" else torch.float32).contiguous()
+        return out
+
+    t0 = time.perf_counter()
+    cfg = dit.make_config(spec)
+    blocks = [dit.Block(cfg, weights(cfg, 0xD17600 + i)) for i in range(B)]
+    heads = []
+    for name, F, seed in (("head-video", 4 * C, 0xD17700), ("head-audio", Ca, 0xD17701)):
+        hs = W.BlockSpec(name, "final", spec.dtype, n=n, D=spec.D, H=spec.H, hd=spec.hd, F=F,
+                         slots=spec.slots, tags=1)
+        hc = dit.make_config(hs)
+        heads.append(dit.Block(hc, weights(hc, seed)))
+    gen.manual_seed(0xD17800)
+    lin = lambda *shp: (0.02 * torch.randn(shp, generator=gen, device="cuda"))  # noqa: E731
+    model = dit.Mmh3Model(blocks, heads[0], heads[1], C, Ca, lin(spec.D, 4 * C).to(torch.bfloat16),
+                          lin(spec.D), lin(spec.D, Ca).to(torch.bfloat16), lin(spec.D))
+    text = torch.randn((512, spec.D), generator=gen, device="cuda")
+    video = torch.randn((C, 16, 64, 96), generator=gen, device="cuda")
+    audio = torch.randn((Ca, 2, 256), generator=gen, device="cuda")
+    pos = torch.from_numpy(lay.pos.astype("float32")).cuda()
+    sigma_v = 0.42
+    torch.cuda.synchronize()
+    log(f"evaluation setup ({B} blocks + heads): {time.perf_counter() - t0:.1f} s")
+
+    def step():
+        return model.forward(lay.segments, pos, text, video, audio, (), sigma_v)
+
+    stream = torch.cuda.current_stream()
+    run = step
+    if args.graph:
+        step()  # sizes the workspace before capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        run = g.replay
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        run()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    res = {
+        "metric": f"one MMH3 denoise evaluation ({B} blocks + embeddings + heads), t2va layout",
+        "value": 1e3 / ms,
+        "unit": "evaluations/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_evaluation": ms,
+        "ms_per_evaluation_median": statistics.median(per),
+        "ms_per_evaluation_min": min(per),
+        "ms_per_block": ms / B,
+        "tokens": n,
+        "block_tokens_per_s": n * B / (ms * 1e-3),
+        "hip_graph": bool(args.graph),
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded device-generated weights and latents; no checkpoint)",
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +306,10 @@ def main():
                     help="time one GPU's share of a P-way token shard of the workload instead "
                          "(the block's token-local phases at n/P tokens and the attention of "
                          "n/P queries against all n keys) and print that line")
+    ap.add_argument("--evaluation", type=int, default=0, metavar="B",
+                    help="time one whole MMH3 denoise evaluation per step instead (embeddings, "
+                         "B blocks of the t2va shape with their own weights, both heads) and "
+                         "print that line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times (the "
                          "calibration kernel for the HBM byte counters) and exit")
@@ -231,6 +335,9 @@ def main():
     spec = W.spec_by_name(args.workload)
     if args.shard > 1:
         shard_bench(args, spec)
+        return
+    if args.evaluation > 0:
+        evaluation_bench(args, spec)
         return
     seq_starts = None
     if args.seqs > 1:

@@ -518,6 +518,15 @@ def test_bench_shard_refuses_uneven_shards(p):
     assert "multiple of 128 tokens" in r.stderr and r.stdout == ""
 
 
+def test_bench_evaluation_refuses_other_layouts():
+    """bench.py --evaluation B runs the t2va layout only: another workload exits
+    with status 2 before any device work."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--evaluation", "2",
+                        "--workload", "edit"], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "t2va layout only" in r.stderr and r.stdout == ""
+
+
 def test_adaln_eval_noalloc_refusals(dit):
     """The no-allocation adaLN entry point refuses a timestep MLP larger than
     its scratch array, and the usual bad arguments, before any launch."""

@@ -187,6 +187,111 @@ def shard_bench(args, spec):
     print(json.dumps(res), flush=True)
 
 
+def device_weights(dit, gen, cfg, seed):
+    """Seeded synthetic weights of one prepared piece, made on the device:
+    linear weights and biases N(0, 0.02), norm gains 1 + N(0, 0.02), adaLN
+    tables N(0, 1)."""
+    import torch
+    gains = ("norm1", "norm2", "q_norm", "k_norm", "post_attn_norm", "post_ffn_norm")
+    gen.manual_seed(seed)
+    out = {}
+    for f, (dt, shp) in dit.weight_shapes(cfg).items():
+        t = torch.randn(shp, generator=gen, device="cuda")
+        if f in gains:
+            t = 1.0 + 0.02 * t
+        elif f != "adaln_table":
+            t = 0.02 * t
+        out[f] = t.to(torch.bfloat16 if dt == "bf16" else torch.float32).contiguous()
+    return out
+
+
+def time_steps(run, steps, warmup):
+    """Mean, median and min milliseconds of `steps` calls of run(i) after
+    `warmup` untimed ones, by events on the current stream."""
+    import statistics
+    import torch
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
+        run(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]) / steps, statistics.median(per), min(per)
+
+
+def zimage_bench(args, spec):
+    """Z-Image denoise steps (dit_zimage_forward) at the zimage block shape: a
+    128 x 128 latent of 16 channels (4096 image tokens) and 512 caption tokens
+    of width 2560, L main layers, 2 noise and 2 context refiners and the final
+    layer, with their own seeded device-generated weights.  Each step timed
+    without the step cache, then with it (the first L/2 main layers reused
+    between refreshes every second step, the caption refined once)."""
+    import torch
+    from packed_sequence_diffusion_amd import dit
+    from synth import workloads as W
+
+    if spec.name != "zimage":
+        print("--zimage runs the zimage shape only (--workload zimage)", file=sys.stderr)
+        sys.exit(2)
+    L, C, cap_len, cap_dim = args.zimage, 16, 512, 2560
+    hw = 128
+    gen = torch.Generator(device="cuda")
+    t0 = time.perf_counter()
+    common = dict(D=spec.D, H=spec.H, hd=spec.hd, rope=spec.rope, rope_axes=spec.rope_axes,
+                  rope_theta=spec.rope_theta, temb_freq=spec.temb_freq, temb_hidden=spec.temb_hidden)
+    cfg = dit.make_config(spec)
+    ccfg = dit.make_config(W.BlockSpec("zctx", "zcontext", spec.dtype, n=cap_len, F=spec.F, **common))
+    fcfg = dit.make_config(W.BlockSpec("zfin", "zfinal", spec.dtype, n=(hw // 2) ** 2, F=4 * C,
+                                       eps=1e-6, **common))
+    mk = lambda c, seed: dit.Block(c, device_weights(dit, gen, c, seed))  # noqa: E731
+    layers = [mk(cfg, 0xD17900 + i) for i in range(L)]
+    noise = [mk(cfg, 0xD17A00 + i) for i in range(2)]
+    context = [mk(ccfg, 0xD17B00 + i) for i in range(2)]
+    final = mk(fcfg, 0xD17C00)
+    gen.manual_seed(0xD17D00)
+    rn = lambda *shp: torch.randn(shp, generator=gen, device="cuda")  # noqa: E731
+    model = dit.ZimageModel(layers, noise, context, final, C, (0.05 * rn(spec.D, 4 * C)).to(torch.bfloat16),
+                            0.02 * rn(spec.D), 1.0 + 0.02 * rn(cap_dim),
+                            (0.02 * rn(spec.D, cap_dim)).to(torch.bfloat16), 0.02 * rn(spec.D), 1e-6)
+    lat = rn(C, hw, hw)
+    cap = rn(cap_len, cap_dim)
+    pos = torch.from_numpy(W.zimage_positions(hw // 2, hw // 2, cap_len).astype("float32")).cuda()
+    torch.cuda.synchronize()
+    log(f"zimage setup ({L} layers + refiners + final): {time.perf_counter() - t0:.1f} s")
+    ts = [1.0 - (i + 0.5) / max(args.steps, 1) for i in range(max(args.steps, args.warmup))]
+    plain = time_steps(lambda i: model.forward(lat, cap, pos, ts[i % len(ts)]), args.steps, args.warmup)
+    cache = dit.ZimageCache(model, hw, hw, cap_len, layers=L // 2, interval=2)
+    for i in range(args.warmup):
+        model.forward(lat, cap, pos, ts[i % len(ts)], step=i, cache=cache)
+    torch.cuda.synchronize()
+    cache.reset()  # the timed steps start a new generation: step 0 refreshes
+    cached = time_steps(lambda i: model.forward(lat, cap, pos, ts[i % len(ts)], step=i, cache=cache),
+                        args.steps, 0)
+    res = {
+        "metric": f"Z-Image denoise step ({L} layers + 2 noise + 2 context refiners + final), "
+                  f"{(hw // 2) ** 2} image + {cap_len} caption tokens",
+        "value": 1e3 / cached[0],
+        "unit": "steps/s with the step cache",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step_uncached": plain[0],
+        "ms_per_step_uncached_median": plain[1],
+        "ms_per_step_cached": cached[0],
+        "ms_per_step_cached_median": cached[1],
+        "cache": {"layers": L // 2, "interval": 2, "caption_refined_once": True},
+        "speedup": plain[0] / cached[0],
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded device-generated weights, latent and caption; no checkpoint)",
+    }
+    print(json.dumps(res), flush=True)
+
+
 def evaluation_bench(args, spec):
     """One whole MMH3 denoise evaluation per step (dit_mmh3_forward): patch and
     audio embeddings, the slot plan and token rows, a stack of B blocks of the
@@ -196,7 +301,6 @@ def evaluation_bench(args, spec):
     on the device (linear weights N(0, 0.02), gains 1 + N(0, 0.02), adaLN basis
     and bias N(0, 0.02), its table N(0, 1); text, latents N(0, 1)); latent
     channels 16 (video) and 64 (audio) are a synthetic choice."""
-    import statistics
     import torch
     from packed_sequence_diffusion_amd import dit
     from synth import workloads as W
@@ -208,19 +312,7 @@ def evaluation_bench(args, spec):
     lay = W.build_layout(512, 16, 64, 96, 256)
     n = lay.seq_len
     gen = torch.Generator(device="cuda")
-    gains = ("norm1", "norm2", "q_norm", "k_norm")
-
-    def weights(cfg, seed):
-        gen.manual_seed(seed)
-        out = {}
-        for f, (dt, shp) in dit.weight_shapes(cfg).items():
-            t = torch.randn(shp, generator=gen, device="cuda")
-            if f in gains:
-                t = 1.0 + 0.02 * t
-            elif f != "adaln_table":
-                t = 0.02 * t
-            out[f] = t.to(torch.bfloat16 if dt == "bf16" else torch.float32).contiguous()
-        return out
+    weights = lambda cfg, seed: device_weights(dit, gen, cfg, seed)  # noqa: E731
 
     t0 = time.perf_counter()
     cfg = dit.make_config(spec)
@@ -246,7 +338,6 @@ def evaluation_bench(args, spec):
     def step():
         return model.forward(lay.segments, pos, text, video, audio, (), sigma_v)
 
-    stream = torch.cuda.current_stream()
     run = step
     if args.graph:
         step()  # sizes the workspace before capture
@@ -256,17 +347,7 @@ def evaluation_bench(args, spec):
             step()
         torch.cuda.synchronize()
         run = g.replay
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    evs[0].record(stream)
-    for i in range(args.steps):
-        run()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
-    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    ms, med, mn = time_steps(lambda i: run(), args.steps, args.warmup)
     res = {
         "metric": f"one MMH3 denoise evaluation ({B} blocks + embeddings + heads), t2va layout",
         "value": 1e3 / ms,
@@ -275,8 +356,8 @@ def evaluation_bench(args, spec):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_evaluation": ms,
-        "ms_per_evaluation_median": statistics.median(per),
-        "ms_per_evaluation_min": min(per),
+        "ms_per_evaluation_median": med,
+        "ms_per_evaluation_min": mn,
         "ms_per_block": ms / B,
         "tokens": n,
         "block_tokens_per_s": n * B / (ms * 1e-3),
@@ -310,6 +391,10 @@ def main():
                     help="time one whole MMH3 denoise evaluation per step instead (embeddings, "
                          "B blocks of the t2va shape with their own weights, both heads) and "
                          "print that line")
+    ap.add_argument("--zimage", type=int, default=0, metavar="L",
+                    help="with --workload zimage: time Z-Image denoise steps instead (L main "
+                         "layers + refiners + final layer), without and with the step cache, "
+                         "and print that line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times (the "
                          "calibration kernel for the HBM byte counters) and exit")
@@ -338,6 +423,9 @@ def main():
         return
     if args.evaluation > 0:
         evaluation_bench(args, spec)
+        return
+    if args.zimage > 0:
+        zimage_bench(args, spec)
         return
     seq_starts = None
     if args.seqs > 1:

@@ -527,6 +527,15 @@ def test_bench_evaluation_refuses_other_layouts():
     assert "t2va layout only" in r.stderr and r.stdout == ""
 
 
+def test_bench_zimage_refuses_other_shapes():
+    """bench.py --zimage L runs the zimage shape only: the default workload
+    exits with status 2 before any device work."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--zimage", "4"],
+                       cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "zimage shape only" in r.stderr and r.stdout == ""
+
+
 def test_adaln_eval_noalloc_refusals(dit):
     """The no-allocation adaLN entry point refuses a timestep MLP larger than
     its scratch array, and the usual bad arguments, before any launch."""
